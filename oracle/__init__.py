@@ -1,0 +1,218 @@
+"""Python face of the CPU oracle (``xq_oracle.c``).
+
+TEST INFRASTRUCTURE. Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. It never imports
+the HIP library's package and the HIP library never loads it.
+
+All functions take and return host numpy arrays. The module-level functions
+use the default build; ``Oracle(path)`` wraps another build of the same
+source (the tests build copies with one planted mistake each and check that
+the pins catch it).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "xq_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fPIC", "-shared",
+          "-Wall", "-Wextra"]
+_lock = threading.Lock()
+_default = None
+
+Q8K_BYTES = 320
+Q4K_BYTES = 144
+
+
+def compile_oracle(out_path: str, defines=()) -> str:
+    """Compile ``xq_oracle.c`` with gcc into ``out_path``."""
+    tmp = out_path + ".tmp%d" % os.getpid()
+    cmd = ["gcc", *CFLAGS, *("-D" + d for d in defines), SOURCE, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out_path)
+    return out_path
+
+
+def build(force: bool = True) -> str:
+    """Compile the default oracle into ``oracle/liboracle.so``."""
+    if force or not os.path.exists(_LIB):
+        compile_oracle(_LIB)
+    return _LIB
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u8(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    return a.reshape(-1).view(np.uint8)
+
+
+def _rows_arg(rows):
+    if rows is None:
+        return None, None, 0
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    return r, _ptr(r), r.size
+
+
+class Oracle:
+    """One loaded build of the oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        I = ctypes.c_int64
+        lib.xqo_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.xqo_f16_to_f64.restype = ctypes.c_double
+        lib.xqo_quantize_q8k.argtypes = [P, I, I, P]
+        lib.xqo_dequant_q8k.argtypes = [P, I, I, P]
+        lib.xqo_q4k_scale_min.argtypes = [P, ctypes.c_int, P, P]
+        lib.xqo_q4k_code.argtypes = [P, ctypes.c_int]
+        lib.xqo_q4k_code.restype = ctypes.c_int
+        lib.xqo_dequant_q4k.argtypes = [P, I, I, P]
+        lib.xqo_q4k_partials.argtypes = [P, P, I, I, P, I, P, P]
+        lib.xqo_gemv_q4k.argtypes = [P, P, I, I, P, I, P, P]
+        lib.xqo_gemm_q4k.argtypes = [P, P, I, I, I, P, P, I, P, P]
+        lib.xqo_iq4nl_codebook.argtypes = [ctypes.c_int]
+        lib.xqo_iq4nl_codebook.restype = ctypes.c_int
+        lib.xqo_dequant_iq4nl.argtypes = [P, I, I, P]
+        lib.xqo_iq4nl_partials.argtypes = [P, P, I, I, P, I, P]
+        lib.xqo_gemv_iq4nl.argtypes = [P, P, I, I, P, I, P, P]
+        self.lib = lib
+        self.path = path
+
+    # ---- f16 -------------------------------------------------------------
+    def f16_to_f64(self, bits: int) -> float:
+        return self.lib.xqo_f16_to_f64(int(bits) & 0xFFFF)
+
+    # ---- q8_K ------------------------------------------------------------
+    def quantize_q8k(self, x: np.ndarray) -> np.ndarray:
+        """f32 [rows, K] -> uint8 [rows, K/256, 320]."""
+        x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+        if x.ndim == 1:
+            x = x.reshape(1, -1)
+        rows, K = x.shape
+        assert K % 256 == 0
+        out = np.empty((rows, K // 256, Q8K_BYTES), dtype=np.uint8)
+        self.lib.xqo_quantize_q8k(_ptr(x), rows, K, _ptr(out))
+        return out
+
+    def dequant_q8k(self, xq: np.ndarray, rows: int, K: int) -> np.ndarray:
+        xq = _u8(xq)
+        out = np.empty((rows, K), dtype=np.float64)
+        self.lib.xqo_dequant_q8k(_ptr(xq), rows, K, _ptr(out))
+        return out
+
+    # ---- Q4_K ------------------------------------------------------------
+    def q4k_scale_min(self, block: np.ndarray, j: int):
+        blk = _u8(block)
+        sc = ctypes.c_int()
+        m = ctypes.c_int()
+        self.lib.xqo_q4k_scale_min(_ptr(blk), j, ctypes.byref(sc), ctypes.byref(m))
+        return sc.value, m.value
+
+    def q4k_code(self, block: np.ndarray, i: int) -> int:
+        return self.lib.xqo_q4k_code(_ptr(_u8(block)), i)
+
+    def dequant_q4k(self, w, N: int, K: int) -> np.ndarray:
+        w = _u8(w)
+        out = np.empty((N, K), dtype=np.float64)
+        self.lib.xqo_dequant_q4k(_ptr(w), N, K, _ptr(out))
+        return out
+
+    def q4k_partials(self, w, xq, N: int, K: int, rows=None):
+        """Exact per-block partials (S, M), int32 [nrows, K/256]."""
+        w = _u8(w)
+        xq = _u8(xq)
+        r, rp, n = _rows_arg(rows)
+        nrows = N if r is None else n
+        S = np.empty((nrows, K // 256), dtype=np.int32)
+        M = np.empty((nrows, K // 256), dtype=np.int32)
+        self.lib.xqo_q4k_partials(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(S), _ptr(M))
+        return S, M
+
+    def gemv_q4k(self, w, xq, N: int, K: int, rows=None):
+        """(y, T), double [nrows]: y by the plain definition, T the sum of the
+        magnitudes of the products that make it up."""
+        w = _u8(w)
+        xq = _u8(xq)
+        r, rp, n = _rows_arg(rows)
+        nrows = N if r is None else n
+        y = np.empty(nrows, dtype=np.float64)
+        T = np.empty(nrows, dtype=np.float64)
+        self.lib.xqo_gemv_q4k(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(y), _ptr(T))
+        return y, T
+
+    def gemm_q4k(self, w, xq, M: int, N: int, K: int, ms=None, ns=None):
+        """(Y, T): full [M, N] arrays, or values at the listed (m, n) pairs."""
+        w = _u8(w)
+        xq = _u8(xq)
+        if ms is None:
+            Y = np.empty(M * N, dtype=np.float64)
+            T = np.empty(M * N, dtype=np.float64)
+            self.lib.xqo_gemm_q4k(_ptr(w), _ptr(xq), M, N, K, None, None, 0, _ptr(Y), _ptr(T))
+            return Y.reshape(M, N), T.reshape(M, N)
+        ms = np.ascontiguousarray(np.asarray(ms, dtype=np.int64))
+        ns = np.ascontiguousarray(np.asarray(ns, dtype=np.int64))
+        assert ms.shape == ns.shape
+        Y = np.empty(ms.size, dtype=np.float64)
+        T = np.empty(ms.size, dtype=np.float64)
+        self.lib.xqo_gemm_q4k(_ptr(w), _ptr(xq), M, N, K, _ptr(ms), _ptr(ns), ms.size,
+                              _ptr(Y), _ptr(T))
+        return Y, T
+
+    # ---- IQ4_NL ----------------------------------------------------------
+    def iq4nl_codebook(self, nibble: int) -> int:
+        return self.lib.xqo_iq4nl_codebook(nibble)
+
+    def dequant_iq4nl(self, w, N: int, K: int) -> np.ndarray:
+        w = _u8(w)
+        out = np.empty((N, K), dtype=np.float64)
+        self.lib.xqo_dequant_iq4nl(_ptr(w), N, K, _ptr(out))
+        return out
+
+    def iq4nl_partials(self, w, xq, N: int, K: int, rows=None):
+        """Exact per-block partials D, int32 [nrows, K/32]."""
+        w = _u8(w)
+        xq = _u8(xq)
+        r, rp, n = _rows_arg(rows)
+        nrows = N if r is None else n
+        D = np.empty((nrows, K // 32), dtype=np.int32)
+        self.lib.xqo_iq4nl_partials(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(D))
+        return D
+
+    def gemv_iq4nl(self, w, xq, N: int, K: int, rows=None):
+        w = _u8(w)
+        xq = _u8(xq)
+        r, rp, n = _rows_arg(rows)
+        nrows = N if r is None else n
+        y = np.empty(nrows, dtype=np.float64)
+        T = np.empty(nrows, dtype=np.float64)
+        self.lib.xqo_gemv_iq4nl(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(y), _ptr(T))
+        return y, T
+
+
+def default() -> Oracle:
+    """The default build, compiled on first use when it is missing."""
+    global _default
+    with _lock:
+        if _default is None:
+            if not os.path.exists(_LIB):
+                build(force=True)
+            _default = Oracle(_LIB)
+    return _default
+
+
+def __getattr__(name):
+    # Module-level aliases of the default build's methods.
+    if not name.startswith("_") and hasattr(Oracle, name):
+        return getattr(default(), name)
+    raise AttributeError(name)
