@@ -1,0 +1,384 @@
+#!/usr/bin/env python3
+"""Bench of the Q4_K x q8_K decode mat-vec on one MI355X.
+
+One step is one pass of the hot path over one token, shaped like an FFN pair:
+quantize x (f32 [1, 4096]) to q8_K, up mat-vec (Q4_K 14336 x 4096), quantize
+h to q8_K, down mat-vec (Q4_K 4096 x 14336). The activation quantizations are
+inside the timed region. Weights are cold: every step reads the next copy of a
+rotation pool of weight pairs larger than twice the 256 MB Infinity Cache plus
+the L2s, so the bytes come from HBM.
+
+Printed (one JSON line on stdout):
+  value          weight bytes of a step (2 x 33,030,144) / step time, in GB/s
+  roofline       for the dominant kernel (the 14336 x 4096 up mat-vec):
+                 algorithmic bytes per launch / its mean duration (1000
+                 back-to-back launches on the step's stream, weights rotating,
+                 one HIP event pair around them), against the 8 TB/s HBM peak;
+                 traffic from the committed rocprofv3 counter summary when it
+                 matches the current kernel source
+  cpu_baseline   the oracle on the host's cores over whole FFN pairs
+  stream_read    the streaming-read ceiling measured by the library's probe
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "weight GB/s and % of HBM roofline, Q4_K×q8_K GEMV 14336×4096 batch 1"
+HBM_PEAK_GBPS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+UP = (14336, 4096)
+DOWN = (4096, 14336)
+COUNTERS = os.path.join(ROOT, "profiles", "gemv_q4k_up_14336x4096_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "quantized_decode_mat_amd", "csrc", "gemv_q4k.hip")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--pool-mb", type=int, default=1100,
+                   help="size of the cold-weight rotation pool")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="lower bound of the oracle's timed host work")
+    p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    p.add_argument("--suite", action="store_true",
+                   help="also time the other workloads; their lines go to stderr and "
+                        "gpurun_out/bench_suite.jsonl")
+    p.add_argument("--json-out", default=None, help="also write the JSON line to this file")
+    return p.parse_args()
+
+
+def sha_of(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(per_launch_bytes):
+    """HBM bytes per launch of the up mat-vec from the committed rocprofv3
+    counter summary, or None when it is missing or was taken on another
+    version of the kernel source."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter summary"
+    if c.get("kernel_source_sha256_16") != sha_of(KERNEL_SRC):
+        return None, "counter summary predates the current kernel source"
+    return int(c["hbm_bytes_per_launch"]), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d refused)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_decode_mat_amd as xq
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+
+    # ---- inputs ----
+    g = wl.rng(wl.SEEDS["ffn_up"])
+    w_up = wl.q4k_weights(*UP, g)
+    x = wl.activations(1, UP[1], g)
+    w_dn = wl.q4k_weights(*DOWN, wl.rng(wl.SEEDS["ffn_down"]))
+    pair_bytes = w_up.nbytes + w_dn.nbytes
+    pool = max(2, (args.pool_mb * 1000 * 1000 + pair_bytes - 1) // pair_bytes)
+    log("weights %d B per pair, pool of %d pairs (%.0f MB)" % (pair_bytes, pool,
+                                                             pool * pair_bytes / 1e6))
+    up0 = torch.from_numpy(w_up.reshape(-1)).to(dev)
+    dn0 = torch.from_numpy(w_dn.reshape(-1)).to(dev)
+    ups = [up0] + [up0.clone() for _ in range(pool - 1)]
+    dns = [dn0] + [dn0.clone() for _ in range(pool - 1)]
+    x_d = torch.from_numpy(x.reshape(-1)).to(dev)
+    xq1 = torch.empty(xq.xq_q8k_bytes(1, UP[1]), dtype=torch.uint8, device=dev)
+    h = torch.empty(UP[0], dtype=torch.float32, device=dev)
+    xq2 = torch.empty(xq.xq_q8k_bytes(1, DOWN[1]), dtype=torch.uint8, device=dev)
+    y = torch.empty(DOWN[0], dtype=torch.float32, device=dev)
+    s = stream.cuda_stream
+
+    L = xq.lib()  # direct C calls in the timed loops: no per-call Python checks
+
+    def step(i):
+        k = i % pool
+        L.xq_quantize_q8k(xq1.data_ptr(), x_d.data_ptr(), 1, UP[1], s)
+        L.xq_gemv_q4k(h.data_ptr(), ups[k].data_ptr(), xq1.data_ptr(), UP[0], UP[1], s)
+        L.xq_quantize_q8k(xq2.data_ptr(), h.data_ptr(), 1, DOWN[1], s)
+        L.xq_gemv_q4k(y.data_ptr(), dns[k].data_ptr(), xq2.data_ptr(), DOWN[0], DOWN[1], s)
+
+    # One checked pass through the binding (raises on any refusal).
+    xq.xq_quantize_q8k(xq1, x_d, 1, UP[1])
+    xq.xq_gemv_q4k(h, ups[0], xq1, UP[0], UP[1])
+    xq.xq_quantize_q8k(xq2, h, 1, DOWN[1])
+    xq.xq_gemv_q4k(y, dns[0], xq2, DOWN[0], DOWN[1])
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+
+    # ---- headline: K plain steps ----
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    value = pair_bytes / (ms * 1e-3) / 1e9
+    log("step %.3f us (host clock %.3f us), weight %.1f GB/s" % (ms * 1e3, wall / args.steps * 1e6,
+                                                               value))
+
+    # ---- per-kernel durations: each kernel of the step launched back to back
+    # n_k times on the step's stream (weights still rotating through the
+    # pool), one HIP event pair around the loop; mean = elapsed / n_k. This is
+    # what a kernel trace averages, launch gaps aside.
+    n_k = 1000
+    calls = {
+        "quantize_x": lambda k: L.xq_quantize_q8k(xq1.data_ptr(), x_d.data_ptr(), 1, UP[1], s),
+        "gemv_up": lambda k: L.xq_gemv_q4k(h.data_ptr(), ups[k % pool].data_ptr(),
+                                           xq1.data_ptr(), UP[0], UP[1], s),
+        "quantize_h": lambda k: L.xq_quantize_q8k(xq2.data_ptr(), h.data_ptr(), 1, DOWN[1], s),
+        "gemv_down": lambda k: L.xq_gemv_q4k(y.data_ptr(), dns[k % pool].data_ptr(),
+                                             xq2.data_ptr(), DOWN[0], DOWN[1], s),
+    }
+    kern_us = {}
+    for nm, call in calls.items():
+        kern_us[nm] = _time_loop(torch, stream, call, n_k)
+    log("kernel means (us): " + ", ".join("%s %.3f" % kv for kv in kern_us.items()))
+
+    # ---- streaming-read ceiling ----
+    def stream_read(nbytes, reps):
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        buf.fill_(1)
+        sink = torch.empty(xq.xq_bench_sink_words(nbytes), dtype=torch.int32, device=dev)
+        xq.xq_bench_stream_read(buf, nbytes, sink)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            L.xq_bench_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), s)
+        b.record(stream)
+        torch.cuda.synchronize()
+        r = nbytes / (a.elapsed_time(b) / reps * 1e-3) / 1e9
+        del buf, sink
+        return r
+
+    stream_gbps = stream_read(2 << 30, 20)
+    log("streaming read, 2 GiB: %.1f GB/s" % stream_gbps)
+
+    # ---- roofline of the up mat-vec ----
+    up_alg_bytes = w_up.nbytes + xq.xq_q8k_bytes(1, UP[1]) + 4 * UP[0]
+    achieved = up_alg_bytes / (kern_us["gemv_up"] * 1e-6) / 1e9
+    traffic, traffic_note = traffic_from_profile(up_alg_bytes)
+    roofline = {
+        "bound": "hbm",
+        "kernel": "gemv_q4k 14336x4096",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "traffic": traffic,
+        "traffic_note": traffic_note,
+        "alg_bytes_per_launch": up_alg_bytes,
+        "mean_launch_us": round(kern_us["gemv_up"], 3),
+        "frac_of_stream_read": round(achieved / stream_gbps, 4),
+    }
+
+    # ---- CPU baseline: the oracle over whole FFN pairs ----
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        o = oracle.default()
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            xq_h = o.quantize_q8k(x)
+            hh, _ = o.gemv_q4k(w_up, xq_h, *UP)
+            xq_h2 = o.quantize_q8k(hh.astype(np.float32).reshape(1, -1))
+            o.gemv_q4k(w_dn, xq_h2, *DOWN)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds:
+                break
+        cpu = {
+            "value": round(reps * pair_bytes / el / 1e9, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": "%d whole FFN pairs (quantize, up 14336x4096, quantize, down "
+                      "4096x14336), single-threaded plain C oracle, %.1f s" % (reps, el),
+        }
+        log("cpu oracle: %s" % cpu)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "ffn_pair_q4k_batch1",
+            "up": list(UP),
+            "down": list(DOWN),
+            "batch": 1,
+            "weight_bytes_per_step": pair_bytes,
+            "weights": "cold: rotation pool of %d pairs (%.0f MB)" % (pool,
+                                                                    pool * pair_bytes / 1e6),
+            "step": "quantize x, up mat-vec, quantize h, down mat-vec",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "stream_read_GBps": round(stream_gbps, 1),
+        "frac_of_stream_read": round(value / stream_gbps, 4),
+        "host_us_per_step": round(wall / args.steps * 1e6, 3),
+    }
+
+    if args.suite:
+        del ups, dns
+        torch.cuda.empty_cache()
+        suite(args, torch, xq, wl, dev, stream, stream_gbps)
+
+    out = json.dumps(line)
+    print(out, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(out + "\n")
+
+
+def _pool_copies(t, pool_mb):
+    n = max(2, (pool_mb * 1000 * 1000 + t.numel() - 1) // t.numel())
+    return [t] + [t.clone() for _ in range(n - 1)]
+
+
+def _time_loop(torch, stream, fn, n, warm=20):
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        fn(warm + i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n * 1e3  # us
+
+
+def suite(args, torch, xq, wl, dev, stream, stream_gbps):
+    """The other workloads, each timed back to back with cold weights."""
+    import oracle  # noqa: F401  (the suite reports no oracle figures)
+    L = xq.lib()
+    s = stream.cuda_stream
+    lines = []
+
+    def emit(d):
+        d["stream_read_GBps"] = round(stream_gbps, 1)
+        lines.append(d)
+        log("suite: " + json.dumps(d))
+
+    # Q4_K mat-vecs alone: 4096x4096 and the two FFN shapes.
+    for name, (N, K), seed in (("q4k_4096x4096", (4096, 4096), wl.SEEDS["q4k_4096"]),
+                               ("q4k_up_14336x4096", UP, wl.SEEDS["ffn_up"]),
+                               ("q4k_down_4096x14336", DOWN, wl.SEEDS["ffn_down"]),
+                               ("q4k_tiny_256x1024", (256, 1024), wl.SEEDS["q4k_tiny"])):
+        g = wl.rng(seed)
+        w = torch.from_numpy(wl.q4k_weights(N, K, g).reshape(-1)).to(dev)
+        xv = torch.from_numpy(wl.activations(1, K, g).reshape(-1)).to(dev)
+        xqb = torch.empty(xq.xq_q8k_bytes(1, K), dtype=torch.uint8, device=dev)
+        xq.xq_quantize_q8k(xqb, xv, 1, K)
+        ws = _pool_copies(w, args.pool_mb)
+        yy = torch.empty(N, dtype=torch.float32, device=dev)
+        us = _time_loop(torch, stream, lambda i: L.xq_gemv_q4k(
+            yy.data_ptr(), ws[i % len(ws)].data_ptr(), xqb.data_ptr(), N, K, s), 1000)
+        wb = w.numel()
+        emit({"workload": name, "us": round(us, 3), "weight_GBps": round(wb / us / 1e3, 1),
+              "frac_of_8TBps": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4),
+              "frac_of_stream_read": round(wb / us / 1e3 / stream_gbps, 4)})
+        del ws, w
+        torch.cuda.empty_cache()
+
+    # IQ4_NL mat-vecs.
+    for name, (N, K), seed in (("iq4nl_4096x4096", (4096, 4096), wl.SEEDS["iq4nl_4096"]),
+                               ("iq4nl_head_128256x4096", (128256, 4096),
+                                wl.SEEDS["iq4nl_head"])):
+        g = wl.rng(seed)
+        w = torch.from_numpy(wl.iq4nl_weights(N, K, g).reshape(-1)).to(dev)
+        xv = torch.from_numpy(wl.activations(1, K, g).reshape(-1)).to(dev)
+        xqb = torch.empty(xq.xq_q8k_bytes(1, K), dtype=torch.uint8, device=dev)
+        xq.xq_quantize_q8k(xqb, xv, 1, K)
+        ws = _pool_copies(w, args.pool_mb)
+        yy = torch.empty(N, dtype=torch.float32, device=dev)
+        n = 1000 if N < 100000 else 200
+        us = _time_loop(torch, stream, lambda i: L.xq_gemv_iq4nl(
+            yy.data_ptr(), ws[i % len(ws)].data_ptr(), xqb.data_ptr(), N, K, s), n)
+        wb = w.numel()
+        emit({"workload": name, "us": round(us, 3), "weight_GBps": round(wb / us / 1e3, 1),
+              "frac_of_8TBps": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4),
+              "frac_of_stream_read": round(wb / us / 1e3 / stream_gbps, 4)})
+        del ws, w
+        torch.cuda.empty_cache()
+
+    # Small-M prefill product.
+    M, (N, K) = 512, UP
+    g = wl.rng(wl.SEEDS["prefill"])
+    w = torch.from_numpy(wl.q4k_weights(N, K, g).reshape(-1)).to(dev)
+    xv = torch.from_numpy(wl.activations(M, K, g).reshape(-1)).to(dev)
+    xqb = torch.empty(xq.xq_q8k_bytes(M, K), dtype=torch.uint8, device=dev)
+    qus = _time_loop(torch, stream, lambda i: L.xq_quantize_q8k(
+        xqb.data_ptr(), xv.data_ptr(), M, K, s), 200)
+    yy = torch.empty(M * N, dtype=torch.float32, device=dev)
+    ws = _pool_copies(w, args.pool_mb)
+    us = _time_loop(torch, stream, lambda i: L.xq_gemm_q4k_small_m(
+        yy.data_ptr(), ws[i % len(ws)].data_ptr(), xqb.data_ptr(), M, N, K, s), 200)
+    ops = 2.0 * M * N * K
+    emit({"workload": "prefill_q4k_512x14336x4096", "us": round(us, 3),
+          "TOPS": round(ops / us / 1e6, 1),
+          "frac_of_int8_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS, 4),
+          "quantize_512x4096_us": round(qus, 3)})
+    del ws, w
+    torch.cuda.empty_cache()
+
+    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
+    with open(os.path.join(ROOT, "gpurun_out", "bench_suite.jsonl"), "w") as f:
+        for d in lines:
+            f.write(json.dumps(d) + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * xq.h — C ABI of libxq, the quantized decode mat-vec for AMD MI355X (gfx950).
+ *
+ * Every entry point validates its arguments on the host, enqueues its kernel
+ * on the caller's HIP stream and returns without synchronising ("25 — Writing
+ * XPU Kernels", section 25.5: chain launches on one stream and wait once on
+ * the read side). Faults during execution surface at the caller's next
+ * synchronisation.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named as device buffers are device memory owned by the caller.
+ *    The library allocates nothing, frees nothing and keeps no per-call state.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *  - Outputs are fully overwritten, never accumulated into. Outputs must not
+ *    alias inputs (documented, not checked).
+ *  - A refused call returns a status other than XQ_OK, launches nothing and
+ *    sets the thread-local text returned by xq_last_error() naming the gate
+ *    that refused (section 25.6: a refusal answers with the gate that
+ *    refused). There is no fallback kernel.
+ *  - The gates run before any HIP call in this order: null pointers, shape,
+ *    alignment, then the device (it must be gfx950).
+ *
+ * Byte layouts (all little-endian):
+ *  q8_K block, 320 B per 256 activations (section 25.2, the integer-route
+ *    bullet, and section 25.2.1): int8 codes at +0, eight int32 sums of 32
+ *    consecutive codes at +256, the f32 scale at +288; bytes 292..319 are
+ *    written as zero and carry no meaning. A q8_K tensor of R rows and K
+ *    columns is [R][K/256] blocks, row-major.
+ *  Q4_K super-block, 144 B per 256 weights ("cajeta.xpu — one kernel, any
+ *    device", section 2.3, the alignment example: nibble group g at
+ *    16 + 32*g): f16 d at +0, f16 dmin at +2, twelve bytes of packed 6-bit
+ *    scales and mins at +4, 128 B of nibbles at +16. Group g's 32 bytes hold
+ *    sub-block 2g in their low nibbles and sub-block 2g+1 in their high
+ *    nibbles. Weight = d*sc_j*q - dmin*m_j. A matrix of N rows and K columns
+ *    is [N][K/256] blocks, row-major.
+ *  IQ4_NL resident row (section 25.2.1): the row's K/32 f16 block scales,
+ *    padded to a multiple of 4 bytes, then K/32 payloads of 16 B; payload
+ *    byte t gives weight t (low nibble) and weight t+16 (high nibble); a
+ *    nibble selects an int8 from the 16-entry IQ4_NL codebook; weight =
+ *    d_c * kv[nibble]. A matrix is N such rows back to back.
+ */
+#ifndef XQ_H
+#define XQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t xq_status;
+
+enum {
+    XQ_OK = 0,
+    XQ_E_NULL = 1,   /* a required pointer is NULL */
+    XQ_E_SHAPE = 2,  /* a size is out of range or not a multiple it must be */
+    XQ_E_ALIGN = 3,  /* a buffer base is short of the alignment its loads need */
+    XQ_E_DEVICE = 4, /* no HIP device, or the current device is not gfx950 */
+    XQ_E_LAUNCH = 5  /* the runtime refused the kernel launch */
+};
+
+/*
+ * Quantize f32 activations to q8_K ("25 — Writing XPU Kernels", section 25.2,
+ * the integer-route bullet: the activation is quantized once to q8_K).
+ * Per 256-block: amax = max|x_i|; d = amax/127 as one IEEE f32 division;
+ * code_i = x_i/d (IEEE f32 division) rounded to nearest, ties to even (0 when
+ * d == 0); sum_j = sum of codes 32j..32j+31.
+ *
+ *  xq    device, out: rows*(K/256) q8_K blocks, 16-byte aligned.
+ *  x     device, in: f32 [rows][K] row-major, 16-byte aligned.
+ *  rows  >= 1.  K >= 256, a multiple of 256.
+ * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH.
+ */
+xq_status xq_quantize_q8k(void *xq, const float *x, int64_t rows, int64_t K, void *stream);
+
+/*
+ * Q4_K x q8_K decode mat-vec, batch 1 ("25 — Writing XPU Kernels", section
+ * 25.2, and section 25.5 for the Q4_K mat-vec's 16-byte loads):
+ *   y[r] = sum_b xs_b * (d_rb * S_rb - dmin_rb * M_rb),
+ *   S_rb = sum_j sc_j * sum_{t<32} q * code   (exact int32),
+ *   M_rb = sum_j m_j * sum_j(q8_K)            (exact int32, from the stored sums),
+ * which is the dot of the dequantized row with the dequantized activation.
+ *
+ *  y   device, out: f32 [N], 4-byte aligned.
+ *  w   device, in: Q4_K [N][K/256], 16-byte aligned.
+ *  xq  device, in: one q8_K row of K/256 blocks, 16-byte aligned.
+ *  1 <= N <= 2^30.  K >= 256, a multiple of 256, K <= XQ_MAX_K.
+ * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH.
+ */
+xq_status xq_gemv_q4k(float *y, const void *w, const void *xq, int64_t N, int64_t K, void *stream);
+
+/*
+ * IQ4_NL x q8_K decode mat-vec, batch 1 ("25 — Writing XPU Kernels", section
+ * 25.2.1): y[r] = sum_c d_rc * xs_(c/8) * D_rc with D_rc = sum_{t<32}
+ * kv[nibble_t] * code_(32c+t) (exact int32).
+ *
+ *  y   device, out: f32 [N], 4-byte aligned.
+ *  w   device, in: N resident IQ4_NL rows (xq_iq4nl_bytes(N, K) bytes),
+ *      16-byte aligned.
+ *  xq  device, in: one q8_K row of K/256 blocks, 16-byte aligned.
+ *  1 <= N <= 2^30.  K >= 256, a multiple of 256 (each 32-block must fall inside a
+ *  q8_K block), K <= XQ_MAX_K.
+ * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH.
+ */
+xq_status xq_gemv_iq4nl(float *y, const void *w, const void *xq, int64_t N, int64_t K,
+                        void *stream);
+
+/*
+ * Q4_K x q8_K small-M product (multi-token prefill; "25 — Writing XPU
+ * Kernels", section 25.3): Y[m][n] = sum_b xs_mb * (d_nb * S_mnb - dmin_nb *
+ * M_mnb), with S and M the exact int32 block partials of xq_gemv_q4k taken
+ * against token m's q8_K row. The integer products run on int8 MFMA.
+ *
+ *  y   device, out: f32 [M][N] row-major (token-major), 4-byte aligned.
+ *  w   device, in: Q4_K [N][K/256], 16-byte aligned.
+ *  xq  device, in: q8_K [M][K/256], 16-byte aligned.
+ *  1 <= M <= 2^30.  1 <= N <= 2^30.  K >= 256, a multiple of 256.
+ * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH.
+ */
+xq_status xq_gemm_q4k_small_m(float *y, const void *w, const void *xq, int64_t M, int64_t N,
+                              int64_t K, void *stream);
+
+/* Largest K the mat-vecs accept: the q8_K activation row is staged whole in
+ * the workgroup's LDS (XQ_MAX_K/256 * 320 bytes = 60 KiB). */
+#define XQ_MAX_K 49152
+
+/* Byte sizes of the layouts above; 0 when the shape is invalid. */
+size_t xq_q8k_bytes(int64_t rows, int64_t K);   /* rows*(K/256)*320 */
+size_t xq_q4k_bytes(int64_t N, int64_t K);      /* N*(K/256)*144 */
+size_t xq_iq4nl_bytes(int64_t N, int64_t K);    /* N*(ceil4(2*(K/32)) + 16*(K/32)) */
+
+/* Static name of a status code ("XQ_OK", "XQ_E_SHAPE", ...). */
+const char *xq_status_name(xq_status s);
+
+/* Thread-local text of the last refusal on this thread ("" after success). */
+const char *xq_last_error(void);
+
+/*
+ * Measurement helper, not part of the method: read `bytes` of device memory
+ * once with 16-byte loads and fold them into one word per workgroup of
+ * `sink` (sink must hold xq_bench_sink_words(bytes) uint32). Its duration
+ * gives the streaming-read ceiling the mat-vecs are held against ("25 —
+ * Writing XPU Kernels", section 25.1: measure the bandwidth once per device
+ * with a streaming pass well past L2).
+ *  buf 16-byte aligned, bytes a positive multiple of 16.
+ */
+xq_status xq_bench_stream_read(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+int64_t xq_bench_sink_words(int64_t bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XQ_H */

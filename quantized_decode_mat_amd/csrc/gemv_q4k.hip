@@ -1,0 +1,210 @@
+// gemv_q4k.hip — Q4_K x q8_K decode mat-vec on gfx950 (wave64).
+//
+// The integer route of "25 — Writing XPU Kernels", section 25.2: the
+// activation arrives quantized to q8_K; every weight nibble meets an int8 code
+// in a signed 4 x int8 dot (v_dot4_i32_i8; the 4-bit codes 0..15 are valid
+// signed bytes); the sub-block scales multiply the integer sub-block dots in
+// 24-bit integer multiplies; the min term is paid from the q8_K's stored
+// sub-block sums; the f16/f32 scales are applied once per block after the
+// integer work ("reduce first, scale once", section 25.2.1).
+//
+// Mapping (MI355X-first, not the pages' wave32 one-lane-per-block design):
+//  * One wave owns R rows. A "unit" is 8 consecutive super-blocks of one row;
+//    lane l takes block 8u + l/8 and its 16-byte nibble chunk c = l%8, which
+//    is half of nibble group g = c/2 (h = c%2). A wave's nibble load covers
+//    8 x 128 B of the 8 x 144 B span, the header load the other 8 x 16 B:
+//    every byte the wave touches is a byte it needs ("count lines touched,
+//    not loads issued", section 25.2).
+//  * Each lane also loads its block's 16-byte header; the eight lanes of a
+//    block load the same 16 bytes, which the cache serves once per line.
+//  * All of a lane's loads for a batch of PF units are issued before any is
+//    used, and the first batch before the activation is staged, so each wave
+//    keeps R*PF*32 bytes per lane in flight.
+//  * The row's q8_K activation is staged once per workgroup in LDS (the only
+//    LDS use); every wave of the workgroup reads its codes, sums and scales
+//    from there.
+//  * Lane partials are f32; the wave reduces them with DPP row sums and four
+//    v_readlane, and lane 0 stores y.
+#include "xq_device.h"
+#include "xq_launch.h"
+
+namespace xq {
+namespace {
+
+constexpr int kWavesPerGroup = 4;
+constexpr int kThreads = kWavesPerGroup * kWave;
+
+struct LaneGeom {
+  int bsub;        // block slot within a unit (0..7)
+  int g;           // nibble group (0..3)
+  int h;           // half of the group (0..1)
+  uint32_t selhi;  // all-ones when the group's scales sit in the 6+2-bit form
+  uint32_t mmask;  // all-ones on the lane that pays the block's min term
+  int shift;       // bit offset of sub-block 2g's byte in the scale word
+};
+
+__device__ __forceinline__ LaneGeom lane_geom(int lane) {
+  LaneGeom L;
+  L.bsub = lane >> 3;
+  const int c = lane & 7;
+  L.g = c >> 1;
+  L.h = c & 1;
+  L.selhi = (L.g >= 2) ? 0xFFFFFFFFu : 0u;
+  L.mmask = (L.h == 0) ? 0xFFFFFFFFu : 0u;
+  L.shift = 16 * (L.g & 1);
+  return L;
+}
+
+// Contribution of one lane's 16-byte nibble chunk of block b.
+__device__ __forceinline__ float unit_partial(const uint4 nib, const uint4 hdr, const uint8_t* act,
+                                              int b, const LaneGeom& L) {
+  const uint8_t* xb = act + b * kQ8KBytes;
+  // Activation codes of the two half sub-blocks this chunk feeds.
+  const uint4 alo = *reinterpret_cast<const uint4*>(xb + 64 * L.g + 16 * L.h);
+  const uint4 ahi = *reinterpret_cast<const uint4*>(xb + 64 * L.g + 32 + 16 * L.h);
+  const int2 sums = *reinterpret_cast<const int2*>(xb + 256 + 8 * L.g);
+  const float xs = *reinterpret_cast<const float*>(xb + 288);
+
+  int dlo = sdot4(nib.x & 0x0F0F0F0Fu, alo.x, 0);
+  dlo = sdot4(nib.y & 0x0F0F0F0Fu, alo.y, dlo);
+  dlo = sdot4(nib.z & 0x0F0F0F0Fu, alo.z, dlo);
+  dlo = sdot4(nib.w & 0x0F0F0F0Fu, alo.w, dlo);
+  int dhi = sdot4((nib.x >> 4) & 0x0F0F0F0Fu, ahi.x, 0);
+  dhi = sdot4((nib.y >> 4) & 0x0F0F0F0Fu, ahi.y, dhi);
+  dhi = sdot4((nib.z >> 4) & 0x0F0F0F0Fu, ahi.z, dhi);
+  dhi = sdot4((nib.w >> 4) & 0x0F0F0F0Fu, ahi.w, dhi);
+
+  // Header: bytes 4..7 (h1) hold sc0..3 in bits 0-5 and the top bits of
+  // sc4..7 in bits 6-7; bytes 8..11 (h2) the same for the mins; bytes 12..15
+  // (h3) the low nibbles of sc4..7 and m4..7.
+  const uint32_t h1 = hdr.y, h2 = hdr.z, h3 = hdr.w;
+  const uint32_t sc_lo = h1 & 0x3F3F3F3Fu;
+  const uint32_t m_lo = h2 & 0x3F3F3F3Fu;
+  const uint32_t sc_hi = (h3 & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);
+  const uint32_t m_hi = ((h3 >> 4) & 0x0F0F0F0Fu) | ((h2 >> 2) & 0x30303030u);
+  const uint32_t scw = (sc_hi & L.selhi) | (sc_lo & ~L.selhi);
+  const uint32_t mw = ((m_hi & L.selhi) | (m_lo & ~L.selhi)) & L.mmask;
+  const int sc0 = (scw >> L.shift) & 0xFF;
+  const int sc1 = (scw >> (L.shift + 8)) & 0xFF;
+  const int m0 = (mw >> L.shift) & 0xFF;
+  const int m1 = (mw >> (L.shift + 8)) & 0xFF;
+
+  const int S = __mul24(sc0, dlo) + __mul24(sc1, dhi);
+  const int M = __mul24(m0, sums.x) + __mul24(m1, sums.y);
+  const float d = half_bits_to_float(hdr.x & 0xFFFFu);
+  const float dmin = half_bits_to_float(hdr.x >> 16);
+  return (d * xs) * static_cast<float>(S) - (dmin * xs) * static_cast<float>(M);
+}
+
+template <int R, int PF>
+__global__ __launch_bounds__(kThreads) void gemv_q4k_kernel(float* __restrict__ y,
+                                                            const uint8_t* __restrict__ w,
+                                                            const uint8_t* __restrict__ xq,
+                                                            int N, int nb) {
+  extern __shared__ __align__(16) uint8_t act[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * kWavesPerGroup + wave) * R;
+  const int units = (nb + 7) >> 3;
+  const LaneGeom L = lane_geom(lane);
+  const int64_t row_bytes = static_cast<int64_t>(nb) * kQ4KBytes;
+
+  uint4 nib[R][PF];
+  uint4 hdr[R][PF];
+  auto load_batch = [&](int u0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(row0 + r, N - 1);
+      const uint8_t* wr = w + static_cast<int64_t>(row) * row_bytes;
+#pragma unroll
+      for (int p = 0; p < PF; ++p) {
+        const int b = (u0 + p) * 8 + L.bsub;
+        if (b < nb) {
+          const uint8_t* blk = wr + static_cast<int64_t>(b) * kQ4KBytes;
+          nib[r][p] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (2 * L.g + L.h));
+          hdr[r][p] = *reinterpret_cast<const uint4*>(blk);
+        } else {
+          nib[r][p] = make_uint4(0, 0, 0, 0);
+          hdr[r][p] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  load_batch(0);
+
+  // Stage the q8_K activation row (nb * 320 bytes) in LDS.
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(xq);
+    uint4* dst = reinterpret_cast<uint4*>(act);
+    const int n16 = nb * (kQ8KBytes / 16);
+    for (int i = threadIdx.x; i < n16; i += kThreads) dst[i] = src[i];
+  }
+  __syncthreads();
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+
+  for (int u0 = 0; u0 < units; u0 += PF) {
+    if (u0 > 0) load_batch(u0);
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int b = (u0 + p) * 8 + L.bsub;
+      if (b < nb) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] += unit_partial(nib[r][p], hdr[r][p], act, b, L);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float tot = wave_sum(acc[r]);
+    if (lane == 0 && row0 + r < N) y[row0 + r] = tot;
+  }
+}
+
+template <int R, int PF>
+hipError_t launch_rpf(float* y, const uint8_t* w, const uint8_t* xq, int N, int nb,
+                      hipStream_t stream) {
+  const int waves = (N + R - 1) / R;
+  const int grid = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+  const size_t lds = static_cast<size_t>(nb) * kQ8KBytes;
+  hipLaunchKernelGGL((gemv_q4k_kernel<R, PF>), dim3(grid), dim3(kThreads), lds, stream, y, w, xq,
+                     N, nb);
+  return hipGetLastError();
+}
+
+template <int R>
+hipError_t launch_r(float* y, const uint8_t* w, const uint8_t* xq, int N, int nb, int pf,
+                    hipStream_t stream) {
+  switch (pf) {
+    case 1: return launch_rpf<R, 1>(y, w, xq, N, nb, stream);
+    case 2: return launch_rpf<R, 2>(y, w, xq, N, nb, stream);
+    case 3: return launch_rpf<R, 3>(y, w, xq, N, nb, stream);
+    case 4: return launch_rpf<R, 4>(y, w, xq, N, nb, stream);
+    case 5: return launch_rpf<R, 5>(y, w, xq, N, nb, stream);
+    case 6: return launch_rpf<R, 6>(y, w, xq, N, nb, stream);
+    case 7: return launch_rpf<R, 7>(y, w, xq, N, nb, stream);
+    default: return launch_rpf<R, 8>(y, w, xq, N, nb, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemv_q4k(float* y, const void* w, const void* xq, int64_t N, int64_t K,
+                           hipStream_t stream) {
+  const int nb = static_cast<int>(K / 256);
+  const int units = (nb + 7) / 8;
+  const int pf = units < 8 ? units : 8;
+  const uint8_t* wb = static_cast<const uint8_t*>(w);
+  const uint8_t* xb = static_cast<const uint8_t*>(xq);
+  const int n = static_cast<int>(N);
+  // Two rows per wave when a row is short (one or two units) and there are
+  // rows enough to still fill 256 CUs several times over.
+  if (units <= 2 && N >= 8192) return launch_r<2>(y, wb, xb, n, nb, pf, stream);
+  return launch_r<1>(y, wb, xb, n, nb, pf, stream);
+}
+
+}  // namespace xq

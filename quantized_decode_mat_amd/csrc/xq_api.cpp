@@ -1,0 +1,187 @@
+// xq_api.cpp — the C ABI declared in include/xq.h.
+//
+// Every entry point checks its arguments on the host (null pointers, shapes,
+// alignment, then the device) before any launch, and answers a refusal with
+// a status plus a thread-local sentence naming the gate ("25 — Writing XPU
+// Kernels", section 25.6: a refusal names the gate that refused; section 25.5:
+// a base short of the alignment the loads need is refused by name). Nothing
+// falls back to another kernel or to the host.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/xq.h"
+#include "xq_launch.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+xq_status fail(xq_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+xq_status ok() {
+  g_err[0] = '\0';
+  return XQ_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int kMaxDevices = 64;
+// 0 = not checked, 1 = gfx950, 2 = other architecture.
+std::atomic<int> g_dev_state[kMaxDevices];
+
+xq_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(XQ_E_DEVICE, "no current HIP device");
+  if (dev >= kMaxDevices) return fail(XQ_E_DEVICE, "device %d beyond the library's table", dev);
+  int st = g_dev_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return fail(XQ_E_DEVICE, "hipGetDeviceProperties failed on device %d", dev);
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_state[dev].store(st, std::memory_order_release);
+  }
+  if (st != 1) return fail(XQ_E_DEVICE, "device %d is not gfx950", dev);
+  return XQ_OK;
+}
+
+xq_status check_k(int64_t K, int64_t kmax) {
+  if (K < 256 || K % 256 != 0) return fail(XQ_E_SHAPE, "K=%lld not a positive multiple of 256", (long long)K);
+  if (kmax > 0 && K > kmax)
+    return fail(XQ_E_SHAPE, "K=%lld above the largest supported K=%lld", (long long)K, (long long)kmax);
+  return XQ_OK;
+}
+
+constexpr int64_t kMaxInt = 2147483647LL;
+// Row counts stay below 2^30 so that no 32-bit row index in a kernel can wrap.
+constexpr int64_t kMaxRows = 1LL << 30;
+
+xq_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(XQ_E_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+xq_status xq_quantize_q8k(void* xq, const float* x, int64_t rows, int64_t K, void* stream) {
+  if (!xq) return fail(XQ_E_NULL, "xq is NULL");
+  if (!x) return fail(XQ_E_NULL, "x is NULL");
+  if (rows < 1) return fail(XQ_E_SHAPE, "rows=%lld below 1", (long long)rows);
+  if (xq_status s = check_k(K, 0)) return s;
+  if (rows > kMaxInt / (K / 256))
+    return fail(XQ_E_SHAPE, "rows*K/256 = %lld*%lld exceeds 2^31-1 blocks", (long long)rows,
+                (long long)(K / 256));
+  if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");
+  if (!aligned(x, 16)) return fail(XQ_E_ALIGN, "x not 16-byte aligned");
+  if (xq_status s = check_device()) return s;
+  return launched(xq::launch_quantize_q8k(xq, x, rows, K, static_cast<hipStream_t>(stream)),
+                  "xq_quantize_q8k");
+}
+
+xq_status xq_gemv_q4k(float* y, const void* w, const void* xq, int64_t N, int64_t K,
+                      void* stream) {
+  if (!y) return fail(XQ_E_NULL, "y is NULL");
+  if (!w) return fail(XQ_E_NULL, "w is NULL");
+  if (!xq) return fail(XQ_E_NULL, "xq is NULL");
+  if (N < 1 || N > kMaxRows) return fail(XQ_E_SHAPE, "N=%lld outside 1..2^30", (long long)N);
+  if (xq_status s = check_k(K, XQ_MAX_K)) return s;
+  if (!aligned(y, 4)) return fail(XQ_E_ALIGN, "y not 4-byte aligned");
+  if (!aligned(w, 16)) return fail(XQ_E_ALIGN, "w not 16-byte aligned");
+  if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");
+  if (xq_status s = check_device()) return s;
+  return launched(xq::launch_gemv_q4k(y, w, xq, N, K, static_cast<hipStream_t>(stream)),
+                  "xq_gemv_q4k");
+}
+
+xq_status xq_gemv_iq4nl(float* y, const void* w, const void* xq, int64_t N, int64_t K,
+                        void* stream) {
+  if (!y) return fail(XQ_E_NULL, "y is NULL");
+  if (!w) return fail(XQ_E_NULL, "w is NULL");
+  if (!xq) return fail(XQ_E_NULL, "xq is NULL");
+  if (N < 1 || N > kMaxRows) return fail(XQ_E_SHAPE, "N=%lld outside 1..2^30", (long long)N);
+  if (xq_status s = check_k(K, XQ_MAX_K)) return s;
+  if (!aligned(y, 4)) return fail(XQ_E_ALIGN, "y not 4-byte aligned");
+  if (!aligned(w, 16)) return fail(XQ_E_ALIGN, "w not 16-byte aligned");
+  if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");
+  if (xq_status s = check_device()) return s;
+  return launched(xq::launch_gemv_iq4nl(y, w, xq, N, K, static_cast<hipStream_t>(stream)),
+                  "xq_gemv_iq4nl");
+}
+
+xq_status xq_gemm_q4k_small_m(float* y, const void* w, const void* xq, int64_t M, int64_t N,
+                              int64_t K, void* stream) {
+  if (!y) return fail(XQ_E_NULL, "y is NULL");
+  if (!w) return fail(XQ_E_NULL, "w is NULL");
+  if (!xq) return fail(XQ_E_NULL, "xq is NULL");
+  if (M < 1 || M > kMaxRows) return fail(XQ_E_SHAPE, "M=%lld outside 1..2^30", (long long)M);
+  if (N < 1 || N > kMaxRows) return fail(XQ_E_SHAPE, "N=%lld outside 1..2^30", (long long)N);
+  if (xq_status s = check_k(K, 0)) return s;
+  if (K / 256 > kMaxInt) return fail(XQ_E_SHAPE, "K=%lld too large", (long long)K);
+  if (((M + 127) / 128) * ((N + 127) / 128) > kMaxInt)
+    return fail(XQ_E_SHAPE, "M*N too large for one launch");
+  if (!aligned(y, 4)) return fail(XQ_E_ALIGN, "y not 4-byte aligned");
+  if (!aligned(w, 16)) return fail(XQ_E_ALIGN, "w not 16-byte aligned");
+  if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");
+  if (xq_status s = check_device()) return s;
+  return launched(xq::launch_gemm_q4k(y, w, xq, M, N, K, static_cast<hipStream_t>(stream)),
+                  "xq_gemm_q4k_small_m");
+}
+
+size_t xq_q8k_bytes(int64_t rows, int64_t K) {
+  if (rows < 1 || K < 256 || K % 256) return 0;
+  return static_cast<size_t>(rows) * static_cast<size_t>(K / 256) * 320u;
+}
+
+size_t xq_q4k_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 256 || K % 256) return 0;
+  return static_cast<size_t>(N) * static_cast<size_t>(K / 256) * 144u;
+}
+
+size_t xq_iq4nl_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 256 || K % 256) return 0;
+  const int64_t bpr = K / 32;
+  const int64_t prefix = ((bpr * 2 + 3) / 4) * 4;
+  return static_cast<size_t>(N) * static_cast<size_t>(prefix + 16 * bpr);
+}
+
+const char* xq_status_name(xq_status s) {
+  switch (s) {
+    case XQ_OK: return "XQ_OK";
+    case XQ_E_NULL: return "XQ_E_NULL";
+    case XQ_E_SHAPE: return "XQ_E_SHAPE";
+    case XQ_E_ALIGN: return "XQ_E_ALIGN";
+    case XQ_E_DEVICE: return "XQ_E_DEVICE";
+    case XQ_E_LAUNCH: return "XQ_E_LAUNCH";
+    default: return "XQ_E_UNKNOWN";
+  }
+}
+
+const char* xq_last_error(void) { return g_err; }
+
+xq_status xq_bench_stream_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf) return fail(XQ_E_NULL, "buf is NULL");
+  if (!sink) return fail(XQ_E_NULL, "sink is NULL");
+  if (bytes < 16 || bytes % 16) return fail(XQ_E_SHAPE, "bytes=%lld not a positive multiple of 16", (long long)bytes);
+  if (!aligned(buf, 16)) return fail(XQ_E_ALIGN, "buf not 16-byte aligned");
+  if (!aligned(sink, 4)) return fail(XQ_E_ALIGN, "sink not 4-byte aligned");
+  if (xq_status s = check_device()) return s;
+  return launched(xq::launch_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream)),
+                  "xq_bench_stream_read");
+}
+
+int64_t xq_bench_sink_words(int64_t bytes) { return xq::stream_read_sink_words(bytes); }
+
+}  // extern "C"

@@ -1,0 +1,22 @@
+// xq_launch.h — internal launchers called by the C ABI (xq_api.cpp) after it
+// has validated every argument. Each returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xq {
+
+hipError_t launch_quantize_q8k(void* xq, const float* x, int64_t rows, int64_t K,
+                               hipStream_t stream);
+hipError_t launch_gemv_q4k(float* y, const void* w, const void* xq, int64_t N, int64_t K,
+                           hipStream_t stream);
+hipError_t launch_gemv_iq4nl(float* y, const void* w, const void* xq, int64_t N, int64_t K,
+                             hipStream_t stream);
+hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, int64_t N,
+                           int64_t K, hipStream_t stream);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink,
+                              hipStream_t stream);
+int64_t stream_read_sink_words(int64_t bytes);
+
+}  // namespace xq

@@ -1,0 +1,123 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/xq.h declares, sizes its layouts, and refuses bad arguments before any
+HIP call (no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_decode_mat_amd as xq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "xq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(xq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = xq.lib()
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(xq.EXPORTS)
+
+
+def test_layout_sizes():
+    assert xq.xq_q8k_bytes(1, 4096) == 16 * 320
+    assert xq.xq_q8k_bytes(512, 4096) == 2621440
+    assert xq.xq_q4k_bytes(14336, 4096) == 33030144
+    assert xq.xq_q4k_bytes(256, 1024) == 147456
+    assert xq.xq_iq4nl_bytes(4096, 4096) == 9437184
+    assert xq.xq_iq4nl_bytes(128256, 4096) == 295501824
+    assert xq.xq_q8k_bytes(1, 1000) == 0 and xq.xq_q4k_bytes(0, 256) == 0
+
+
+def test_status_names():
+    assert [xq.xq_status_name(s) for s in range(6)] == [
+        "XQ_OK", "XQ_E_NULL", "XQ_E_SHAPE", "XQ_E_ALIGN", "XQ_E_DEVICE", "XQ_E_LAUNCH"]
+
+
+# Fake device addresses: the gates tested here refuse before anything is
+# dereferenced or launched.
+A16 = 0x7F0000000000
+A4 = A16 + 4
+A1 = A16 + 1
+
+
+def _call(name, *args):
+    L = xq.lib()
+    s = getattr(L, name)(*args)
+    return s, L.xq_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status,text", [
+    ((0, A16, 1, 256, None), xq.XQ_E_NULL, "xq is NULL"),
+    ((A16, 0, 1, 256, None), xq.XQ_E_NULL, "x is NULL"),
+    ((A16, A16, 0, 256, None), xq.XQ_E_SHAPE, "rows=0"),
+    ((A16, A16, 1, 1000, None), xq.XQ_E_SHAPE, "K=1000"),
+    ((A16, A16, 1, 0, None), xq.XQ_E_SHAPE, "K=0"),
+    ((A16, A16, 2 ** 40, 256, None), xq.XQ_E_SHAPE, "exceeds"),
+    ((A4, A16, 1, 256, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
+    ((A16, A4, 1, 256, None), xq.XQ_E_ALIGN, "x not 16-byte"),
+])
+def test_quantize_refusals(args, status, text):
+    s, err = _call("xq_quantize_q8k", *args)
+    assert s == status and text in err
+
+
+@pytest.mark.parametrize("fn", ["xq_gemv_q4k", "xq_gemv_iq4nl"])
+@pytest.mark.parametrize("args,status,text", [
+    ((0, A16, A16, 8, 256, None), xq.XQ_E_NULL, "y is NULL"),
+    ((A16, 0, A16, 8, 256, None), xq.XQ_E_NULL, "w is NULL"),
+    ((A16, A16, 0, 8, 256, None), xq.XQ_E_NULL, "xq is NULL"),
+    ((A16, A16, A16, 0, 256, None), xq.XQ_E_SHAPE, "N=0"),
+    ((A16, A16, A16, 2 ** 30 + 1, 256, None), xq.XQ_E_SHAPE, "N=1073741825"),
+    ((A16, A16, A16, 8, 300, None), xq.XQ_E_SHAPE, "K=300"),
+    ((A16, A16, A16, 8, 49152 + 256, None), xq.XQ_E_SHAPE, "above the largest"),
+    ((A1, A16, A16, 8, 256, None), xq.XQ_E_ALIGN, "y not 4-byte"),
+    ((A16, A4, A16, 8, 256, None), xq.XQ_E_ALIGN, "w not 16-byte"),
+    ((A16, A16, A4, 8, 256, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
+])
+def test_gemv_refusals(fn, args, status, text):
+    s, err = _call(fn, *args)
+    assert s == status and text in err
+
+
+@pytest.mark.parametrize("args,status,text", [
+    ((0, A16, A16, 4, 8, 256, None), xq.XQ_E_NULL, "y is NULL"),
+    ((A16, A16, A16, 0, 8, 256, None), xq.XQ_E_SHAPE, "M=0"),
+    ((A16, A16, A16, 4, 0, 256, None), xq.XQ_E_SHAPE, "N=0"),
+    ((A16, A16, A16, 4, 8, 257, None), xq.XQ_E_SHAPE, "K=257"),
+    ((A16, A4, A16, 4, 8, 256, None), xq.XQ_E_ALIGN, "w not 16-byte"),
+    ((A16, A16, A1, 4, 8, 256, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
+])
+def test_gemm_refusals(args, status, text):
+    s, err = _call("xq_gemm_q4k_small_m", *args)
+    assert s == status and text in err
+
+
+def test_refusal_raises_in_binding():
+    with pytest.raises(xq.XQError) as e:
+        xq.xq_gemv_q4k(A16, A16, A16, 8, 1000)
+    assert e.value.status == xq.XQ_E_SHAPE and "K=1000" in str(e.value)
+
+
+def test_binding_refuses_host_and_short_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        xq.xq_gemv_q4k(torch.zeros(8), A16, A16, 8, 256)   # host tensor
+
+
+def test_device_gate_without_gpu():
+    """With no HIP device visible, a call whose other arguments pass is refused
+    at the device gate, before any launch."""
+    import torch
+    if torch.cuda.device_count() != 0:
+        pytest.skip("a GPU is visible; this gate is exercised only where none is")
+    s, err = _call("xq_gemv_q4k", A16, A16, A16, 8, 256, None)
+    assert s == xq.XQ_E_DEVICE, err

@@ -1,0 +1,352 @@
+"""HIP path against the oracle, element by element, through the C ABI.
+
+Bars (the pages' comparison rules, "The kernel reference interpreter",
+section Comparing against it, and "25 — Writing XPU Kernels", section 25.7):
+  * q8_K bytes 0..291 of every block: bit-exact (bytes 292..319 carry no
+    meaning and are skipped).
+  * Per-block integer partials: bit-exact. They are isolated through the
+    production entry points: weights with d = 1, dmin = 0 (or d = 0, dmin = 1)
+    against an activation whose only nonzero block has scale 1 make each
+    output equal one block's S (or -M) exactly.
+  * f32 outputs: |y - y_oracle| <= 1e-5 * T per output, T the sum of the
+    magnitudes of the products that make it up; T = 0 demands y = 0.
+  * No NaN, and outputs written in full: every output buffer is poisoned with
+    0xFF bytes first, and a canary tail past its end must stay untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_decode_mat_amd as xq
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+REL = 1e-5
+CANARY = 64
+
+
+def _note(msg):
+    print("[gpu-case] " + msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).reshape(-1).copy()).cuda()
+
+
+def poisoned_f32(n: int) -> torch.Tensor:
+    return torch.full(((n + CANARY) * 4,), 255, dtype=torch.uint8, device="cuda").view(torch.float32)
+
+
+def poisoned_u8(n: int) -> torch.Tensor:
+    return torch.full((n + CANARY * 4,), 255, dtype=torch.uint8, device="cuda")
+
+
+def take_f32(buf: torch.Tensor, n: int) -> np.ndarray:
+    torch.cuda.synchronize()
+    tail = buf[n:].view(torch.int32)
+    assert bool((tail == -1).all()), "canary past the output was overwritten"
+    return buf[:n].cpu().numpy().astype(np.float64)
+
+
+def take_u8(buf: torch.Tensor, n: int) -> np.ndarray:
+    torch.cuda.synchronize()
+    assert bool((buf[n:] == 255).all()), "canary past the output was overwritten"
+    return buf[:n].cpu().numpy()
+
+
+def assert_close(y: np.ndarray, ref: np.ndarray, T: np.ndarray, what: str):
+    assert not np.isnan(y).any(), "%s: %d NaN outputs" % (what, int(np.isnan(y).sum()))
+    err = np.abs(y - ref)
+    bad = err > REL * T
+    assert not bad.any(), "%s: %d outputs outside 1e-5*T, first at %d: gpu %r oracle %r T %r" % (
+        what, int(bad.sum()), int(np.argmax(bad)), y[bad][0], ref[bad][0], T[bad][0])
+    assert np.all(y[T == 0] == 0)
+    assert np.any(y != 0), "%s: all outputs zero" % what
+
+
+def gpu_quantize(x: np.ndarray) -> np.ndarray:
+    rows, K = x.shape
+    n = xq.xq_q8k_bytes(rows, K)
+    out = poisoned_u8(n)
+    xq.xq_quantize_q8k(out, dev(x.astype(np.float32)), rows, K)
+    return take_u8(out, n).reshape(rows, K // 256, 320)
+
+
+def gpu_gemv_q4k(w: np.ndarray, xqb: np.ndarray, N: int, K: int) -> np.ndarray:
+    y = poisoned_f32(N)
+    xq.xq_gemv_q4k(y, dev(w), dev(xqb), N, K)
+    return take_f32(y, N)
+
+
+def gpu_gemv_iq4nl(w: np.ndarray, xqb: np.ndarray, N: int, K: int) -> np.ndarray:
+    y = poisoned_f32(N)
+    xq.xq_gemv_iq4nl(y, dev(w), dev(xqb), N, K)
+    return take_f32(y, N)
+
+
+def gpu_gemm(w: np.ndarray, xqb: np.ndarray, M: int, N: int, K: int) -> np.ndarray:
+    y = poisoned_f32(M * N)
+    xq.xq_gemm_q4k_small_m(y, dev(w), dev(xqb), M, N, K)
+    return take_f32(y, M * N).reshape(M, N)
+
+
+# ---------------------------------------------------------------------------
+# q8_K quantizer: bit-exact
+# ---------------------------------------------------------------------------
+
+def _quant_cases():
+    cases = {}
+    g = wl.rng(wl.SEEDS["q4k_tiny"])
+    wl.q4k_weights(256, 1024, g)
+    cases["tiny_1x1024"] = wl.activations(1, 1024, g)
+    g = wl.rng(wl.SEEDS["q4k_4096"])
+    wl.q4k_weights(1, 4096, g)
+    cases["c1_1x4096"] = wl.activations(1, 4096, wl.rng(2001))
+    cases["h_1x14336"] = 3.0 * wl.activations(1, 14336, wl.rng(2002))
+    cases["prefill_512x4096"] = wl.activations(512, 4096, wl.rng(wl.SEEDS["prefill"]))
+    cases["ragged_3x768"] = wl.activations(3, 768, wl.rng(2003))
+    cases["pages_1x2048"] = wl.pages_activation(2048).reshape(1, -1)
+    t = np.round(wl.rng(2004).uniform(-126, 126, 512) * 2) / 2
+    t[0], t[1:8] = 127.0, [0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 62.5]
+    t[256] = -127.0
+    cases["ties_1x512"] = t.reshape(1, -1)
+    z = np.zeros((2, 512), np.float32)
+    z[1, :256] = 0.37
+    z[1, 300] = -5.0
+    cases["zero_const_2x512"] = z
+    s = wl.activations(5, 256, wl.rng(2005))
+    s *= np.array([[1e-37], [1e-30], [1e-3], [1e3], [1e30]], np.float32)
+    cases["magnitudes_5x256"] = s
+    return cases
+
+
+QUANT_CASES = _quant_cases()
+
+
+@pytest.mark.parametrize("name", sorted(QUANT_CASES))
+def test_quantize_q8k_bit_exact(name):
+    x = QUANT_CASES[name].astype(np.float32)
+    _note("quantize %s" % name)
+    got = gpu_quantize(x)
+    want = oracle.quantize_q8k(x)
+    diff = got[:, :, :292] != want[:, :, :292]
+    assert not diff.any(), "%s: %d bytes differ, first block %s" % (
+        name, int(diff.sum()), np.argwhere(diff.any(axis=2))[0])
+    assert np.all(got[:, :, 292:] == 0)
+
+
+# ---------------------------------------------------------------------------
+# Q4_K mat-vec
+# ---------------------------------------------------------------------------
+
+Q4K_SHAPES = [
+    ("tiny", 256, 1024, wl.SEEDS["q4k_tiny"]),
+    ("c1_4096x4096", 4096, 4096, wl.SEEDS["q4k_4096"]),
+    ("ffn_up_14336x4096", 14336, 4096, wl.SEEDS["ffn_up"]),
+    ("ffn_down_4096x14336", 4096, 14336, wl.SEEDS["ffn_down"]),
+    ("n1_k256", 1, 256, 3001),
+    ("n37_k768", 37, 768, 3002),
+    ("n130_k2304", 130, 2304, 3003),
+    ("n9000_k4352", 9000, 4352, 3004),
+    ("n8193_k2048_tworow", 8193, 2048, 3005),
+    ("n64_kmax", 64, 49152, 3006),
+]
+
+
+@pytest.mark.parametrize("name,N,K,seed", Q4K_SHAPES, ids=[s[0] for s in Q4K_SHAPES])
+def test_gemv_q4k(name, N, K, seed):
+    g = wl.rng(seed)
+    w = wl.q4k_weights(N, K, g)
+    x = wl.activations(1, K, g)
+    xqb = oracle.quantize_q8k(x)
+    _note("gemv_q4k %s N=%d K=%d" % (name, N, K))
+    y = gpu_gemv_q4k(w, xqb, N, K)
+    ref, T = oracle.gemv_q4k(w, xqb, N, K)
+    assert_close(y, ref, T, name)
+
+
+ISO_Q4K = [
+    ("c1", 4096, 4096, list(range(16))),
+    ("ffn_down", 4096, 14336, [0, 13, 27, 41, 55]),
+    ("ragged", 37, 768, [0, 1, 2]),
+]
+
+
+@pytest.mark.parametrize("which", ["S", "M"])
+@pytest.mark.parametrize("name,N,K,blocks", ISO_Q4K, ids=[s[0] for s in ISO_Q4K])
+def test_gemv_q4k_partials_bit_exact(name, N, K, blocks, which):
+    g = wl.rng(4000 + N + K)
+    w = wl.q4k_isolation_weights(N, K, g, which)
+    wd = dev(w)
+    for b in blocks:
+        x = wl.isolating_activation(1, K, g, b)
+        xqb = oracle.quantize_q8k(x)
+        assert xqb[0, b, 288:292].view("<f4")[0] == 1.0
+        S, Mp = oracle.q4k_partials(w, xqb, N, K)
+        want = S[:, b] if which == "S" else -Mp[:, b]
+        _note("gemv_q4k partial %s %s block %d" % (name, which, b))
+        y = poisoned_f32(N)
+        xq.xq_gemv_q4k(y, wd, dev(xqb), N, K)
+        got = take_f32(y, N)
+        assert np.array_equal(got, want.astype(np.float64)), (
+            "block %d: %d rows differ" % (b, int((got != want).sum())))
+
+
+def test_ffn_pair_chain():
+    """The FFN pair with the GPU quantizer in the loop: x -> q8_K -> up ->
+    h -> q8_K -> down. Each quantization is bit-exact against the oracle
+    quantizing the same f32 input (the GPU's own h for the second)."""
+    K, H = 4096, 14336
+    gu = wl.rng(wl.SEEDS["ffn_up"])
+    wu = wl.q4k_weights(H, K, gu)
+    x = wl.activations(1, K, gu)
+    wdn = wl.q4k_weights(K, H, wl.rng(wl.SEEDS["ffn_down"]))
+    _note("ffn chain")
+    xq1 = torch.full((xq.xq_q8k_bytes(1, K),), 255, dtype=torch.uint8, device="cuda")
+    h = torch.empty(H, dtype=torch.float32, device="cuda")
+    xq2 = torch.full((xq.xq_q8k_bytes(1, H),), 255, dtype=torch.uint8, device="cuda")
+    y = torch.empty(K, dtype=torch.float32, device="cuda")
+    wu_d, wd_d, x_d = dev(wu), dev(wdn), dev(x)
+    xq.xq_quantize_q8k(xq1, x_d, 1, K)
+    xq.xq_gemv_q4k(h, wu_d, xq1, H, K)
+    xq.xq_quantize_q8k(xq2, h, 1, H)
+    xq.xq_gemv_q4k(y, wd_d, xq2, K, H)
+    torch.cuda.synchronize()
+    q1 = xq1.cpu().numpy().reshape(1, K // 256, 320)
+    q1o = oracle.quantize_q8k(x)
+    assert np.array_equal(q1[:, :, :292], q1o[:, :, :292])
+    hh = h.cpu().numpy().astype(np.float64)
+    ref, T = oracle.gemv_q4k(wu, q1o, H, K)
+    assert_close(hh, ref, T, "up")
+    q2 = xq2.cpu().numpy().reshape(1, H // 256, 320)
+    q2o = oracle.quantize_q8k(h.cpu().numpy().reshape(1, H))
+    assert np.array_equal(q2[:, :, :292], q2o[:, :, :292])
+    ref2, T2 = oracle.gemv_q4k(wdn, q2o, K, H)
+    assert_close(y.cpu().numpy().astype(np.float64), ref2, T2, "down")
+
+
+# ---------------------------------------------------------------------------
+# IQ4_NL mat-vec
+# ---------------------------------------------------------------------------
+
+IQ4_SHAPES = [
+    ("c3_4096x4096", 4096, 4096, wl.SEEDS["iq4nl_4096"]),
+    ("c3_head_128256x4096", 128256, 4096, wl.SEEDS["iq4nl_head"]),
+    ("n5_k256", 5, 256, 5001),
+    ("n33_k768", 33, 768, 5002),
+    ("n1000_k2304", 1000, 2304, 5003),
+    ("n8193_k2048_tworow", 8193, 2048, 5004),
+    ("n16_k14336", 16, 14336, 5005),
+]
+
+
+@pytest.mark.parametrize("name,N,K,seed", IQ4_SHAPES, ids=[s[0] for s in IQ4_SHAPES])
+def test_gemv_iq4nl(name, N, K, seed):
+    g = wl.rng(seed)
+    w = wl.iq4nl_weights(N, K, g)
+    x = wl.activations(1, K, g)
+    xqb = oracle.quantize_q8k(x)
+    _note("gemv_iq4nl %s N=%d K=%d" % (name, N, K))
+    y = gpu_gemv_iq4nl(w, xqb, N, K)
+    ref, T = oracle.gemv_iq4nl(w, xqb, N, K)
+    assert_close(y, ref, T, name)
+
+
+@pytest.mark.parametrize("N,K,blocks", [(4096, 4096, [0, 7, 8, 63, 64, 127]), (33, 768, [0, 5, 23])])
+def test_gemv_iq4nl_partials_bit_exact(N, K, blocks):
+    g = wl.rng(6000 + N)
+    w = wl.iq4nl_unit_scale_weights(N, K, g)
+    wd = dev(w)
+    for c in blocks:
+        x = wl.isolating_activation(1, K, g, c // 8, width=32, offset=32 * (c % 8))
+        xqb = oracle.quantize_q8k(x)
+        D = oracle.iq4nl_partials(w, xqb, N, K)
+        _note("gemv_iq4nl partial block %d" % c)
+        y = poisoned_f32(N)
+        xq.xq_gemv_iq4nl(y, wd, dev(xqb), N, K)
+        got = take_f32(y, N)
+        assert np.array_equal(got, D[:, c].astype(np.float64)), c
+
+
+# ---------------------------------------------------------------------------
+# Small-M product (int8 MFMA)
+# ---------------------------------------------------------------------------
+
+GEMM_SMALL = [
+    (1, 37, 256, 7001),
+    (3, 130, 768, 7002),
+    (130, 200, 512, 7003),
+    (129, 128, 1024, 7004),
+    (256, 256, 2048, 7005),
+]
+
+
+@pytest.mark.parametrize("M,N,K,seed", GEMM_SMALL)
+def test_gemm_full_compare(M, N, K, seed):
+    g = wl.rng(seed)
+    w = wl.q4k_weights(N, K, g)
+    x = wl.activations(M, K, g)
+    xqb = oracle.quantize_q8k(x)
+    _note("gemm M=%d N=%d K=%d" % (M, N, K))
+    Y = gpu_gemm(w, xqb, M, N, K)
+    ref, T = oracle.gemm_q4k(w, xqb, M, N, K)
+    assert_close(Y.reshape(-1), ref.reshape(-1), T.reshape(-1), "gemm")
+
+
+def test_gemm_prefill_512x14336x4096():
+    M, N, K = 512, 14336, 4096
+    g = wl.rng(wl.SEEDS["prefill"])
+    w = wl.q4k_weights(N, K, g)
+    x = wl.activations(M, K, g)
+    xqb = oracle.quantize_q8k(x)
+    _note("gemm prefill full size")
+    Y = gpu_gemm(w, xqb, M, N, K)
+    assert not np.isnan(Y).any()
+    # Sampled outputs, including every tile corner.
+    s = wl.rng(7100)
+    ms = np.concatenate([s.integers(0, M, 3000), [0, 0, M - 1, M - 1, 127, 128, 255, 256]])
+    ns = np.concatenate([s.integers(0, N, 3000), [0, N - 1, 0, N - 1, 127, 128, 14207, 14208]])
+    ref, T = oracle.gemm_q4k(w, xqb, M, N, K, ms, ns)
+    assert_close(Y[ms, ns], ref, T, "prefill sampled")
+    # Whole rows of Y for a few tokens.
+    for m in (0, 200, 511):
+        ref, T = oracle.gemv_q4k(w, xqb[m], N, K)
+        assert_close(Y[m], ref, T, "prefill row %d" % m)
+
+
+@pytest.mark.parametrize("which", ["S", "M"])
+def test_gemm_partials_bit_exact(which):
+    M, N, K = 3, 200, 1024
+    g = wl.rng(7200)
+    w = wl.q4k_isolation_weights(N, K, g, which)
+    wd = dev(w)
+    for b in range(K // 256):
+        x = wl.isolating_activation(M, K, g, b)
+        xqb = oracle.quantize_q8k(x)
+        _note("gemm partial %s block %d" % (which, b))
+        y = poisoned_f32(M * N)
+        xq.xq_gemm_q4k_small_m(y, wd, dev(xqb), M, N, K)
+        got = take_f32(y, M * N).reshape(M, N)
+        for m in range(M):
+            S, Mp = oracle.q4k_partials(w, xqb[m], N, K)
+            want = S[:, b] if which == "S" else -Mp[:, b]
+            assert np.array_equal(got[m], want.astype(np.float64)), (m, b)
+
+
+def test_stream_read_probe_runs():
+    nbytes = 1 << 24
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(xq.xq_bench_sink_words(nbytes), dtype=torch.int32, device="cuda")
+    xq.xq_bench_stream_read(buf, nbytes, sink)
+    torch.cuda.synchronize()

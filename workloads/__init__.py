@@ -155,3 +155,60 @@ def q4k_block(d: float, dmin: float, sc, m, nibble_bytes) -> np.ndarray:
 def f16_bits(value: float) -> int:
     """The binary16 bit pattern of ``value`` (numpy round-to-nearest-even)."""
     return int(np.array(value, dtype=np.float16).view(np.uint16))
+
+
+def q4k_from_fields(d, dmin, sc, m, nibble_bytes) -> np.ndarray:
+    """A Q4_K matrix [N, nb, 144] assembled from its fields: f32 d and dmin
+    [N, nb] (stored as f16), 6-bit sc and m [N, nb, 8], nibble bytes
+    [N, nb, 128]."""
+    d = np.asarray(d, dtype=np.float32)
+    N, nb = d.shape
+    out = np.empty((N, nb, Q4K_BLOCK_BYTES), dtype=np.uint8)
+    out[:, :, 0:2] = _f16_bytes(d)
+    out[:, :, 2:4] = _f16_bytes(np.asarray(dmin, dtype=np.float32))
+    out[:, :, 4:16] = pack_q4k_scales(sc, m)
+    out[:, :, 16:] = np.asarray(nibble_bytes, dtype=np.uint8)
+    return out
+
+
+def q4k_isolation_weights(N: int, K: int, g: np.random.Generator, which: str) -> np.ndarray:
+    """Weights that make a mat-vec output equal one exact integer partial.
+
+    which == "S": d = 1, dmin = 0, sub-block scales in 0..31, so against an
+    activation whose only nonzero block has scale 1 the output is that block's
+    S partial exactly (|S| < 2^24). which == "M": d = 0, dmin = 1, so the
+    output is minus the block's M partial."""
+    nb = K // Q4K_BLOCK_WEIGHTS
+    sc = g.integers(0, 32 if which == "S" else 64, size=(N, nb, 8))
+    m = g.integers(0, 64, size=(N, nb, 8))
+    nib = g.integers(0, 256, size=(N, nb, 128), dtype=np.uint8)
+    one = np.ones((N, nb), np.float32)
+    zero = np.zeros((N, nb), np.float32)
+    if which == "S":
+        return q4k_from_fields(one, zero, sc, m, nib)
+    if which == "M":
+        return q4k_from_fields(zero, one, sc, m, nib)
+    raise ValueError(which)
+
+
+def isolating_activation(R: int, K: int, g: np.random.Generator, block: int,
+                         width: int = 256, offset: int = 0) -> np.ndarray:
+    """f32 [R, K], zero except elements [block*256 + offset, + width) of every
+    row, which hold values in [-127, 127] with one element exactly 127, so
+    that the block's q8_K scale is exactly 1 and its codes are the values
+    rounded to integers."""
+    x = np.zeros((R, K), np.float32)
+    lo = block * 256 + offset
+    vals = g.uniform(-127.0, 127.0, size=(R, width)).astype(np.float32)
+    vals[:, g.integers(0, width)] = 127.0
+    x[:, lo:lo + width] = vals
+    return x
+
+
+def iq4nl_unit_scale_weights(N: int, K: int, g: np.random.Generator) -> np.ndarray:
+    """Resident IQ4_NL rows with every block scale 1.0 and random payloads."""
+    bpr, prefix, row_bytes = iq4nl_row_geometry(K)
+    out = np.zeros((N, row_bytes), dtype=np.uint8)
+    out[:, 0:2 * bpr] = _f16_bytes(np.ones((N, bpr), np.float32)).reshape(N, 2 * bpr)
+    out[:, prefix:] = g.integers(0, 256, size=(N, bpr * 16), dtype=np.uint8)
+    return out
