@@ -62,6 +62,10 @@ def parse():
                    help="also time the other workloads; their lines go to stderr and "
                         "gpurun_out/bench_suite.jsonl")
     p.add_argument("--json-out", default=None, help="also write the JSON line to this file")
+    p.add_argument("--counters", action="store_true",
+                   help="short run for rocprofv3 --pmc: 20 up and 20 down mat-vec launches over "
+                        "the cold pool, then 5 device copies and 5 streaming reads of 64 MiB "
+                        "(the counters' calibration), then exit")
     return p.parse_args()
 
 
@@ -139,6 +143,10 @@ def main():
     torch.cuda.synchronize()
     assert bool(torch.isfinite(y).all())
 
+    if args.counters:
+        counters_run(torch, xq, L, dev, stream, ups, dns, xq1, xq2, h, y, x_d, pool)
+        return
+
     # ---- headline: K plain steps ----
     for i in range(args.warmup):
         step(i)
@@ -194,6 +202,13 @@ def main():
 
     stream_gbps = stream_read(2 << 30, 20)
     log("streaming read, 2 GiB: %.1f GB/s" % stream_gbps)
+    # Like-for-like: the probe over the same rotation pool as the up mat-vec,
+    # 33 MB per launch, so launch and ramp costs weigh the same.
+    sink_s = torch.empty(xq.xq_bench_sink_words(w_up.nbytes), dtype=torch.int32, device=dev)
+    us_small = _time_loop(torch, stream, lambda k: L.xq_bench_stream_read(
+        ups[k % pool].data_ptr(), w_up.nbytes, sink_s.data_ptr(), s), 1000)
+    stream_small_gbps = w_up.nbytes / us_small / 1e3
+    log("streaming read, 33 MB cold: %.3f us, %.1f GB/s" % (us_small, stream_small_gbps))
 
     # ---- roofline of the up mat-vec ----
     up_alg_bytes = w_up.nbytes + xq.xq_q8k_bytes(1, UP[1]) + 4 * UP[0]
@@ -211,6 +226,7 @@ def main():
         "alg_bytes_per_launch": up_alg_bytes,
         "mean_launch_us": round(kern_us["gemv_up"], 3),
         "frac_of_stream_read": round(achieved / stream_gbps, 4),
+        "frac_of_stream_read_same_size": round(achieved / stream_small_gbps, 4),
     }
 
     # ---- CPU baseline: the oracle over whole FFN pairs ----
@@ -266,6 +282,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
         "stream_read_GBps": round(stream_gbps, 1),
+        "stream_read_33MB_GBps": round(stream_small_gbps, 1),
         "frac_of_stream_read": round(value / stream_gbps, 4),
         "host_us_per_step": round(wall / args.steps * 1e6, 3),
     }
@@ -280,6 +297,33 @@ def main():
     if args.json_out:
         with open(args.json_out, "w") as f:
             f.write(out + "\n")
+
+
+def counters_run(torch, xq, L, dev, stream, ups, dns, xq1, xq2, h, y, x_d, pool):
+    """Launch sequence profiled by the rocprofv3 --pmc runs: dispatch order is
+    up x20, down x20, copy x5 (64 MiB), stream read x5 (64 MiB)."""
+    s = stream.cuda_stream
+    L.xq_quantize_q8k(xq1.data_ptr(), x_d.data_ptr(), 1, UP[1], s)
+    L.xq_quantize_q8k(xq2.data_ptr(), h.data_ptr(), 1, DOWN[1], s)
+    torch.cuda.synchronize()
+    for i in range(20):
+        L.xq_gemv_q4k(h.data_ptr(), ups[(i + 3) % pool].data_ptr(), xq1.data_ptr(), UP[0], UP[1], s)
+    for i in range(20):
+        L.xq_gemv_q4k(y.data_ptr(), dns[(i + 7) % pool].data_ptr(), xq2.data_ptr(), DOWN[0],
+                      DOWN[1], s)
+    torch.cuda.synchronize()
+    n = 64 << 20
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    c = torch.empty_like(a)
+    sink = torch.empty(xq.xq_bench_sink_words(n), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        c.copy_(a)
+    for _ in range(5):
+        L.xq_bench_stream_read(a.data_ptr(), n, sink.data_ptr(), s)
+    torch.cuda.synchronize()
+    log("counters run done")
 
 
 def _pool_copies(t, pool_mb):

@@ -18,11 +18,12 @@
 //  * Each lane also loads its block's 16-byte header; the eight lanes of a
 //    block load the same 16 bytes, which the cache serves once per line.
 //  * All of a lane's loads for a batch of PF units are issued before any is
-//    used, and the first batch before the activation is staged, so each wave
-//    keeps R*PF*32 bytes per lane in flight.
+//    used, and the first batch before the activation's LDS stores (whose
+//    loads come first), so each wave keeps R*PF*32 bytes per lane in flight.
 //  * The row's q8_K activation is staged once per workgroup in LDS (the only
 //    LDS use); every wave of the workgroup reads its codes, sums and scales
 //    from there.
+//  * The per-block float work is one pass: xs * (d*S - dmin*M).
 //  * Lane partials are f32; the wave reduces them with DPP row sums and four
 //    v_readlane, and lane 0 stores y.
 #include "xq_device.h"
@@ -30,9 +31,6 @@
 
 namespace xq {
 namespace {
-
-constexpr int kWavesPerGroup = 4;
-constexpr int kThreads = kWavesPerGroup * kWave;
 
 struct LaneGeom {
   int bsub;        // block slot within a unit (0..7)
@@ -93,34 +91,69 @@ __device__ __forceinline__ float unit_partial(const uint4 nib, const uint4 hdr, 
   const int M = __mul24(m0, sums.x) + __mul24(m1, sums.y);
   const float d = half_bits_to_float(hdr.x & 0xFFFFu);
   const float dmin = half_bits_to_float(hdr.x >> 16);
-  return (d * xs) * static_cast<float>(S) - (dmin * xs) * static_cast<float>(M);
+  return xs * (d * static_cast<float>(S) - dmin * static_cast<float>(M));
 }
 
-template <int R, int PF>
-__global__ __launch_bounds__(kThreads) void gemv_q4k_kernel(float* __restrict__ y,
-                                                            const uint8_t* __restrict__ w,
-                                                            const uint8_t* __restrict__ xq,
-                                                            int N, int nb) {
+// Loads of the activation row into registers, issued before the weight
+// loads; the LDS stores follow them.
+template <int NA, int THREADS>
+__device__ __forceinline__ void act_load(uint4 (&a)[NA], const uint8_t* xq, int n16) {
+#pragma unroll
+  for (int k = 0; k < NA; ++k) {
+    const int i = threadIdx.x + k * THREADS;
+    a[k] = (i < n16) ? reinterpret_cast<const uint4*>(xq)[i] : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int NA, int THREADS>
+__device__ __forceinline__ void act_store(const uint4 (&a)[NA], uint8_t* lds, const uint8_t* xq,
+                                          int n16) {
+#pragma unroll
+  for (int k = 0; k < NA; ++k) {
+    const int i = threadIdx.x + k * THREADS;
+    if (i < n16) reinterpret_cast<uint4*>(lds)[i] = a[k];
+  }
+  // Rows longer than NA*THREADS chunks stage the rest directly.
+  for (int i = threadIdx.x + NA * THREADS; i < n16; i += THREADS)
+    reinterpret_cast<uint4*>(lds)[i] = reinterpret_cast<const uint4*>(xq)[i];
+}
+
+// R rows per wave, PF units per load batch, W waves per workgroup, NA
+// activation chunks per thread held in registers. CLAMP: every load is
+// issued (block index clamped into the row, the contribution of a clamped
+// block masked), which keeps the loads unconditional so the wait counts
+// stay static; without CLAMP, loads and compute of blocks past the row end
+// are skipped (cheaper when PF does not divide the row's units).
+template <int R, int PF, int W, int NA, bool CLAMP>
+__global__ __launch_bounds__(W * kWave) void gemv_q4k_kernel(float* __restrict__ y,
+                                                             const uint8_t* __restrict__ w,
+                                                             const uint8_t* __restrict__ xq,
+                                                             int N, int nb) {
   extern __shared__ __align__(16) uint8_t act[];
+  constexpr int kThreads = W * kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
-  const int row0 = (blockIdx.x * kWavesPerGroup + wave) * R;
+  const int row0 = (blockIdx.x * W + wave) * R;
   const int units = (nb + 7) >> 3;
   const LaneGeom L = lane_geom(lane);
   const int64_t row_bytes = static_cast<int64_t>(nb) * kQ4KBytes;
+  const int n16 = nb * (kQ8KBytes / 16);
+
+  uint4 areg[NA];
+  act_load<NA, kThreads>(areg, xq, n16);
 
   uint4 nib[R][PF];
   uint4 hdr[R][PF];
   auto load_batch = [&](int u0) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int row = min(row0 + r, N - 1);
-      const uint8_t* wr = w + static_cast<int64_t>(row) * row_bytes;
+    for (int p = 0; p < PF; ++p)
 #pragma unroll
-      for (int p = 0; p < PF; ++p) {
-        const int b = (u0 + p) * 8 + L.bsub;
-        if (b < nb) {
-          const uint8_t* blk = wr + static_cast<int64_t>(b) * kQ4KBytes;
+      for (int r = 0; r < R; ++r) {
+        const int row = min(row0 + r, N - 1);
+        const int bb = (u0 + p) * 8 + L.bsub;
+        const uint8_t* wr = w + static_cast<int64_t>(row) * row_bytes;
+        if (CLAMP || bb < nb) {
+          const uint8_t* blk = wr + static_cast<int64_t>(min(bb, nb - 1)) * kQ4KBytes;
           nib[r][p] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (2 * L.g + L.h));
           hdr[r][p] = *reinterpret_cast<const uint4*>(blk);
         } else {
@@ -128,18 +161,10 @@ __global__ __launch_bounds__(kThreads) void gemv_q4k_kernel(float* __restrict__ 
           hdr[r][p] = make_uint4(0, 0, 0, 0);
         }
       }
-    }
   };
 
   load_batch(0);
-
-  // Stage the q8_K activation row (nb * 320 bytes) in LDS.
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(xq);
-    uint4* dst = reinterpret_cast<uint4*>(act);
-    const int n16 = nb * (kQ8KBytes / 16);
-    for (int i = threadIdx.x; i < n16; i += kThreads) dst[i] = src[i];
-  }
+  act_store<NA, kThreads>(areg, act, xq, n16);
   __syncthreads();
 
   float acc[R];
@@ -150,10 +175,17 @@ __global__ __launch_bounds__(kThreads) void gemv_q4k_kernel(float* __restrict__ 
     if (u0 > 0) load_batch(u0);
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      const int b = (u0 + p) * 8 + L.bsub;
-      if (b < nb) {
+      const int bb = (u0 + p) * 8 + L.bsub;
+      if (CLAMP) {
+        const int b = min(bb, nb - 1);
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] += unit_partial(nib[r][p], hdr[r][p], act, b, L);
+        for (int r = 0; r < R; ++r) {
+          const float v = unit_partial(nib[r][p], hdr[r][p], act, b, L);
+          acc[r] += (bb < nb) ? v : 0.0f;
+        }
+      } else if (bb < nb) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] += unit_partial(nib[r][p], hdr[r][p], act, bb, L);
       }
     }
   }
@@ -165,30 +197,15 @@ __global__ __launch_bounds__(kThreads) void gemv_q4k_kernel(float* __restrict__ 
   }
 }
 
-template <int R, int PF>
-hipError_t launch_rpf(float* y, const uint8_t* w, const uint8_t* xq, int N, int nb,
+template <int R, int PF, int W, int NA, bool CLAMP>
+hipError_t launch_cfg(float* y, const uint8_t* w, const uint8_t* xq, int N, int nb,
                       hipStream_t stream) {
   const int waves = (N + R - 1) / R;
-  const int grid = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+  const int grid = (waves + W - 1) / W;
   const size_t lds = static_cast<size_t>(nb) * kQ8KBytes;
-  hipLaunchKernelGGL((gemv_q4k_kernel<R, PF>), dim3(grid), dim3(kThreads), lds, stream, y, w, xq,
-                     N, nb);
+  hipLaunchKernelGGL((gemv_q4k_kernel<R, PF, W, NA, CLAMP>), dim3(grid), dim3(W * kWave), lds,
+                     stream, y, w, xq, N, nb);
   return hipGetLastError();
-}
-
-template <int R>
-hipError_t launch_r(float* y, const uint8_t* w, const uint8_t* xq, int N, int nb, int pf,
-                    hipStream_t stream) {
-  switch (pf) {
-    case 1: return launch_rpf<R, 1>(y, w, xq, N, nb, stream);
-    case 2: return launch_rpf<R, 2>(y, w, xq, N, nb, stream);
-    case 3: return launch_rpf<R, 3>(y, w, xq, N, nb, stream);
-    case 4: return launch_rpf<R, 4>(y, w, xq, N, nb, stream);
-    case 5: return launch_rpf<R, 5>(y, w, xq, N, nb, stream);
-    case 6: return launch_rpf<R, 6>(y, w, xq, N, nb, stream);
-    case 7: return launch_rpf<R, 7>(y, w, xq, N, nb, stream);
-    default: return launch_rpf<R, 8>(y, w, xq, N, nb, stream);
-  }
 }
 
 }  // namespace
@@ -197,14 +214,25 @@ hipError_t launch_gemv_q4k(float* y, const void* w, const void* xq, int64_t N, i
                            hipStream_t stream) {
   const int nb = static_cast<int>(K / 256);
   const int units = (nb + 7) / 8;
-  const int pf = units < 8 ? units : 8;
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   const uint8_t* xb = static_cast<const uint8_t*>(xq);
   const int n = static_cast<int>(N);
-  // Two rows per wave when a row is short (one or two units) and there are
-  // rows enough to still fill 256 CUs several times over.
-  if (units <= 2 && N >= 8192) return launch_r<2>(y, wb, xb, n, nb, pf, stream);
-  return launch_r<1>(y, wb, xb, n, nb, pf, stream);
+  // Launch shapes chosen by measurement on MI355X (cold weights):
+  //  * rows of one or two units: every load of a row in flight at once,
+  //    two rows per wave when there are enough rows to fill the device;
+  //  * longer rows: batches of four units, eight waves per workgroup (the
+  //    activation row is staged half as often), loads past the row skipped.
+  if (units == 1) {
+    if (N >= 8192) return launch_cfg<2, 1, 4, 2, true>(y, wb, xb, n, nb, stream);
+    return launch_cfg<1, 1, 4, 2, true>(y, wb, xb, n, nb, stream);
+  }
+  if (units == 2) {
+    if (N >= 8192) return launch_cfg<2, 2, 4, 2, true>(y, wb, xb, n, nb, stream);
+    return launch_cfg<1, 2, 4, 2, true>(y, wb, xb, n, nb, stream);
+  }
+  if (units == 3) return launch_cfg<1, 3, 8, 2, true>(y, wb, xb, n, nb, stream);
+  if (units == 4) return launch_cfg<1, 4, 8, 3, true>(y, wb, xb, n, nb, stream);
+  return launch_cfg<1, 4, 8, 3, false>(y, wb, xb, n, nb, stream);
 }
 
 }  // namespace xq
