@@ -115,7 +115,8 @@ xq_status xq_gemv_iq4nl(float *y, const void *w, const void *xq, int64_t N, int6
  *  y   device, out: f32 [M][N] row-major (token-major), 4-byte aligned.
  *  w   device, in: Q4_K [N][K/256], 16-byte aligned.
  *  xq  device, in: q8_K [M][K/256], 16-byte aligned.
- *  1 <= M <= 2^30.  1 <= N <= 2^30.  K >= 256, a multiple of 256.
+ *  1 <= M <= 2^30.  1 <= N <= 2^30.  K >= 256, a multiple of 256. Each of
+ *  xq and w below 2 GiB (the kernel's loads use 32-bit offsets).
  * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH.
  */
 xq_status xq_gemm_q4k_small_m(float *y, const void *w, const void *xq, int64_t M, int64_t N,

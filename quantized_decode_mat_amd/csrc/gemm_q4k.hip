@@ -15,15 +15,16 @@
 // scale goes into the weight operand, exactly: sc = 8a + b with a, b in 0..7,
 // and the two int8 planes a*q and b*q (each <= 105) give S = 8*S_a + S_b.
 // The min term is a third plane whose bytes are m_j (<= 63) over sub-block j,
-// contracted with the same codes. All three accumulate exactly in int32
-// (|S| <= 30.7M, |M| <= 2.1M per block); f32 appears only in the per-block
-// epilogue.
+// contracted with the same codes. All partials are exact int32 (|S| <= 30.7M,
+// |M| <= 2.1M per block); f32 appears only in the per-block epilogue.
 //
-// Tile: 128 tokens x 128 weight rows per 512-thread workgroup, eight waves as
-// 2 (tokens) x 4 (rows), each wave 64 x 32 = 4 x 2 MFMA tiles of 16 x 16. Per
-// super-block the workgroup stages the 128 tokens' codes and scales and the
-// 128 rows' raw Q4_K blocks in LDS; waves decode their weight fragments from
-// LDS into the three planes in registers. Workgroups are laid out so that the
+// Tile: 64 tokens x 128 weight rows per 256-thread workgroup, four waves side
+// by side along the rows, each wave 64 x 32 = 4 x 2 MFMA tiles of 16 x 16, so
+// every weight fragment is decoded by exactly one wave. Super-blocks stream
+// through a two-stage LDS ring filled by direct global-to-LDS loads (no
+// registers): super-block b+1 is in flight while b is computed. Two
+// workgroups share a CU and run out of phase, so one's VALU work (decode,
+// epilogue) overlaps the other's MFMAs. Workgroups are laid out so that the
 // token tiles sharing one weight tile land on one XCD (one L2).
 #include "xq_device.h"
 #include "xq_launch.h"
@@ -34,14 +35,25 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128;          // tokens per workgroup tile
+constexpr int BM = 64;           // tokens per workgroup tile
 constexpr int BN = 128;          // weight rows per workgroup tile
-constexpr int kThreads = 512;    // 8 waves
-constexpr int kActStride = 272;  // 256 codes + 16 B pad: conflict-free 16-B reads
-constexpr int kActBytes = BM * kActStride;
-constexpr int kXsBytes = BM * 4;
-constexpr int kWBytes = BN * kQ4KBytes;
-constexpr int kLdsBytes = kActBytes + kXsBytes + kWBytes;
+constexpr int kWaves = BN / 32;  // waves side by side along the weight rows
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStages = 2;       // LDS ring: compute b while b+1 lands
+
+// One LDS stage holds one super-block of the tile:
+//  act  BM rows x 256 codes; row m's 16-byte chunk c sits in slot c ^ (m & 15)
+//       (the XOR spreads the 16 rows of an MFMA operand read over all banks);
+//  xs   BM f32 token scales;
+//  w    BN raw 144-byte Q4_K blocks, back to back.
+constexpr int kActBytes = BM * 256;
+constexpr int kXsOff = kActBytes;
+constexpr int kWOff = kXsOff + BM * 4;
+constexpr int kStageBytes = kWOff + BN * kQ4KBytes;
+constexpr int kActInstr = kActBytes / 1024;        // 16 (64-lane x 16-byte loads)
+constexpr int kWInstr = BN * kQ4KBytes / 1024;     // 18 (BN * 9 chunks, 64 per load)
+static_assert(BN * 9 % 64 == 0, "weight chunks fill whole 64-lane loads");
+static_assert(2 * kStages * kStageBytes <= 160 * 1024, "two workgroups' rings exceed 160 KiB");
 
 __device__ __forceinline__ uint32_t mul_bytes(uint32_t nib, uint32_t f) {
   // Each byte of `nib` is 0..15 and f <= 7, so no product crosses its byte.
@@ -54,15 +66,116 @@ __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(kThreads) void gemm_q4k_kernel(float* __restrict__ y,
-                                                            const uint8_t* __restrict__ w,
-                                                            const uint8_t* __restrict__ xq,
-                                                            int M, int N, int nb, int mtiles,
-                                                            int ntiles) {
-  __shared__ __align__(16) uint8_t lds[kLdsBytes];
-  uint8_t* act = lds;
-  float* xs_s = reinterpret_cast<float*>(lds + kActBytes);
-  uint8_t* wblk = lds + kActBytes + kXsBytes;
+// Stage loads per wave: wave w takes act rows 4j..4j+3 for j = w, w+4, w+8,
+// w+12; weight chunks 64j.. for j = w, w+4, w+8, w+12 (and w+16 < 18); wave 3
+// loads the 64 token scales; wave 2 repeats its first act load (same bytes to
+// the same place) so that every wave issues kLoadsPerWave loads per stage and
+// "the previous stage has landed" is the constant wait vmcnt(kLoadsPerWave).
+constexpr int kLoadsPerWave = 9;
+static_assert(kWaves == 4 && kActInstr == 16 && kWInstr == 18 && BM == 64,
+              "the load split below is written for this tile");
+
+// Per-lane byte offsets of this wave's stage loads relative to super-block
+// 0 (xq or w base); super-block b adds b*320 (codes, scales) or b*144
+// (weights). Offsets stay below 2^31 (the entry point refuses larger
+// inputs), so the loads use a scalar base plus a 32-bit lane offset.
+struct StageOffsets {
+  uint32_t act[4];
+  uint32_t wt[4];
+  uint32_t extra;   // fifth weight load, a repeated act load, or token scales
+};
+
+__device__ __forceinline__ StageOffsets stage_offsets(int M, int N, int nb, int m0, int n0,
+                                                      int wave, int lane) {
+  StageOffsets o;
+  auto act_off = [&](int j) {
+    const int m = 4 * j + (lane >> 4);
+    const int c = (lane & 15) ^ (m & 15);      // source chunk of this lane's slot
+    const int gm = min(m0 + m, M - 1);
+    return static_cast<uint32_t>(gm) * static_cast<uint32_t>(nb) * kQ8KBytes + 16u * c;
+  };
+  auto w_off = [&](int j) {
+    const int i = 64 * j + lane;
+    const int n = i / 9, c = i - 9 * (i / 9);
+    const int gn = min(n0 + n, N - 1);
+    return static_cast<uint32_t>(gn) * static_cast<uint32_t>(nb) * kQ4KBytes + 16u * c;
+  };
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o.act[k] = act_off(wave + 4 * k);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o.wt[k] = w_off(wave + 4 * k);
+  if (wave < 2) {
+    o.extra = w_off(wave + 16);
+  } else if (wave == 2) {
+    o.extra = act_off(wave);
+  } else {
+    const int gm = min(m0 + lane, M - 1);
+    o.extra = static_cast<uint32_t>(gm) * static_cast<uint32_t>(nb) * kQ8KBytes + 288u;
+  }
+  return o;
+}
+
+// One direct global -> LDS load (gfx950 global_load_lds_dwordx4 /
+// global_load_lds_dword): lane l's bytes land at LDS address m0 + size*l.
+// Issued as inline assembly so the compiler's wait-count pass does not treat
+// the in-flight refill of one stage as a hazard for reads of the other; the
+// kernel waits for these loads itself (vmcnt) before the barrier that
+// publishes a stage.
+__device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1\n\t"
+      :
+      : "v"(off), "s"(base), "s"(lds_addr)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ void lds_dma4(const uint8_t* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %0, %1\n\t"
+      :
+      : "v"(off), "s"(base), "s"(lds_addr)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+__device__ __forceinline__ void issue_stage(uint8_t* base, const uint8_t* xq, const uint8_t* w,
+                                            const StageOffsets& o, int b, int wave) {
+  const uint32_t xb = static_cast<uint32_t>(b) * kQ8KBytes;
+  const uint32_t wb = static_cast<uint32_t>(b) * kQ4KBytes;
+  // The LDS destination of each load is wave-uniform.
+  const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_u32(base));
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) lds_dma16(xq, o.act[k] + xb, lb + 1024 * (wv + 4 * k));
+#pragma unroll
+  for (int k = 0; k < 4; ++k) lds_dma16(w, o.wt[k] + wb, lb + kWOff + 1024 * (wv + 4 * k));
+  if (wv < 2) {
+    lds_dma16(w, o.extra + wb, lb + kWOff + 1024 * (wv + 16));
+  } else if (wv == 2) {
+    lds_dma16(xq, o.extra + xb, lb + 1024 * wv);
+  } else {
+    lds_dma4(xq, o.extra + xb, lb + kXsOff);
+  }
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4] and lgkmcnt [11:8] left at their maxima, i.e. not waited on).
+constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitVmStage = 0x0F70 | kLoadsPerWave;
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
+                     const uint8_t* __restrict__ xq, int M, int N, int nb, int mtiles,
+                     int ntiles) {
+  __shared__ __align__(16) uint8_t stage0[kStageBytes];
+  __shared__ __align__(16) uint8_t stage1[kStageBytes];
 
   // Workgroup -> tile. When the tile count is a multiple of the 8 XCDs,
   // XCD x (= id % 8) takes a contiguous run of tiles in which the token tiles
@@ -77,9 +190,7 @@ __global__ __launch_bounds__(kThreads) void gemm_q4k_kernel(float* __restrict__ 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 2;        // 0..1: 64-token half
-  const int wn = wave & 3;         // 0..3: 32-row quarter
+  const int wave = tid >> 6;       // 32-row slice of the weight tile
   const int l16 = lane & 15;
   const int q = lane >> 4;         // k-quarter of an MFMA operand: k = 16q..16q+15
 
@@ -89,44 +200,42 @@ __global__ __launch_bounds__(kThreads) void gemm_q4k_kernel(float* __restrict__ 
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
-
   const v4i zero = {0, 0, 0, 0};
 
-  for (int b = 0; b < nb; ++b) {
-    // ---- stage super-block b ----
-    for (int i = tid; i < BM * 16; i += kThreads) {
-      const int m = i >> 4, c = i & 15;
-      const int gm = min(m0 + m, M - 1);
-      const uint8_t* src = xq + (static_cast<int64_t>(gm) * nb + b) * kQ8KBytes;
-      *reinterpret_cast<uint4*>(act + m * kActStride + 16 * c) =
-          *reinterpret_cast<const uint4*>(src + 16 * c);
-    }
-    for (int i = tid; i < BM; i += kThreads) {
-      const int gm = min(m0 + i, M - 1);
-      xs_s[i] = *reinterpret_cast<const float*>(xq + (static_cast<int64_t>(gm) * nb + b) *
-                                                         kQ8KBytes + 288);
-    }
-    for (int i = tid; i < BN * 9; i += kThreads) {
-      const int n = i / 9, c = i % 9;
-      const int gn = min(n0 + n, N - 1);
-      const uint8_t* src = w + (static_cast<int64_t>(gn) * nb + b) * kQ4KBytes;
-      *reinterpret_cast<uint4*>(wblk + n * kQ4KBytes + 16 * c) =
-          *reinterpret_cast<const uint4*>(src + 16 * c);
-    }
-    __syncthreads();
+  const StageOffsets so = stage_offsets(M, N, nb, m0, n0, wave, lane);
+  issue_stage(stage0, xq, w, so, 0, wave);
 
-    // ---- this lane's weight rows: header words ----
-    uint32_t sc_lo[2], sc_hi[2], m_lo[2], m_hi[2];
+  // One super-block: wait for its stage, refill the other stage with
+  // super-block b+1 (every wave finished reading it: it passed the barrier
+  // below, which follows the compute of b-1), then compute from `stg`.
+  auto step = [&](int b, const uint8_t* stg, uint8_t* refill) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    if (b + 1 < nb) issue_stage(refill, xq, w, so, b + 1, wave);
+
+    const uint8_t* act = stg;
+    const float* xs_s = reinterpret_cast<const float*>(stg + kXsOff);
+    const uint8_t* wblk = stg + kWOff;
+
+    // ---- this lane's weight rows: the sub-block scale and min of each
+    // (row, group) for this lane's k-quarter, and the block's d, dmin ----
+    uint32_t scj[2][4], mj[2][4];
     float dn[2], dminn[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const uint8_t* blk = wblk + (32 * wn + 16 * nt + l16) * kQ4KBytes;
+      const uint8_t* blk = wblk + (32 * wave + 16 * nt + l16) * kQ4KBytes;
       const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
       const uint32_t h1 = hdr.y, h2 = hdr.z, h3 = hdr.w;
-      sc_lo[nt] = h1 & 0x3F3F3F3Fu;
-      m_lo[nt] = h2 & 0x3F3F3F3Fu;
-      sc_hi[nt] = (h3 & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);
-      m_hi[nt] = ((h3 >> 4) & 0x0F0F0F0Fu) | ((h2 >> 2) & 0x30303030u);
+      const uint32_t sc_lo = h1 & 0x3F3F3F3Fu;
+      const uint32_t m_lo = h2 & 0x3F3F3F3Fu;
+      const uint32_t sc_hi = (h3 & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);
+      const uint32_t m_hi = ((h3 >> 4) & 0x0F0F0F0Fu) | ((h2 >> 2) & 0x30303030u);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int shift = 8 * (2 * (g & 1) + (q >> 1));
+        scj[nt][g] = (((g < 2) ? sc_lo : sc_hi) >> shift) & 0xFFu;
+        mj[nt][g] = (((g < 2) ? m_lo : m_hi) >> shift) & 0xFFu;
+      }
       dn[nt] = half_bits_to_float(hdr.x & 0xFFFFu);
       dminn[nt] = half_bits_to_float(hdr.x >> 16);
     }
@@ -136,31 +245,27 @@ __global__ __launch_bounds__(kThreads) void gemm_q4k_kernel(float* __restrict__ 
       // A operands: token rows, codes k = 64g + 16q .. +15.
       v4i a[4];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        a[mt] = *reinterpret_cast<const v4i*>(act + (64 * wm + 16 * mt + l16) * kActStride +
-                                              64 * g + 16 * q);
-      // B operands: weight row n, k = 16q..16q+15 of group g. q = 0, 1: low
-      // nibbles of group bytes 0..15 / 16..31 (sub-block 2g); q = 2, 3: high
-      // nibbles of the same bytes (sub-block 2g+1).
-      const int shift = 8 * (2 * (g & 1) + (q >> 1));
+      for (int mt = 0; mt < 4; ++mt) {
+        const int r = 16 * mt + l16;
+        a[mt] = *reinterpret_cast<const v4i*>(act + 256 * r + 16 * ((4 * g + q) ^ (r & 15)));
+      }
+      // B operands (weight row n, k = 16q..16q+15 of group g): q = 0, 1
+      // take the low nibbles of group bytes 0..15 / 16..31 (sub-block 2g),
+      // q = 2, 3 the high nibbles of the same bytes (sub-block 2g+1).
       v4i ba[2], bb[2], bm[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const uint8_t* blk = wblk + (32 * wn + 16 * nt + l16) * kQ4KBytes;
+        const uint8_t* blk = wblk + (32 * wave + 16 * nt + l16) * kQ4KBytes;
         const uint4 raw = *reinterpret_cast<const uint4*>(blk + 16 + 32 * g + 16 * (q & 1));
         const uint32_t hs = (q >> 1) ? 4u : 0u;
-        const uint32_t n0w = (raw.x >> hs) & 0x0F0F0F0Fu, n1w = (raw.y >> hs) & 0x0F0F0F0Fu;
-        const uint32_t n2w = (raw.z >> hs) & 0x0F0F0F0Fu, n3w = (raw.w >> hs) & 0x0F0F0F0Fu;
-        const uint32_t scw = (g < 2) ? sc_lo[nt] : sc_hi[nt];
-        const uint32_t mw = (g < 2) ? m_lo[nt] : m_hi[nt];
-        const uint32_t sc = (scw >> shift) & 0xFFu;
-        const uint32_t mj = (mw >> shift) & 0xFFu;
-        const uint32_t fa = sc >> 3, fb = sc & 7u;
-        ba[nt] = (v4i){(int)mul_bytes(n0w, fa), (int)mul_bytes(n1w, fa), (int)mul_bytes(n2w, fa),
-                       (int)mul_bytes(n3w, fa)};
-        bb[nt] = (v4i){(int)mul_bytes(n0w, fb), (int)mul_bytes(n1w, fb), (int)mul_bytes(n2w, fb),
-                       (int)mul_bytes(n3w, fb)};
-        const int mb = static_cast<int>(__builtin_amdgcn_perm(0u, mj, 0u));
+        const uint32_t c0 = (raw.x >> hs) & 0x0F0F0F0Fu, c1 = (raw.y >> hs) & 0x0F0F0F0Fu;
+        const uint32_t c2 = (raw.z >> hs) & 0x0F0F0F0Fu, c3 = (raw.w >> hs) & 0x0F0F0F0Fu;
+        const uint32_t fa = scj[nt][g] >> 3, fb = scj[nt][g] & 7u;
+        ba[nt] = (v4i){(int)mul_bytes(c0, fa), (int)mul_bytes(c1, fa), (int)mul_bytes(c2, fa),
+                       (int)mul_bytes(c3, fa)};
+        bb[nt] = (v4i){(int)mul_bytes(c0, fb), (int)mul_bytes(c1, fb), (int)mul_bytes(c2, fb),
+                       (int)mul_bytes(c3, fb)};
+        const int mb = static_cast<int>(__builtin_amdgcn_perm(0u, mj[nt][g], 0u));
         bm[nt] = (v4i){mb, mb, mb, mb};
       }
 #pragma unroll
@@ -177,20 +282,25 @@ __global__ __launch_bounds__(kThreads) void gemm_q4k_kernel(float* __restrict__ 
     // C layout of a 16x16 tile: lane holds column l16, rows 4q..4q+3.
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const int mr = 64 * wm + 16 * mt + 4 * q;
+      const int mr = 16 * mt + 4 * q;
       const float x0 = xs_s[mr], x1 = xs_s[mr + 1], x2 = xs_s[mr + 2], x3 = xs_s[mr + 3];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const v4i s = (sa[mt][nt] << 3) + sb[mt][nt];
+        const v4i sv = (sa[mt][nt] << 3) + sb[mt][nt];
         const v4i mm = sm[mt][nt];
         const float d = dn[nt], dm = dminn[nt];
-        acc[mt][nt].x += x0 * (d * static_cast<float>(s.x) - dm * static_cast<float>(mm.x));
-        acc[mt][nt].y += x1 * (d * static_cast<float>(s.y) - dm * static_cast<float>(mm.y));
-        acc[mt][nt].z += x2 * (d * static_cast<float>(s.z) - dm * static_cast<float>(mm.z));
-        acc[mt][nt].w += x3 * (d * static_cast<float>(s.w) - dm * static_cast<float>(mm.w));
+        acc[mt][nt].x += x0 * (d * static_cast<float>(sv.x) - dm * static_cast<float>(mm.x));
+        acc[mt][nt].y += x1 * (d * static_cast<float>(sv.y) - dm * static_cast<float>(mm.y));
+        acc[mt][nt].z += x2 * (d * static_cast<float>(sv.z) - dm * static_cast<float>(mm.z));
+        acc[mt][nt].w += x3 * (d * static_cast<float>(sv.w) - dm * static_cast<float>(mm.w));
       }
     }
-    __syncthreads();
+  };
+
+  // The ring unrolled by two so each stage is a distinct LDS object.
+  for (int b = 0; b < nb; b += 2) {
+    step(b, stage0, stage1);
+    if (b + 1 < nb) step(b + 1, stage1, stage0);
   }
 
   // ---- store ----
@@ -198,8 +308,8 @@ __global__ __launch_bounds__(kThreads) void gemm_q4k_kernel(float* __restrict__ 
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int n = n0 + 32 * wn + 16 * nt + l16;
-      const int mr = m0 + 64 * wm + 16 * mt + 4 * q;
+      const int n = n0 + 32 * wave + 16 * nt + l16;
+      const int mr = m0 + 16 * mt + 4 * q;
       if (n < N) {
         const float v[4] = {acc[mt][nt].x, acc[mt][nt].y, acc[mt][nt].z, acc[mt][nt].w};
 #pragma unroll

@@ -130,8 +130,13 @@ xq_status xq_gemm_q4k_small_m(float* y, const void* w, const void* xq, int64_t M
   if (N < 1 || N > kMaxRows) return fail(XQ_E_SHAPE, "N=%lld outside 1..2^30", (long long)N);
   if (xq_status s = check_k(K, 0)) return s;
   if (K / 256 > kMaxInt) return fail(XQ_E_SHAPE, "K=%lld too large", (long long)K);
-  if (((M + 127) / 128) * ((N + 127) / 128) > kMaxInt)
+  if (((M + 63) / 64) * ((N + 127) / 128) > kMaxInt)
     return fail(XQ_E_SHAPE, "M*N too large for one launch");
+  // The kernel addresses its inputs with 32-bit byte offsets.
+  if (M * (K / 256) * 320 >= (1LL << 31))
+    return fail(XQ_E_SHAPE, "xq of M=%lld rows reaches 2 GiB", (long long)M);
+  if (N * (K / 256) * 144 >= (1LL << 31))
+    return fail(XQ_E_SHAPE, "w of N=%lld rows reaches 2 GiB", (long long)N);
   if (!aligned(y, 4)) return fail(XQ_E_ALIGN, "y not 4-byte aligned");
   if (!aligned(w, 16)) return fail(XQ_E_ALIGN, "w not 16-byte aligned");
   if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");

@@ -95,6 +95,8 @@ def test_gemv_refusals(fn, args, status, text):
     ((A16, A16, A16, 4, 8, 257, None), xq.XQ_E_SHAPE, "K=257"),
     ((A16, A4, A16, 4, 8, 256, None), xq.XQ_E_ALIGN, "w not 16-byte"),
     ((A16, A16, A1, 4, 8, 256, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
+    ((A16, A16, A16, 2 ** 20, 8, 2048, None), xq.XQ_E_SHAPE, "reaches 2 GiB"),
+    ((A16, A16, A16, 4, 2 ** 21, 2048, None), xq.XQ_E_SHAPE, "reaches 2 GiB"),
 ])
 def test_gemm_refusals(args, status, text):
     s, err = _call("xq_gemm_q4k_small_m", *args)
