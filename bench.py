@@ -13,7 +13,8 @@ Printed (one JSON line on stdout):
   roofline       for the dominant kernel (the 14336 x 4096 up mat-vec):
                  algorithmic bytes per launch / its mean duration (1000
                  back-to-back launches on the step's stream, weights rotating,
-                 one HIP event pair around them), against the 8 TB/s HBM peak;
+                 one HIP event pair around them, after WARM_MS of the same
+                 launches), against the 8 TB/s HBM peak;
                  traffic from the committed rocprofv3 counter summary when it
                  matches the current kernel source
   cpu_baseline   the oracle on the host's cores over whole FFN pairs
@@ -44,6 +45,14 @@ COUNTERS = os.path.join(ROOT, "profiles", "gemv_q4k_up_14336x4096_counters.json"
 KERNEL_SRC = os.path.join(ROOT, "quantized_decode_mat_amd", "csrc", "gemv_q4k.hip")
 
 
+# Sustained work before every timed region. After an idle spell (host-side
+# input generation, a synchronize) the device needs some tens of milliseconds
+# of load before its clocks settle: measured on MI355X, 50-launch windows of
+# the 128256 x 4096 IQ4_NL mat-vec fell from 80.6 to 47.5 us over the first
+# ~50 ms after a 2 s idle. Timing from a cold start would measure the ramp.
+WARM_MS = 250.0
+
+
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
@@ -51,8 +60,10 @@ def log(msg):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=2000)
-    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--steps", type=int, default=10000)
+    p.add_argument("--warmup", type=int, default=100,
+                   help="untimed steps before the timed ones; more untimed steps follow "
+                        "until %.0f ms of sustained work have passed" % WARM_MS)
     p.add_argument("--pool-mb", type=int, default=1100,
                    help="size of the cold-weight rotation pool")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -150,13 +161,15 @@ def main():
     # ---- headline: K plain steps ----
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
+    tw = time.perf_counter()
+    nxt = _warm(torch, step, args.warmup)
+    warm_ms = (time.perf_counter() - tw) * 1e3
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(nxt + i)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -168,7 +181,8 @@ def main():
     # ---- per-kernel durations: each kernel of the step launched back to back
     # n_k times on the step's stream (weights still rotating through the
     # pool), one HIP event pair around the loop; mean = elapsed / n_k. This is
-    # what a kernel trace averages, launch gaps aside.
+    # what a kernel trace averages, launch gaps aside. Each loop follows
+    # WARM_MS of the same launches.
     n_k = 1000
     calls = {
         "quantize_x": lambda k: L.xq_quantize_q8k(xq1.data_ptr(), x_d.data_ptr(), 1, UP[1], s),
@@ -190,17 +204,13 @@ def main():
         sink = torch.empty(xq.xq_bench_sink_words(nbytes), dtype=torch.int32, device=dev)
         xq.xq_bench_stream_read(buf, nbytes, sink)
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            L.xq_bench_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), s)
-        b.record(stream)
-        torch.cuda.synchronize()
-        r = nbytes / (a.elapsed_time(b) / reps * 1e-3) / 1e9
+        us = _time_loop(torch, stream, lambda k: L.xq_bench_stream_read(
+            buf.data_ptr(), nbytes, sink.data_ptr(), s), reps)
+        r = nbytes / us / 1e3
         del buf, sink
         return r
 
-    stream_gbps = stream_read(2 << 30, 20)
+    stream_gbps = stream_read(2 << 30, 100)
     log("streaming read, 2 GiB: %.1f GB/s" % stream_gbps)
     # Like-for-like: the probe over the same rotation pool as the up mat-vec,
     # 33 MB per launch, so launch and ramp costs weigh the same.
@@ -262,6 +272,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_ms": round(warm_ms, 1),
         "ms_per_step": round(ms, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -331,10 +342,22 @@ def _pool_copies(t, pool_mb):
     return [t] + [t.clone() for _ in range(n - 1)]
 
 
-def _time_loop(torch, stream, fn, n, warm=20):
-    for i in range(warm):
-        fn(i)
-    torch.cuda.synchronize()
+def _warm(torch, fn, start, ms=WARM_MS):
+    """Call fn(start), fn(start + 1), ... until `ms` of wall time have passed
+    (a synchronize every 32 calls keeps the queue short); return the next index."""
+    i = start
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(32):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= ms:
+            return i
+
+
+def _time_loop(torch, stream, fn, n):
+    warm = _warm(torch, fn, 0)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for i in range(n):

@@ -13,7 +13,17 @@
 // bits of the nibble, and a third perm that takes each byte from the first or
 // the second result by the nibble's bit 3. (A single v_perm_b32 addresses
 // only eight table bytes, so a 16-entry table needs the pair plus the select.)
-// The q8_K activation is staged once per workgroup in LDS.
+//
+// Two kernels:
+//  * rows of up to kResidentUnits units (K <= 8192): a persistent grid. The
+//    workgroup stages the q8_K row in LDS once; every lane then copies the
+//    slice it will need for every row (its block of each unit: 32 codes and
+//    the block's f32 scale) into registers, and the wave walks rows with a
+//    grid stride, the next row's payload (non-temporal: it is read once) and
+//    scales loaded before the current row is reduced. No LDS traffic and no
+//    barrier per row; the activation leaves L2 once per workgroup.
+//  * longer rows: one row per wave, the whole row's loads in flight, the
+//    activation read from the LDS copy per row.
 #include "xq_device.h"
 #include "xq_launch.h"
 
@@ -130,6 +140,115 @@ __global__ __launch_bounds__(kThreads) void gemv_iq4nl_kernel(float* __restrict_
   }
 }
 
+constexpr int kResidentUnits = 4;
+constexpr int kResWaves = 8;
+constexpr int kResThreads = kResWaves * kWave;
+constexpr int kResMaxGroups = 2048;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_nt16(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// U: units per row (1..kResidentUnits). One row per wave per step.
+template <int U>
+__global__ __launch_bounds__(kResThreads) void gemv_iq4nl_resident_kernel(
+    float* __restrict__ y, const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, int N,
+    int bpr, int prefix, int64_t row_bytes, int nq8) {
+  extern __shared__ __align__(16) uint8_t act[];
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(xq);
+    uint4* dst = reinterpret_cast<uint4*>(act);
+    const int n16 = nq8 * (kQ8KBytes / 16);
+    for (int i = threadIdx.x; i < n16; i += kResThreads) dst[i] = src[i];
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int row_first = blockIdx.x * kResWaves + (threadIdx.x >> 6);
+  const int row_step = gridDim.x * kResWaves;
+  if (row_first >= N) return;  // no barrier follows
+
+  // This lane's block of every unit: its codes and q8_K scale stay in
+  // registers for all rows. Lanes past the row's last block repeat the last
+  // block's loads and drop their contribution.
+  uint4 a0[U], a1[U];
+  float xs[U];
+  int cc[U];
+  bool live[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = u * kWave + lane;
+    live[u] = c < bpr;
+    cc[u] = min(c, bpr - 1);
+    const uint8_t* xb = act + (cc[u] >> 3) * kQ8KBytes;
+    a0[u] = *reinterpret_cast<const uint4*>(xb + (cc[u] & 7) * 32);
+    a1[u] = *reinterpret_cast<const uint4*>(xb + (cc[u] & 7) * 32 + 16);
+    xs[u] = *reinterpret_cast<const float*>(xb + 288);
+  }
+
+  uint4 pa[U], pb[U];
+  uint32_t da[U], db[U];
+  auto load_row = [&](uint4 (&p)[U], uint32_t (&d)[U], int row) {
+    const uint8_t* wr = w + static_cast<int64_t>(row) * row_bytes;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      p[u] = load_nt16(wr + prefix + 16 * cc[u]);
+      d[u] = *reinterpret_cast<const uint16_t*>(wr + 2 * cc[u]);
+    }
+  };
+  auto reduce_row = [&](const uint4 (&p)[U], const uint32_t (&d)[U], int row) {
+    float acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int dot = sdot4(lut4(p[u].x), a0[u].x, 0);
+      dot = sdot4(lut4(p[u].y), a0[u].y, dot);
+      dot = sdot4(lut4(p[u].z), a0[u].z, dot);
+      dot = sdot4(lut4(p[u].w), a0[u].w, dot);
+      dot = sdot4(lut4(p[u].x >> 4), a1[u].x, dot);
+      dot = sdot4(lut4(p[u].y >> 4), a1[u].y, dot);
+      dot = sdot4(lut4(p[u].z >> 4), a1[u].z, dot);
+      dot = sdot4(lut4(p[u].w >> 4), a1[u].w, dot);
+      const float v = (half_bits_to_float(d[u]) * xs[u]) * static_cast<float>(dot);
+      acc += live[u] ? v : 0.0f;
+    }
+    const float tot = wave_sum(acc);
+    if (lane == 0) y[row] = tot;
+  };
+
+  // Two register sets, the loop unrolled by two so that no copy stands
+  // between a row's loads and its use. The row after the last is replaced
+  // by a reload of the last (an L2 hit) so every load is unconditional.
+  int r0 = row_first;
+  load_row(pa, da, r0);
+  while (true) {
+    const int r1 = r0 + row_step;
+    const bool more1 = r1 < N;
+    load_row(pb, db, more1 ? r1 : r0);
+    reduce_row(pa, da, r0);
+    if (!more1) break;
+    const int r2 = r1 + row_step;
+    const bool more2 = r2 < N;
+    load_row(pa, da, more2 ? r2 : r1);
+    reduce_row(pb, db, r1);
+    if (!more2) break;
+    r0 = r2;
+  }
+}
+
+template <int U>
+hipError_t launch_resident(float* y, const uint8_t* w, const uint8_t* xq, int N, int bpr,
+                           int prefix, int64_t row_bytes, int nq8, hipStream_t stream) {
+  int grid = (N + kResWaves - 1) / kResWaves;
+  if (grid > kResMaxGroups) grid = kResMaxGroups;
+  const size_t lds = static_cast<size_t>(nq8) * kQ8KBytes;
+  hipLaunchKernelGGL((gemv_iq4nl_resident_kernel<U>), dim3(grid), dim3(kResThreads), lds, stream,
+                     y, w, xq, N, bpr, prefix, row_bytes, nq8);
+  return hipGetLastError();
+}
+
 template <int R, int PF>
 hipError_t launch_rpf(float* y, const uint8_t* w, const uint8_t* xq, int N, int bpr, int prefix,
                       int64_t row_bytes, int nq8, hipStream_t stream) {
@@ -169,6 +288,16 @@ hipError_t launch_gemv_iq4nl(float* y, const void* w, const void* xq, int64_t N,
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   const uint8_t* xb = static_cast<const uint8_t*>(xq);
   const int n = static_cast<int>(N);
+  // Launch shapes chosen by measurement on MI355X (cold weights; 128256 x
+  // 4096: 76.4 us with one row-pair per wave and the activation read from LDS
+  // per row, 47.5 us resident).
+  switch (units) {
+    case 1: return launch_resident<1>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, stream);
+    case 2: return launch_resident<2>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, stream);
+    case 3: return launch_resident<3>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, stream);
+    case 4: return launch_resident<4>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, stream);
+    default: break;
+  }
   if (units <= 2 && N >= 8192)
     return launch_r<2>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, pf, stream);
   return launch_r<1>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, pf, stream);

@@ -3,18 +3,21 @@
 // bandwidth once per device with a streaming pass well past L2).
 //
 // Every 16-byte chunk of the buffer is read exactly once with a 16-byte
-// non-temporal load (the data is used once); a workgroup's chunks are folded
-// into one word so no load is dead. Four loads per lane are in flight per
-// loop trip, two workgroups per CU: the fastest of the grid sizes, unroll
-// depths and load kinds measured on MI355X for a 2 GiB read.
+// non-temporal load (the data is used once), all of them issued at once: one
+// workgroup of 512 lanes per 16 KiB, two loads per lane, no loop. This was the
+// fastest shape measured on MI355X at 33 MB and at 295 MB (against looping
+// grids of 512 workgroups, more or fewer loads per lane, 256 or 1024 lanes,
+// and plain loads), so the ceiling it reports holds at the mat-vecs' own
+// sizes. A workgroup's chunks are folded into one word so no load is dead.
 #include "xq_device.h"
 #include "xq_launch.h"
 
 namespace xq {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kGrid = 256 * 2;  // two workgroups per CU
+constexpr int kThreads = 512;
+constexpr int kLoads = 2;  // 16-byte loads per lane
+constexpr int64_t kChunksPerGroup = static_cast<int64_t>(kThreads) * kLoads;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -26,31 +29,30 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __re
                                                                int64_t n16,
                                                                uint32_t* __restrict__ sink) {
   __shared__ uint32_t part[kThreads / kWave];
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = ldnt(buf + i), b = ldnt(buf + i + stride), c = ldnt(buf + i + 2 * stride),
-                d = ldnt(buf + i + 3 * stride);
-    acc ^= (a.x ^ a.y ^ a.z ^ a.w) + (b.x ^ b.y ^ b.z ^ b.w) + (c.x ^ c.y ^ c.z ^ c.w) +
-           (d.x ^ d.y ^ d.z ^ d.w);
-  }
-  for (; i < n16; i += stride) {
-    const u32x4 a = ldnt(buf + i);
-    acc ^= a.x ^ a.y ^ a.z ^ a.w;
-  }
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kChunksPerGroup + threadIdx.x;
+  const int64_t i1 = i0 + kThreads;
+  // The last workgroup may pass the end: its extra lanes re-read the last
+  // chunk and drop it.
+  const u32x4 a = ldnt(buf + (i0 < n16 ? i0 : n16 - 1));
+  const u32x4 b = ldnt(buf + (i1 < n16 ? i1 : n16 - 1));
+  uint32_t acc = (i0 < n16 ? (a.x ^ a.y ^ a.z ^ a.w) : 0u) + (i1 < n16 ? (b.x ^ b.y ^ b.z ^ b.w) : 0u);
   const float f = wave_sum(static_cast<float>(acc & 0xFFFF));
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = __builtin_bit_cast(uint32_t, f);
   __syncthreads();
-  if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int k = 0; k < kThreads / kWave; ++k) r ^= part[k];
+    sink[blockIdx.x] = r;
+  }
 }
 
 }  // namespace
 
 int64_t stream_read_sink_words(int64_t bytes) {
   const int64_t n16 = bytes / 16;
-  const int64_t need = (n16 + kThreads - 1) / kThreads;
-  return need < kGrid ? (need < 1 ? 1 : need) : kGrid;
+  const int64_t groups = (n16 + kChunksPerGroup - 1) / kChunksPerGroup;
+  return groups < 1 ? 1 : groups;
 }
 
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink,

@@ -248,6 +248,9 @@ IQ4_SHAPES = [
     ("n1000_k2304", 1000, 2304, 5003),
     ("n8193_k2048_tworow", 8193, 2048, 5004),
     ("n16_k14336", 16, 14336, 5005),
+    ("n300_k8192_four_units", 300, 8192, 5006),
+    ("n70_k10240_five_units", 70, 10240, 5007),
+    ("n20000_k512_two_rows_per_wave", 20000, 512, 5008),
 ]
 
 
@@ -344,9 +347,30 @@ def test_gemm_partials_bit_exact(which):
             assert np.array_equal(got[m], want.astype(np.float64)), (m, b)
 
 
-def test_stream_read_probe_runs():
-    nbytes = 1 << 24
-    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+def _stream_fold_model(words: np.ndarray) -> np.ndarray:
+    """Host model of the streaming probe's fold: 512 lanes per workgroup, lane t
+    reads 16-byte chunks g*1024+t and g*1024+512+t (chunks past the end count
+    zero), xors each chunk's four words, adds the two (mod 2^32), and the
+    workgroup stores the xor of its eight wave sums of (acc & 0xFFFF) as f32 bits."""
+    n16 = words.size // 4
+    chunk = np.bitwise_xor.reduce(words.reshape(n16, 4).astype(np.uint32), axis=1)
+    groups = (n16 + 1023) // 1024
+    padded = np.zeros(groups * 1024, dtype=np.uint32)
+    padded[:n16] = chunk
+    per = padded.reshape(groups, 2, 512)
+    acc = (per[:, 0, :].astype(np.uint64) + per[:, 1, :]) & 0xFFFFFFFF
+    lo = (acc & 0xFFFF).astype(np.float64).reshape(groups, 8, 64).sum(axis=2)
+    bits = lo.astype(np.float32).view(np.uint32)
+    return np.bitwise_xor.reduce(bits, axis=1).view(np.int32)
+
+
+@pytest.mark.parametrize("nbytes", [1 << 24, (1 << 20) + 16 * 777])
+def test_stream_read_probe_reads_every_chunk(nbytes):
+    g = wl.rng(9100 + nbytes % 1000)
+    words = g.integers(0, 2**32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).to("cuda")
     sink = torch.zeros(xq.xq_bench_sink_words(nbytes), dtype=torch.int32, device="cuda")
+    _note("stream_read probe nbytes=%d" % nbytes)
     xq.xq_bench_stream_read(buf, nbytes, sink)
     torch.cuda.synchronize()
+    assert np.array_equal(sink.cpu().numpy(), _stream_fold_model(words))
