@@ -7,20 +7,12 @@
 //
 // One wave per 256-block, four blocks per 256-thread workgroup. Lane l holds
 // elements 4l..4l+3 (one 16-byte load), so the block's 1 KiB is read by one
-// coalesced wave load. The scale is amax/127 and each code x/d, both as IEEE
-// f32 divisions (HIP's default division is correctly rounded; nothing here is
-// built with fast-math), rounded to nearest-even by v_rndne_f32.
-#include "xq_device.h"
+// coalesced wave load; the block arithmetic is q8k_block_wave.
+#include "q8k_block.h"
 #include "xq_launch.h"
 
 namespace xq {
 namespace {
-
-__device__ __forceinline__ int code_of(float x, float d) {
-  float r = rintf(x / d);
-  r = fminf(fmaxf(r, -127.0f), 127.0f);  // never active: |x/d| <= 127*(1+2^-23)
-  return static_cast<int>(r);
-}
 
 __global__ __launch_bounds__(256) void q8k_quantize_kernel(uint8_t* __restrict__ xq,
                                                            const float* __restrict__ x,
@@ -30,28 +22,7 @@ __global__ __launch_bounds__(256) void q8k_quantize_kernel(uint8_t* __restrict__
   if (blk >= nblocks) return;  // wave-uniform: no cross-wave sync follows
 
   const float4 v = *reinterpret_cast<const float4*>(x + blk * 256 + lane * 4);
-  const float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  const float amax = wave_max(a);
-  const float d = amax / 127.0f;
-
-  int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-  if (d != 0.0f) {
-    q0 = code_of(v.x, d);
-    q1 = code_of(v.y, d);
-    q2 = code_of(v.z, d);
-    q3 = code_of(v.w, d);
-  }
-  const uint32_t packed = (static_cast<uint32_t>(q0) & 0xFFu) |
-                          ((static_cast<uint32_t>(q1) & 0xFFu) << 8) |
-                          ((static_cast<uint32_t>(q2) & 0xFFu) << 16) |
-                          ((static_cast<uint32_t>(q3) & 0xFFu) << 24);
-  const int s = lane8_sum(q0 + q1 + q2 + q3);  // lanes 8j..8j+7 hold codes 32j..32j+31
-
-  uint8_t* out = xq + blk * kQ8KBytes;
-  reinterpret_cast<uint32_t*>(out)[lane] = packed;
-  if ((lane & 7) == 0) reinterpret_cast<int32_t*>(out + 256)[lane >> 3] = s;
-  if (lane == 0) *reinterpret_cast<float*>(out + 288) = d;
-  if (lane >= 1 && lane < 8) reinterpret_cast<uint32_t*>(out + 288)[lane] = 0u;  // 292..319
+  q8k_block_wave(v, xq + blk * kQ8KBytes, lane);
 }
 
 }  // namespace
