@@ -421,6 +421,44 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
         del ws, w
         torch.cuda.empty_cache()
 
+    # Expert-grouped mat-vecs: one launch over a bank of small experts against
+    # the per-expert dense launches it replaces (the pages' grouped dispatch,
+    # "25 — Writing XPU Kernels", section 25.2.2). Slabs rotate through the pool.
+    E, rows, K, ids = 64, 1408, 2048, [3, 17, 25, 40, 41, 50, 58, 63]
+    used = len(ids)
+    for name, wfn, nbytes, grouped, dense in (
+            ("q4k_id_E64_r1408_k2048_used8", wl.q4k_weights, xq.xq_q4k_bytes,
+             L.xq_gemv_q4k_id, L.xq_gemv_q4k),
+            ("iq4nl_id_E64_r1408_k2048_used8", wl.iq4nl_weights, xq.xq_iq4nl_bytes,
+             L.xq_gemv_iq4nl_id, L.xq_gemv_iq4nl)):
+        g = wl.rng(wl.SEEDS["q4k_4096"] + 77)
+        slab = torch.from_numpy(np.concatenate(
+            [wfn(rows, K, g).reshape(rows, -1) for _ in range(E)], axis=0).reshape(-1)).to(dev)
+        xv = torch.from_numpy(wl.activations(1, K, g).reshape(-1)).to(dev)
+        xqb = torch.empty(xq.xq_q8k_bytes(1, K), dtype=torch.uint8, device=dev)
+        xq.xq_quantize_q8k(xqb, xv, 1, K)
+        sel = torch.tensor(ids, dtype=torch.int32, device=dev)
+        slabs = _pool_copies(slab, args.pool_mb)
+        yy = torch.empty(used * rows, dtype=torch.float32, device=dev)
+        rb = nbytes(1, K)
+        us = _time_loop(torch, stream, lambda i: grouped(
+            yy.data_ptr(), slabs[i % len(slabs)].data_ptr(), xqb.data_ptr(), sel.data_ptr(),
+            E, used, rows, K, 0, s), 1000)
+
+        def dense_all(i):
+            base = slabs[i % len(slabs)].data_ptr()
+            for kk, e in enumerate(ids):
+                dense(yy.data_ptr() + 4 * kk * rows, base + e * rows * rb, xqb.data_ptr(),
+                      rows, K, s)
+
+        dus = _time_loop(torch, stream, dense_all, 300)
+        wb = used * rows * rb
+        emit({"workload": name, "us": round(us, 3), "weight_GBps": round(wb / us / 1e3, 1),
+              "frac_of_stream_read": round(wb / us / 1e3 / stream_gbps, 4),
+              "dense_launches_us": round(dus, 3), "speedup_vs_dense": round(dus / us, 3)})
+        del slabs, slab
+        torch.cuda.empty_cache()
+
     # Small-M prefill product.
     M, (N, K) = 512, UP
     g = wl.rng(wl.SEEDS["prefill"])

@@ -138,6 +138,34 @@ const char *xq_status_name(xq_status s);
 const char *xq_last_error(void);
 
 /*
+ * Expert-grouped mat-vecs ("25 — Writing XPU Kernels", section 25.2.2: one
+ * launch over a bank of experts, the dot loop of the dense kernel unchanged;
+ * the expert is picked on the device through a selection buffer, nothing is
+ * read back). For each selection slot kk in 0..used-1 and row r in
+ * 0..rows-1:
+ *   y[kk*rows + r] = row (sel[kk]*rows + r) of `slab` . activation kk
+ * where activation kk is the q8_K row starting x_stride_blocks*kk blocks into
+ * `xq` (x_stride_blocks = 0: every slot reads the one token, as in decode;
+ * = K/256: slot kk reads row kk of a [used][K/256] q8_K tensor).
+ *  slab  [n_experts][rows] rows of the format (Q4_K: [.][K/256] blocks of
+ *        144 B; IQ4_NL: resident rows), experts back to back, 16-byte aligned.
+ *  sel   device int32[used], 4-byte aligned. A value outside
+ *        0..n_experts-1 makes that slot's `rows` outputs NaN (nothing is
+ *        read for it); the other slots are unaffected.
+ *  y     f32[used][rows], slot-major.
+ *  1 <= used <= 65535, 1 <= rows, n_experts*rows <= 2^30, K as for the
+ *  dense entry point, x_stride_blocks in {0, K/256}.
+ * Each slot's outputs are bit-identical to the dense entry point (xq_gemv_q4k
+ * or xq_gemv_iq4nl) on that expert's rows and that activation.
+ */
+xq_status xq_gemv_q4k_id(float *y, const void *slab, const void *xq, const int32_t *sel,
+                         int64_t n_experts, int64_t used, int64_t rows, int64_t K,
+                         int64_t x_stride_blocks, void *stream);
+xq_status xq_gemv_iq4nl_id(float *y, const void *slab, const void *xq, const int32_t *sel,
+                           int64_t n_experts, int64_t used, int64_t rows, int64_t K,
+                           int64_t x_stride_blocks, void *stream);
+
+/*
  * Measurement helper, not part of the method: read `bytes` of device memory
  * once with 16-byte loads and fold them into one word per workgroup of
  * `sink` (sink must hold xq_bench_sink_words(bytes) uint32). Its duration

@@ -27,7 +27,7 @@ XQ_MAX_K = 49152
 EXPORTS = (
     "xq_quantize_q8k", "xq_gemv_q4k", "xq_gemv_iq4nl", "xq_gemm_q4k_small_m",
     "xq_q8k_bytes", "xq_q4k_bytes", "xq_iq4nl_bytes", "xq_status_name", "xq_last_error",
-    "xq_bench_stream_read", "xq_bench_sink_words",
+    "xq_bench_stream_read", "xq_bench_sink_words", "xq_gemv_q4k_id", "xq_gemv_iq4nl_id",
 )
 
 
@@ -52,8 +52,10 @@ def lib() -> ctypes.CDLL:
             L.xq_gemv_iq4nl.argtypes = [P, P, P, I, I, P]
             L.xq_gemm_q4k_small_m.argtypes = [P, P, P, I, I, I, P]
             L.xq_bench_stream_read.argtypes = [P, I, P, P]
+            L.xq_gemv_q4k_id.argtypes = [P, P, P, P, I, I, I, I, I, P]
+            L.xq_gemv_iq4nl_id.argtypes = [P, P, P, P, I, I, I, I, I, P]
             for f in ("xq_quantize_q8k", "xq_gemv_q4k", "xq_gemv_iq4nl", "xq_gemm_q4k_small_m",
-                      "xq_bench_stream_read"):
+                      "xq_bench_stream_read", "xq_gemv_q4k_id", "xq_gemv_iq4nl_id"):
                 getattr(L, f).restype = S
             for f in ("xq_q8k_bytes", "xq_q4k_bytes", "xq_iq4nl_bytes"):
                 getattr(L, f).argtypes = [I, I]
@@ -139,6 +141,27 @@ def xq_gemv_iq4nl(y, w, xq, N: int, K: int, stream=None) -> None:
     _check(lib().xq_gemv_iq4nl(_ptr(y, 4 * N, "y"), _ptr(w, xq_iq4nl_bytes(N, K), "w"),
                                _ptr(xq, xq_q8k_bytes(1, K), "xq"), N, K, _stream(stream)),
            "xq_gemv_iq4nl")
+
+
+def xq_gemv_q4k_id(y, slab, xq, sel, n_experts: int, used: int, rows: int, K: int,
+                   x_stride_blocks: int = 0, stream=None) -> None:
+    xrows = used if x_stride_blocks else 1
+    _check(lib().xq_gemv_q4k_id(_ptr(y, 4 * used * rows, "y"),
+                                _ptr(slab, xq_q4k_bytes(n_experts * rows, K), "slab"),
+                                _ptr(xq, xq_q8k_bytes(xrows, K), "xq"), _ptr(sel, 4 * used, "sel"),
+                                n_experts, used, rows, K, x_stride_blocks, _stream(stream)),
+           "xq_gemv_q4k_id")
+
+
+def xq_gemv_iq4nl_id(y, slab, xq, sel, n_experts: int, used: int, rows: int, K: int,
+                     x_stride_blocks: int = 0, stream=None) -> None:
+    xrows = used if x_stride_blocks else 1
+    _check(lib().xq_gemv_iq4nl_id(_ptr(y, 4 * used * rows, "y"),
+                                  _ptr(slab, xq_iq4nl_bytes(n_experts * rows, K), "slab"),
+                                  _ptr(xq, xq_q8k_bytes(xrows, K), "xq"),
+                                  _ptr(sel, 4 * used, "sel"), n_experts, used, rows, K,
+                                  x_stride_blocks, _stream(stream)),
+           "xq_gemv_iq4nl_id")
 
 
 def xq_gemm_q4k_small_m(y, w, xq, M: int, N: int, K: int, stream=None) -> None:

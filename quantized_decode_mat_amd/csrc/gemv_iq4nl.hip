@@ -22,8 +22,8 @@
 //    grid stride, the next row's payload (non-temporal: it is read once) and
 //    scales loaded before the current row is reduced. No LDS traffic and no
 //    barrier per row; the activation leaves L2 once per workgroup.
-//  * longer rows: one row per wave, the whole row's loads in flight, the
-//    activation read from the LDS copy per row.
+//  * longer rows: one row per wave, up to eight units of loads in flight,
+//    the activation read from the LDS copy per row.
 #include "xq_device.h"
 #include "xq_launch.h"
 
@@ -75,17 +75,54 @@ __device__ __forceinline__ float block_partial(const uint4 pay, uint32_t dbits,
   return (d * xs) * static_cast<float>(dot);
 }
 
-template <int R, int PF>
+// Expert-grouped launches (ID): blockIdx.y is the selection slot kk; the
+// workgroup reads sel[kk] once and works on expert sel[kk]'s N rows of the
+// slab, the activation kk * x_stride bytes into xq, and output rows kk * N ..
+// kk * N + N - 1. A selection outside 0..n_experts-1 writes NaN to the slot's
+// rows and reads nothing. The rows then run the dense code unchanged, so the
+// result is bit-identical to a dense launch on the expert's rows.
+struct IdArgs {
+  const int32_t* sel;  // device selection buffer (null: dense launch)
+  int used;            // selection slots (grid.y)
+  int n_experts;       // experts in the slab
+  int64_t x_stride;    // bytes between the slots' activations (0: shared)
+};
+
+// Applies the slot's offsets; false when the selection is out of range
+// (the slot's rows row0 .. row0 + nrows - 1 have been set to NaN).
+template <bool ID, typename YPtr, typename BPtr>
+__device__ __forceinline__ bool select_slot(YPtr& y, BPtr& w, BPtr& xq, int N, int64_t row_bytes,
+                                            const IdArgs& id, int lane, int row0, int nrows,
+                                            int row_step) {
+  if constexpr (ID) {
+    const int kk = blockIdx.y;
+    const int e = id.sel[kk];
+    y += static_cast<int64_t>(kk) * N;
+    if (e < 0 || e >= id.n_experts) {
+      for (int r = row0; r < N && nrows > 0; r += row_step, --nrows)
+        if (lane == 0) y[r] = __builtin_nanf("");
+      return false;
+    }
+    w += static_cast<int64_t>(e) * N * row_bytes;
+    xq += static_cast<int64_t>(kk) * id.x_stride;
+  }
+  return true;
+}
+
+template <int R, int PF, bool ID>
 __global__ __launch_bounds__(kThreads) void gemv_iq4nl_kernel(float* __restrict__ y,
                                                               const uint8_t* __restrict__ w,
                                                               const uint8_t* __restrict__ xq,
                                                               int N, int bpr, int prefix,
-                                                              int64_t row_bytes, int nq8) {
+                                                              int64_t row_bytes, int nq8,
+                                                              IdArgs id) {
   extern __shared__ __align__(16) uint8_t act[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * kWavesPerGroup + wave) * R;
   const int units = (bpr + kWave - 1) / kWave;
+  // Workgroup-uniform: no barrier is skipped.
+  if (!select_slot<ID>(y, w, xq, N, row_bytes, id, lane, row0, R, 1)) return;
 
   uint4 pay[R][PF];
   uint32_t dsc[R][PF];
@@ -153,11 +190,16 @@ __device__ __forceinline__ uint4 load_nt16(const uint8_t* p) {
 }
 
 // U: units per row (1..kResidentUnits). One row per wave per step.
-template <int U>
+template <int U, bool ID>
 __global__ __launch_bounds__(kResThreads) void gemv_iq4nl_resident_kernel(
     float* __restrict__ y, const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, int N,
-    int bpr, int prefix, int64_t row_bytes, int nq8) {
+    int bpr, int prefix, int64_t row_bytes, int nq8, IdArgs id) {
   extern __shared__ __align__(16) uint8_t act[];
+  // Workgroup-uniform: no barrier is skipped.
+  if (!select_slot<ID>(y, w, xq, N, row_bytes, id, threadIdx.x & (kWave - 1),
+                       blockIdx.x * kResWaves + (threadIdx.x >> 6), 1 << 30,
+                       gridDim.x * kResWaves))
+    return;
   {
     const uint4* src = reinterpret_cast<const uint4*>(xq);
     uint4* dst = reinterpret_cast<uint4*>(act);
@@ -240,51 +282,43 @@ __global__ __launch_bounds__(kResThreads) void gemv_iq4nl_resident_kernel(
 
 template <int U>
 hipError_t launch_resident(float* y, const uint8_t* w, const uint8_t* xq, int N, int bpr,
-                           int prefix, int64_t row_bytes, int nq8, hipStream_t stream) {
+                           int prefix, int64_t row_bytes, int nq8, const IdArgs& id,
+                           hipStream_t stream) {
   int grid = (N + kResWaves - 1) / kResWaves;
   if (grid > kResMaxGroups) grid = kResMaxGroups;
   const size_t lds = static_cast<size_t>(nq8) * kQ8KBytes;
-  hipLaunchKernelGGL((gemv_iq4nl_resident_kernel<U>), dim3(grid), dim3(kResThreads), lds, stream,
-                     y, w, xq, N, bpr, prefix, row_bytes, nq8);
+  if (id.sel)
+    hipLaunchKernelGGL((gemv_iq4nl_resident_kernel<U, true>), dim3(grid, id.used),
+                       dim3(kResThreads), lds, stream, y, w, xq, N, bpr, prefix, row_bytes, nq8,
+                       id);
+  else
+    hipLaunchKernelGGL((gemv_iq4nl_resident_kernel<U, false>), dim3(grid), dim3(kResThreads),
+                       lds, stream, y, w, xq, N, bpr, prefix, row_bytes, nq8, id);
   return hipGetLastError();
 }
 
-template <int R, int PF>
-hipError_t launch_rpf(float* y, const uint8_t* w, const uint8_t* xq, int N, int bpr, int prefix,
-                      int64_t row_bytes, int nq8, hipStream_t stream) {
-  const int waves = (N + R - 1) / R;
-  const int grid = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+template <int PF>
+hipError_t launch_staged(float* y, const uint8_t* w, const uint8_t* xq, int N, int bpr, int prefix,
+                         int64_t row_bytes, int nq8, const IdArgs& id, hipStream_t stream) {
+  const int grid = (N + kWavesPerGroup - 1) / kWavesPerGroup;
   const size_t lds = static_cast<size_t>(nq8) * kQ8KBytes;
-  hipLaunchKernelGGL((gemv_iq4nl_kernel<R, PF>), dim3(grid), dim3(kThreads), lds, stream, y, w,
-                     xq, N, bpr, prefix, row_bytes, nq8);
+  if (id.sel)
+    hipLaunchKernelGGL((gemv_iq4nl_kernel<1, PF, true>), dim3(grid, id.used), dim3(kThreads), lds,
+                       stream, y, w, xq, N, bpr, prefix, row_bytes, nq8, id);
+  else
+    hipLaunchKernelGGL((gemv_iq4nl_kernel<1, PF, false>), dim3(grid), dim3(kThreads), lds, stream,
+                       y, w, xq, N, bpr, prefix, row_bytes, nq8, id);
   return hipGetLastError();
 }
 
-template <int R>
-hipError_t launch_r(float* y, const uint8_t* w, const uint8_t* xq, int N, int bpr, int prefix,
-                    int64_t row_bytes, int nq8, int pf, hipStream_t stream) {
-  switch (pf) {
-    case 1: return launch_rpf<R, 1>(y, w, xq, N, bpr, prefix, row_bytes, nq8, stream);
-    case 2: return launch_rpf<R, 2>(y, w, xq, N, bpr, prefix, row_bytes, nq8, stream);
-    case 3: return launch_rpf<R, 3>(y, w, xq, N, bpr, prefix, row_bytes, nq8, stream);
-    case 4: return launch_rpf<R, 4>(y, w, xq, N, bpr, prefix, row_bytes, nq8, stream);
-    case 5: return launch_rpf<R, 5>(y, w, xq, N, bpr, prefix, row_bytes, nq8, stream);
-    case 6: return launch_rpf<R, 6>(y, w, xq, N, bpr, prefix, row_bytes, nq8, stream);
-    case 7: return launch_rpf<R, 7>(y, w, xq, N, bpr, prefix, row_bytes, nq8, stream);
-    default: return launch_rpf<R, 8>(y, w, xq, N, bpr, prefix, row_bytes, nq8, stream);
-  }
-}
-
-}  // namespace
-
-hipError_t launch_gemv_iq4nl(float* y, const void* w, const void* xq, int64_t N, int64_t K,
-                             hipStream_t stream) {
+// Dense (id.sel null) or expert-grouped launch of N rows per slot.
+hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64_t K,
+                       const IdArgs& id, hipStream_t stream) {
   const int bpr = static_cast<int>(K / 32);
   const int prefix = ((bpr * 2 + 3) / 4) * 4;
   const int64_t row_bytes = prefix + 16 * static_cast<int64_t>(bpr);
   const int nq8 = static_cast<int>(K / 256);
   const int units = (bpr + kWave - 1) / kWave;
-  const int pf = units < 8 ? units : 8;
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   const uint8_t* xb = static_cast<const uint8_t*>(xq);
   const int n = static_cast<int>(N);
@@ -292,15 +326,30 @@ hipError_t launch_gemv_iq4nl(float* y, const void* w, const void* xq, int64_t N,
   // 4096: 76.4 us with one row-pair per wave and the activation read from LDS
   // per row, 47.5 us resident).
   switch (units) {
-    case 1: return launch_resident<1>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, stream);
-    case 2: return launch_resident<2>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, stream);
-    case 3: return launch_resident<3>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, stream);
-    case 4: return launch_resident<4>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, stream);
-    default: break;
+    case 1: return launch_resident<1>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    case 2: return launch_resident<2>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    case 3: return launch_resident<3>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    case 4: return launch_resident<4>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    case 5: return launch_staged<5>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    case 6: return launch_staged<6>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    case 7: return launch_staged<7>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    default: return launch_staged<8>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
   }
-  if (units <= 2 && N >= 8192)
-    return launch_r<2>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, pf, stream);
-  return launch_r<1>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, pf, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_iq4nl(float* y, const void* w, const void* xq, int64_t N, int64_t K,
+                             hipStream_t stream) {
+  return launch_rows(y, w, xq, N, K, IdArgs{nullptr, 1, 0, 0}, stream);
+}
+
+hipError_t launch_gemv_iq4nl_id(float* y, const void* slab, const void* xq, const int32_t* sel,
+                                int64_t n_experts, int64_t used, int64_t rows, int64_t K,
+                                int64_t x_stride_blocks, hipStream_t stream) {
+  const IdArgs id{sel, static_cast<int>(used), static_cast<int>(n_experts),
+                  x_stride_blocks * kQ8KBytes};
+  return launch_rows(y, slab, xq, rows, K, id, stream);
 }
 
 }  // namespace xq

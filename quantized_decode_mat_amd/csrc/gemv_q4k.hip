@@ -62,11 +62,20 @@ __device__ __forceinline__ void act_store(const uint4 (&a)[NA], uint8_t* lds, co
 // block masked), which keeps the loads unconditional so the wait counts
 // stay static; without CLAMP, loads and compute of blocks past the row end
 // are skipped (cheaper when PF does not divide the row's units).
-template <int R, int PF, int W, int NA, bool CLAMP>
+// ID: the expert-grouped form. blockIdx.y is the selection slot kk; the
+// workgroup reads sel[kk] once and works on expert sel[kk]'s N rows of the
+// slab `w`, the activation kk * x_stride bytes into `xq`, and the output rows
+// kk * N .. kk * N + N - 1. A selection outside 0..n_experts-1 writes NaN to
+// the slot's rows and reads nothing. Every row then runs the dense code
+// below unchanged, so the result is bit-identical to a dense launch on the
+// expert's rows.
+template <int R, int PF, int W, int NA, bool CLAMP, bool ID>
 __global__ __launch_bounds__(W * kWave) void gemv_q4k_kernel(float* __restrict__ y,
                                                              const uint8_t* __restrict__ w,
                                                              const uint8_t* __restrict__ xq,
-                                                             int N, int nb) {
+                                                             int N, int nb,
+                                                             const int32_t* __restrict__ sel,
+                                                             int n_experts, int64_t x_stride) {
   extern __shared__ __align__(16) uint8_t act[];
   constexpr int kThreads = W * kWave;
   const int lane = threadIdx.x & (kWave - 1);
@@ -76,6 +85,20 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_kernel(float* __restrict__
   const LaneGeom L = lane_geom(lane);
   const int64_t row_bytes = static_cast<int64_t>(nb) * kQ4KBytes;
   const int n16 = nb * (kQ8KBytes / 16);
+
+  if constexpr (ID) {
+    const int kk = blockIdx.y;
+    const int e = sel[kk];
+    y += static_cast<int64_t>(kk) * N;
+    if (e < 0 || e >= n_experts) {  // workgroup-uniform: no barrier is skipped
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (lane == 0 && row0 + r < N) y[row0 + r] = __builtin_nanf("");
+      return;
+    }
+    w += static_cast<int64_t>(e) * N * row_bytes;
+    xq += static_cast<int64_t>(kk) * x_stride;
+  }
 
   uint4 nib[R][PF];
   uint4 hdr[R][PF];
@@ -134,21 +157,32 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_kernel(float* __restrict__
   }
 }
 
+struct IdArgs {
+  const int32_t* sel;  // device selection buffer (null: dense launch)
+  int used;            // selection slots (grid.y)
+  int n_experts;       // experts in the slab
+  int64_t x_stride;    // bytes between the slots' activations (0: shared)
+};
+
 template <int R, int PF, int W, int NA, bool CLAMP>
 hipError_t launch_cfg(float* y, const uint8_t* w, const uint8_t* xq, int N, int nb,
-                      hipStream_t stream) {
+                      const IdArgs& id, hipStream_t stream) {
   const int waves = (N + R - 1) / R;
   const int grid = (waves + W - 1) / W;
   const size_t lds = static_cast<size_t>(nb) * kQ8KBytes;
-  hipLaunchKernelGGL((gemv_q4k_kernel<R, PF, W, NA, CLAMP>), dim3(grid), dim3(W * kWave), lds,
-                     stream, y, w, xq, N, nb);
+  if (id.sel)
+    hipLaunchKernelGGL((gemv_q4k_kernel<R, PF, W, NA, CLAMP, true>), dim3(grid, id.used),
+                       dim3(W * kWave), lds, stream, y, w, xq, N, nb, id.sel, id.n_experts,
+                       id.x_stride);
+  else
+    hipLaunchKernelGGL((gemv_q4k_kernel<R, PF, W, NA, CLAMP, false>), dim3(grid),
+                       dim3(W * kWave), lds, stream, y, w, xq, N, nb, nullptr, 0, int64_t{0});
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_gemv_q4k(float* y, const void* w, const void* xq, int64_t N, int64_t K,
-                           hipStream_t stream) {
+// Dense (id.sel null) or expert-grouped launch of N rows per slot.
+hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64_t K,
+                       const IdArgs& id, hipStream_t stream) {
   const int nb = static_cast<int>(K / 256);
   const int units = (nb + 7) / 8;
   const uint8_t* wb = static_cast<const uint8_t*>(w);
@@ -160,16 +194,31 @@ hipError_t launch_gemv_q4k(float* y, const void* w, const void* xq, int64_t N, i
   //  * longer rows: batches of four units, eight waves per workgroup (the
   //    activation row is staged half as often), loads past the row skipped.
   if (units == 1) {
-    if (N >= 8192) return launch_cfg<2, 1, 4, 2, true>(y, wb, xb, n, nb, stream);
-    return launch_cfg<1, 1, 4, 2, true>(y, wb, xb, n, nb, stream);
+    if (N >= 8192) return launch_cfg<2, 1, 4, 2, true>(y, wb, xb, n, nb, id, stream);
+    return launch_cfg<1, 1, 4, 2, true>(y, wb, xb, n, nb, id, stream);
   }
   if (units == 2) {
-    if (N >= 8192) return launch_cfg<2, 2, 4, 2, true>(y, wb, xb, n, nb, stream);
-    return launch_cfg<1, 2, 4, 2, true>(y, wb, xb, n, nb, stream);
+    if (N >= 8192) return launch_cfg<2, 2, 4, 2, true>(y, wb, xb, n, nb, id, stream);
+    return launch_cfg<1, 2, 4, 2, true>(y, wb, xb, n, nb, id, stream);
   }
-  if (units == 3) return launch_cfg<1, 3, 8, 2, true>(y, wb, xb, n, nb, stream);
-  if (units == 4) return launch_cfg<1, 4, 8, 3, true>(y, wb, xb, n, nb, stream);
-  return launch_cfg<1, 4, 8, 3, false>(y, wb, xb, n, nb, stream);
+  if (units == 3) return launch_cfg<1, 3, 8, 2, true>(y, wb, xb, n, nb, id, stream);
+  if (units == 4) return launch_cfg<1, 4, 8, 3, true>(y, wb, xb, n, nb, id, stream);
+  return launch_cfg<1, 4, 8, 3, false>(y, wb, xb, n, nb, id, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_q4k(float* y, const void* w, const void* xq, int64_t N, int64_t K,
+                           hipStream_t stream) {
+  return launch_rows(y, w, xq, N, K, IdArgs{nullptr, 1, 0, 0}, stream);
+}
+
+hipError_t launch_gemv_q4k_id(float* y, const void* slab, const void* xq, const int32_t* sel,
+                              int64_t n_experts, int64_t used, int64_t rows, int64_t K,
+                              int64_t x_stride_blocks, hipStream_t stream) {
+  const IdArgs id{sel, static_cast<int>(used), static_cast<int>(n_experts),
+                  x_stride_blocks * kQ8KBytes};
+  return launch_rows(y, slab, xq, rows, K, id, stream);
 }
 
 }  // namespace xq

@@ -121,6 +121,55 @@ xq_status xq_gemv_iq4nl(float* y, const void* w, const void* xq, int64_t N, int6
                   "xq_gemv_iq4nl");
 }
 
+static xq_status check_id(const char* fn, float* y, const void* slab, const void* xq,
+                   const int32_t* sel, int64_t n_experts, int64_t used, int64_t rows, int64_t K,
+                   int64_t x_stride_blocks) {
+  (void)fn;
+  if (!y) return fail(XQ_E_NULL, "y is NULL");
+  if (!slab) return fail(XQ_E_NULL, "slab is NULL");
+  if (!xq) return fail(XQ_E_NULL, "xq is NULL");
+  if (!sel) return fail(XQ_E_NULL, "sel is NULL");
+  if (n_experts < 1) return fail(XQ_E_SHAPE, "n_experts=%lld below 1", (long long)n_experts);
+  if (used < 1 || used > 65535)
+    return fail(XQ_E_SHAPE, "used=%lld outside 1..65535", (long long)used);
+  if (rows < 1 || rows > kMaxRows)
+    return fail(XQ_E_SHAPE, "rows=%lld outside 1..2^30", (long long)rows);
+  if (n_experts > kMaxRows / rows)
+    return fail(XQ_E_SHAPE, "n_experts*rows = %lld*%lld above 2^30", (long long)n_experts,
+                (long long)rows);
+  if (xq_status s = check_k(K, XQ_MAX_K)) return s;
+  if (x_stride_blocks != 0 && x_stride_blocks != K / 256)
+    return fail(XQ_E_SHAPE, "x_stride_blocks=%lld is neither 0 nor K/256=%lld",
+                (long long)x_stride_blocks, (long long)(K / 256));
+  if (!aligned(y, 4)) return fail(XQ_E_ALIGN, "y not 4-byte aligned");
+  if (!aligned(slab, 16)) return fail(XQ_E_ALIGN, "slab not 16-byte aligned");
+  if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");
+  if (!aligned(sel, 4)) return fail(XQ_E_ALIGN, "sel not 4-byte aligned");
+  return check_device();
+}
+
+xq_status xq_gemv_q4k_id(float* y, const void* slab, const void* xq, const int32_t* sel,
+                         int64_t n_experts, int64_t used, int64_t rows, int64_t K,
+                         int64_t x_stride_blocks, void* stream) {
+  if (xq_status s = check_id("xq_gemv_q4k_id", y, slab, xq, sel, n_experts, used, rows, K,
+                             x_stride_blocks))
+    return s;
+  return launched(xq::launch_gemv_q4k_id(y, slab, xq, sel, n_experts, used, rows, K,
+                                         x_stride_blocks, static_cast<hipStream_t>(stream)),
+                  "xq_gemv_q4k_id");
+}
+
+xq_status xq_gemv_iq4nl_id(float* y, const void* slab, const void* xq, const int32_t* sel,
+                           int64_t n_experts, int64_t used, int64_t rows, int64_t K,
+                           int64_t x_stride_blocks, void* stream) {
+  if (xq_status s = check_id("xq_gemv_iq4nl_id", y, slab, xq, sel, n_experts, used, rows, K,
+                             x_stride_blocks))
+    return s;
+  return launched(xq::launch_gemv_iq4nl_id(y, slab, xq, sel, n_experts, used, rows, K,
+                                           x_stride_blocks, static_cast<hipStream_t>(stream)),
+                  "xq_gemv_iq4nl_id");
+}
+
 xq_status xq_gemm_q4k_small_m(float* y, const void* w, const void* xq, int64_t M, int64_t N,
                               int64_t K, void* stream) {
   if (!y) return fail(XQ_E_NULL, "y is NULL");

@@ -13,6 +13,15 @@ hipError_t launch_gemv_q4k(float* y, const void* w, const void* xq, int64_t N, i
                            hipStream_t stream);
 hipError_t launch_gemv_iq4nl(float* y, const void* w, const void* xq, int64_t N, int64_t K,
                              hipStream_t stream);
+// Expert-grouped mat-vecs: `used` slots, slot kk reads expert sel[kk] (rows
+// rows of the slab) and the activation x_stride_blocks q8_K blocks per slot
+// into xq; output slot-major.
+hipError_t launch_gemv_q4k_id(float* y, const void* slab, const void* xq, const int32_t* sel,
+                              int64_t n_experts, int64_t used, int64_t rows, int64_t K,
+                              int64_t x_stride_blocks, hipStream_t stream);
+hipError_t launch_gemv_iq4nl_id(float* y, const void* slab, const void* xq, const int32_t* sel,
+                                int64_t n_experts, int64_t used, int64_t rows, int64_t K,
+                                int64_t x_stride_blocks, hipStream_t stream);
 hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, int64_t N,
                            int64_t K, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink,

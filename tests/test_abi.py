@@ -103,6 +103,32 @@ def test_gemm_refusals(args, status, text):
     assert s == status and text in err
 
 
+@pytest.mark.parametrize("fn", ["xq_gemv_q4k_id", "xq_gemv_iq4nl_id"])
+@pytest.mark.parametrize("args,status,text", [
+    ((0, A16, A16, A16, 6, 3, 64, 2048, 0, None), xq.XQ_E_NULL, "y is NULL"),
+    ((A16, 0, A16, A16, 6, 3, 64, 2048, 0, None), xq.XQ_E_NULL, "slab is NULL"),
+    ((A16, A16, 0, A16, 6, 3, 64, 2048, 0, None), xq.XQ_E_NULL, "xq is NULL"),
+    ((A16, A16, A16, 0, 6, 3, 64, 2048, 0, None), xq.XQ_E_NULL, "sel is NULL"),
+    ((A16, A16, A16, A16, 0, 3, 64, 2048, 0, None), xq.XQ_E_SHAPE, "n_experts=0"),
+    ((A16, A16, A16, A16, 6, 0, 64, 2048, 0, None), xq.XQ_E_SHAPE, "used=0"),
+    ((A16, A16, A16, A16, 6, 65536, 64, 2048, 0, None), xq.XQ_E_SHAPE, "used=65536"),
+    ((A16, A16, A16, A16, 6, 3, 0, 2048, 0, None), xq.XQ_E_SHAPE, "rows=0"),
+    ((A16, A16, A16, A16, 2 ** 20, 3, 2 ** 11, 2048, 0, None), xq.XQ_E_SHAPE, "above 2^30"),
+    ((A16, A16, A16, A16, 6, 3, 64, 2000, 0, None), xq.XQ_E_SHAPE, "K=2000"),
+    ((A16, A16, A16, A16, 6, 3, 64, 2048, 3, None), xq.XQ_E_SHAPE, "x_stride_blocks=3"),
+    ((A4, A16, A16, A16, 6, 3, 64, 2048, 0, None), xq.XQ_E_ALIGN, None),
+    ((A16, A4, A16, A16, 6, 3, 64, 2048, 0, None), xq.XQ_E_ALIGN, "slab not 16-byte"),
+    ((A16, A16, A4, A16, 6, 3, 64, 2048, 8, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
+    ((A16, A16, A16, A1, 6, 3, 64, 2048, 0, None), xq.XQ_E_ALIGN, "sel not 4-byte"),
+])
+def test_id_refusals(fn, args, status, text):
+    s, err = _call(fn, *args)
+    if text is None:  # a 4-byte-aligned y passes its gate; the next gate decides
+        assert s != xq.XQ_OK
+        return
+    assert s == status and text in err, (s, err)
+
+
 def test_refusal_raises_in_binding():
     with pytest.raises(xq.XQError) as e:
         xq.xq_gemv_q4k(A16, A16, A16, 8, 1000)
