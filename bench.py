@@ -41,8 +41,26 @@ HBM_PEAK_GBPS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 UP = (14336, 4096)
 DOWN = (4096, 14336)
-COUNTERS = os.path.join(ROOT, "profiles", "gemv_q4k_up_14336x4096_counters.json")
-KERNEL_SRC = os.path.join(ROOT, "quantized_decode_mat_amd", "csrc", "gemv_q4k.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+CSRC = os.path.join(ROOT, "quantized_decode_mat_amd", "csrc")
+# Each counted kernel: the name rocprofv3 reports (a prefix), the launches of a
+# --counters run, its algorithmic bytes per launch, and the sources its code
+# comes from (the summary is void once any of them changes).
+COUNTED = {
+    "gemv_q4k_up_14336x4096": (
+        "void xq::(anonymous namespace)::gemv_q4k_kernel<2, 2, 4, 2, true, false>", 20,
+        33030144 + 5120 + 4 * 14336, ("gemv_q4k.hip", "q4k_row.h", "xq_device.h")),
+    "gemv_q4k_down_4096x14336": (
+        "void xq::(anonymous namespace)::gemv_q4k_kernel<1, 4, 8, 3, false, false>", 20,
+        33030144 + 17920 + 4 * 4096, ("gemv_q4k.hip", "q4k_row.h", "xq_device.h")),
+    "gemv_iq4nl_head_128256x4096": (
+        "void xq::(anonymous namespace)::gemv_iq4nl_resident_kernel<2, false>", 8,
+        295501824 + 5120 + 4 * 128256, ("gemv_iq4nl.hip", "xq_device.h")),
+    "gemm_q4k_512x14336x4096": (
+        "xq::(anonymous namespace)::gemm_q4k_kernel", 4,
+        33030144 + 512 * 16 * 320 + 4 * 512 * 14336, ("gemm_q4k.hip", "xq_device.h")),
+}
+HEADLINE = "gemv_q4k_up_14336x4096"
 
 
 # Sustained work before every timed region. After an idle spell (host-side
@@ -70,13 +88,24 @@ def parse():
                    help="lower bound of the oracle's timed host work")
     p.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     p.add_argument("--suite", action="store_true",
-                   help="also time the other workloads; their lines go to stderr and "
-                        "gpurun_out/bench_suite.jsonl")
+                   help="also time the other workloads; their lines go to stderr (and to "
+                        "--suite-out when given)")
+    p.add_argument("--suite-out", default=None,
+                   help="file that receives the suite's lines, one JSON object per line")
     p.add_argument("--json-out", default=None, help="also write the JSON line to this file")
     p.add_argument("--counters", action="store_true",
                    help="short run for rocprofv3 --pmc: 20 up and 20 down mat-vec launches over "
-                        "the cold pool, then 5 device copies and 5 streaming reads of 64 MiB "
-                        "(the counters' calibration), then exit")
+                        "the cold pool, 8 IQ4_NL 128256x4096 mat-vecs, 4 small-M products, then "
+                        "5 device copies and 5 streaming reads of 64 MiB (the counters' "
+                        "calibration), then exit")
+    p.add_argument("--trace-summary", metavar="TRACE_DIR",
+                   help="read the *_kernel_trace.csv of a rocprofv3 --kernel-trace run under "
+                        "TRACE_DIR and print one JSON line per kernel (calls, mean/min/max us, "
+                        "mean of the last 1000 launches), then exit (no GPU needed)")
+    p.add_argument("--counters-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="read the rocprofv3 CSVs of a --counters run under FETCH_SIZE and "
+                        "WRITE_SIZE, write " + os.path.relpath(COUNTERS, ROOT) + " and exit "
+                        "(no GPU needed)")
     return p.parse_args()
 
 
@@ -85,22 +114,100 @@ def sha_of(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(per_launch_bytes):
-    """HBM bytes per launch of the up mat-vec from the committed rocprofv3
+def sources_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(name):
+    """HBM bytes per launch of a counted kernel from the committed rocprofv3
     counter summary, or None when it is missing or was taken on another
-    version of the kernel source."""
+    version of the kernel's sources."""
     try:
         with open(COUNTERS) as f:
-            c = json.load(f)
-    except (OSError, ValueError):
+            c = json.load(f)["kernels"][name]
+    except (OSError, ValueError, KeyError):
         return None, "no counter summary"
-    if c.get("kernel_source_sha256_16") != sha_of(KERNEL_SRC):
+    if c.get("sources_sha256_16") != sources_sha(COUNTED[name][3]):
         return None, "counter summary predates the current kernel source"
     return int(c["hbm_bytes_per_launch"]), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated"
 
 
+def trace_summary(trace_dir):
+    """Per-kernel durations (End - Start, ns) from a rocprofv3 kernel trace."""
+    import csv
+    import glob
+    per = {}
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                per.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    for name, v in sorted(per.items(), key=lambda kv: -len(kv[1])):
+        v.sort()
+        d = [x[1] / 1e3 for x in v]
+        last = d[-1000:]
+        print(json.dumps({"kernel": name, "calls": len(d), "mean_us": round(sum(d) / len(d), 3),
+                          "min_us": round(min(d), 3), "max_us": round(max(d), 3),
+                          "last1000_mean_us": round(sum(last) / len(last), 3)}))
+
+
+def counters_summary(fetch_dir, write_dir):
+    """Per-kernel HBM bytes from the two --pmc runs of `bench.py --counters`.
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read
+    for the run's five 64 MiB device copies (64 MiB read, 64 MiB written)."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        out = []
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r["Counter_Name"] == counter:
+                        out.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
+                                    float(r["Counter_Value"])))
+        return sorted(out)
+
+    def calib(rows, known_kib):
+        # The run's last five device copies are the 64 MiB calibration copies.
+        cp = [v for (_, nm, v) in rows if "copyBuffer" in nm][-5:]
+        assert len(cp) == 5 and max(cp) - min(cp) < 0.01 * max(cp), cp
+        return known_kib / (sum(cp) / len(cp))
+
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    fcal, wcal = calib(fetch, 65536.0), calib(write, 65536.0)
+    kernels = {}
+    for name, (kname, n, alg, srcs) in COUNTED.items():
+        fv = [v for (_, nm, v) in fetch if nm.startswith(kname)][-n:]
+        wv = [v for (_, nm, v) in write if nm.startswith(kname)][-n:]
+        assert len(fv) == n and len(wv) == n, "%s: %d/%d dispatches" % (name, len(fv), len(wv))
+        fk, wk = sum(fv) / n, sum(wv) / n
+        hbm = fk * 1024 * fcal + wk * 1024 * wcal
+        kernels[name] = {"kernel": kname, "launches": n, "fetch_size_kib_per_launch": round(fk, 3),
+                         "write_size_kib_per_launch": round(wk, 3),
+                         "hbm_bytes_per_launch": int(round(hbm)), "alg_bytes_per_launch": alg,
+                         "traffic_over_alg": round(hbm / alg, 4),
+                         "sources_sha256_16": sources_sha(srcs)}
+    out = {"fetch_calibration": round(fcal, 5), "write_calibration": round(wcal, 5),
+           "kernels": kernels}
+    with open(COUNTERS, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def main():
     args = parse()
+    if args.counters_summary:
+        counters_summary(*args.counters_summary)
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d refused)" % args.gpus, file=sys.stderr)
@@ -223,7 +330,7 @@ def main():
     # ---- roofline of the up mat-vec ----
     up_alg_bytes = w_up.nbytes + xq.xq_q8k_bytes(1, UP[1]) + 4 * UP[0]
     achieved = up_alg_bytes / (kern_us["gemv_up"] * 1e-6) / 1e9
-    traffic, traffic_note = traffic_from_profile(up_alg_bytes)
+    traffic, traffic_note = traffic_from_profile(HEADLINE)
     roofline = {
         "bound": "hbm",
         "kernel": "gemv_q4k 14336x4096",
@@ -311,8 +418,11 @@ def main():
 
 
 def counters_run(torch, xq, L, dev, stream, ups, dns, xq1, xq2, h, y, x_d, pool):
-    """Launch sequence profiled by the rocprofv3 --pmc runs: dispatch order is
-    up x20, down x20, copy x5 (64 MiB), stream read x5 (64 MiB)."""
+    """Launch sequence profiled by the rocprofv3 --pmc runs: up x20, down x20
+    (cold pool), IQ4_NL 128256x4096 x8 (four rotating copies), small-M
+    product 512x14336x4096 x4 (rotating through the up pool), then copy x5
+    and stream read x5 of 64 MiB."""
+    import workloads as wl
     s = stream.cuda_stream
     L.xq_quantize_q8k(xq1.data_ptr(), x_d.data_ptr(), 1, UP[1], s)
     L.xq_quantize_q8k(xq2.data_ptr(), h.data_ptr(), 1, DOWN[1], s)
@@ -322,6 +432,29 @@ def counters_run(torch, xq, L, dev, stream, ups, dns, xq1, xq2, h, y, x_d, pool)
     for i in range(20):
         L.xq_gemv_q4k(y.data_ptr(), dns[(i + 7) % pool].data_ptr(), xq2.data_ptr(), DOWN[0],
                       DOWN[1], s)
+    torch.cuda.synchronize()
+    N, K = 128256, 4096
+    g = wl.rng(wl.SEEDS["iq4nl_head"])
+    w = torch.from_numpy(wl.iq4nl_weights(N, K, g).reshape(-1)).to(dev)
+    ws = [w] + [w.clone() for _ in range(3)]
+    xh = torch.from_numpy(wl.activations(1, K, g).reshape(-1)).to(dev)
+    xqh = torch.empty(xq.xq_q8k_bytes(1, K), dtype=torch.uint8, device=dev)
+    L.xq_quantize_q8k(xqh.data_ptr(), xh.data_ptr(), 1, K, s)
+    yh = torch.empty(N, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    for i in range(8):
+        L.xq_gemv_iq4nl(yh.data_ptr(), ws[i % 4].data_ptr(), xqh.data_ptr(), N, K, s)
+    torch.cuda.synchronize()
+    del ws, w
+    M = 512
+    xm = torch.from_numpy(wl.activations(M, UP[1], wl.rng(wl.SEEDS["prefill"])).reshape(-1)).to(dev)
+    xqm = torch.empty(xq.xq_q8k_bytes(M, UP[1]), dtype=torch.uint8, device=dev)
+    L.xq_quantize_q8k(xqm.data_ptr(), xm.data_ptr(), M, UP[1], s)
+    ym = torch.empty(M * UP[0], dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    for i in range(4):
+        L.xq_gemm_q4k_small_m(ym.data_ptr(), ups[(i + 11) % pool].data_ptr(), xqm.data_ptr(), M,
+                              UP[0], UP[1], s)
     torch.cuda.synchronize()
     n = 64 << 20
     a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -431,7 +564,7 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
              L.xq_gemv_q4k_id, L.xq_gemv_q4k),
             ("iq4nl_id_E64_r1408_k2048_used8", wl.iq4nl_weights, xq.xq_iq4nl_bytes,
              L.xq_gemv_iq4nl_id, L.xq_gemv_iq4nl)):
-        g = wl.rng(wl.SEEDS["q4k_4096"] + 77)
+        g = wl.rng(wl.SEEDS["grouped"])
         slab = torch.from_numpy(np.concatenate(
             [wfn(rows, K, g).reshape(rows, -1) for _ in range(E)], axis=0).reshape(-1)).to(dev)
         xv = torch.from_numpy(wl.activations(1, K, g).reshape(-1)).to(dev)
@@ -479,10 +612,10 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
     del ws, w
     torch.cuda.empty_cache()
 
-    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
-    with open(os.path.join(ROOT, "gpurun_out", "bench_suite.jsonl"), "w") as f:
-        for d in lines:
-            f.write(json.dumps(d) + "\n")
+    if args.suite_out:
+        with open(args.suite_out, "w") as f:
+            for d in lines:
+                f.write(json.dumps(d) + "\n")
 
 
 if __name__ == "__main__":

@@ -51,6 +51,7 @@ SEEDS = {
     "iq4nl_4096": 1004,
     "iq4nl_head": 1005,
     "prefill": 1006,
+    "grouped": 1007,
 }
 
 
