@@ -592,6 +592,22 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
         del slabs, slab
         torch.cuda.empty_cache()
 
+    # Bind-time repack of the head's IQ4_NL file blocks (18 B each) into
+    # resident rows: bytes read + written per second.
+    N, K = 128256, 4096
+    bpr = K // 32
+    blocks = torch.from_numpy(wl.iq4nl_file_blocks(N * bpr, wl.rng(wl.SEEDS["iq4nl_head"]))
+                              .reshape(-1)).to(dev)
+    res = torch.empty(N * xq.iq4nl_row_bytes(bpr), dtype=torch.uint8, device=dev)
+    us = _time_loop(torch, stream, lambda i: L.xq_repack_iq4nl(
+        res.data_ptr(), blocks.data_ptr(), N * bpr, 0, bpr, s), 100)
+    moved = blocks.numel() + res.numel()
+    emit({"workload": "repack_iq4nl_head_128256x4096", "us": round(us, 3),
+          "read_plus_write_GBps": round(moved / us / 1e3, 1),
+          "frac_of_stream_read": round(moved / us / 1e3 / stream_gbps, 4)})
+    del blocks, res
+    torch.cuda.empty_cache()
+
     # Small-M prefill product.
     M, (N, K) = 512, UP
     g = wl.rng(wl.SEEDS["prefill"])

@@ -166,6 +166,33 @@ xq_status xq_gemv_iq4nl_id(float *y, const void *slab, const void *xq, const int
                            int64_t x_stride_blocks, void *stream);
 
 /*
+ * Bind-time repack of IQ4_NL file blocks into resident rows ("25 — Writing XPU
+ * Kernels", section 25.4: weights are converted once, at upload, into the one
+ * resident layout the kernels read; section 25.4.1: one work item per payload
+ * dword). A file block is 18 bytes: the f16 scale, then the 16 payload bytes
+ * (byte t: weight t in the low nibble, weight t+16 in the high nibble).
+ *  file_blocks  the chunk: n_blocks blocks back to back, global blocks
+ *               block_base .. block_base + n_blocks - 1 of a matrix of bpr
+ *               blocks per row (block g is block g % bpr of row g / bpr);
+ *               2-byte aligned.
+ *  resident     row 0 of the matrix in resident rows (xq_iq4nl_bytes per row
+ *               for K = 32*bpr: bpr f16 scales, zero-padded to a multiple of
+ *               4 bytes, then bpr payloads of 16 B); 4-byte aligned; must hold
+ *               rows 0 .. (block_base + n_blocks - 1) / bpr. Only the bytes of
+ *               the chunk's blocks are written (and a row's 2 pad bytes, when
+ *               bpr is odd, by the chunk holding the row's last block).
+ *  1 <= n_blocks <= 2^29, 0 <= block_base <= 2^40, 1 <= bpr <= 2^24.
+ * One pass reads each source byte once. A chunk that starts and ends on row
+ * boundaries writes its scale prefix as whole dwords; any other chunk writes
+ * each scale as a 16-bit half. xq_repack_dword_prefix_launches() counts the
+ * launches of the first route in this process (section 25.7.2: a test that
+ * the route fires, and one that it does not).
+ */
+xq_status xq_repack_iq4nl(void *resident, const void *file_blocks, int64_t n_blocks,
+                          int64_t block_base, int64_t bpr, void *stream);
+int64_t xq_repack_dword_prefix_launches(void);
+
+/*
  * Measurement helper, not part of the method: read `bytes` of device memory
  * once with 16-byte loads and fold them into one word per workgroup of
  * `sink` (sink must hold xq_bench_sink_words(bytes) uint32). Its duration

@@ -200,6 +200,31 @@ class Oracle:
         return y, T
 
 
+def repack_iq4nl(file_blocks, n_blocks: int, block_base: int, bpr: int, resident=None):
+    """IQ4_NL file blocks -> resident rows, by the layouts' definitions
+    ("25 — Writing XPU Kernels", section 25.4: a resident row is the row's f16
+    block scales, zero-padded to a multiple of 4 bytes, then its 16-byte
+    payloads; a file block is the f16 scale followed by its 16 payload bytes).
+    Blocks block_base .. block_base + n_blocks - 1 (block g is block g % bpr of
+    row g // bpr) are written into `resident` (uint8[rows, row_bytes]; a new
+    zero-filled array when None), with a row's pad bytes when the chunk holds
+    the row's last block. Plain numpy, one block at a time."""
+    blocks = np.asarray(file_blocks, dtype=np.uint8).reshape(n_blocks, 18)
+    prefix = ((2 * bpr + 3) // 4) * 4
+    row_bytes = prefix + 16 * bpr
+    rows = (block_base + n_blocks + bpr - 1) // bpr
+    if resident is None:
+        resident = np.zeros((rows, row_bytes), dtype=np.uint8)
+    for b in range(n_blocks):
+        g = block_base + b
+        r, j = divmod(g, bpr)
+        resident[r, 2 * j:2 * j + 2] = blocks[b, 0:2]
+        resident[r, prefix + 16 * j:prefix + 16 * j + 16] = blocks[b, 2:18]
+        if j == bpr - 1:
+            resident[r, 2 * bpr:prefix] = 0
+    return resident
+
+
 def default() -> Oracle:
     """The default build, compiled on first use when it is missing."""
     global _default

@@ -28,6 +28,7 @@ EXPORTS = (
     "xq_quantize_q8k", "xq_gemv_q4k", "xq_gemv_iq4nl", "xq_gemm_q4k_small_m",
     "xq_q8k_bytes", "xq_q4k_bytes", "xq_iq4nl_bytes", "xq_status_name", "xq_last_error",
     "xq_bench_stream_read", "xq_bench_sink_words", "xq_gemv_q4k_id", "xq_gemv_iq4nl_id",
+    "xq_repack_iq4nl", "xq_repack_dword_prefix_launches",
 )
 
 
@@ -54,8 +55,11 @@ def lib() -> ctypes.CDLL:
             L.xq_bench_stream_read.argtypes = [P, I, P, P]
             L.xq_gemv_q4k_id.argtypes = [P, P, P, P, I, I, I, I, I, P]
             L.xq_gemv_iq4nl_id.argtypes = [P, P, P, P, I, I, I, I, I, P]
+            L.xq_repack_iq4nl.argtypes = [P, P, I, I, I, P]
+            L.xq_repack_dword_prefix_launches.argtypes = []
+            L.xq_repack_dword_prefix_launches.restype = I
             for f in ("xq_quantize_q8k", "xq_gemv_q4k", "xq_gemv_iq4nl", "xq_gemm_q4k_small_m",
-                      "xq_bench_stream_read", "xq_gemv_q4k_id", "xq_gemv_iq4nl_id"):
+                      "xq_bench_stream_read", "xq_gemv_q4k_id", "xq_gemv_iq4nl_id", "xq_repack_iq4nl"):
                 getattr(L, f).restype = S
             for f in ("xq_q8k_bytes", "xq_q4k_bytes", "xq_iq4nl_bytes"):
                 getattr(L, f).argtypes = [I, I]
@@ -162,6 +166,24 @@ def xq_gemv_iq4nl_id(y, slab, xq, sel, n_experts: int, used: int, rows: int, K: 
                                   _ptr(sel, 4 * used, "sel"), n_experts, used, rows, K,
                                   x_stride_blocks, _stream(stream)),
            "xq_gemv_iq4nl_id")
+
+
+def xq_repack_iq4nl(resident, file_blocks, n_blocks: int, block_base: int, bpr: int,
+                    stream=None) -> None:
+    rows = (block_base + n_blocks + bpr - 1) // bpr
+    _check(lib().xq_repack_iq4nl(_ptr(resident, rows * iq4nl_row_bytes(bpr), "resident"),
+                                 _ptr(file_blocks, 18 * n_blocks, "file_blocks"), n_blocks,
+                                 block_base, bpr, _stream(stream)),
+           "xq_repack_iq4nl")
+
+
+def xq_repack_dword_prefix_launches() -> int:
+    return lib().xq_repack_dword_prefix_launches()
+
+
+def iq4nl_row_bytes(bpr: int) -> int:
+    """Bytes of one resident IQ4_NL row of bpr blocks (any bpr >= 1)."""
+    return ((2 * bpr + 3) // 4) * 4 + 16 * bpr
 
 
 def xq_gemm_q4k_small_m(y, w, xq, M: int, N: int, K: int, stream=None) -> None:

@@ -27,6 +27,7 @@ SOURCES = [
     "gemv_q4k.hip",
     "gemv_iq4nl.hip",
     "gemm_q4k.hip",
+    "repack_iq4nl.hip",
     "stream_read.hip",
     "xq_api.cpp",
 ]

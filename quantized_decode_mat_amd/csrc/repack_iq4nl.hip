@@ -1,0 +1,108 @@
+// repack_iq4nl.hip — IQ4_NL file blocks -> resident rows, once, at upload.
+//
+// "25 — Writing XPU Kernels", section 25.4: weights are converted once when
+// they are bound, into the one resident layout every kernel reads (a row is
+// its f16 block scales padded to a dword, then its 16-byte payloads), and the
+// copy follows the decode rules: one work item per payload dword, not one
+// wave per block; a separate pass over the scattered scale bytes pulls a
+// cache line per block for two useful bytes, so the scale goes with the pass
+// that already reads those lines (section 25.4.1 leaves that fold open).
+//
+// Source: a chunk of the file's 18-byte blocks (f16 scale at +0, then the 16
+// payload bytes), global blocks block_base .. block_base + n - 1 of a matrix
+// of bpr blocks per row. The source is 2-byte aligned at best (18-byte
+// stride), so it is read as 16-bit halves; every resident store is a dword or
+// a 16-bit half at its natural alignment.
+//
+// Two routes, both one pass:
+//  * any chunk: work item t writes payload dword t%4 of block t/4; the item
+//    with t%4 == 0 also writes the block's scale as a 16-bit store, and, for
+//    the last block of a row with an odd bpr, the zero pad half after it;
+//  * a chunk that starts and ends on row boundaries: the payload items as
+//    above, plus one item per prefix dword writing two scales (or a scale and
+//    the zero pad) at once, so every resident store is a full dword. The host
+//    counts launches of this route so a test can see that it fires.
+#include <atomic>
+
+#include "xq_device.h"
+#include "xq_launch.h"
+
+namespace xq {
+namespace {
+
+constexpr int kRepackThreads = 256;
+constexpr int kFileBlockBytes = 18;
+
+__device__ __forceinline__ uint32_t src_half(const uint16_t* src, int64_t byte_off) {
+  return src[byte_off >> 1];
+}
+
+template <bool DWORD_PREFIX>
+__global__ __launch_bounds__(kRepackThreads) void repack_iq4nl_kernel(
+    uint8_t* __restrict__ out, const uint16_t* __restrict__ src, int64_t n, int64_t block_base,
+    int64_t bpr, int64_t prefix, int64_t row_bytes, int64_t prefix_items) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRepackThreads + threadIdx.x;
+  const int64_t pay_items = 4 * n;
+  if (t < pay_items) {
+    const int64_t b = t >> 2;  // block within the chunk
+    const int k = static_cast<int>(t & 3);
+    const int64_t gb = block_base + b;
+    const int64_t row = gb / bpr;
+    const int64_t j = gb - row * bpr;
+    const int64_t so = b * kFileBlockBytes + 2 + 4 * k;
+    const uint32_t w = src_half(src, so) | (src_half(src, so + 2) << 16);
+    uint8_t* orow = out + row * row_bytes;
+    *reinterpret_cast<uint32_t*>(orow + prefix + 16 * j + 4 * k) = w;
+    if (!DWORD_PREFIX && k == 0) {
+      reinterpret_cast<uint16_t*>(orow)[j] = static_cast<uint16_t>(src_half(src, b * kFileBlockBytes));
+      if (j == bpr - 1 && (bpr & 1)) reinterpret_cast<uint16_t*>(orow)[j + 1] = 0;
+    }
+    return;
+  }
+  if (DWORD_PREFIX) {
+    const int64_t p = t - pay_items;  // prefix dword over the chunk's rows
+    if (p >= prefix_items) return;
+    const int64_t pw = prefix >> 2;
+    const int64_t r = p / pw;                 // row within the chunk
+    const int64_t i = p - r * pw;             // dword within the prefix
+    const int64_t b0 = r * bpr + 2 * i;       // block within the chunk
+    const uint32_t lo = src_half(src, b0 * kFileBlockBytes);
+    const uint32_t hi = (2 * i + 1 < bpr) ? src_half(src, (b0 + 1) * kFileBlockBytes) : 0u;
+    const int64_t row = block_base / bpr + r;
+    *reinterpret_cast<uint32_t*>(out + row * row_bytes + 4 * i) = lo | (hi << 16);
+  }
+}
+
+std::atomic<int64_t> g_dword_prefix_launches{0};
+
+}  // namespace
+
+int64_t repack_dword_prefix_launches() {
+  return g_dword_prefix_launches.load(std::memory_order_relaxed);
+}
+
+hipError_t launch_repack_iq4nl(void* resident, const void* file_blocks, int64_t n,
+                               int64_t block_base, int64_t bpr, hipStream_t stream) {
+  const int64_t prefix = ((2 * bpr + 3) / 4) * 4;
+  const int64_t row_bytes = prefix + 16 * bpr;
+  const bool row_aligned = (block_base % bpr == 0) && (n % bpr == 0);
+  const int64_t prefix_items = row_aligned ? (n / bpr) * (prefix / 4) : 0;
+  const int64_t items = 4 * n + prefix_items;
+  const int64_t grid = (items + kRepackThreads - 1) / kRepackThreads;
+  uint8_t* out = static_cast<uint8_t*>(resident);
+  const uint16_t* src = static_cast<const uint16_t*>(file_blocks);
+  if (row_aligned) {
+    hipLaunchKernelGGL(repack_iq4nl_kernel<true>, dim3(static_cast<uint32_t>(grid)),
+                       dim3(kRepackThreads), 0, stream, out, src, n, block_base, bpr, prefix,
+                       row_bytes, prefix_items);
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess) g_dword_prefix_launches.fetch_add(1, std::memory_order_relaxed);
+    return e;
+  }
+  hipLaunchKernelGGL(repack_iq4nl_kernel<false>, dim3(static_cast<uint32_t>(grid)),
+                     dim3(kRepackThreads), 0, stream, out, src, n, block_base, bpr, prefix,
+                     row_bytes, prefix_items);
+  return hipGetLastError();
+}
+
+}  // namespace xq

@@ -194,6 +194,26 @@ xq_status xq_gemm_q4k_small_m(float* y, const void* w, const void* xq, int64_t M
                   "xq_gemm_q4k_small_m");
 }
 
+xq_status xq_repack_iq4nl(void* resident, const void* file_blocks, int64_t n_blocks,
+                          int64_t block_base, int64_t bpr, void* stream) {
+  if (!resident) return fail(XQ_E_NULL, "resident is NULL");
+  if (!file_blocks) return fail(XQ_E_NULL, "file_blocks is NULL");
+  if (n_blocks < 1 || n_blocks > (1LL << 29))
+    return fail(XQ_E_SHAPE, "n_blocks=%lld outside 1..2^29", (long long)n_blocks);
+  if (block_base < 0 || block_base > (1LL << 40))
+    return fail(XQ_E_SHAPE, "block_base=%lld outside 0..2^40", (long long)block_base);
+  if (bpr < 1 || bpr > (1LL << 24))
+    return fail(XQ_E_SHAPE, "bpr=%lld outside 1..2^24", (long long)bpr);
+  if (!aligned(resident, 4)) return fail(XQ_E_ALIGN, "resident not 4-byte aligned");
+  if (!aligned(file_blocks, 2)) return fail(XQ_E_ALIGN, "file_blocks not 2-byte aligned");
+  if (xq_status s = check_device()) return s;
+  return launched(xq::launch_repack_iq4nl(resident, file_blocks, n_blocks, block_base, bpr,
+                                          static_cast<hipStream_t>(stream)),
+                  "xq_repack_iq4nl");
+}
+
+int64_t xq_repack_dword_prefix_launches(void) { return xq::repack_dword_prefix_launches(); }
+
 size_t xq_q8k_bytes(int64_t rows, int64_t K) {
   if (rows < 1 || K < 256 || K % 256) return 0;
   return static_cast<size_t>(rows) * static_cast<size_t>(K / 256) * 320u;

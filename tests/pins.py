@@ -403,4 +403,45 @@ def pin_iq4nl_brute_force_and_partials(o):
     assert np.all(np.abs(y - wd @ x[0].astype(np.float64)) <= bound + 1e-12 * T)
 
 
+def _iq4nl_file_dequant(blocks: np.ndarray, rows: int, bpr: int) -> np.ndarray:
+    """Weights of IQ4_NL file blocks straight from the format: block c of a row
+    holds w[32c + t] = d * kv[low nibble of payload byte t] and
+    w[32c + 16 + t] = d * kv[high nibble of byte t] for t < 16, d the f16 at
+    the block's first two bytes (numpy's float16 decoder), kv the table in
+    tests/golden/iq4nl_codebook.txt."""
+    kv = np.array(_codebook_golden(), dtype=np.float64)
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(rows, bpr, 18)
+    d = b[:, :, 0:2].copy().view("<f2").astype(np.float64)
+    q = b[:, :, 2:18]
+    w = np.concatenate([kv[q & 15], kv[q >> 4]], axis=2) * d
+    return w.reshape(rows, 32 * bpr)
+
+
+def pin_iq4nl_repack_layout(o):
+    """Repacked rows dequantize (through the oracle's resident-row decoder) to
+    the weights the file blocks define; a row's pad bytes are zero."""
+    import oracle
+    for rows, bpr in ((3, 9), (2, 8), (1, 1), (2, 317)):
+        blocks = wl.iq4nl_file_blocks(rows * bpr, wl.rng(7000 + 10 * rows + bpr))
+        res = oracle.repack_iq4nl(blocks, rows * bpr, 0, bpr)
+        K = 32 * bpr
+        got = o.dequant_iq4nl(res, rows, K).reshape(rows, K)
+        assert np.array_equal(got, _iq4nl_file_dequant(blocks, rows, bpr)), (rows, bpr)
+        prefix = ((2 * bpr + 3) // 4) * 4
+        assert not res[:, 2 * bpr:prefix].any()
+
+
+def pin_iq4nl_repack_chunks(o):
+    """Repacking in chunks that start and end mid-row writes every byte of the
+    resident rows (a poisoned buffer comes out whole) and equals one chunk."""
+    import oracle
+    rows, bpr = 3, 9
+    blocks = wl.iq4nl_file_blocks(rows * bpr, wl.rng(7100))
+    whole = oracle.repack_iq4nl(blocks, rows * bpr, 0, bpr)
+    part = np.full_like(whole, 0xAB)
+    for a, b in ((0, 5), (5, 17), (17, 27)):
+        oracle.repack_iq4nl(blocks[a:b], b - a, a, bpr, resident=part)
+    assert np.array_equal(whole, part)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -129,6 +129,22 @@ def test_id_refusals(fn, args, status, text):
     assert s == status and text in err, (s, err)
 
 
+@pytest.mark.parametrize("args,status,text", [
+    ((0, A16, 10, 0, 9, None), xq.XQ_E_NULL, "resident is NULL"),
+    ((A16, 0, 10, 0, 9, None), xq.XQ_E_NULL, "file_blocks is NULL"),
+    ((A16, A16, 0, 0, 9, None), xq.XQ_E_SHAPE, "n_blocks=0"),
+    ((A16, A16, 2 ** 29 + 1, 0, 9, None), xq.XQ_E_SHAPE, "n_blocks=536870913"),
+    ((A16, A16, 10, -1, 9, None), xq.XQ_E_SHAPE, "block_base=-1"),
+    ((A16, A16, 10, 0, 0, None), xq.XQ_E_SHAPE, "bpr=0"),
+    ((A16, A16, 10, 0, 2 ** 24 + 1, None), xq.XQ_E_SHAPE, "bpr=16777217"),
+    ((A16 + 2, A16, 10, 0, 9, None), xq.XQ_E_ALIGN, "resident not 4-byte"),
+    ((A16, A1, 10, 0, 9, None), xq.XQ_E_ALIGN, "file_blocks not 2-byte"),
+])
+def test_repack_refusals(args, status, text):
+    s, err = _call("xq_repack_iq4nl", *args)
+    assert s == status and text in err, (s, err)
+
+
 def test_refusal_raises_in_binding():
     with pytest.raises(xq.XQError) as e:
         xq.xq_gemv_q4k(A16, A16, A16, 8, 1000)

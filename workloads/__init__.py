@@ -102,6 +102,17 @@ def iq4nl_weights(N: int, K: int, g: np.random.Generator,
     return out
 
 
+def iq4nl_file_blocks(n_blocks: int, g: np.random.Generator,
+                      d_range=(0.001, 0.02)) -> np.ndarray:
+    """IQ4_NL blocks in the file layout as uint8[n_blocks, 18]: the f16 scale,
+    then 16 payload bytes (uniform)."""
+    d = g.uniform(d_range[0], d_range[1], size=n_blocks)
+    out = np.empty((n_blocks, 18), dtype=np.uint8)
+    out[:, 0:2] = _f16_bytes(d)
+    out[:, 2:] = g.integers(0, 256, size=(n_blocks, 16), dtype=np.uint8)
+    return out
+
+
 def activations(R: int, K: int, g: np.random.Generator) -> np.ndarray:
     """f32 [R, K] drawn from N(0, 1)."""
     return g.standard_normal(size=(R, K), dtype=np.float32)
