@@ -86,6 +86,9 @@ class Oracle:
         lib.xqo_dequant_iq4nl.argtypes = [P, I, I, P]
         lib.xqo_iq4nl_partials.argtypes = [P, P, I, I, P, I, P]
         lib.xqo_gemv_iq4nl.argtypes = [P, P, I, I, P, I, P, P]
+        lib.xqo_dequant_q4_0.argtypes = [P, I, I, P]
+        lib.xqo_q4_0_partials.argtypes = [P, P, I, I, P, I, P]
+        lib.xqo_gemv_q4_0.argtypes = [P, P, I, I, P, I, P, P]
         self.lib = lib
         self.path = path
 
@@ -197,6 +200,33 @@ class Oracle:
         y = np.empty(nrows, dtype=np.float64)
         T = np.empty(nrows, dtype=np.float64)
         self.lib.xqo_gemv_iq4nl(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(y), _ptr(T))
+        return y, T
+
+    def dequant_q4_0(self, w, N: int, K: int) -> np.ndarray:
+        """Q4_0 resident rows (the IQ4_NL row shape) -> f64 weights d*(nibble-8)."""
+        w = _u8(w)
+        out = np.empty((N, K), dtype=np.float64)
+        self.lib.xqo_dequant_q4_0(_ptr(w), N, K, _ptr(out))
+        return out
+
+    def q4_0_partials(self, w, xq, N: int, K: int, rows=None):
+        """Exact per-block partials D = sum (nibble-8)*code, int32 [nrows, K/32]."""
+        w = _u8(w)
+        xq = _u8(xq)
+        r, rp, n = _rows_arg(rows)
+        nrows = N if r is None else n
+        D = np.empty((nrows, K // 32), dtype=np.int32)
+        self.lib.xqo_q4_0_partials(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(D))
+        return D
+
+    def gemv_q4_0(self, w, xq, N: int, K: int, rows=None):
+        w = _u8(w)
+        xq = _u8(xq)
+        r, rp, n = _rows_arg(rows)
+        nrows = N if r is None else n
+        y = np.empty(nrows, dtype=np.float64)
+        T = np.empty(nrows, dtype=np.float64)
+        self.lib.xqo_gemv_q4_0(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(y), _ptr(T))
         return y, T
 
 

@@ -411,3 +411,84 @@ void xqo_gemv_iq4nl(const uint8_t *w, const uint8_t *xq, int64_t N, int64_t K,
         T[k] = mag;
     }
 }
+
+/* ---- Q4_0 ---------------------------------------------------------------- */
+/* Q4_0 shares the IQ4_NL block shape and resident row (f16 scale per 32
+ * weights, 16 payload bytes: byte t holds weight t in its low nibble and weight
+ * t+16 in its high nibble); the weight is d * (nibble - 8) ("25 — Writing XPU
+ * Kernels", section 25.2: the Q4_0 twin of the IQ4_NL kernel, whose -8 rides on
+ * the activation's sum). */
+
+static int q4_0_value(int nibble)
+{
+#ifdef XQO_FAULT_Q40_OFFSET
+    return nibble - 7;
+#else
+    return nibble - 8;
+#endif
+}
+
+void xqo_dequant_q4_0(const uint8_t *w, int64_t N, int64_t K, double *out)
+{
+    int64_t bpr, prefix, row_bytes;
+    iq4nl_geometry(K, &bpr, &prefix, &row_bytes);
+    for (int64_t r = 0; r < N; r++) {
+        const uint8_t *row = w + r * row_bytes;
+        for (int64_t c = 0; c < bpr; c++) {
+            double d = xqo_f16_to_f64(rd_u16(row + 2 * c));
+            const uint8_t *pay = row + prefix + 16 * c;
+            for (int t = 0; t < 32; t++)
+                out[r * K + 32 * c + t] = d * (double)q4_0_value(iq4nl_nibble(pay, t));
+        }
+    }
+}
+
+/* D[r][c] = sum_t (nibble_t - 8) * code_(32c+t): int32 [nrows][K/32]. */
+void xqo_q4_0_partials(const uint8_t *w, const uint8_t *xq, int64_t N, int64_t K,
+                       const int64_t *rows, int64_t nrows, int32_t *D)
+{
+    int64_t bpr, prefix, row_bytes;
+    iq4nl_geometry(K, &bpr, &prefix, &row_bytes);
+    if (!rows) nrows = N;
+    for (int64_t k = 0; k < nrows; k++) {
+        int64_t r = rows ? rows[k] : k;
+        const uint8_t *row = w + r * row_bytes;
+        for (int64_t c = 0; c < bpr; c++) {
+            const uint8_t *pay = row + prefix + 16 * c;
+            int64_t acc = 0;
+            for (int t = 0; t < 32; t++) {
+                int64_t i = 32 * c + t;
+                int code = (int8_t)xq[(i / QK) * Q8K_BYTES + (i % QK)];
+                acc += (int64_t)q4_0_value(iq4nl_nibble(pay, t)) * code;
+            }
+            D[k * bpr + c] = (int32_t)acc;
+        }
+    }
+}
+
+void xqo_gemv_q4_0(const uint8_t *w, const uint8_t *xq, int64_t N, int64_t K,
+                   const int64_t *rows, int64_t nrows, double *y, double *T)
+{
+    int64_t bpr, prefix, row_bytes;
+    iq4nl_geometry(K, &bpr, &prefix, &row_bytes);
+    if (!rows) nrows = N;
+    for (int64_t k = 0; k < nrows; k++) {
+        int64_t r = rows ? rows[k] : k;
+        const uint8_t *row = w + r * row_bytes;
+        double acc = 0.0, mag = 0.0;
+        for (int64_t c = 0; c < bpr; c++) {
+            double d = xqo_f16_to_f64(rd_u16(row + 2 * c));
+            const uint8_t *pay = row + prefix + 16 * c;
+            for (int t = 0; t < 32; t++) {
+                int64_t i = 32 * c + t;
+                const uint8_t *xb = xq + (i / QK) * Q8K_BYTES;
+                double xhat = (double)rd_f32(xb + 288) * (double)(int8_t)xb[i % QK];
+                double term = d * (double)q4_0_value(iq4nl_nibble(pay, t)) * xhat;
+                acc += term;
+                mag += fabs(term);
+            }
+        }
+        y[k] = acc;
+        T[k] = mag;
+    }
+}

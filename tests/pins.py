@@ -403,6 +403,62 @@ def pin_iq4nl_brute_force_and_partials(o):
     assert np.all(np.abs(y - wd @ x[0].astype(np.float64)) <= bound + 1e-12 * T)
 
 
+def pin_q4_0_layout(o):
+    """A constructed Q4_0 row (the IQ4_NL row shape): block c has scale
+    (c+1)/8, payload byte t holds nibble lo_t for weight t and hi_t for weight
+    t+16, so the weights are scale*(nibble-8) by construction; one-hot dots read
+    them back, and a row of nibbles 8 is zero against any activation."""
+    K = 512
+    bpr = K // 32
+    scales = (np.arange(bpr) + 1) / 8.0
+    payload = np.zeros((bpr, 16), np.uint8)
+    want = np.zeros(K, np.float64)
+    for c in range(bpr):
+        for t in range(16):
+            lo = (5 * t + c) % 16
+            hi = (t + 3 * c + 2) % 16
+            payload[c, t] = lo | (hi << 4)
+            want[32 * c + t] = scales[c] * (lo - 8)
+            want[32 * c + 16 + t] = scales[c] * (hi - 8)
+    row = _iq4nl_row(K, scales, payload)
+    assert np.array_equal(o.dequant_q4_0(row, 1, K)[0], want)
+    for p in (0, 15, 16, 31, 32, 300, 511):
+        x = np.zeros((1, K), np.float32)
+        x[0, p] = 127.0
+        y, _ = o.gemv_q4_0(row, o.quantize_q8k(x), 1, K)
+        assert y[0] == 127.0 * want[p], p
+    eight = _iq4nl_row(K, scales, np.full((bpr, 16), 0x88, np.uint8))
+    xq = o.quantize_q8k(wl.activations(1, K, wl.rng(61)))
+    y, T = o.gemv_q4_0(eight, xq, 1, K)
+    assert y[0] == 0.0 and T[0] == 0.0
+    assert not o.q4_0_partials(eight, xq, 1, K).any()
+
+
+def pin_q4_0_brute_force_and_partials(o):
+    """Random rows: the mat-vec against a numpy f64 dot of the separately
+    dequantized operands; the partials equal sum(nibble*code) - 8*s_c with s_c
+    the activation's stored 32-code sums (the -8 riding on the activation sum)
+    and recombine to the mat-vec."""
+    g = wl.rng(67)
+    N, K = 5, 1024
+    w = wl.iq4nl_weights(N, K, g)
+    x = wl.activations(1, K, g)
+    xq = o.quantize_q8k(x)
+    y, T = o.gemv_q4_0(w, xq, N, K)
+    wd = o.dequant_q4_0(w, N, K)
+    assert np.all(np.abs(y - wd @ o.dequant_q8k(xq, 1, K)[0]) <= 1e-12 * T)
+    bpr, prefix, _ = wl.iq4nl_row_geometry(K)
+    pay = w[:, prefix:].reshape(N, bpr, 16).astype(np.int64)
+    nib = np.concatenate([pay & 15, pay >> 4], axis=2)                      # [N, bpr, 32]
+    codes = np.stack([_q8k_fields(xq[0, b])[0] for b in range(K // 256)]).reshape(bpr, 32)
+    sums = np.stack([_q8k_fields(xq[0, b])[1] for b in range(K // 256)]).reshape(bpr)
+    D = o.q4_0_partials(w, xq, N, K)
+    assert np.array_equal(D, (nib * codes[None]).sum(axis=2) - 8 * sums[None])
+    dc = w[:, 0:2 * bpr].copy().view("<f2").astype(np.float64)
+    xs = np.repeat(xq[0, :, 288:292].copy().view("<f4").astype(np.float64).reshape(-1), 8)
+    assert np.all(np.abs((dc * xs[None, :] * D).sum(axis=1) - y) <= 1e-12 * T)
+
+
 def _iq4nl_file_dequant(blocks: np.ndarray, rows: int, bpr: int) -> np.ndarray:
     """Weights of IQ4_NL file blocks straight from the format: block c of a row
     holds w[32c + t] = d * kv[low nibble of payload byte t] and

@@ -15,6 +15,7 @@ FAULTS = {
     "XQO_FAULT_MIN_SIGN": "pin_q4k_brute_force",
     "XQO_FAULT_SCALE_HIBITS": "pin_q4k_pack_roundtrip",
     "XQO_FAULT_IQ4_HALVES": "pin_iq4nl_layout",
+    "XQO_FAULT_Q40_OFFSET": "pin_q4_0_layout",
 }
 
 
