@@ -54,7 +54,7 @@ COUNTED = {
         "void xq::(anonymous namespace)::gemv_q4k_kernel<1, 4, 8, 3, false, false>", 20,
         33030144 + 17920 + 4 * 4096, ("gemv_q4k.hip", "q4k_row.h", "xq_device.h")),
     "gemv_iq4nl_head_128256x4096": (
-        "void xq::(anonymous namespace)::gemv_iq4nl_resident_kernel<2, false>", 8,
+        "void xq::(anonymous namespace)::gemv_iq4nl_resident_kernel<2, false, 0>", 8,
         295501824 + 5120 + 4 * 128256, ("gemv_iq4nl.hip", "xq_device.h")),
     "gemm_q4k_512x14336x4096": (
         "xq::(anonymous namespace)::gemm_q4k_kernel", 4,
@@ -546,6 +546,26 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
         yy = torch.empty(N, dtype=torch.float32, device=dev)
         n = 1000 if N < 100000 else 200
         us = _time_loop(torch, stream, lambda i: L.xq_gemv_iq4nl(
+            yy.data_ptr(), ws[i % len(ws)].data_ptr(), xqb.data_ptr(), N, K, s), n)
+        wb = w.numel()
+        emit({"workload": name, "us": round(us, 3), "weight_GBps": round(wb / us / 1e3, 1),
+              "frac_of_8TBps": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4),
+              "frac_of_stream_read": round(wb / us / 1e3 / stream_gbps, 4)})
+        del ws, w
+        torch.cuda.empty_cache()
+
+    # Q4_0 mat-vecs on the same row shape (the IQ4_NL twin).
+    for name, (N, K), seed in (("q4_0_4096x4096", (4096, 4096), wl.SEEDS["iq4nl_4096"]),
+                               ("q4_0_head_128256x4096", (128256, 4096), wl.SEEDS["iq4nl_head"])):
+        g = wl.rng(seed)
+        w = torch.from_numpy(wl.iq4nl_weights(N, K, g).reshape(-1)).to(dev)
+        xv = torch.from_numpy(wl.activations(1, K, g).reshape(-1)).to(dev)
+        xqb = torch.empty(xq.xq_q8k_bytes(1, K), dtype=torch.uint8, device=dev)
+        xq.xq_quantize_q8k(xqb, xv, 1, K)
+        ws = _pool_copies(w, args.pool_mb)
+        yy = torch.empty(N, dtype=torch.float32, device=dev)
+        n = 1000 if N < 100000 else 200
+        us = _time_loop(torch, stream, lambda i: L.xq_gemv_q4_0(
             yy.data_ptr(), ws[i % len(ws)].data_ptr(), xqb.data_ptr(), N, K, s), n)
         wb = w.numel()
         emit({"workload": name, "us": round(us, 3), "weight_GBps": round(wb / us / 1e3, 1),

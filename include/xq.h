@@ -138,6 +138,19 @@ const char *xq_status_name(xq_status s);
 const char *xq_last_error(void);
 
 /*
+ * Q4_0 x q8_K mat-vec: y[n] = sum_k w[n][k] * xhat[k] with w = d_c * (nibble - 8)
+ * ("25 — Writing XPU Kernels", section 25.2: the Q4_0 twin of the IQ4_NL
+ * kernel; its -8 rides on the activation's sum). The weight rows have the
+ * IQ4_NL resident shape (K/32 f16 scales padded to a dword, then K/32 payloads
+ * of 16 B; xq_iq4nl_bytes(N, K) bytes; xq_repack_iq4nl converts Q4_0 file
+ * blocks too, they share the 18-byte shape); each 32-block's integer dot
+ * sum(nibble*code) - 8*s uses the q8_K's stored sum s of its 32 codes.
+ *  Same arguments, alignment and limits as xq_gemv_iq4nl.
+ */
+xq_status xq_gemv_q4_0(float *y, const void *w_q4_0, const void *xq, int64_t N, int64_t K,
+                       void *stream);
+
+/*
  * Expert-grouped mat-vecs ("25 — Writing XPU Kernels", section 25.2.2: one
  * launch over a bank of experts, the dot loop of the dense kernel unchanged;
  * the expert is picked on the device through a selection buffer, nothing is

@@ -28,7 +28,7 @@ EXPORTS = (
     "xq_quantize_q8k", "xq_gemv_q4k", "xq_gemv_iq4nl", "xq_gemm_q4k_small_m",
     "xq_q8k_bytes", "xq_q4k_bytes", "xq_iq4nl_bytes", "xq_status_name", "xq_last_error",
     "xq_bench_stream_read", "xq_bench_sink_words", "xq_gemv_q4k_id", "xq_gemv_iq4nl_id",
-    "xq_repack_iq4nl", "xq_repack_dword_prefix_launches",
+    "xq_repack_iq4nl", "xq_repack_dword_prefix_launches", "xq_gemv_q4_0",
 )
 
 
@@ -51,6 +51,7 @@ def lib() -> ctypes.CDLL:
             L.xq_quantize_q8k.argtypes = [P, P, I, I, P]
             L.xq_gemv_q4k.argtypes = [P, P, P, I, I, P]
             L.xq_gemv_iq4nl.argtypes = [P, P, P, I, I, P]
+            L.xq_gemv_q4_0.argtypes = [P, P, P, I, I, P]
             L.xq_gemm_q4k_small_m.argtypes = [P, P, P, I, I, I, P]
             L.xq_bench_stream_read.argtypes = [P, I, P, P]
             L.xq_gemv_q4k_id.argtypes = [P, P, P, P, I, I, I, I, I, P]
@@ -59,7 +60,8 @@ def lib() -> ctypes.CDLL:
             L.xq_repack_dword_prefix_launches.argtypes = []
             L.xq_repack_dword_prefix_launches.restype = I
             for f in ("xq_quantize_q8k", "xq_gemv_q4k", "xq_gemv_iq4nl", "xq_gemm_q4k_small_m",
-                      "xq_bench_stream_read", "xq_gemv_q4k_id", "xq_gemv_iq4nl_id", "xq_repack_iq4nl"):
+                      "xq_bench_stream_read", "xq_gemv_q4k_id", "xq_gemv_iq4nl_id", "xq_repack_iq4nl",
+                      "xq_gemv_q4_0"):
                 getattr(L, f).restype = S
             for f in ("xq_q8k_bytes", "xq_q4k_bytes", "xq_iq4nl_bytes"):
                 getattr(L, f).argtypes = [I, I]
@@ -145,6 +147,12 @@ def xq_gemv_iq4nl(y, w, xq, N: int, K: int, stream=None) -> None:
     _check(lib().xq_gemv_iq4nl(_ptr(y, 4 * N, "y"), _ptr(w, xq_iq4nl_bytes(N, K), "w"),
                                _ptr(xq, xq_q8k_bytes(1, K), "xq"), N, K, _stream(stream)),
            "xq_gemv_iq4nl")
+
+
+def xq_gemv_q4_0(y, w, xq, N: int, K: int, stream=None) -> None:
+    _check(lib().xq_gemv_q4_0(_ptr(y, 4 * N, "y"), _ptr(w, xq_iq4nl_bytes(N, K), "w"),
+                              _ptr(xq, xq_q8k_bytes(1, K), "xq"), N, K, _stream(stream)),
+           "xq_gemv_q4_0")
 
 
 def xq_gemv_q4k_id(y, slab, xq, sel, n_experts: int, used: int, rows: int, K: int,

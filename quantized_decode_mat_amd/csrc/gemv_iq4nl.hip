@@ -56,21 +56,49 @@ __device__ __forceinline__ uint32_t lut4(uint32_t nib) {
   return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// The two formats on this row shape. IQ4_NL: weight = d * kv[nibble].
+// Q4_0: weight = d * (nibble - 8), the -8 paid once per 32-block from the
+// activation's stored sum of those 32 codes ("25 — Writing XPU Kernels",
+// section 25.2: the Q4_0 twin, whose offset rides on the activation sum).
+constexpr int kFmtIQ4NL = 0;
+constexpr int kFmtQ4_0 = 1;
+
+// Integer dot of one 32-block: payload byte t gives weight t (low nibble,
+// against a0) and weight t+16 (high nibble, against a1); s is the block's
+// activation code sum (read only by Q4_0).
+template <int FMT>
+__device__ __forceinline__ int block_dot(const uint4 pay, const uint4 a0, const uint4 a1, int s) {
+  if constexpr (FMT == kFmtIQ4NL) {
+    int dot = sdot4(lut4(pay.x), a0.x, 0);
+    dot = sdot4(lut4(pay.y), a0.y, dot);
+    dot = sdot4(lut4(pay.z), a0.z, dot);
+    dot = sdot4(lut4(pay.w), a0.w, dot);
+    dot = sdot4(lut4(pay.x >> 4), a1.x, dot);
+    dot = sdot4(lut4(pay.y >> 4), a1.y, dot);
+    dot = sdot4(lut4(pay.z >> 4), a1.z, dot);
+    return sdot4(lut4(pay.w >> 4), a1.w, dot);
+  } else {
+    // The 4-bit codes 0..15 are valid signed bytes.
+    int dot = sdot4(pay.x & 0x0F0F0F0Fu, a0.x, -8 * s);
+    dot = sdot4(pay.y & 0x0F0F0F0Fu, a0.y, dot);
+    dot = sdot4(pay.z & 0x0F0F0F0Fu, a0.z, dot);
+    dot = sdot4(pay.w & 0x0F0F0F0Fu, a0.w, dot);
+    dot = sdot4((pay.x >> 4) & 0x0F0F0F0Fu, a1.x, dot);
+    dot = sdot4((pay.y >> 4) & 0x0F0F0F0Fu, a1.y, dot);
+    dot = sdot4((pay.z >> 4) & 0x0F0F0F0Fu, a1.z, dot);
+    return sdot4((pay.w >> 4) & 0x0F0F0F0Fu, a1.w, dot);
+  }
+}
+
+template <int FMT>
 __device__ __forceinline__ float block_partial(const uint4 pay, uint32_t dbits,
                                                const uint8_t* act, int c) {
   const uint8_t* xb = act + (c >> 3) * kQ8KBytes;
   const uint4 a0 = *reinterpret_cast<const uint4*>(xb + (c & 7) * 32);
   const uint4 a1 = *reinterpret_cast<const uint4*>(xb + (c & 7) * 32 + 16);
   const float xs = *reinterpret_cast<const float*>(xb + 288);
-  // Byte t of the payload: low nibble = weight t, high nibble = weight t+16.
-  int dot = sdot4(lut4(pay.x), a0.x, 0);
-  dot = sdot4(lut4(pay.y), a0.y, dot);
-  dot = sdot4(lut4(pay.z), a0.z, dot);
-  dot = sdot4(lut4(pay.w), a0.w, dot);
-  dot = sdot4(lut4(pay.x >> 4), a1.x, dot);
-  dot = sdot4(lut4(pay.y >> 4), a1.y, dot);
-  dot = sdot4(lut4(pay.z >> 4), a1.z, dot);
-  dot = sdot4(lut4(pay.w >> 4), a1.w, dot);
+  const int s = (FMT == kFmtQ4_0) ? *reinterpret_cast<const int*>(xb + 256 + 4 * (c & 7)) : 0;
+  const int dot = block_dot<FMT>(pay, a0, a1, s);
   const float d = half_bits_to_float(dbits);
   return (d * xs) * static_cast<float>(dot);
 }
@@ -109,7 +137,7 @@ __device__ __forceinline__ bool select_slot(YPtr& y, BPtr& w, BPtr& xq, int N, i
   return true;
 }
 
-template <int R, int PF, bool ID>
+template <int R, int PF, bool ID, int FMT>
 __global__ __launch_bounds__(kThreads) void gemv_iq4nl_kernel(float* __restrict__ y,
                                                               const uint8_t* __restrict__ w,
                                                               const uint8_t* __restrict__ xq,
@@ -165,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void gemv_iq4nl_kernel(float* __restrict_
       const int c = (u0 + p) * kWave + lane;
       if (c < bpr) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] += block_partial(pay[r][p], dsc[r][p], act, c);
+        for (int r = 0; r < R; ++r) acc[r] += block_partial<FMT>(pay[r][p], dsc[r][p], act, c);
       }
     }
   }
@@ -190,7 +218,7 @@ __device__ __forceinline__ uint4 load_nt16(const uint8_t* p) {
 }
 
 // U: units per row (1..kResidentUnits). One row per wave per step.
-template <int U, bool ID>
+template <int U, bool ID, int FMT>
 __global__ __launch_bounds__(kResThreads) void gemv_iq4nl_resident_kernel(
     float* __restrict__ y, const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, int N,
     int bpr, int prefix, int64_t row_bytes, int nq8, IdArgs id) {
@@ -218,6 +246,7 @@ __global__ __launch_bounds__(kResThreads) void gemv_iq4nl_resident_kernel(
   // block's loads and drop their contribution.
   uint4 a0[U], a1[U];
   float xs[U];
+  int sums[U];
   int cc[U];
   bool live[U];
 #pragma unroll
@@ -229,6 +258,7 @@ __global__ __launch_bounds__(kResThreads) void gemv_iq4nl_resident_kernel(
     a0[u] = *reinterpret_cast<const uint4*>(xb + (cc[u] & 7) * 32);
     a1[u] = *reinterpret_cast<const uint4*>(xb + (cc[u] & 7) * 32 + 16);
     xs[u] = *reinterpret_cast<const float*>(xb + 288);
+    sums[u] = (FMT == kFmtQ4_0) ? *reinterpret_cast<const int*>(xb + 256 + 4 * (cc[u] & 7)) : 0;
   }
 
   uint4 pa[U], pb[U];
@@ -245,14 +275,7 @@ __global__ __launch_bounds__(kResThreads) void gemv_iq4nl_resident_kernel(
     float acc = 0.0f;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      int dot = sdot4(lut4(p[u].x), a0[u].x, 0);
-      dot = sdot4(lut4(p[u].y), a0[u].y, dot);
-      dot = sdot4(lut4(p[u].z), a0[u].z, dot);
-      dot = sdot4(lut4(p[u].w), a0[u].w, dot);
-      dot = sdot4(lut4(p[u].x >> 4), a1[u].x, dot);
-      dot = sdot4(lut4(p[u].y >> 4), a1[u].y, dot);
-      dot = sdot4(lut4(p[u].z >> 4), a1[u].z, dot);
-      dot = sdot4(lut4(p[u].w >> 4), a1[u].w, dot);
+      const int dot = block_dot<FMT>(p[u], a0[u], a1[u], sums[u]);
       const float v = (half_bits_to_float(d[u]) * xs[u]) * static_cast<float>(dot);
       acc += live[u] ? v : 0.0f;
     }
@@ -280,7 +303,7 @@ __global__ __launch_bounds__(kResThreads) void gemv_iq4nl_resident_kernel(
   }
 }
 
-template <int U>
+template <int U, int FMT>
 hipError_t launch_resident(float* y, const uint8_t* w, const uint8_t* xq, int N, int bpr,
                            int prefix, int64_t row_bytes, int nq8, const IdArgs& id,
                            hipStream_t stream) {
@@ -288,30 +311,31 @@ hipError_t launch_resident(float* y, const uint8_t* w, const uint8_t* xq, int N,
   if (grid > kResMaxGroups) grid = kResMaxGroups;
   const size_t lds = static_cast<size_t>(nq8) * kQ8KBytes;
   if (id.sel)
-    hipLaunchKernelGGL((gemv_iq4nl_resident_kernel<U, true>), dim3(grid, id.used),
+    hipLaunchKernelGGL((gemv_iq4nl_resident_kernel<U, true, FMT>), dim3(grid, id.used),
                        dim3(kResThreads), lds, stream, y, w, xq, N, bpr, prefix, row_bytes, nq8,
                        id);
   else
-    hipLaunchKernelGGL((gemv_iq4nl_resident_kernel<U, false>), dim3(grid), dim3(kResThreads),
+    hipLaunchKernelGGL((gemv_iq4nl_resident_kernel<U, false, FMT>), dim3(grid), dim3(kResThreads),
                        lds, stream, y, w, xq, N, bpr, prefix, row_bytes, nq8, id);
   return hipGetLastError();
 }
 
-template <int PF>
+template <int PF, int FMT>
 hipError_t launch_staged(float* y, const uint8_t* w, const uint8_t* xq, int N, int bpr, int prefix,
                          int64_t row_bytes, int nq8, const IdArgs& id, hipStream_t stream) {
   const int grid = (N + kWavesPerGroup - 1) / kWavesPerGroup;
   const size_t lds = static_cast<size_t>(nq8) * kQ8KBytes;
   if (id.sel)
-    hipLaunchKernelGGL((gemv_iq4nl_kernel<1, PF, true>), dim3(grid, id.used), dim3(kThreads), lds,
+    hipLaunchKernelGGL((gemv_iq4nl_kernel<1, PF, true, FMT>), dim3(grid, id.used), dim3(kThreads), lds,
                        stream, y, w, xq, N, bpr, prefix, row_bytes, nq8, id);
   else
-    hipLaunchKernelGGL((gemv_iq4nl_kernel<1, PF, false>), dim3(grid), dim3(kThreads), lds, stream,
+    hipLaunchKernelGGL((gemv_iq4nl_kernel<1, PF, false, FMT>), dim3(grid), dim3(kThreads), lds, stream,
                        y, w, xq, N, bpr, prefix, row_bytes, nq8, id);
   return hipGetLastError();
 }
 
 // Dense (id.sel null) or expert-grouped launch of N rows per slot.
+template <int FMT>
 hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64_t K,
                        const IdArgs& id, hipStream_t stream) {
   const int bpr = static_cast<int>(K / 32);
@@ -326,14 +350,14 @@ hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64
   // 4096: 76.4 us with one row-pair per wave and the activation read from LDS
   // per row, 47.5 us resident).
   switch (units) {
-    case 1: return launch_resident<1>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
-    case 2: return launch_resident<2>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
-    case 3: return launch_resident<3>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
-    case 4: return launch_resident<4>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
-    case 5: return launch_staged<5>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
-    case 6: return launch_staged<6>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
-    case 7: return launch_staged<7>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
-    default: return launch_staged<8>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    case 1: return launch_resident<1, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    case 2: return launch_resident<2, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    case 3: return launch_resident<3, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    case 4: return launch_resident<4, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    case 5: return launch_staged<5, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    case 6: return launch_staged<6, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    case 7: return launch_staged<7, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    default: return launch_staged<8, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
   }
 }
 
@@ -341,7 +365,12 @@ hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64
 
 hipError_t launch_gemv_iq4nl(float* y, const void* w, const void* xq, int64_t N, int64_t K,
                              hipStream_t stream) {
-  return launch_rows(y, w, xq, N, K, IdArgs{nullptr, 1, 0, 0}, stream);
+  return launch_rows<kFmtIQ4NL>(y, w, xq, N, K, IdArgs{nullptr, 1, 0, 0}, stream);
+}
+
+hipError_t launch_gemv_q4_0(float* y, const void* w, const void* xq, int64_t N, int64_t K,
+                            hipStream_t stream) {
+  return launch_rows<kFmtQ4_0>(y, w, xq, N, K, IdArgs{nullptr, 1, 0, 0}, stream);
 }
 
 hipError_t launch_gemv_iq4nl_id(float* y, const void* slab, const void* xq, const int32_t* sel,
@@ -349,7 +378,7 @@ hipError_t launch_gemv_iq4nl_id(float* y, const void* slab, const void* xq, cons
                                 int64_t x_stride_blocks, hipStream_t stream) {
   const IdArgs id{sel, static_cast<int>(used), static_cast<int>(n_experts),
                   x_stride_blocks * kQ8KBytes};
-  return launch_rows(y, slab, xq, rows, K, id, stream);
+  return launch_rows<kFmtIQ4NL>(y, slab, xq, rows, K, id, stream);
 }
 
 }  // namespace xq

@@ -121,6 +121,21 @@ xq_status xq_gemv_iq4nl(float* y, const void* w, const void* xq, int64_t N, int6
                   "xq_gemv_iq4nl");
 }
 
+xq_status xq_gemv_q4_0(float* y, const void* w, const void* xq, int64_t N, int64_t K,
+                       void* stream) {
+  if (!y) return fail(XQ_E_NULL, "y is NULL");
+  if (!w) return fail(XQ_E_NULL, "w is NULL");
+  if (!xq) return fail(XQ_E_NULL, "xq is NULL");
+  if (N < 1 || N > kMaxRows) return fail(XQ_E_SHAPE, "N=%lld outside 1..2^30", (long long)N);
+  if (xq_status s = check_k(K, XQ_MAX_K)) return s;
+  if (!aligned(y, 4)) return fail(XQ_E_ALIGN, "y not 4-byte aligned");
+  if (!aligned(w, 16)) return fail(XQ_E_ALIGN, "w not 16-byte aligned");
+  if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");
+  if (xq_status s = check_device()) return s;
+  return launched(xq::launch_gemv_q4_0(y, w, xq, N, K, static_cast<hipStream_t>(stream)),
+                  "xq_gemv_q4_0");
+}
+
 static xq_status check_id(const char* fn, float* y, const void* slab, const void* xq,
                    const int32_t* sel, int64_t n_experts, int64_t used, int64_t rows, int64_t K,
                    int64_t x_stride_blocks) {

@@ -27,6 +27,8 @@ hipError_t launch_gemv_iq4nl_id(float* y, const void* slab, const void* xq, cons
 hipError_t launch_repack_iq4nl(void* resident, const void* file_blocks, int64_t n,
                                int64_t block_base, int64_t bpr, hipStream_t stream);
 int64_t repack_dword_prefix_launches();
+hipError_t launch_gemv_q4_0(float* y, const void* w, const void* xq, int64_t N, int64_t K,
+                            hipStream_t stream);
 hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, int64_t N,
                            int64_t K, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink,

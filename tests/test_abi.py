@@ -70,7 +70,7 @@ def test_quantize_refusals(args, status, text):
     assert s == status and text in err
 
 
-@pytest.mark.parametrize("fn", ["xq_gemv_q4k", "xq_gemv_iq4nl"])
+@pytest.mark.parametrize("fn", ["xq_gemv_q4k", "xq_gemv_iq4nl", "xq_gemv_q4_0"])
 @pytest.mark.parametrize("args,status,text", [
     ((0, A16, A16, 8, 256, None), xq.XQ_E_NULL, "y is NULL"),
     ((A16, 0, A16, 8, 256, None), xq.XQ_E_NULL, "w is NULL"),
