@@ -51,7 +51,7 @@ COUNTED = {
         "void xq::(anonymous namespace)::gemv_q4k_kernel<2, 2, 4, 2, true, false>", 20,
         33030144 + 5120 + 4 * 14336, ("gemv_q4k.hip", "q4k_row.h", "xq_device.h")),
     "gemv_q4k_down_4096x14336": (
-        "void xq::(anonymous namespace)::gemv_q4k_kernel<1, 4, 8, 3, false, false>", 20,
+        "void xq::(anonymous namespace)::gemv_q4k_kernel<1, 7, 8, 3, true, false>", 20,
         33030144 + 17920 + 4 * 4096, ("gemv_q4k.hip", "q4k_row.h", "xq_device.h")),
     "gemv_iq4nl_head_128256x4096": (
         "void xq::(anonymous namespace)::gemv_iq4nl_resident_kernel<2, false, 0>", 8,
@@ -61,6 +61,12 @@ COUNTED = {
         33030144 + 512 * 16 * 320 + 4 * 512 * 14336, ("gemm_q4k.hip", "xq_device.h")),
 }
 HEADLINE = "gemv_q4k_up_14336x4096"
+# The prefill product's MFMA pass: int8 MFMA work executed (in units of 512
+# ops), MFMA busy cycles summed over SIMDs, and the active cycles of the run.
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_I8", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES",
+                 "GRBM_GUI_ACTIVE")
+PREFILL = ("gemm_q4k_512x14336x4096", 2 * 512 * 14336 * 4096)
+XCDS, SIMDS = 8, 256 * 4
 
 
 # Sustained work before every timed region. After an idle spell (host-side
@@ -102,10 +108,11 @@ def parse():
                    help="read the *_kernel_trace.csv of a rocprofv3 --kernel-trace run under "
                         "TRACE_DIR and print one JSON line per kernel (calls, mean/min/max us, "
                         "mean of the last 1000 launches), then exit (no GPU needed)")
-    p.add_argument("--counters-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                   help="read the rocprofv3 CSVs of a --counters run under FETCH_SIZE and "
-                        "WRITE_SIZE, write " + os.path.relpath(COUNTERS, ROOT) + " and exit "
-                        "(no GPU needed)")
+    p.add_argument("--counters-summary", nargs="+", metavar="DIR",
+                   help="FETCH_DIR WRITE_DIR [MFMA_DIR]: read the rocprofv3 CSVs of the "
+                        "--counters runs (FETCH_SIZE; WRITE_SIZE; optionally " +
+                        " ".join(MFMA_COUNTERS) + "), write " + os.path.relpath(COUNTERS, ROOT) +
+                        " and exit (no GPU needed)")
     return p.parse_args()
 
 
@@ -155,7 +162,7 @@ def trace_summary(trace_dir):
                           "last1000_mean_us": round(sum(last) / len(last), 3)}))
 
 
-def counters_summary(fetch_dir, write_dir):
+def counters_summary(fetch_dir, write_dir, mfma_dir=None):
     """Per-kernel HBM bytes from the two --pmc runs of `bench.py --counters`.
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by what they read
     for the run's five 64 MiB device copies (64 MiB read, 64 MiB written)."""
@@ -194,6 +201,28 @@ def counters_summary(fetch_dir, write_dir):
                          "sources_sha256_16": sources_sha(srcs)}
     out = {"fetch_calibration": round(fcal, 5), "write_calibration": round(wcal, 5),
            "kernels": kernels}
+    if mfma_dir:
+        name, alg_ops = PREFILL
+        kname, n = COUNTED[name][0], COUNTED[name][1]
+        raw = {}
+        for cn in MFMA_COUNTERS:
+            v = [val for (_, nm, val) in load(mfma_dir, cn) if nm.startswith(kname)][-n:]
+            assert len(v) == n, "%s: %d dispatches of %s" % (cn, len(v), kname)
+            raw[cn] = sum(v) / n
+        kernels[name]["mfma"] = {
+            "per_launch": {k: round(v, 1) for k, v in raw.items()},
+            "int8_ops_executed": int(raw["SQ_INSTS_VALU_MFMA_MOPS_I8"] * 512),
+            "executed_over_algorithmic": round(raw["SQ_INSTS_VALU_MFMA_MOPS_I8"] * 512 / alg_ops, 4),
+            # GRBM_GUI_ACTIVE sums the eight XCDs' busy cycles; MFMA busy
+            # cycles sum over the 1024 SIMDs (256 CUs x 4).
+            "cycles_per_xcd": round(raw["GRBM_GUI_ACTIVE"] / XCDS, 1),
+            "mfma_busy_frac": round(raw["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                    (SIMDS * raw["GRBM_GUI_ACTIVE"] / XCDS), 4),
+            "useful_mfma_frac": round(raw["SQ_VALU_MFMA_BUSY_CYCLES"] /
+                                      (SIMDS * raw["GRBM_GUI_ACTIVE"] / XCDS) /
+                                      (raw["SQ_INSTS_VALU_MFMA_MOPS_I8"] * 512 / alg_ops), 4),
+            "sources_sha256_16": sources_sha(COUNTED[name][3]),
+        }
     with open(COUNTERS, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
@@ -203,6 +232,8 @@ def counters_summary(fetch_dir, write_dir):
 def main():
     args = parse()
     if args.counters_summary:
+        if len(args.counters_summary) not in (2, 3):
+            sys.exit("--counters-summary takes FETCH_DIR WRITE_DIR [MFMA_DIR]")
         counters_summary(*args.counters_summary)
         return
     if args.trace_summary:
@@ -246,7 +277,7 @@ def main():
 
     L = xq.lib()  # direct C calls in the timed loops: no per-call Python checks
 
-    def step(i):
+    def step(i, s=s):
         k = i % pool
         L.xq_quantize_q8k(xq1.data_ptr(), x_d.data_ptr(), 1, UP[1], s)
         L.xq_gemv_q4k(h.data_ptr(), ups[k].data_ptr(), xq1.data_ptr(), UP[0], UP[1], s)
@@ -284,6 +315,12 @@ def main():
     value = pair_bytes / (ms * 1e-3) / 1e9
     log("step %.3f us (host clock %.3f us), weight %.1f GB/s" % (ms * 1e3, wall / args.steps * 1e6,
                                                                value))
+
+    # ---- the same step replayed from a HIP graph (beside the plain figure,
+    # never instead of it): one graph holds one pass over the weight pool.
+    # Every replay is checked against the eager result first.
+    graph = graph_step(torch, step, pool, y, stream)
+    log("graph replay: %s" % graph)
 
     # ---- per-kernel durations: each kernel of the step launched back to back
     # n_k times on the step's stream (weights still rotating through the
@@ -347,30 +384,11 @@ def main():
     }
 
     # ---- CPU baseline: the oracle over whole FFN pairs ----
-    cpu = None
+    cpu = cpu_all = None
     if not args.no_cpu:
-        import oracle
-        o = oracle.default()
-        reps = 0
-        t0 = time.perf_counter()
-        while True:
-            xq_h = o.quantize_q8k(x)
-            hh, _ = o.gemv_q4k(w_up, xq_h, *UP)
-            xq_h2 = o.quantize_q8k(hh.astype(np.float32).reshape(1, -1))
-            o.gemv_q4k(w_dn, xq_h2, *DOWN)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= args.cpu_seconds:
-                break
-        cpu = {
-            "value": round(reps * pair_bytes / el / 1e9, 4),
-            "unit": "GB/s",
-            "cores": 1,
-            "kind": "oracle",
-            "sample": "%d whole FFN pairs (quantize, up 14336x4096, quantize, down "
-                      "4096x14336), single-threaded plain C oracle, %.1f s" % (reps, el),
-        }
+        cpu, cpu_all = cpu_legs(args, x, w_up, w_dn, pair_bytes)
         log("cpu oracle: %s" % cpu)
+        log("cpu oracle, all cores: %s" % cpu_all)
 
     line = {
         "metric": METRIC,
@@ -403,7 +421,10 @@ def main():
         "stream_read_33MB_GBps": round(stream_small_gbps, 1),
         "frac_of_stream_read": round(value / stream_gbps, 4),
         "host_us_per_step": round(wall / args.steps * 1e6, 3),
+        "graph_replay": graph,
     }
+    if cpu_all is not None:
+        line["cpu_baseline_all_cores"] = cpu_all
 
     if args.suite:
         del ups, dns
@@ -415,6 +436,103 @@ def main():
     if args.json_out:
         with open(args.json_out, "w") as f:
             f.write(out + "\n")
+
+
+def graph_step(torch, step, pool, y, stream):
+    """Capture `pool` consecutive steps into one HIP graph on a side stream,
+    check three replays (with eager steps between them) against the eager
+    output, then time 300 replays. Returns the per-step figure, or the reason
+    there is none."""
+    step(0)
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    cs = torch.cuda.Stream()
+    gr = torch.cuda.CUDAGraph()
+    s_main = stream.cuda_stream
+    with torch.cuda.graph(gr, stream=cs, capture_error_mode="thread_local"):
+        sc = torch.cuda.current_stream().cuda_stream
+        for k in range(pool):
+            step(k, sc)
+    torch.cuda.synchronize()
+    for r in range(3):
+        y.zero_()
+        gr.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(y, y_eager):
+            return {"us_per_step": None, "note": "replay %d differs from the eager step" % r}
+        step(r, s_main)
+        torch.cuda.synchronize()
+    us = _time_loop(torch, stream, lambda i: gr.replay(), 300) / pool
+    return {"us_per_step": round(us, 3), "steps_per_replay": pool,
+            "note": "replays checked equal to the eager step"}
+
+
+def cpu_legs(args, x, w_up, w_dn, pair_bytes):
+    """The oracle, as it stands, over whole FFN pairs: single-threaded, then
+    row-split over the host's cores (the same C calls on row lists, one per
+    thread; ctypes drops the GIL for the call). Each leg is the median of
+    three rounds that together take about args.cpu_seconds."""
+    import concurrent.futures as cf
+    import oracle
+    o = oracle.default()
+    cores = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16")), 16)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+
+    def pair_1():
+        xq_h = o.quantize_q8k(x)
+        hh, _ = o.gemv_q4k(w_up, xq_h, *UP)
+        xq_h2 = o.quantize_q8k(hh.astype(np.float32).reshape(1, -1))
+        o.gemv_q4k(w_dn, xq_h2, *DOWN)
+
+    pool = cf.ThreadPoolExecutor(max_workers=cores)
+    up_parts = np.array_split(np.arange(UP[0]), cores)
+    dn_parts = np.array_split(np.arange(DOWN[0]), cores)
+
+    def split_gemv(w, xq_b, shape, parts):
+        outs = list(pool.map(lambda r: o.gemv_q4k(w, xq_b, *shape, rows=r)[0], parts))
+        return np.concatenate(outs)
+
+    def pair_n():
+        xq_h = o.quantize_q8k(x)
+        hh = split_gemv(w_up, xq_h, UP, up_parts)
+        xq_h2 = o.quantize_q8k(hh.astype(np.float32).reshape(1, -1))
+        split_gemv(w_dn, xq_h2, DOWN, dn_parts)
+
+    def leg(fn, seconds):
+        rates, total = [], 0
+        for _ in range(3):
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                fn()
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= seconds / 3:
+                    break
+            rates.append(reps * pair_bytes / el / 1e9)
+            total += reps
+        return sorted(rates)[1], rates, total
+
+    v1, r1, n1 = leg(pair_1, args.cpu_seconds)
+    vn, rn, nn = leg(pair_n, args.cpu_seconds / 2)
+    pool.shutdown()
+    sample = ("whole FFN pairs (quantize, up 14336x4096, quantize, down 4096x14336) on the "
+              "plain C oracle; median of 3 rounds")
+    one = {"value": round(v1, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": "%d %s, single-threaded, %.0f s" % (n1, sample, args.cpu_seconds),
+           "rounds_GBps": [round(r, 4) for r in r1], "cpu": model}
+    alln = {"value": round(vn, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "%d %s, rows split over %d threads, %.0f s" % (
+                nn, sample, cores, args.cpu_seconds / 2),
+            "rounds_GBps": [round(r, 4) for r in rn], "cpu": model}
+    return one, alln
 
 
 def counters_run(torch, xq, L, dev, stream, ups, dns, xq1, xq2, h, y, x_d, pool):
@@ -512,6 +630,49 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
         lines.append(d)
         log("suite: " + json.dumps(d))
 
+    def matvec_line(name, ws, wb, call, n):
+        """Time `call` over the rotating pool `ws`, then the streaming read of
+        the same wb bytes over the same pool (like for like: same launch and
+        ramp costs), and emit both."""
+        us = _time_loop(torch, stream, call, n)
+        sink = torch.empty(xq.xq_bench_sink_words(wb), dtype=torch.int32, device=dev)
+        sus = _time_loop(torch, stream, lambda i: L.xq_bench_stream_read(
+            ws[i % len(ws)].data_ptr(), wb, sink.data_ptr(), s), n)
+        emit({"workload": name, "us": round(us, 3), "weight_GBps": round(wb / us / 1e3, 1),
+              "frac_of_8TBps": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4),
+              "frac_of_stream_read": round(wb / us / 1e3 / stream_gbps, 4),
+              "stream_read_same_size_us": round(sus, 3),
+              "frac_of_stream_read_same_size": round(sus / us, 4)})
+
+    # The streaming read itself over sizes, each cold (windows rotate through
+    # a pool past the caches), and the fit t = b + bytes / rate that splits
+    # the fixed cost of a launch from the rate.
+    pool_bytes = (args.pool_mb * 1000 * 1000) // 4096 * 4096
+    big = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+    big.fill_(1)
+    pts = []
+    for sz, n in ((9437184, 1000), (33030144, 1000), (132120576, 300), (295501824, 100),
+                  (1 << 30, 30)):
+        nwin = max(1, pool_bytes // sz)
+        sink = torch.empty(xq.xq_bench_sink_words(sz), dtype=torch.int32, device=dev)
+        us = _time_loop(torch, stream, lambda i: L.xq_bench_stream_read(
+            big.data_ptr() + (i % nwin) * sz, sz, sink.data_ptr(), s), n)
+        pts.append((sz, us))
+    A = np.array([[1.0, b] for b, _ in pts])
+    coef, *_ = np.linalg.lstsq(A, np.array([u for _, u in pts]), rcond=None)
+    emit({"workload": "stream_read_sizes", "points": [
+        {"bytes": b, "us": round(u, 3), "GBps": round(b / u / 1e3, 1)} for b, u in pts],
+        "fit_fixed_us": round(float(coef[0]), 3), "fit_rate_GBps": round(1e-3 / float(coef[1]), 1),
+        "windows": "rotating over %d MB" % (pool_bytes // 1000000)})
+    # A plain device-to-device copy of up to 1 GiB (torch's copy_, read + write).
+    cb = min(1 << 30, pool_bytes)
+    dst = torch.empty(cb, dtype=torch.uint8, device=dev)
+    us = _time_loop(torch, stream, lambda i: dst.copy_(big[:cb]), 30)
+    emit({"workload": "copy_dtod", "bytes": cb, "us": round(us, 3),
+          "read_plus_write_GBps": round(2 * cb / us / 1e3, 1)})
+    del big, dst
+    torch.cuda.empty_cache()
+
     # Q4_K mat-vecs alone: 4096x4096 and the two FFN shapes.
     for name, (N, K), seed in (("q4k_4096x4096", (4096, 4096), wl.SEEDS["q4k_4096"]),
                                ("q4k_up_14336x4096", UP, wl.SEEDS["ffn_up"]),
@@ -524,12 +685,8 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
         xq.xq_quantize_q8k(xqb, xv, 1, K)
         ws = _pool_copies(w, args.pool_mb)
         yy = torch.empty(N, dtype=torch.float32, device=dev)
-        us = _time_loop(torch, stream, lambda i: L.xq_gemv_q4k(
+        matvec_line(name, ws, w.numel(), lambda i: L.xq_gemv_q4k(
             yy.data_ptr(), ws[i % len(ws)].data_ptr(), xqb.data_ptr(), N, K, s), 1000)
-        wb = w.numel()
-        emit({"workload": name, "us": round(us, 3), "weight_GBps": round(wb / us / 1e3, 1),
-              "frac_of_8TBps": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4),
-              "frac_of_stream_read": round(wb / us / 1e3 / stream_gbps, 4)})
         del ws, w
         torch.cuda.empty_cache()
 
@@ -545,12 +702,8 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
         ws = _pool_copies(w, args.pool_mb)
         yy = torch.empty(N, dtype=torch.float32, device=dev)
         n = 1000 if N < 100000 else 200
-        us = _time_loop(torch, stream, lambda i: L.xq_gemv_iq4nl(
+        matvec_line(name, ws, w.numel(), lambda i: L.xq_gemv_iq4nl(
             yy.data_ptr(), ws[i % len(ws)].data_ptr(), xqb.data_ptr(), N, K, s), n)
-        wb = w.numel()
-        emit({"workload": name, "us": round(us, 3), "weight_GBps": round(wb / us / 1e3, 1),
-              "frac_of_8TBps": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4),
-              "frac_of_stream_read": round(wb / us / 1e3 / stream_gbps, 4)})
         del ws, w
         torch.cuda.empty_cache()
 
@@ -565,12 +718,8 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
         ws = _pool_copies(w, args.pool_mb)
         yy = torch.empty(N, dtype=torch.float32, device=dev)
         n = 1000 if N < 100000 else 200
-        us = _time_loop(torch, stream, lambda i: L.xq_gemv_q4_0(
+        matvec_line(name, ws, w.numel(), lambda i: L.xq_gemv_q4_0(
             yy.data_ptr(), ws[i % len(ws)].data_ptr(), xqb.data_ptr(), N, K, s), n)
-        wb = w.numel()
-        emit({"workload": name, "us": round(us, 3), "weight_GBps": round(wb / us / 1e3, 1),
-              "frac_of_8TBps": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4),
-              "frac_of_stream_read": round(wb / us / 1e3 / stream_gbps, 4)})
         del ws, w
         torch.cuda.empty_cache()
 

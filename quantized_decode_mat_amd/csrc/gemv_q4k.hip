@@ -191,8 +191,12 @@ hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64
   // Launch shapes chosen by measurement on MI355X (cold weights):
   //  * rows of one or two units: every load of a row in flight at once,
   //    two rows per wave when there are enough rows to fill the device;
-  //  * longer rows: batches of four units, eight waves per workgroup (the
-  //    activation row is staged half as often), loads past the row skipped.
+  //  * rows of five to seven units: the whole row in flight at once (clamped
+  //    loads, static wait counts), eight waves per workgroup (the activation
+  //    row is staged half as often): 3-15% faster than two batches;
+  //  * longer rows: batches of four units, eight waves per workgroup, loads
+  //    past the row skipped (a whole row of eight or more units in flight
+  //    is slower).
   if (units == 1) {
     if (N >= 8192) return launch_cfg<2, 1, 4, 2, true>(y, wb, xb, n, nb, id, stream);
     return launch_cfg<1, 1, 4, 2, true>(y, wb, xb, n, nb, id, stream);
@@ -203,6 +207,9 @@ hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64
   }
   if (units == 3) return launch_cfg<1, 3, 8, 2, true>(y, wb, xb, n, nb, id, stream);
   if (units == 4) return launch_cfg<1, 4, 8, 3, true>(y, wb, xb, n, nb, id, stream);
+  if (units == 5) return launch_cfg<1, 5, 8, 3, true>(y, wb, xb, n, nb, id, stream);
+  if (units == 6) return launch_cfg<1, 6, 8, 3, true>(y, wb, xb, n, nb, id, stream);
+  if (units == 7) return launch_cfg<1, 7, 8, 3, true>(y, wb, xb, n, nb, id, stream);
   return launch_cfg<1, 4, 8, 3, false>(y, wb, xb, n, nb, id, stream);
 }
 

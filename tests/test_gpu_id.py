@@ -133,7 +133,8 @@ def test_id_out_of_range_selection(fmt):
 ID_SHAPES = [
     # fmt, E, rows, K, ids: the other launch shapes of the dense kernels
     ("q4k", 4, 8192, 4096, [3, 1]),         # two rows per wave
-    ("q4k", 3, 300, 14336, [2, 0]),         # loads past the row skipped (7 units)
+    ("q4k", 3, 300, 14336, [2, 0]),         # whole row in flight (7 units)
+    ("q4k", 3, 130, 20480, [1, 0]),         # loads past the row skipped (10 units)
     ("q4k", 3, 257, 6144, [1, 2, 0]),       # three units
     ("iq4nl", 3, 20000, 512, [2, 0]),       # persistent grid, waves take a second row
     ("iq4nl", 3, 1000, 10240, [0, 2]),      # staged kernel (five units)

@@ -161,6 +161,12 @@ Q4K_SHAPES = [
     ("n9000_k4352", 9000, 4352, 3004),
     ("n8193_k2048_tworow", 8193, 2048, 3005),
     ("n64_kmax", 64, 49152, 3006),
+    ("n77_k10240_five_units", 77, 10240, 3007),
+    ("n300_k9472_five_units_ragged", 300, 9472, 3008),
+    ("n257_k12288_six_units", 257, 12288, 3009),
+    ("n33_k11264_six_units_ragged", 33, 11264, 3010),
+    ("n1000_k14080_seven_units_ragged", 1000, 14080, 3011),
+    ("n50_k16384_eight_units", 50, 16384, 3012),
 ]
 
 
