@@ -797,6 +797,28 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
     del ws, w
     torch.cuda.empty_cache()
 
+    # The same product at token counts and shapes that leave the plain grid
+    # short of the device (K split over workgroups): a 16-token batch on the
+    # up matrix, 64 and 512 tokens on the down matrix.
+    for M, (N, K), seed in ((16, UP, wl.SEEDS["prefill"]), (64, DOWN, wl.SEEDS["ffn_down"]),
+                            (512, DOWN, wl.SEEDS["ffn_down"])):
+        g = wl.rng(seed)
+        w = torch.from_numpy(wl.q4k_weights(N, K, g).reshape(-1)).to(dev)
+        xv = torch.from_numpy(wl.activations(M, K, g).reshape(-1)).to(dev)
+        xqb = torch.empty(xq.xq_q8k_bytes(M, K), dtype=torch.uint8, device=dev)
+        xq.xq_quantize_q8k(xqb, xv, M, K)
+        yy = torch.empty(M * N, dtype=torch.float32, device=dev)
+        ws = _pool_copies(w, args.pool_mb)
+        us = _time_loop(torch, stream, lambda i: L.xq_gemm_q4k_small_m(
+            yy.data_ptr(), ws[i % len(ws)].data_ptr(), xqb.data_ptr(), M, N, K, s), 200)
+        ops = 2.0 * M * N * K
+        emit({"workload": "gemm_q4k_%dx%dx%d" % (M, N, K), "us": round(us, 3),
+              "TOPS": round(ops / us / 1e6, 1),
+              "frac_of_int8_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS, 4),
+              "weight_GBps": round(w.numel() / us / 1e3, 1)})
+        del ws, w
+        torch.cuda.empty_cache()
+
     if args.suite_out:
         with open(args.suite_out, "w") as f:
             for d in lines:

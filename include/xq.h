@@ -117,7 +117,16 @@ xq_status xq_gemv_iq4nl(float *y, const void *w, const void *xq, int64_t N, int6
  *  xq  device, in: q8_K [M][K/256], 16-byte aligned.
  *  1 <= M <= 2^30.  1 <= N <= 2^30.  K >= 256, a multiple of 256. Each of
  *  xq and w below 2 GiB (the kernel's loads use 32-bit offsets).
- * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH.
+ * Shapes with at most 256 tiles of 64 tokens x 128 rows split K over several
+ * workgroups (section 25.3: fill the device first); the partials go through
+ * a workspace the library owns, one per (device, stream): 16 MiB allocated,
+ * zeroed and synchronized on the first such call on a stream, kept until the
+ * process ends. That first call therefore cannot be captured into a graph;
+ * later ones allocate nothing. Splits are summed in a fixed order, so
+ * results are bit-identical from call to call. Calls on one stream are
+ * ordered; calls on different streams use different workspaces.
+ * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH (also
+ * when the workspace cannot be allocated).
  */
 xq_status xq_gemm_q4k_small_m(float *y, const void *w, const void *xq, int64_t M, int64_t N,
                               int64_t K, void *stream);

@@ -26,6 +26,20 @@
 // workgroups share a CU and run out of phase, so one's VALU work (decode,
 // epilogue) overlaps the other's MFMAs. Workgroups are laid out so that the
 // token tiles sharing one weight tile land on one XCD (one L2).
+//
+// Split-K (section 25.3: a launch that cannot fill the device cannot be
+// fast). With few tiles (a short token batch, or few weight rows) the grid
+// is tiles x ks: split s of a tile takes super-blocks [s*nb/ks, (s+1)*nb/ks),
+// writes its f32 partial to a workspace slot and counts its arrival; the
+// split that arrives last sums the ks partials in the fixed order 0..ks-1
+// and writes Y, so the result does not depend on arrival order. Partials
+// and counters cross XCDs through agent-scope atomic loads and stores
+// (coherent without an L2 write-back); the last arrival resets the counter,
+// so counters are zero between launches.
+#include <algorithm>
+#include <mutex>
+#include <unordered_map>
+
 #include "xq_device.h"
 #include "xq_launch.h"
 
@@ -170,23 +184,34 @@ __device__ __forceinline__ void issue_stage(uint8_t* base, const uint8_t* xq, co
 constexpr int kWaitVm0 = 0x0F70;
 constexpr int kWaitVmStage = 0x0F70 | kLoadsPerWave;
 
+// A partial slot: the 32 f32 accumulators of each of the 256 threads,
+// element r of thread i at r * kThreads + i (one wave store covers 256
+// consecutive bytes).
+constexpr int kPartFloats = kThreads * 32;
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
                      const uint8_t* __restrict__ xq, int M, int N, int nb, int mtiles,
-                     int ntiles) {
+                     int ntiles, int ks, float* __restrict__ part, int* __restrict__ cnt) {
   __shared__ __align__(16) uint8_t stage0[kStageBytes];
   __shared__ __align__(16) uint8_t stage1[kStageBytes];
+  __shared__ int last_arrival;
 
-  // Workgroup -> tile. When the tile count is a multiple of the 8 XCDs,
-  // XCD x (= id % 8) takes a contiguous run of tiles in which the token tiles
-  // of one weight tile are adjacent.
-  const int T = mtiles * ntiles;
+  // Workgroup -> (split, tile). When the workgroup count is a multiple of the
+  // 8 XCDs, XCD x (= id % 8) takes a contiguous run in which the token tiles
+  // of one weight tile (same split) are adjacent.
+  const int tiles = mtiles * ntiles;
+  const int T = tiles * ks;
   int t = blockIdx.x;
   if (T % 8 == 0) t = (blockIdx.x % 8) * (T / 8) + blockIdx.x / 8;
-  const int ntile = t / mtiles;
-  const int mtile = t % mtiles;
+  const int split = t / tiles;
+  const int tile = t - split * tiles;
+  const int ntile = tile / mtiles;
+  const int mtile = tile % mtiles;
   const int m0 = mtile * BM;
   const int n0 = ntile * BN;
+  const int b_lo = static_cast<int>(static_cast<int64_t>(split) * nb / ks);
+  const int b_hi = static_cast<int>(static_cast<int64_t>(split + 1) * nb / ks);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -203,7 +228,7 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
   const v4i zero = {0, 0, 0, 0};
 
   const StageOffsets so = stage_offsets(M, N, nb, m0, n0, wave, lane);
-  issue_stage(stage0, xq, w, so, 0, wave);
+  issue_stage(stage0, xq, w, so, b_lo, wave);
 
   // One super-block: wait for its stage, refill the other stage with
   // super-block b+1 (every wave finished reading it: it passed the barrier
@@ -211,7 +236,7 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
   auto step = [&](int b, const uint8_t* stg, uint8_t* refill) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    if (b + 1 < nb) issue_stage(refill, xq, w, so, b + 1, wave);
+    if (b + 1 < b_hi) issue_stage(refill, xq, w, so, b + 1, wave);
 
     const uint8_t* act = stg;
     const float* xs_s = reinterpret_cast<const float*>(stg + kXsOff);
@@ -298,9 +323,72 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
   };
 
   // The ring unrolled by two so each stage is a distinct LDS object.
-  for (int b = 0; b < nb; b += 2) {
+  for (int b = b_lo; b < b_hi; b += 2) {
     step(b, stage0, stage1);
-    if (b + 1 < nb) step(b + 1, stage1, stage0);
+    if (b + 1 < b_hi) step(b + 1, stage1, stage0);
+  }
+
+  if (ks > 1) {
+    // ---- split-K: publish this split's partial, count the arrival ----
+    float* mine = part + static_cast<int64_t>(tile * ks + split) * kPartFloats + tid;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int r = 4 * (2 * mt + nt);
+        __hip_atomic_store(mine + (r + 0) * kThreads, acc[mt][nt].x, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(mine + (r + 1) * kThreads, acc[mt][nt].y, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(mine + (r + 2) * kThreads, acc[mt][nt].z, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(mine + (r + 3) * kThreads, acc[mt][nt].w, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    // Every store of this wave has completed before the workgroup counts its
+    // arrival, so the split that sees the count reach ks - 1 reads whole
+    // partials.
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    if (tid == 0)
+      last_arrival = __hip_atomic_fetch_add(cnt + tile, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) == ks - 1;
+    __syncthreads();
+    if (!last_arrival) return;  // workgroup-uniform
+    if (tid == 0) __hip_atomic_store(cnt + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The sum over splits in the fixed order 0..ks-1 (this split's own
+    // values from registers).
+    float4 sum[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) sum[mt][nt] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < ks; ++j) {
+      const float* pj = part + static_cast<int64_t>(tile * ks + j) * kPartFloats + tid;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          float4 v;
+          if (j == split) {
+            v = acc[mt][nt];
+          } else {
+            const int r = 4 * (2 * mt + nt);
+            v.x = __hip_atomic_load(pj + (r + 0) * kThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v.y = __hip_atomic_load(pj + (r + 1) * kThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v.z = __hip_atomic_load(pj + (r + 2) * kThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v.w = __hip_atomic_load(pj + (r + 3) * kThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          sum[mt][nt].x += v.x;
+          sum[mt][nt].y += v.y;
+          sum[mt][nt].z += v.z;
+          sum[mt][nt].w += v.w;
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = sum[mt][nt];
   }
 
   // ---- store ----
@@ -319,18 +407,83 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
     }
 }
 
+// Split-K workspace: kSplitSlots partial slots (16 MiB) and one counter per
+// tile for up to kSplitTiles tiles, one per (device, stream) so that calls on
+// different streams never share it; allocated and zeroed on a stream's
+// first split launch, kept until the process ends.
+constexpr int kSplitSlots = 512;   // tiles * ks stays within this
+constexpr int kSplitTiles = 256;   // above this many tiles, no split
+constexpr size_t kSplitBytes =
+    static_cast<size_t>(kSplitSlots) * kPartFloats * sizeof(float) + kSplitTiles * sizeof(int);
+
+struct Workspace {
+  float* part;
+  int* cnt;
+};
+
+hipError_t split_workspace(hipStream_t stream, Workspace* out) {
+  static std::mutex mu;
+  static std::unordered_map<uint64_t, Workspace> spaces;  // key: device << 48 ^ stream
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t key = (static_cast<uint64_t>(dev) << 48) ^ reinterpret_cast<uintptr_t>(stream);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = spaces.find(key);
+  if (it != spaces.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  if ((e = hipMalloc(&p, kSplitBytes)) != hipSuccess) return e;
+  float* part = static_cast<float*>(p);
+  int* cnt = reinterpret_cast<int*>(part + static_cast<size_t>(kSplitSlots) * kPartFloats);
+  if ((e = hipMemset(cnt, 0, kSplitTiles * sizeof(int))) != hipSuccess ||
+      (e = hipDeviceSynchronize()) != hipSuccess) {
+    (void)hipFree(p);
+    return e;
+  }
+  *out = spaces[key] = Workspace{part, cnt};
+  return hipSuccess;
+}
+
 }  // namespace
 
-hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, int64_t N,
-                           int64_t K, hipStream_t stream) {
+int gemm_q4k_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t nb = K / 256;
+  if (tiles > kSplitTiles) return 1;
+  // Measured on MI355X (cold weights, 14336x4096 and 4096x14336): the best
+  // launches stay within one round of resident workgroups (two per CU, 512)
+  // and give each split at least ~7 super-blocks; more, shorter splits pay
+  // the per-workgroup prologue and the partial exchange.
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(kSplitSlots / tiles, nb / 7)));
+}
+
+hipError_t launch_gemm_q4k_split(float* y, const void* w, const void* xq, int64_t M, int64_t N,
+                                 int64_t K, int ks, hipStream_t stream) {
   const int nb = static_cast<int>(K / 256);
   const int mtiles = static_cast<int>((M + BM - 1) / BM);
   const int ntiles = static_cast<int>((N + BN - 1) / BN);
-  const int grid = mtiles * ntiles;
-  hipLaunchKernelGGL(gemm_q4k_kernel, dim3(grid), dim3(kThreads), 0, stream, y,
+  const int tiles = mtiles * ntiles;
+  Workspace ws{nullptr, nullptr};
+  if (ks > 1) {
+    if (tiles > kSplitTiles || tiles * ks > kSplitSlots || ks > nb) return hipErrorInvalidValue;
+    const hipError_t e = split_workspace(stream, &ws);
+    if (e != hipSuccess) return e;
+  } else {
+    ks = 1;
+  }
+  hipLaunchKernelGGL(gemm_q4k_kernel, dim3(tiles * ks), dim3(kThreads), 0, stream, y,
                      static_cast<const uint8_t*>(w), static_cast<const uint8_t*>(xq),
-                     static_cast<int>(M), static_cast<int>(N), nb, mtiles, ntiles);
+                     static_cast<int>(M), static_cast<int>(N), nb, mtiles, ntiles, ks, ws.part,
+                     ws.cnt);
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, int64_t N,
+                           int64_t K, hipStream_t stream) {
+  return launch_gemm_q4k_split(y, w, xq, M, N, K, gemm_q4k_splits(M, N, K), stream);
 }
 
 }  // namespace xq

@@ -31,6 +31,12 @@ hipError_t launch_gemv_q4_0(float* y, const void* w, const void* xq, int64_t N, 
                             hipStream_t stream);
 hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, int64_t N,
                            int64_t K, hipStream_t stream);
+// Splits of K the small-M product uses for this shape (1: none), and the
+// product with an explicit split count (ks > 1 needs at most 256 tiles of
+// 64 x 128, tiles * ks <= 512 and ks <= K/256).
+int gemm_q4k_splits(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_q4k_split(float* y, const void* w, const void* xq, int64_t M, int64_t N,
+                                 int64_t K, int ks, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink,
                               hipStream_t stream);
 int64_t stream_read_sink_words(int64_t bytes);

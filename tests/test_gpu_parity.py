@@ -313,6 +313,72 @@ def test_gemm_full_compare(M, N, K, seed):
     assert_close(Y.reshape(-1), ref.reshape(-1), T.reshape(-1), "gemm")
 
 
+# Split-K shapes (few tiles: the grid is tiles x splits; the last split of a
+# tile to arrive sums the partials in split order).
+GEMM_SPLIT = [
+    (37, 1000, 4352, 7011),    # 17 super-blocks in two splits of 8 and 9
+    (16, 300, 14336, 7012),    # eight splits of seven super-blocks
+    (70, 129, 7936, 7013),     # 31 super-blocks, four splits, ragged M and N
+]
+
+
+@pytest.mark.parametrize("M,N,K,seed", GEMM_SPLIT)
+def test_gemm_split_full_compare(M, N, K, seed):
+    g = wl.rng(seed)
+    w = wl.q4k_weights(N, K, g)
+    x = wl.activations(M, K, g)
+    xqb = oracle.quantize_q8k(x)
+    _note("gemm split M=%d N=%d K=%d" % (M, N, K))
+    Y = gpu_gemm(w, xqb, M, N, K)
+    ref, T = oracle.gemm_q4k(w, xqb, M, N, K)
+    assert_close(Y.reshape(-1), ref.reshape(-1), T.reshape(-1), "gemm split")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 14336, 4096), (64, 4096, 14336), (256, 4096, 14336)])
+def test_gemm_split_full_size(M, N, K):
+    """The FFN shapes at token counts that split K: sampled outputs with the
+    tile corners, plus whole rows against the mat-vec oracle."""
+    g = wl.rng(7300 + M)
+    w = wl.q4k_weights(N, K, g)
+    x = wl.activations(M, K, g)
+    xqb = oracle.quantize_q8k(x)
+    _note("gemm split full size M=%d N=%d K=%d" % (M, N, K))
+    Y = gpu_gemm(w, xqb, M, N, K)
+    assert not np.isnan(Y).any()
+    s = wl.rng(7310 + M)
+    ms = np.concatenate([s.integers(0, M, 600), [0, M - 1, min(63, M - 1), min(64, M - 1)]])
+    ns = np.concatenate([s.integers(0, N, 600), [0, N - 1, 127, 128]])
+    ref, T = oracle.gemm_q4k(w, xqb, M, N, K, ms, ns)
+    assert_close(Y[ms, ns], ref, T, "split sampled")
+    for m in sorted({0, M - 1}):
+        ref, T = oracle.gemv_q4k(w, xqb[m], N, K)
+        assert_close(Y[m], ref, T, "split row %d" % m)
+
+
+def test_gemm_split_repeatable_across_calls_and_streams():
+    """Bit-identical results on repeated calls (the arrival counters reset
+    themselves) and on a second stream (its own workspace)."""
+    M, N, K = 40, 640, 8192
+    g = wl.rng(7400)
+    wd = dev(wl.q4k_weights(N, K, g))
+    xd = dev(oracle.quantize_q8k(wl.activations(M, K, g)))
+    _note("gemm split repeat")
+    outs = []
+    for _ in range(3):
+        y = poisoned_f32(M * N)
+        xq.xq_gemm_q4k_small_m(y, wd, xd, M, N, K)
+        outs.append(take_f32(y, M * N))
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        y = poisoned_f32(M * N)
+        xq.xq_gemm_q4k_small_m(y, wd, xd, M, N, K)
+    side.synchronize()
+    outs.append(take_f32(y, M * N))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    assert not np.isnan(outs[0]).any()
+
+
 def test_gemm_prefill_512x14336x4096():
     M, N, K = 512, 14336, 4096
     g = wl.rng(wl.SEEDS["prefill"])
@@ -335,8 +401,9 @@ def test_gemm_prefill_512x14336x4096():
 
 
 @pytest.mark.parametrize("which", ["S", "M"])
-def test_gemm_partials_bit_exact(which):
-    M, N, K = 3, 200, 1024
+@pytest.mark.parametrize("K", [1024, 3584])  # 3584: two splits of 7 super-blocks
+def test_gemm_partials_bit_exact(which, K):
+    M, N = 3, 200
     g = wl.rng(7200)
     w = wl.q4k_isolation_weights(N, K, g, which)
     wd = dev(w)
