@@ -819,6 +819,47 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
         del ws, w
         torch.cuda.empty_cache()
 
+    # Grouped product (mul_mat_id): 512 tokens routed top-8 over 64 experts of
+    # 1408 x 2048, one routing launch plus one product launch, against one
+    # dense product per expert over its pre-gathered token rows (the gather
+    # is not timed).
+    E, rows, K, T, U = 64, 1408, 2048, 512, 8
+    g = wl.rng(wl.SEEDS["grouped"])
+    slab_np = np.concatenate([wl.q4k_weights(rows, K, g).reshape(rows, -1) for _ in range(E)],
+                             axis=0)
+    slab = torch.from_numpy(slab_np.reshape(-1)).to(dev)
+    xv = torch.from_numpy(wl.activations(T, K, g).reshape(-1)).to(dev)
+    xqb = torch.empty(xq.xq_q8k_bytes(T, K), dtype=torch.uint8, device=dev)
+    xq.xq_quantize_q8k(xqb, xv, T, K)
+    ids_np = np.stack([g.choice(E, size=U, replace=False) for _ in range(T)]).astype(np.int32)
+    ids = torch.from_numpy(ids_np).to(dev)
+    slabs = _pool_copies(slab, args.pool_mb)
+    yy = torch.empty(T * U * rows, dtype=torch.float32, device=dev)
+    us = _time_loop(torch, stream, lambda i: L.xq_gemm_q4k_id(
+        yy.data_ptr(), slabs[i % len(slabs)].data_ptr(), xqb.data_ptr(), ids.data_ptr(), T, U, E,
+        rows, K, 0, s), 200)
+    nb8, rb = xq.xq_q8k_bytes(1, K), xq.xq_q4k_bytes(rows, K)
+    xr = xqb.view(T, nb8)
+    per = []
+    for e in range(E):
+        toks = torch.from_numpy(np.nonzero((ids_np == e).any(axis=1))[0]).to(dev)
+        if len(toks):
+            per.append((e, len(toks), xr[toks].contiguous(),
+                        torch.empty(len(toks) * rows, dtype=torch.float32, device=dev)))
+
+    def dense_all(i):
+        base = slabs[i % len(slabs)].data_ptr()
+        for e, m, xe, ye in per:
+            L.xq_gemm_q4k_small_m(ye.data_ptr(), base + e * rb, xe.data_ptr(), m, rows, K, s)
+
+    dus = _time_loop(torch, stream, dense_all, 50)
+    ops = 2.0 * T * U * rows * K
+    emit({"workload": "gemm_q4k_id_T512_top8_E64_r1408_k2048", "us": round(us, 3),
+          "TOPS": round(ops / us / 1e6, 1), "frac_of_int8_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS, 4),
+          "dense_per_expert_us": round(dus, 3), "speedup_vs_dense": round(dus / us, 3)})
+    del slabs, slab
+    torch.cuda.empty_cache()
+
     if args.suite_out:
         with open(args.suite_out, "w") as f:
             for d in lines:

@@ -131,6 +131,38 @@ xq_status xq_gemv_iq4nl(float *y, const void *w, const void *xq, int64_t N, int6
 xq_status xq_gemm_q4k_small_m(float *y, const void *w, const void *xq, int64_t M, int64_t N,
                               int64_t K, void *stream);
 
+/*
+ * Grouped Q4_K x q8_K small-M product over an expert slab (mul_mat_id; "25 —
+ * Writing XPU Kernels", section 25.3: a mixture-of-experts prefill is one
+ * launch over an expert map, padded only to the finest tile, never one
+ * product per expert). Token t's slot k uses expert e = ids[t][k]:
+ *   y[t][k][n] = sum_b xs_b * (d_enb * S_b - dmin_enb * M_b)
+ * with S, M the exact int32 block partials of expert e's row n against the
+ * pair's q8_K row, which is row t of xq (x_per_slot = 0: the slots of a
+ * token share its activation, as for up and gate) or row t * n_used + k
+ * (x_per_slot = 1: each slot has its own, as for down).
+ *
+ *  y     device, out: f32 [n_tokens][n_used][rows], 4-byte aligned. The rows
+ *        of a pair whose selection lies outside 0..n_experts-1 are NaN.
+ *  slab  device, in: n_experts experts of rows x K Q4_K weights back to back
+ *        (expert e's row n is row e * rows + n), 16-byte aligned.
+ *  xq    device, in: q8_K [n_tokens or n_tokens * n_used][K/256], 16-byte aligned.
+ *  ids   device, in: int32 [n_tokens][n_used], 4-byte aligned.
+ *  1 <= n_tokens * n_used <= 2^20.  1 <= n_experts <= 1024.  1 <= rows <= 2^30.
+ *  K >= 256, a multiple of 256. One expert's weights and all of xq below
+ *  2 GiB (32-bit offsets).
+ * A first kernel groups the pairs by expert into a tile list of at most 64
+ * pairs each, in a workspace the library owns (4.3 MB per (device, stream),
+ * allocated, zeroed and synchronized on a stream's first call, kept until
+ * the process ends; that first call cannot be captured into a graph). The
+ * product then runs once over the list. Every output is computed from its
+ * own pair alone, so results do not depend on how pairs fall into tiles.
+ * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH.
+ */
+xq_status xq_gemm_q4k_id(float *y, const void *slab, const void *xq, const int32_t *ids,
+                         int64_t n_tokens, int64_t n_used, int64_t n_experts, int64_t rows,
+                         int64_t K, int64_t x_per_slot, void *stream);
+
 /* Largest K the mat-vecs accept: the q8_K activation row is staged whole in
  * the workgroup's LDS (XQ_MAX_K/256 * 320 bytes = 60 KiB). */
 #define XQ_MAX_K 49152

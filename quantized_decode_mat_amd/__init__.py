@@ -28,7 +28,7 @@ EXPORTS = (
     "xq_quantize_q8k", "xq_gemv_q4k", "xq_gemv_iq4nl", "xq_gemm_q4k_small_m",
     "xq_q8k_bytes", "xq_q4k_bytes", "xq_iq4nl_bytes", "xq_status_name", "xq_last_error",
     "xq_bench_stream_read", "xq_bench_sink_words", "xq_gemv_q4k_id", "xq_gemv_iq4nl_id",
-    "xq_repack_iq4nl", "xq_repack_dword_prefix_launches", "xq_gemv_q4_0",
+    "xq_repack_iq4nl", "xq_repack_dword_prefix_launches", "xq_gemv_q4_0", "xq_gemm_q4k_id",
 )
 
 
@@ -57,11 +57,12 @@ def lib() -> ctypes.CDLL:
             L.xq_gemv_q4k_id.argtypes = [P, P, P, P, I, I, I, I, I, P]
             L.xq_gemv_iq4nl_id.argtypes = [P, P, P, P, I, I, I, I, I, P]
             L.xq_repack_iq4nl.argtypes = [P, P, I, I, I, P]
+            L.xq_gemm_q4k_id.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
             L.xq_repack_dword_prefix_launches.argtypes = []
             L.xq_repack_dword_prefix_launches.restype = I
             for f in ("xq_quantize_q8k", "xq_gemv_q4k", "xq_gemv_iq4nl", "xq_gemm_q4k_small_m",
                       "xq_bench_stream_read", "xq_gemv_q4k_id", "xq_gemv_iq4nl_id", "xq_repack_iq4nl",
-                      "xq_gemv_q4_0"):
+                      "xq_gemv_q4_0", "xq_gemm_q4k_id"):
                 getattr(L, f).restype = S
             for f in ("xq_q8k_bytes", "xq_q4k_bytes", "xq_iq4nl_bytes"):
                 getattr(L, f).argtypes = [I, I]
@@ -199,6 +200,18 @@ def xq_gemm_q4k_small_m(y, w, xq, M: int, N: int, K: int, stream=None) -> None:
                                      _ptr(xq, xq_q8k_bytes(M, K), "xq"), M, N, K,
                                      _stream(stream)),
            "xq_gemm_q4k_small_m")
+
+
+def xq_gemm_q4k_id(y, slab, xq, ids, n_tokens: int, n_used: int, n_experts: int, rows: int,
+                   K: int, x_per_slot: int = 0, stream=None) -> None:
+    pairs = n_tokens * n_used
+    xrows = pairs if x_per_slot else n_tokens
+    _check(lib().xq_gemm_q4k_id(_ptr(y, 4 * pairs * rows, "y"),
+                                _ptr(slab, xq_q4k_bytes(n_experts * rows, K), "slab"),
+                                _ptr(xq, xq_q8k_bytes(xrows, K), "xq"), _ptr(ids, 4 * pairs, "ids"),
+                                n_tokens, n_used, n_experts, rows, K, x_per_slot,
+                                _stream(stream)),
+           "xq_gemm_q4k_id")
 
 
 def xq_bench_sink_words(nbytes: int) -> int:

@@ -28,6 +28,7 @@ SOURCES = [
     "gemv_iq4nl.hip",
     "gemm_q4k.hip",
     "repack_iq4nl.hip",
+    "route_experts.hip",
     "stream_read.hip",
     "xq_api.cpp",
 ]

@@ -36,6 +36,14 @@
 // and counters cross XCDs through agent-scope atomic loads and stores
 // (coherent without an L2 write-back); the last arrival resets the counter,
 // so counters are zero between launches.
+//
+// Grouped form (mul_mat_id, section 25.3: one launch over an expert map,
+// never one per expert): the same kernel over a device tile list built by
+// route_experts. A tile holds up to 64 (token, slot) pairs routed to one
+// expert; the workgroup gathers their q8_K rows, multiplies them by that
+// expert's weight tile and scatters the outputs to the pairs' rows. The grid
+// is sized by an upper bound on the tile count; workgroups past the list's
+// end return at once. Tiles of out-of-range selections write NaN.
 #include <algorithm>
 #include <mutex>
 #include <unordered_map>
@@ -99,13 +107,15 @@ struct StageOffsets {
   uint32_t extra;   // fifth weight load, a repeated act load, or token scales
 };
 
+// ID: token rows come from xrow[m] (the gathered pairs' q8_K rows).
+template <bool ID>
 __device__ __forceinline__ StageOffsets stage_offsets(int M, int N, int nb, int m0, int n0,
-                                                      int wave, int lane) {
+                                                      int wave, int lane, const int* xrow) {
   StageOffsets o;
   auto act_off = [&](int j) {
     const int m = 4 * j + (lane >> 4);
     const int c = (lane & 15) ^ (m & 15);      // source chunk of this lane's slot
-    const int gm = min(m0 + m, M - 1);
+    const int gm = ID ? xrow[m] : min(m0 + m, M - 1);
     return static_cast<uint32_t>(gm) * static_cast<uint32_t>(nb) * kQ8KBytes + 16u * c;
   };
   auto w_off = [&](int j) {
@@ -123,11 +133,22 @@ __device__ __forceinline__ StageOffsets stage_offsets(int M, int N, int nb, int 
   } else if (wave == 2) {
     o.extra = act_off(wave);
   } else {
-    const int gm = min(m0 + lane, M - 1);
+    const int gm = ID ? xrow[lane] : min(m0 + lane, M - 1);
     o.extra = static_cast<uint32_t>(gm) * static_cast<uint32_t>(nb) * kQ8KBytes + 288u;
   }
   return o;
 }
+
+// The grouped form's tile list (see route_experts.hip).
+struct IdGemm {
+  const int32_t* sorted;  // pairs p = t * n_used + k, grouped by expert
+  const int4* desc;       // tile: (bucket, first index into sorted, pairs)
+  const int32_t* n_tiles; // tiles in the list
+  int n_experts;          // bucket n_experts: out-of-range selections
+  int n_used;
+  int per_slot_x;         // 1: pair p reads q8_K row p; 0: row p / n_used
+  int64_t expert_bytes;   // one expert's weights in the slab
+};
 
 // One direct global -> LDS load (gfx950 global_load_lds_dwordx4 /
 // global_load_lds_dword): lane l's bytes land at LDS address m0 + size*l.
@@ -159,8 +180,20 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
-__device__ __forceinline__ void issue_stage(uint8_t* base, const uint8_t* xq, const uint8_t* w,
-                                            const StageOffsets& o, int b, int wave) {
+// A pointer every lane holds the same value of, as a scalar (the direct
+// loads take their base in scalar registers).
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ void issue_stage(uint8_t* base, const uint8_t* xq_in,
+                                            const uint8_t* w_in, const StageOffsets& o, int b,
+                                            int wave) {
+  const uint8_t* xq = uniform_ptr(xq_in);
+  const uint8_t* w = uniform_ptr(w_in);
   const uint32_t xb = static_cast<uint32_t>(b) * kQ8KBytes;
   const uint32_t wb = static_cast<uint32_t>(b) * kQ4KBytes;
   // The LDS destination of each load is wave-uniform.
@@ -189,13 +222,17 @@ constexpr int kWaitVmStage = 0x0F70 | kLoadsPerWave;
 // consecutive bytes).
 constexpr int kPartFloats = kThreads * 32;
 
+template <bool ID>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
                      const uint8_t* __restrict__ xq, int M, int N, int nb, int mtiles,
-                     int ntiles, int ks, float* __restrict__ part, int* __restrict__ cnt) {
+                     int ntiles, int ks, float* __restrict__ part, int* __restrict__ cnt,
+                     IdGemm id) {
   __shared__ __align__(16) uint8_t stage0[kStageBytes];
   __shared__ __align__(16) uint8_t stage1[kStageBytes];
   __shared__ int last_arrival;
+  __shared__ int pair_s[ID ? BM : 1];
+  __shared__ int xrow_s[ID ? BM : 1];
 
   // Workgroup -> (split, tile). When the workgroup count is a multiple of the
   // 8 XCDs, XCD x (= id % 8) takes a contiguous run in which the token tiles
@@ -208,12 +245,39 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
   const int tile = t - split * tiles;
   const int ntile = tile / mtiles;
   const int mtile = tile % mtiles;
-  const int m0 = mtile * BM;
+  int m0 = mtile * BM;
   const int n0 = ntile * BN;
   const int b_lo = static_cast<int>(static_cast<int64_t>(split) * nb / ks);
   const int b_hi = static_cast<int>(static_cast<int64_t>(split + 1) * nb / ks);
 
   const int tid = threadIdx.x;
+  if constexpr (ID) {
+    // mtile indexes the tile list; its pairs become the tile's token rows.
+    // Every lane reads the same words; readfirstlane makes that explicit, so
+    // the expert's weight base is a scalar (the direct-to-LDS loads take a
+    // scalar base).
+    if (mtile >= __builtin_amdgcn_readfirstlane(*id.n_tiles)) return;  // workgroup-uniform
+    const int4 dv = id.desc[mtile];
+    const int4 d = make_int4(__builtin_amdgcn_readfirstlane(dv.x),
+                             __builtin_amdgcn_readfirstlane(dv.y),
+                             __builtin_amdgcn_readfirstlane(dv.z), 0);
+    if (tid < BM) {
+      const int p = id.sorted[d.y + min(tid, d.z - 1)];
+      pair_s[tid] = p;
+      xrow_s[tid] = id.per_slot_x ? p : p / id.n_used;
+    }
+    __syncthreads();
+    if (d.x == id.n_experts) {  // out-of-range selections: NaN rows
+      for (int i = tid; i < d.z * BN; i += kThreads) {
+        const int n = n0 + i % BN;
+        if (n < N) y[static_cast<int64_t>(pair_s[i / BN]) * N + n] = __builtin_nanf("");
+      }
+      return;
+    }
+    w += static_cast<int64_t>(d.x) * id.expert_bytes;
+    M = d.z;
+    m0 = 0;
+  }
   const int lane = tid & 63;
   const int wave = tid >> 6;       // 32-row slice of the weight tile
   const int l16 = lane & 15;
@@ -227,7 +291,7 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
     for (int j = 0; j < 2; ++j) acc[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
   const v4i zero = {0, 0, 0, 0};
 
-  const StageOffsets so = stage_offsets(M, N, nb, m0, n0, wave, lane);
+  const StageOffsets so = stage_offsets<ID>(M, N, nb, m0, n0, wave, lane, xrow_s);
   issue_stage(stage0, xq, w, so, b_lo, wave);
 
   // One super-block: wait for its stage, refill the other stage with
@@ -401,8 +465,11 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
       if (n < N) {
         const float v[4] = {acc[mt][nt].x, acc[mt][nt].y, acc[mt][nt].z, acc[mt][nt].w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (mr + i < M) y[static_cast<int64_t>(mr + i) * N + n] = v[i];
+        for (int i = 0; i < 4; ++i) {
+          if (mr + i >= M) continue;
+          const int64_t row = ID ? pair_s[mr + i] : mr + i;
+          y[row * N + n] = v[i];
+        }
       }
     }
 }
@@ -416,18 +483,25 @@ constexpr int kSplitTiles = 256;   // above this many tiles, no split
 constexpr size_t kSplitBytes =
     static_cast<size_t>(kSplitSlots) * kPartFloats * sizeof(float) + kSplitTiles * sizeof(int);
 
-struct Workspace {
-  float* part;
-  int* cnt;
-};
+// The grouped form's tile list: up to kIdMaxPairs pairs.
+constexpr int64_t kIdMaxPairs = int64_t{1} << 20;
+constexpr int kIdMaxExperts = 1024;
+constexpr int64_t kIdMaxTiles = kIdMaxPairs / BM + kIdMaxExperts + 1;
+constexpr size_t kIdBytes = kIdMaxPairs * sizeof(int32_t) + kIdMaxTiles * sizeof(int4) + 256;
 
-hipError_t split_workspace(hipStream_t stream, Workspace* out) {
+enum WorkspaceKind { kWsSplit = 0, kWsRoute = 1 };
+
+// Library-owned device memory, one buffer per (kind, device, stream) so that
+// calls on different streams never share one; allocated and zeroed on first
+// use, kept until the process ends.
+hipError_t stream_workspace(int kind, size_t bytes, hipStream_t stream, void** out) {
   static std::mutex mu;
-  static std::unordered_map<uint64_t, Workspace> spaces;  // key: device << 48 ^ stream
+  static std::unordered_map<uint64_t, void*> spaces;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  const uint64_t key = (static_cast<uint64_t>(dev) << 48) ^ reinterpret_cast<uintptr_t>(stream);
+  const uint64_t key = (static_cast<uint64_t>(dev) << 52) ^ (static_cast<uint64_t>(kind) << 48) ^
+                       reinterpret_cast<uintptr_t>(stream);
   std::lock_guard<std::mutex> lock(mu);
   auto it = spaces.find(key);
   if (it != spaces.end()) {
@@ -435,15 +509,12 @@ hipError_t split_workspace(hipStream_t stream, Workspace* out) {
     return hipSuccess;
   }
   void* p = nullptr;
-  if ((e = hipMalloc(&p, kSplitBytes)) != hipSuccess) return e;
-  float* part = static_cast<float*>(p);
-  int* cnt = reinterpret_cast<int*>(part + static_cast<size_t>(kSplitSlots) * kPartFloats);
-  if ((e = hipMemset(cnt, 0, kSplitTiles * sizeof(int))) != hipSuccess ||
-      (e = hipDeviceSynchronize()) != hipSuccess) {
+  if ((e = hipMalloc(&p, bytes)) != hipSuccess) return e;
+  if ((e = hipMemset(p, 0, bytes)) != hipSuccess || (e = hipDeviceSynchronize()) != hipSuccess) {
     (void)hipFree(p);
     return e;
   }
-  *out = spaces[key] = Workspace{part, cnt};
+  *out = spaces[key] = p;
   return hipSuccess;
 }
 
@@ -466,18 +537,48 @@ hipError_t launch_gemm_q4k_split(float* y, const void* w, const void* xq, int64_
   const int mtiles = static_cast<int>((M + BM - 1) / BM);
   const int ntiles = static_cast<int>((N + BN - 1) / BN);
   const int tiles = mtiles * ntiles;
-  Workspace ws{nullptr, nullptr};
+  float* part = nullptr;
+  int* cnt = nullptr;
   if (ks > 1) {
     if (tiles > kSplitTiles || tiles * ks > kSplitSlots || ks > nb) return hipErrorInvalidValue;
-    const hipError_t e = split_workspace(stream, &ws);
+    void* p = nullptr;
+    const hipError_t e = stream_workspace(kWsSplit, kSplitBytes, stream, &p);
     if (e != hipSuccess) return e;
+    part = static_cast<float*>(p);
+    cnt = reinterpret_cast<int*>(part + static_cast<size_t>(kSplitSlots) * kPartFloats);
   } else {
     ks = 1;
   }
-  hipLaunchKernelGGL(gemm_q4k_kernel, dim3(tiles * ks), dim3(kThreads), 0, stream, y,
+  hipLaunchKernelGGL(gemm_q4k_kernel<false>, dim3(tiles * ks), dim3(kThreads), 0, stream, y,
                      static_cast<const uint8_t*>(w), static_cast<const uint8_t*>(xq),
-                     static_cast<int>(M), static_cast<int>(N), nb, mtiles, ntiles, ks, ws.part,
-                     ws.cnt);
+                     static_cast<int>(M), static_cast<int>(N), nb, mtiles, ntiles, ks, part, cnt,
+                     IdGemm{});
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_q4k_id(float* y, const void* slab, const void* xq, const int32_t* ids,
+                              int64_t n_tokens, int64_t n_used, int64_t n_experts, int64_t rows,
+                              int64_t K, int per_slot_x, hipStream_t stream) {
+  const int64_t n_pairs = n_tokens * n_used;
+  if (n_pairs > kIdMaxPairs || n_experts > kIdMaxExperts) return hipErrorInvalidValue;
+  void* p = nullptr;
+  hipError_t e = stream_workspace(kWsRoute, kIdBytes, stream, &p);
+  if (e != hipSuccess) return e;
+  int4* desc = static_cast<int4*>(p);
+  int32_t* sorted = reinterpret_cast<int32_t*>(desc + kIdMaxTiles);
+  int32_t* n_tiles = sorted + kIdMaxPairs;
+  if ((e = launch_route_experts(ids, n_pairs, n_experts, BM, sorted, desc, n_tiles, stream)) !=
+      hipSuccess)
+    return e;
+  const int nb = static_cast<int>(K / 256);
+  const int mtiles = static_cast<int>(route_max_tiles(n_pairs, n_experts, BM));
+  const int ntiles = static_cast<int>((rows + BN - 1) / BN);
+  const IdGemm id{sorted, desc, n_tiles, static_cast<int>(n_experts), static_cast<int>(n_used),
+                  per_slot_x, rows * nb * static_cast<int64_t>(kQ4KBytes)};
+  hipLaunchKernelGGL(gemm_q4k_kernel<true>, dim3(mtiles * ntiles), dim3(kThreads), 0, stream, y,
+                     static_cast<const uint8_t*>(slab), static_cast<const uint8_t*>(xq),
+                     static_cast<int>(n_pairs), static_cast<int>(rows), nb, mtiles, ntiles, 1,
+                     nullptr, nullptr, id);
   return hipGetLastError();
 }
 

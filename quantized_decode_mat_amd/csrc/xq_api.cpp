@@ -66,6 +66,8 @@ xq_status check_k(int64_t K, int64_t kmax) {
 constexpr int64_t kMaxInt = 2147483647LL;
 // Row counts stay below 2^30 so that no 32-bit row index in a kernel can wrap.
 constexpr int64_t kMaxRows = 1LL << 30;
+constexpr int64_t kIdMaxPairs = 1LL << 20;  // (token, slot) pairs of one grouped product
+constexpr int64_t kIdMaxExperts = 1024;
 
 xq_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(XQ_E_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
@@ -207,6 +209,47 @@ xq_status xq_gemm_q4k_small_m(float* y, const void* w, const void* xq, int64_t M
   if (xq_status s = check_device()) return s;
   return launched(xq::launch_gemm_q4k(y, w, xq, M, N, K, static_cast<hipStream_t>(stream)),
                   "xq_gemm_q4k_small_m");
+}
+
+xq_status xq_gemm_q4k_id(float* y, const void* slab, const void* xq, const int32_t* ids,
+                         int64_t n_tokens, int64_t n_used, int64_t n_experts, int64_t rows,
+                         int64_t K, int64_t x_per_slot, void* stream) {
+  if (!y) return fail(XQ_E_NULL, "y is NULL");
+  if (!slab) return fail(XQ_E_NULL, "slab is NULL");
+  if (!xq) return fail(XQ_E_NULL, "xq is NULL");
+  if (!ids) return fail(XQ_E_NULL, "ids is NULL");
+  if (n_used < 1 || n_used > kIdMaxPairs)
+    return fail(XQ_E_SHAPE, "n_used=%lld outside 1..2^20", (long long)n_used);
+  if (n_tokens < 1 || n_tokens > kIdMaxPairs / n_used)
+    return fail(XQ_E_SHAPE, "n_tokens*n_used = %lld*%lld outside 1..2^20", (long long)n_tokens,
+                (long long)n_used);
+  if (n_experts < 1 || n_experts > kIdMaxExperts)
+    return fail(XQ_E_SHAPE, "n_experts=%lld outside 1..1024", (long long)n_experts);
+  if (rows < 1 || rows > kMaxRows)
+    return fail(XQ_E_SHAPE, "rows=%lld outside 1..2^30", (long long)rows);
+  if (xq_status s = check_k(K, 0)) return s;
+  if (K / 256 > kMaxInt) return fail(XQ_E_SHAPE, "K=%lld too large", (long long)K);
+  if (x_per_slot != 0 && x_per_slot != 1)
+    return fail(XQ_E_SHAPE, "x_per_slot=%lld is neither 0 nor 1", (long long)x_per_slot);
+  const int64_t n_pairs = n_tokens * n_used;
+  const int64_t xrows = x_per_slot ? n_pairs : n_tokens;
+  // The kernel addresses one expert's weights and all of xq with 32-bit byte
+  // offsets.
+  if (rows * (K / 256) * 144 >= (1LL << 31))
+    return fail(XQ_E_SHAPE, "one expert of rows=%lld reaches 2 GiB", (long long)rows);
+  if (xrows * (K / 256) * 320 >= (1LL << 31))
+    return fail(XQ_E_SHAPE, "xq of %lld rows reaches 2 GiB", (long long)xrows);
+  if (xq::route_max_tiles(n_pairs, n_experts, 64) * ((rows + 127) / 128) > kMaxInt)
+    return fail(XQ_E_SHAPE, "too many tiles for one launch");
+  if (!aligned(y, 4)) return fail(XQ_E_ALIGN, "y not 4-byte aligned");
+  if (!aligned(slab, 16)) return fail(XQ_E_ALIGN, "slab not 16-byte aligned");
+  if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");
+  if (!aligned(ids, 4)) return fail(XQ_E_ALIGN, "ids not 4-byte aligned");
+  if (xq_status s = check_device()) return s;
+  return launched(xq::launch_gemm_q4k_id(y, slab, xq, ids, n_tokens, n_used, n_experts, rows, K,
+                                         static_cast<int>(x_per_slot),
+                                         static_cast<hipStream_t>(stream)),
+                  "xq_gemm_q4k_id");
 }
 
 xq_status xq_repack_iq4nl(void* resident, const void* file_blocks, int64_t n_blocks,

@@ -37,6 +37,19 @@ hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, i
 int gemm_q4k_splits(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_q4k_split(float* y, const void* w, const void* xq, int64_t M, int64_t N,
                                  int64_t K, int ks, hipStream_t stream);
+// Grouped small-M product: route the (token, slot) pairs of ids by expert,
+// then one product launch over the tile list (at most 2^20 pairs and 1024
+// experts).
+hipError_t launch_gemm_q4k_id(float* y, const void* slab, const void* xq, const int32_t* ids,
+                              int64_t n_tokens, int64_t n_used, int64_t n_experts, int64_t rows,
+                              int64_t K, int per_slot_x, hipStream_t stream);
+// The expert map: pairs grouped by expert into `sorted`, tiles of at most
+// tile_m pairs of one bucket into `desc` (int4: bucket, first, count, 0) and
+// their count into *n_tiles; route_max_tiles bounds that count.
+hipError_t launch_route_experts(const int32_t* ids, int64_t n_pairs, int64_t n_experts,
+                                int tile_m, int32_t* sorted, void* desc, int32_t* n_tiles,
+                                hipStream_t stream);
+int64_t route_max_tiles(int64_t n_pairs, int64_t n_experts, int tile_m);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink,
                               hipStream_t stream);
 int64_t stream_read_sink_words(int64_t bytes);

@@ -130,6 +130,32 @@ def test_id_refusals(fn, args, status, text):
 
 
 @pytest.mark.parametrize("args,status,text", [
+    ((0, A16, A16, A16, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_NULL, "y is NULL"),
+    ((A16, 0, A16, A16, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_NULL, "slab is NULL"),
+    ((A16, A16, 0, A16, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_NULL, "xq is NULL"),
+    ((A16, A16, A16, 0, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_NULL, "ids is NULL"),
+    ((A16, A16, A16, A16, 8, 0, 6, 64, 2048, 0, None), xq.XQ_E_SHAPE, "n_used=0"),
+    ((A16, A16, A16, A16, 0, 2, 6, 64, 2048, 0, None), xq.XQ_E_SHAPE, "n_tokens*n_used"),
+    ((A16, A16, A16, A16, 2 ** 19 + 1, 2, 6, 64, 2048, 0, None), xq.XQ_E_SHAPE,
+     "n_tokens*n_used"),
+    ((A16, A16, A16, A16, 8, 2, 0, 64, 2048, 0, None), xq.XQ_E_SHAPE, "n_experts=0"),
+    ((A16, A16, A16, A16, 8, 2, 1025, 64, 2048, 0, None), xq.XQ_E_SHAPE, "n_experts=1025"),
+    ((A16, A16, A16, A16, 8, 2, 6, 0, 2048, 0, None), xq.XQ_E_SHAPE, "rows=0"),
+    ((A16, A16, A16, A16, 8, 2, 6, 64, 2000, 0, None), xq.XQ_E_SHAPE, "K=2000"),
+    ((A16, A16, A16, A16, 8, 2, 6, 64, 2048, 2, None), xq.XQ_E_SHAPE, "x_per_slot=2"),
+    ((A16, A16, A16, A16, 8, 2, 6, 2 ** 21, 2048, 0, None), xq.XQ_E_SHAPE, "reaches 2 GiB"),
+    ((A16, A16, A16, A16, 2 ** 19, 2, 6, 64, 4096, 1, None), xq.XQ_E_SHAPE, "reaches 2 GiB"),
+    ((A16 + 2, A16, A16, A16, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_ALIGN, "y not 4-byte"),
+    ((A16, A4, A16, A16, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_ALIGN, "slab not 16-byte"),
+    ((A16, A16, A4, A16, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
+    ((A16, A16, A16, A1, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_ALIGN, "ids not 4-byte"),
+])
+def test_gemm_id_refusals(args, status, text):
+    s, err = _call("xq_gemm_q4k_id", *args)
+    assert s == status and text in err, (s, err)
+
+
+@pytest.mark.parametrize("args,status,text", [
     ((0, A16, 10, 0, 9, None), xq.XQ_E_NULL, "resident is NULL"),
     ((A16, 0, 10, 0, 9, None), xq.XQ_E_NULL, "file_blocks is NULL"),
     ((A16, A16, 0, 0, 9, None), xq.XQ_E_SHAPE, "n_blocks=0"),

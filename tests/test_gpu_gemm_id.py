@@ -1,0 +1,163 @@
+"""Grouped small-M product (xq_gemm_q4k_id) through the C ABI.
+
+Every (token, slot) pair is held to the oracle's mat-vec of its expert's rows
+against its own q8_K row (|y - ref| <= 1e-5 * T); outputs of out-of-range
+selections must be NaN and nothing else may be; block partials are bit-exact
+through the entry point (unit-scale isolation weights); and because each output
+is computed from its own pair alone, permuting the tokens permutes the outputs
+bit for bit (the pairs land in different tiles).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_decode_mat_amd as xq
+import workloads as wl
+from test_gpu_parity import _note, assert_close, dev, poisoned_f32, take_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _slab(E, rows, K, seed):
+    parts = [wl.q4k_weights(rows, K, wl.rng(seed + 31 * e)) for e in range(E)]
+    return np.concatenate([p.reshape(rows, -1) for p in parts], axis=0)
+
+
+def _run(slab, xqb, ids, E, rows, K, per_slot):
+    T, U = ids.shape
+    y = poisoned_f32(T * U * rows)
+    xq.xq_gemm_q4k_id(y, dev(slab), dev(xqb), dev(ids.astype(np.int32)), T, U, E, rows, K,
+                      per_slot)
+    return take_f32(y, T * U * rows).reshape(T, U, rows)
+
+
+def _check(Y, slab, xqb, ids, E, rows, K, per_slot, pairs=None):
+    T, U = ids.shape
+    todo = [(t, k) for t in range(T) for k in range(U)] if pairs is None else pairs
+    for t, k in todo:
+        e = int(ids[t, k])
+        got = Y[t, k]
+        if not 0 <= e < E:
+            assert np.isnan(got).all(), (t, k, e)
+            continue
+        assert not np.isnan(got).any(), (t, k)
+        xrow = xqb[t * U + k] if per_slot else xqb[t]
+        ref, Tm = oracle.gemv_q4k(slab[e * rows:(e + 1) * rows], xrow, rows, K)
+        assert_close(got, ref, Tm, "pair (%d, %d) expert %d" % (t, k, e))
+
+
+def _top_k(T, U, E, g):
+    return np.stack([g.choice(E, size=U, replace=False) for _ in range(T)]).astype(np.int32)
+
+
+def test_gemm_id_six_experts_three_slots():
+    E, rows, K, T, U = 6, 64, 2048, 5, 3
+    slab = _slab(E, rows, K, 9500)
+    g = wl.rng(9501)
+    xqb = oracle.quantize_q8k(wl.activations(T, K, g))
+    ids = np.array([[4, 0, 3], [1, 4, 2], [0, 5, 3], [2, 1, 4], [3, 0, 5]], dtype=np.int32)
+    _note("gemm id six experts")
+    Y = _run(slab, xqb, ids, E, rows, K, 0)
+    assert (Y != 0).any()
+    _check(Y, slab, xqb, ids, E, rows, K, 0)
+
+
+@pytest.mark.parametrize("T,U,E,rows,K,per_slot,seed", [
+    (200, 2, 8, 200, 4096, 0, 9600),     # top-2 of 8, rows not a multiple of 128
+    (150, 4, 16, 128, 1024, 1, 9610),    # a q8_K row per slot (down projection)
+    (40, 8, 64, 96, 2048, 0, 9620),      # many experts, most with a few pairs
+])
+def test_gemm_id_routed(T, U, E, rows, K, per_slot, seed):
+    slab = _slab(E, rows, K, seed)
+    g = wl.rng(seed + 1)
+    xrows = T * U if per_slot else T
+    xqb = oracle.quantize_q8k(wl.activations(xrows, K, g))
+    ids = _top_k(T, U, E, g)
+    _note("gemm id routed T=%d U=%d E=%d rows=%d K=%d per_slot=%d" % (T, U, E, rows, K, per_slot))
+    Y = _run(slab, xqb, ids, E, rows, K, per_slot)
+    s = wl.rng(seed + 2)
+    pairs = sorted({(int(s.integers(T)), int(s.integers(U))) for _ in range(60)} |
+                   {(0, 0), (T - 1, U - 1)})
+    _check(Y, slab, xqb, ids, E, rows, K, per_slot, pairs)
+    # Each expert's outputs as a whole: the oracle's product over the
+    # expert's gathered rows.
+    for e in range(E):
+        tk = np.argwhere(ids == e)
+        if len(tk) == 0:
+            continue
+        xr = np.stack([xqb[t * U + k] if per_slot else xqb[t] for t, k in tk])
+        ref, Tm = oracle.gemm_q4k(slab[e * rows:(e + 1) * rows], xr, len(tk), rows, K)
+        got = np.stack([Y[t, k] for t, k in tk])
+        assert_close(got.reshape(-1), ref.reshape(-1), Tm.reshape(-1), "expert %d" % e)
+
+
+def test_gemm_id_skewed_and_out_of_range():
+    """One expert takes 300 pairs (five tiles, the last ragged), others none;
+    out-of-range selections give NaN rows and leave the rest intact."""
+    E, rows, K, T, U = 5, 130, 1536, 150, 2
+    slab = _slab(E, rows, K, 9700)
+    g = wl.rng(9701)
+    xqb = oracle.quantize_q8k(wl.activations(T, K, g))
+    ids = np.full((T, U), 2, dtype=np.int32)
+    ids[:, 1] = 2
+    ids[7, 0], ids[8, 1], ids[100, 0] = -1, 5, 1 << 30
+    ids[9, 1] = 4
+    _note("gemm id skewed")
+    Y = _run(slab, xqb, ids, E, rows, K, 0)
+    bad = [(7, 0), (8, 1), (100, 0)]
+    for t, k in bad:
+        assert np.isnan(Y[t, k]).all()
+    good = np.ones((T, U), bool)
+    for t, k in bad:
+        good[t, k] = False
+    assert not np.isnan(Y[good]).any()
+    _check(Y, slab, xqb, ids, E, rows, K, 0, [(0, 0), (7, 1), (9, 1), (63, 1), (64, 0), (149, 1)])
+
+
+def test_gemm_id_permutation_is_bit_exact():
+    E, rows, K, T, U = 8, 256, 2048, 97, 2
+    slab = _slab(E, rows, K, 9800)
+    g = wl.rng(9801)
+    xqb = oracle.quantize_q8k(wl.activations(T, K, g))
+    ids = _top_k(T, U, E, g)
+    perm = wl.rng(9802).permutation(T)
+    _note("gemm id permutation")
+    Y = _run(slab, xqb, ids, E, rows, K, 0)
+    Yp = _run(slab, xqb[perm], ids[perm], E, rows, K, 0)
+    assert np.array_equal(Yp, Y[perm])
+    # and again on a second stream (its own routing workspace)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        Y2 = _run(slab, xqb, ids, E, rows, K, 0)
+    side.synchronize()
+    assert np.array_equal(Y2, Y)
+
+
+@pytest.mark.parametrize("which", ["S", "M"])
+def test_gemm_id_partials_bit_exact(which):
+    E, rows, K, T, U = 3, 40, 1024, 6, 2
+    g = wl.rng(9900)
+    slab = np.concatenate([wl.q4k_isolation_weights(rows, K, g, which).reshape(rows, -1)
+                           for _ in range(E)], axis=0)
+    ids = np.array([[0, 2], [1, 0], [2, 1], [0, 1], [2, 0], [1, 2]], dtype=np.int32)
+    for b in range(K // 256):
+        x = wl.isolating_activation(T, K, g, b)
+        xqb = oracle.quantize_q8k(x)
+        _note("gemm id partial %s block %d" % (which, b))
+        Y = _run(slab, xqb, ids, E, rows, K, 0)
+        for t in range(T):
+            for k in range(U):
+                e = ids[t, k]
+                S, Mp = oracle.q4k_partials(slab[e * rows:(e + 1) * rows], xqb[t], rows, K)
+                want = S[:, b] if which == "S" else -Mp[:, b]
+                assert np.array_equal(Y[t, k], want.astype(np.float64)), (t, k, b)
