@@ -797,11 +797,12 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
     del ws, w
     torch.cuda.empty_cache()
 
-    # The same product at token counts and shapes that leave the plain grid
-    # short of the device (K split over workgroups): a 16-token batch on the
-    # up matrix, 64 and 512 tokens on the down matrix.
-    for M, (N, K), seed in ((16, UP, wl.SEEDS["prefill"]), (64, DOWN, wl.SEEDS["ffn_down"]),
-                            (512, DOWN, wl.SEEDS["ffn_down"])):
+    # The same product at other token counts: a 4-token batch on the up
+    # matrix (served by the batched mat-vec), 16 tokens on the up matrix and
+    # 64 and 512 tokens on the down matrix (int8 MFMA, K split over
+    # workgroups where the tile grid cannot fill the device).
+    for M, (N, K), seed in ((4, UP, wl.SEEDS["prefill"]), (16, UP, wl.SEEDS["prefill"]),
+                            (64, DOWN, wl.SEEDS["ffn_down"]), (512, DOWN, wl.SEEDS["ffn_down"])):
         g = wl.rng(seed)
         w = torch.from_numpy(wl.q4k_weights(N, K, g).reshape(-1)).to(dev)
         xv = torch.from_numpy(wl.activations(M, K, g).reshape(-1)).to(dev)

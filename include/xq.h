@@ -110,13 +110,18 @@ xq_status xq_gemv_iq4nl(float *y, const void *w, const void *xq, int64_t N, int6
  * Q4_K x q8_K small-M product (multi-token prefill; "25 — Writing XPU
  * Kernels", section 25.3): Y[m][n] = sum_b xs_mb * (d_nb * S_mnb - dmin_nb *
  * M_mnb), with S and M the exact int32 block partials of xq_gemv_q4k taken
- * against token m's q8_K row. The integer products run on int8 MFMA.
+ * against token m's q8_K row.
  *
  *  y   device, out: f32 [M][N] row-major (token-major), 4-byte aligned.
  *  w   device, in: Q4_K [N][K/256], 16-byte aligned.
  *  xq  device, in: q8_K [M][K/256], 16-byte aligned.
  *  1 <= M <= 2^30.  1 <= N <= 2^30.  K >= 256, a multiple of 256. Each of
  *  xq and w below 2 GiB (the kernel's loads use 32-bit offsets).
+ * A short batch (M = 1; M <= 6, or M <= 8 when N*K <= 2^25, while the M q8_K
+ * rows fit 64 KB) is a weight stream rather than a dense contraction: it runs
+ * on the mat-vec kernels, one pass over the weights for all M tokens, and
+ * row m is then bit-identical to xq_gemv_q4k on token m. Larger M runs on
+ * int8 MFMA.
  * Shapes with at most 256 tiles of 64 tokens x 128 rows split K over several
  * workgroups (section 25.3: fill the device first); the partials go through
  * a workspace the library owns, one per (device, stream): 16 MiB allocated,

@@ -44,6 +44,11 @@
 // (coherent without an L2 write-back); the last arrival resets the counter,
 // so counters are zero between launches.
 //
+// Short batches (M = 1, or up to the LDS token cap while M <= 6, or 8 on
+// matrices of at most 2^25 weights) skip the MFMA tile: they are a weight
+// stream, and the dot4 mat-vec reads the weights once for all M tokens
+// (launch_gemv_q4k_multi; each token's row is the mat-vec's bits).
+//
 // Grouped form (mul_mat_id, section 25.3: one launch over an expert map,
 // never one per expert): the same kernel over a device tile list built by
 // route_experts. A tile holds up to 64 (token, slot) pairs routed to one
@@ -631,8 +636,20 @@ hipError_t launch_gemm_q4k_id(float* y, const void* slab, const void* xq, const 
   return hipGetLastError();
 }
 
+bool gemm_q4k_uses_matvec(int64_t M, int64_t N, int64_t K) {
+  // A short batch is a weight stream, not a dense contraction: one pass of
+  // the dot4 mat-vec over the weights for all M tokens costs less than the
+  // MFMA tile's fixed per-step latency. Measured on MI355X (cold weights):
+  // 14336x4096 at 6 tokens 20.2 us against 21.3 (7 tokens: 22.0 against 21.2),
+  // 4096x4096 at 8 tokens 9.7 us against 20.3.
+  return M == 1 ||
+         (M <= gemv_q4k_multi_max_tokens(K) && (M <= 6 || N * K <= (int64_t{1} << 25)));
+}
+
 hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, int64_t N,
                            int64_t K, hipStream_t stream) {
+  if (M == 1) return launch_gemv_q4k(y, w, xq, N, K, stream);
+  if (gemm_q4k_uses_matvec(M, N, K)) return launch_gemv_q4k_multi(y, w, xq, M, N, K, stream);
   return launch_gemm_q4k_split(y, w, xq, M, N, K, gemm_q4k_splits(M, N, K), stream);
 }
 

@@ -26,6 +26,8 @@
 //  * The per-block float work is one pass: xs * (d*S - dmin*M).
 //  * Lane partials are f32; the wave reduces them with DPP row sums and four
 //    v_readlane, and lane 0 stores y.
+#include <algorithm>
+
 #include "q4k_row.h"
 #include "xq_launch.h"
 
@@ -157,6 +159,104 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_kernel(float* __restrict__
   }
 }
 
+// A short batch against one pass over the weights: up to TM tokens
+// (`tokens` of them live, a workgroup-uniform count), their q8_K rows staged
+// back to back in LDS. The weight chunk's header is decoded once per chunk
+// and every token then runs the mat-vec's integer dots and float pass in the
+// mat-vec's order, so token t's outputs are the bits xq_gemv_q4k gives for
+// its row alone (same launch table, same clamping).
+template <int TM, int R, int PF, int W, int NA, bool CLAMP>
+__global__ __launch_bounds__(W * kWave) void gemv_q4k_multi_kernel(float* __restrict__ y,
+                                                                   const uint8_t* __restrict__ w,
+                                                                   const uint8_t* __restrict__ xq,
+                                                                   int N, int nb, int tokens) {
+  extern __shared__ __align__(16) uint8_t act[];
+  constexpr int kThreads = W * kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x >> 6;
+  const int row0 = (blockIdx.x * W + wave) * R;
+  const int units = (nb + 7) >> 3;
+  const LaneGeom L = lane_geom(lane);
+  const int64_t row_bytes = static_cast<int64_t>(nb) * kQ4KBytes;
+  const int xrow = nb * kQ8KBytes;
+  const int n16 = tokens * nb * (kQ8KBytes / 16);
+
+  uint4 nib[R][PF];
+  uint4 hdr[R][PF];
+  auto load_batch = [&](int u0) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = min(row0 + r, N - 1);
+        const int bb = (u0 + p) * 8 + L.bsub;
+        const uint8_t* wr = w + static_cast<int64_t>(row) * row_bytes;
+        if (CLAMP || bb < nb) {
+          const uint8_t* blk = wr + static_cast<int64_t>(min(bb, nb - 1)) * kQ4KBytes;
+          nib[r][p] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (2 * L.g + L.h));
+          hdr[r][p] = *reinterpret_cast<const uint4*>(blk);
+        } else {
+          nib[r][p] = make_uint4(0, 0, 0, 0);
+          hdr[r][p] = make_uint4(0, 0, 0, 0);
+        }
+      }
+  };
+
+  uint4 areg[NA];
+  act_load<NA, kThreads>(areg, xq, n16);
+  load_batch(0);
+  act_store<NA, kThreads>(areg, act, xq, n16);
+  __syncthreads();
+
+  float acc[R][TM];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < TM; ++t) acc[r][t] = 0.0f;
+
+  for (int u0 = 0; u0 < units; u0 += PF) {
+    if (u0 > 0) load_batch(u0);
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int bb = (u0 + p) * 8 + L.bsub;
+      if (CLAMP) {
+        const int b = min(bb, nb - 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const ChunkDecode c = chunk_decode(nib[r][p], hdr[r][p], L);
+#pragma unroll
+          for (int t = 0; t < TM; ++t) {
+            if (t < tokens) {
+              const float v = chunk_token(c, act + t * xrow, b, L);
+              acc[r][t] += (bb < nb) ? v : 0.0f;
+            }
+          }
+        }
+      } else if (bb < nb) {
+        // Rows of eight or more units hold at most three tokens in 64 KB, so
+        // the header is decoded per token here, through the mat-vec's own
+        // unit_partial: the compiler then contracts the float pass the same
+        // way in both kernels.
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int t = 0; t < TM; ++t)
+            if (t < tokens) acc[r][t] += unit_partial(nib[r][p], hdr[r][p], act + t * xrow, bb, L);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    if (t >= tokens) break;  // workgroup-uniform
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float tot = wave_sum(acc[r][t]);
+      if (lane == 0 && row0 + r < N) y[static_cast<int64_t>(t) * N + row0 + r] = tot;
+    }
+  }
+}
+
 struct IdArgs {
   const int32_t* sel;  // device selection buffer (null: dense launch)
   int used;            // selection slots (grid.y)
@@ -213,7 +313,57 @@ hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64
   return launch_cfg<1, 4, 8, 3, false>(y, wb, xb, n, nb, id, stream);
 }
 
+template <int TM, int R, int PF, int W, int NA, bool CLAMP>
+hipError_t launch_multi_cfg(float* y, const uint8_t* w, const uint8_t* xq, int N, int nb,
+                            int tokens, hipStream_t stream) {
+  const int waves = (N + R - 1) / R;
+  const int grid = (waves + W - 1) / W;
+  const size_t lds = static_cast<size_t>(tokens) * nb * kQ8KBytes;
+  hipLaunchKernelGGL((gemv_q4k_multi_kernel<TM, R, PF, W, NA, CLAMP>), dim3(grid),
+                     dim3(W * kWave), lds, stream, y, w, xq, N, nb, tokens);
+  return hipGetLastError();
+}
+
+// The mat-vec's launch table with a token cap TM.
+template <int TM>
+hipError_t launch_multi_rows(float* y, const void* w, const void* xq, int64_t N, int64_t K,
+                             int tokens, hipStream_t stream) {
+  const int nb = static_cast<int>(K / 256);
+  const int units = (nb + 7) / 8;
+  const uint8_t* wb = static_cast<const uint8_t*>(w);
+  const uint8_t* xb = static_cast<const uint8_t*>(xq);
+  const int n = static_cast<int>(N);
+  if (units == 1) {
+    if (N >= 8192) return launch_multi_cfg<TM, 2, 1, 4, 2, true>(y, wb, xb, n, nb, tokens, stream);
+    return launch_multi_cfg<TM, 1, 1, 4, 2, true>(y, wb, xb, n, nb, tokens, stream);
+  }
+  if (units == 2) {
+    if (N >= 8192) return launch_multi_cfg<TM, 2, 2, 4, 2, true>(y, wb, xb, n, nb, tokens, stream);
+    return launch_multi_cfg<TM, 1, 2, 4, 2, true>(y, wb, xb, n, nb, tokens, stream);
+  }
+  if (units == 3) return launch_multi_cfg<TM, 1, 3, 8, 2, true>(y, wb, xb, n, nb, tokens, stream);
+  if (units == 4) return launch_multi_cfg<TM, 1, 4, 8, 3, true>(y, wb, xb, n, nb, tokens, stream);
+  if (units == 5) return launch_multi_cfg<TM, 1, 5, 8, 3, true>(y, wb, xb, n, nb, tokens, stream);
+  if (units == 6) return launch_multi_cfg<TM, 1, 6, 8, 3, true>(y, wb, xb, n, nb, tokens, stream);
+  if (units == 7) return launch_multi_cfg<TM, 1, 7, 8, 3, true>(y, wb, xb, n, nb, tokens, stream);
+  return launch_multi_cfg<TM, 1, 4, 8, 3, false>(y, wb, xb, n, nb, tokens, stream);
+}
+
 }  // namespace
+
+int64_t gemv_q4k_multi_max_tokens(int64_t K) {
+  // The tokens' q8_K rows share 64 KB of LDS (two workgroups per CU).
+  return std::min<int64_t>(8, 65536 / ((K / 256) * kQ8KBytes));
+}
+
+hipError_t launch_gemv_q4k_multi(float* y, const void* w, const void* xq, int64_t M, int64_t N,
+                                 int64_t K, hipStream_t stream) {
+  if (M < 1 || M > gemv_q4k_multi_max_tokens(K)) return hipErrorInvalidValue;
+  const int t = static_cast<int>(M);
+  if (M <= 2) return launch_multi_rows<2>(y, w, xq, N, K, t, stream);
+  if (M <= 4) return launch_multi_rows<4>(y, w, xq, N, K, t, stream);
+  return launch_multi_rows<8>(y, w, xq, N, K, t, stream);
+}
 
 hipError_t launch_gemv_q4k(float* y, const void* w, const void* xq, int64_t N, int64_t K,
                            hipStream_t stream) {

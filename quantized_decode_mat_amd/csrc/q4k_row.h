@@ -79,4 +79,55 @@ __device__ __forceinline__ float unit_partial(const uint4 nib, const uint4 hdr, 
   return xs * (d * static_cast<float>(S) - dmin * static_cast<float>(M));
 }
 
+// The same contribution split in two for several tokens against one weight
+// chunk: the weight side (nibbles and header decode) once, then per token the
+// integer dots and the one float pass, in the same order and form as
+// unit_partial, so each token gets the bits unit_partial gives it.
+struct ChunkDecode {
+  uint4 nib;
+  int sc0, sc1, m0, m1;
+  float d, dmin;
+};
+
+__device__ __forceinline__ ChunkDecode chunk_decode(const uint4 nib, const uint4 hdr,
+                                                    const LaneGeom& L) {
+  ChunkDecode c;
+  c.nib = nib;
+  const uint32_t h1 = hdr.y, h2 = hdr.z, h3 = hdr.w;
+  const uint32_t sc_lo = h1 & 0x3F3F3F3Fu;
+  const uint32_t m_lo = h2 & 0x3F3F3F3Fu;
+  const uint32_t sc_hi = (h3 & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);
+  const uint32_t m_hi = ((h3 >> 4) & 0x0F0F0F0Fu) | ((h2 >> 2) & 0x30303030u);
+  const uint32_t scw = (sc_hi & L.selhi) | (sc_lo & ~L.selhi);
+  const uint32_t mw = ((m_hi & L.selhi) | (m_lo & ~L.selhi)) & L.mmask;
+  c.sc0 = (scw >> L.shift) & 0xFF;
+  c.sc1 = (scw >> (L.shift + 8)) & 0xFF;
+  c.m0 = (mw >> L.shift) & 0xFF;
+  c.m1 = (mw >> (L.shift + 8)) & 0xFF;
+  c.d = half_bits_to_float(hdr.x & 0xFFFFu);
+  c.dmin = half_bits_to_float(hdr.x >> 16);
+  return c;
+}
+
+__device__ __forceinline__ float chunk_token(const ChunkDecode& c, const uint8_t* act, int b,
+                                             const LaneGeom& L) {
+  const uint8_t* xb = act + b * kQ8KBytes;
+  const uint4 alo = *reinterpret_cast<const uint4*>(xb + 64 * L.g + 16 * L.h);
+  const uint4 ahi = *reinterpret_cast<const uint4*>(xb + 64 * L.g + 32 + 16 * L.h);
+  const int2 sums = *reinterpret_cast<const int2*>(xb + 256 + 8 * L.g);
+  const float xs = *reinterpret_cast<const float*>(xb + 288);
+  const uint4 nib = c.nib;
+  int dlo = sdot4(nib.x & 0x0F0F0F0Fu, alo.x, 0);
+  dlo = sdot4(nib.y & 0x0F0F0F0Fu, alo.y, dlo);
+  dlo = sdot4(nib.z & 0x0F0F0F0Fu, alo.z, dlo);
+  dlo = sdot4(nib.w & 0x0F0F0F0Fu, alo.w, dlo);
+  int dhi = sdot4((nib.x >> 4) & 0x0F0F0F0Fu, ahi.x, 0);
+  dhi = sdot4((nib.y >> 4) & 0x0F0F0F0Fu, ahi.y, dhi);
+  dhi = sdot4((nib.z >> 4) & 0x0F0F0F0Fu, ahi.z, dhi);
+  dhi = sdot4((nib.w >> 4) & 0x0F0F0F0Fu, ahi.w, dhi);
+  const int S = __mul24(c.sc0, dlo) + __mul24(c.sc1, dhi);
+  const int M = __mul24(c.m0, sums.x) + __mul24(c.m1, sums.y);
+  return xs * (c.d * static_cast<float>(S) - c.dmin * static_cast<float>(M));
+}
+
 }  // namespace xq

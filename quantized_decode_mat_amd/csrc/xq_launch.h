@@ -29,8 +29,15 @@ hipError_t launch_repack_iq4nl(void* resident, const void* file_blocks, int64_t 
 int64_t repack_dword_prefix_launches();
 hipError_t launch_gemv_q4_0(float* y, const void* w, const void* xq, int64_t N, int64_t K,
                             hipStream_t stream);
+// M tokens (M <= gemv_q4k_multi_max_tokens(K)) against one pass over the Q4_K
+// weights: y [M][N], each row the bits of the mat-vec on that token.
+int64_t gemv_q4k_multi_max_tokens(int64_t K);
+hipError_t launch_gemv_q4k_multi(float* y, const void* w, const void* xq, int64_t M, int64_t N,
+                                 int64_t K, hipStream_t stream);
 hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, int64_t N,
                            int64_t K, hipStream_t stream);
+// Whether launch_gemm_q4k serves this shape with the mat-vec kernels.
+bool gemm_q4k_uses_matvec(int64_t M, int64_t N, int64_t K);
 // Splits of K the small-M product uses for this shape (1: none), and the
 // product with an explicit split count (ks > 1 needs at most 256 tiles of
 // 64 x 128, tiles * ks <= 512 and ks <= K/256).

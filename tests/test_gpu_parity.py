@@ -355,6 +355,49 @@ def test_gemm_split_full_size(M, N, K):
         assert_close(Y[m], ref, T, "split row %d" % m)
 
 
+# Short batches run on the mat-vec kernels: one pass over the weights for all
+# M tokens, each token's row bit-identical to xq_gemv_q4k on that token.
+GEMM_SHORT = [
+    (2, 14336, 4096, 7501),    # two rows per wave, clamped
+    (6, 14336, 4096, 7502),    # the longest batch on this shape
+    (3, 4096, 14336, 7503),    # seven units, three tokens fill the LDS cap
+    (8, 4096, 4096, 7504),     # eight tokens on a 2^24-weight matrix
+    (5, 300, 2304, 7505),      # ragged unit tail
+    (2, 130, 20480, 7506),     # ten units (two tokens fit): batches of four, loads past the row skipped
+    (7, 8193, 2048, 7507),     # two rows per wave with an odd tail
+]
+
+
+@pytest.mark.parametrize("M,N,K,seed", GEMM_SHORT)
+def test_gemm_short_batch_rows_equal_matvec(M, N, K, seed):
+    g = wl.rng(seed)
+    w = wl.q4k_weights(N, K, g)
+    xqb = oracle.quantize_q8k(wl.activations(M, K, g))
+    wd = dev(w)
+    _note("gemm short batch M=%d N=%d K=%d" % (M, N, K))
+    Y = gpu_gemm(w, xqb, M, N, K)
+    for m in range(M):
+        y = poisoned_f32(N)
+        xq.xq_gemv_q4k(y, wd, dev(xqb[m]), N, K)
+        assert np.array_equal(Y[m], take_f32(y, N)), m
+    for m in sorted({0, M - 1}):
+        ref, T = oracle.gemv_q4k(w, xqb[m], N, K)
+        assert_close(Y[m], ref, T, "short batch row %d" % m)
+
+
+def test_gemm_mfma_below_eight_tokens():
+    """Five tokens whose q8_K rows exceed the mat-vec's LDS cap (K = 14336
+    holds three): the MFMA product, split over K."""
+    M, N, K = 5, 200, 14336
+    g = wl.rng(7510)
+    w = wl.q4k_weights(N, K, g)
+    xqb = oracle.quantize_q8k(wl.activations(M, K, g))
+    _note("gemm mfma five tokens")
+    Y = gpu_gemm(w, xqb, M, N, K)
+    ref, T = oracle.gemm_q4k(w, xqb, M, N, K)
+    assert_close(Y.reshape(-1), ref.reshape(-1), T.reshape(-1), "mfma five tokens")
+
+
 def test_gemm_split_repeatable_across_calls_and_streams():
     """Bit-identical results on repeated calls (the arrival counters reset
     themselves) and on a second stream (its own workspace)."""
@@ -401,9 +444,11 @@ def test_gemm_prefill_512x14336x4096():
 
 
 @pytest.mark.parametrize("which", ["S", "M"])
-@pytest.mark.parametrize("K", [1024, 3584])  # 3584: two splits of 7 super-blocks
-def test_gemm_partials_bit_exact(which, K):
-    M, N = 3, 200
+@pytest.mark.parametrize("M,K", [(3, 1024), (9, 1024), (9, 3584)])
+def test_gemm_partials_bit_exact(which, M, K):
+    """M = 3 runs on the batched mat-vec, M = 9 on int8 MFMA (K = 3584: two
+    splits of 7 super-blocks)."""
+    N = 200
     g = wl.rng(7200)
     w = wl.q4k_isolation_weights(N, K, g, which)
     wd = dev(w)
