@@ -57,7 +57,7 @@ COUNTED = {
         "void xq::(anonymous namespace)::gemv_iq4nl_resident_kernel<2, false, 0>", 8,
         295501824 + 5120 + 4 * 128256, ("gemv_iq4nl.hip", "xq_device.h")),
     "gemm_q4k_512x14336x4096": (
-        "xq::(anonymous namespace)::gemm_q4k_kernel", 4,
+        "void xq::(anonymous namespace)::gemm_q4k_kernel<false>", 4,
         33030144 + 512 * 16 * 320 + 4 * 512 * 14336, ("gemm_q4k.hip", "xq_device.h")),
 }
 HEADLINE = "gemv_q4k_up_14336x4096"
@@ -67,6 +67,7 @@ MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_I8", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_B
                  "GRBM_GUI_ACTIVE")
 PREFILL = ("gemm_q4k_512x14336x4096", 2 * 512 * 14336 * 4096)
 XCDS, SIMDS = 8, 256 * 4
+INT8_OPS_PER_CYCLE = 2 * 16 * 16 * 64 / 16   # per SIMD
 
 
 # Sustained work before every timed region. After an idle spell (host-side
@@ -144,21 +145,24 @@ def traffic_from_profile(name):
 
 
 def trace_summary(trace_dir):
-    """Per-kernel durations (End - Start, ns) from a rocprofv3 kernel trace."""
+    """Durations (End - Start, ns) from a rocprofv3 kernel trace, one line per
+    kernel and grid size (so one kernel's launch shapes stay apart)."""
     import csv
     import glob
     per = {}
     for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
         with open(path) as f:
             for r in csv.DictReader(f):
-                per.setdefault(r["Kernel_Name"], []).append(
+                grid = "x".join(r.get(k, "?") for k in ("Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"))
+                per.setdefault((r["Kernel_Name"], grid), []).append(
                     (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
-    for name, v in sorted(per.items(), key=lambda kv: -len(kv[1])):
+    for (name, grid), v in sorted(per.items(), key=lambda kv: -len(kv[1])):
         v.sort()
         d = [x[1] / 1e3 for x in v]
         last = d[-1000:]
-        print(json.dumps({"kernel": name, "calls": len(d), "mean_us": round(sum(d) / len(d), 3),
-                          "min_us": round(min(d), 3), "max_us": round(max(d), 3),
+        print(json.dumps({"kernel": name, "grid": grid, "calls": len(d),
+                          "mean_us": round(sum(d) / len(d), 3), "min_us": round(min(d), 3),
+                          "max_us": round(max(d), 3),
                           "last1000_mean_us": round(sum(last) / len(last), 3)}))
 
 
@@ -216,11 +220,16 @@ def counters_summary(fetch_dir, write_dir, mfma_dir=None):
             # GRBM_GUI_ACTIVE sums the eight XCDs' busy cycles; MFMA busy
             # cycles sum over the 1024 SIMDs (256 CUs x 4).
             "cycles_per_xcd": round(raw["GRBM_GUI_ACTIVE"] / XCDS, 1),
+            # every MFMA (int8 and the f32 min term) over the SIMD cycles
             "mfma_busy_frac": round(raw["SQ_VALU_MFMA_BUSY_CYCLES"] /
                                     (SIMDS * raw["GRBM_GUI_ACTIVE"] / XCDS), 4),
-            "useful_mfma_frac": round(raw["SQ_VALU_MFMA_BUSY_CYCLES"] /
-                                      (SIMDS * raw["GRBM_GUI_ACTIVE"] / XCDS) /
-                                      (raw["SQ_INSTS_VALU_MFMA_MOPS_I8"] * 512 / alg_ops), 4),
+            # the int8 MFMA share, at 2048 int8 ops per cycle per SIMD
+            # (v_mfma_i32_16x16x64_i8: 2 * 16 * 16 * 64 ops in 16 cycles)
+            "int8_busy_frac": round(raw["SQ_INSTS_VALU_MFMA_MOPS_I8"] * 512 / INT8_OPS_PER_CYCLE /
+                                    (SIMDS * raw["GRBM_GUI_ACTIVE"] / XCDS), 4),
+            # algorithmic ops over the int8 capacity of the run
+            "useful_int8_frac": round(alg_ops / INT8_OPS_PER_CYCLE /
+                                      (SIMDS * raw["GRBM_GUI_ACTIVE"] / XCDS), 4),
             "sources_sha256_16": sources_sha(COUNTED[name][3]),
         }
     with open(COUNTERS, "w") as f:
