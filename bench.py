@@ -48,10 +48,10 @@ CSRC = os.path.join(ROOT, "quantized_decode_mat_amd", "csrc")
 # comes from (the summary is void once any of them changes).
 COUNTED = {
     "gemv_q4k_up_14336x4096": (
-        "void xq::(anonymous namespace)::gemv_q4k_kernel<2, 2, 4, 2, true, false>", 20,
+        "void xq::(anonymous namespace)::gemv_q4k_kernel<2, 2, 4, 2, true, false, false>", 20,
         33030144 + 5120 + 4 * 14336, ("gemv_q4k.hip", "q4k_row.h", "xq_device.h")),
     "gemv_q4k_down_4096x14336": (
-        "void xq::(anonymous namespace)::gemv_q4k_kernel<1, 7, 8, 3, true, false>", 20,
+        "void xq::(anonymous namespace)::gemv_q4k_kernel<1, 7, 8, 3, true, false, false>", 20,
         33030144 + 17920 + 4 * 4096, ("gemv_q4k.hip", "q4k_row.h", "xq_device.h")),
     "gemv_iq4nl_head_128256x4096": (
         "void xq::(anonymous namespace)::gemv_iq4nl_resident_kernel<2, false, 0>", 8,
@@ -325,6 +325,21 @@ def main():
     log("step %.3f us (host clock %.3f us), weight %.1f GB/s" % (ms * 1e3, wall / args.steps * 1e6,
                                                                value))
 
+    # ---- the same step in three launches: the up mat-vec quantizes its own
+    # output (xq_gemv_q4k_q8k, the fused tail), beside the plain figure.
+    def step_fused(i, s=s):
+        k = i % pool
+        L.xq_quantize_q8k(xq1.data_ptr(), x_d.data_ptr(), 1, UP[1], s)
+        L.xq_gemv_q4k_q8k(h.data_ptr(), xq2.data_ptr(), ups[k].data_ptr(), xq1.data_ptr(), UP[0],
+                          UP[1], s)
+        L.xq_gemv_q4k(y.data_ptr(), dns[k].data_ptr(), xq2.data_ptr(), DOWN[0], DOWN[1], s)
+
+    fused_us = _time_loop(torch, stream, step_fused, args.steps)
+    fused = {"us_per_step": round(fused_us, 3),
+             "weight_GBps": round(pair_bytes / fused_us / 1e3, 1),
+             "step": "quantize x, up mat-vec quantizing its own output, down mat-vec"}
+    log("fused-tail step: %s" % fused)
+
     # ---- the same step replayed from a HIP graph (beside the plain figure,
     # never instead of it): one graph holds one pass over the weight pool.
     # Every replay is checked against the eager result first.
@@ -431,6 +446,7 @@ def main():
         "frac_of_stream_read": round(value / stream_gbps, 4),
         "host_us_per_step": round(wall / args.steps * 1e6, 3),
         "graph_replay": graph,
+        "fused_tail_step": fused,
     }
     if cpu_all is not None:
         line["cpu_baseline_all_cores"] = cpu_all

@@ -91,6 +91,31 @@ xq_status xq_quantize_q8k(void *xq, const float *x, int64_t rows, int64_t K, voi
 xq_status xq_gemv_q4k(float *y, const void *w, const void *xq, int64_t N, int64_t K, void *stream);
 
 /*
+ * Q4_K x q8_K mat-vec with its output quantized in the same launch ("25 —
+ * Writing XPU Kernels", section 25.5: the FFN pair's fused tail; the up
+ * product hands the down product its q8_K activation):
+ *   y  = the result of xq_gemv_q4k(y, w, xq, N, K), bit for bit;
+ *   yq = the bytes xq_quantize_q8k(yq, y, 1, N) writes, bytes 0..291 of every
+ *        block bit for bit (292..319 zero).
+ * The 256/(rows per workgroup) workgroups of each q8_K block of y count
+ * their arrival on a counter; the last quantizes the block.
+ *
+ *  y   device, out: f32 [N], 16-byte aligned.
+ *  yq  device, out: q8_K [N/256] blocks (xq_q8k_bytes(1, N)), 16-byte aligned.
+ *  w, xq, K as xq_gemv_q4k.
+ *  N a multiple of 256, 256 <= N <= 2^24.
+ * The arrival counters live in a 256 KB workspace the library owns, one per
+ * (device, stream): allocated, zeroed and synchronized on a stream's first
+ * call, kept until the process ends (that first call cannot be captured into
+ * a graph). The last arrival resets its counter, so they are zero between
+ * calls; calls on one stream are ordered, calls on different streams use
+ * different counters.
+ * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH.
+ */
+xq_status xq_gemv_q4k_q8k(float *y, void *yq, const void *w, const void *xq, int64_t N, int64_t K,
+                          void *stream);
+
+/*
  * IQ4_NL x q8_K decode mat-vec, batch 1 ("25 — Writing XPU Kernels", section
  * 25.2.1): y[r] = sum_c d_rc * xs_(c/8) * D_rc with D_rc = sum_{t<32}
  * kv[nibble_t] * code_(32c+t) (exact int32).

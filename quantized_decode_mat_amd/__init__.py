@@ -29,6 +29,7 @@ EXPORTS = (
     "xq_q8k_bytes", "xq_q4k_bytes", "xq_iq4nl_bytes", "xq_status_name", "xq_last_error",
     "xq_bench_stream_read", "xq_bench_sink_words", "xq_gemv_q4k_id", "xq_gemv_iq4nl_id",
     "xq_repack_iq4nl", "xq_repack_dword_prefix_launches", "xq_gemv_q4_0", "xq_gemm_q4k_id",
+    "xq_gemv_q4k_q8k",
 )
 
 
@@ -58,11 +59,12 @@ def lib() -> ctypes.CDLL:
             L.xq_gemv_iq4nl_id.argtypes = [P, P, P, P, I, I, I, I, I, P]
             L.xq_repack_iq4nl.argtypes = [P, P, I, I, I, P]
             L.xq_gemm_q4k_id.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
+            L.xq_gemv_q4k_q8k.argtypes = [P, P, P, P, I, I, P]
             L.xq_repack_dword_prefix_launches.argtypes = []
             L.xq_repack_dword_prefix_launches.restype = I
             for f in ("xq_quantize_q8k", "xq_gemv_q4k", "xq_gemv_iq4nl", "xq_gemm_q4k_small_m",
                       "xq_bench_stream_read", "xq_gemv_q4k_id", "xq_gemv_iq4nl_id", "xq_repack_iq4nl",
-                      "xq_gemv_q4_0", "xq_gemm_q4k_id"):
+                      "xq_gemv_q4_0", "xq_gemm_q4k_id", "xq_gemv_q4k_q8k"):
                 getattr(L, f).restype = S
             for f in ("xq_q8k_bytes", "xq_q4k_bytes", "xq_iq4nl_bytes"):
                 getattr(L, f).argtypes = [I, I]
@@ -148,6 +150,13 @@ def xq_gemv_iq4nl(y, w, xq, N: int, K: int, stream=None) -> None:
     _check(lib().xq_gemv_iq4nl(_ptr(y, 4 * N, "y"), _ptr(w, xq_iq4nl_bytes(N, K), "w"),
                                _ptr(xq, xq_q8k_bytes(1, K), "xq"), N, K, _stream(stream)),
            "xq_gemv_iq4nl")
+
+
+def xq_gemv_q4k_q8k(y, yq, w, xq, N: int, K: int, stream=None) -> None:
+    _check(lib().xq_gemv_q4k_q8k(_ptr(y, 4 * N, "y"), _ptr(yq, xq_q8k_bytes(1, N), "yq"),
+                                 _ptr(w, xq_q4k_bytes(N, K), "w"), _ptr(xq, xq_q8k_bytes(1, K), "xq"),
+                                 N, K, _stream(stream)),
+           "xq_gemv_q4k_q8k")
 
 
 def xq_gemv_q4_0(y, w, xq, N: int, K: int, stream=None) -> None:

@@ -30,6 +30,7 @@ SOURCES = [
     "repack_iq4nl.hip",
     "route_experts.hip",
     "stream_read.hip",
+    "workspace.cpp",
     "xq_api.cpp",
 ]
 

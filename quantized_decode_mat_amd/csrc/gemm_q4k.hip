@@ -57,8 +57,6 @@
 // is sized by an upper bound on the tile count; workgroups past the list's
 // end return at once. Tiles of out-of-range selections write NaN.
 #include <algorithm>
-#include <mutex>
-#include <unordered_map>
 
 #include "xq_device.h"
 #include "xq_launch.h"
@@ -243,6 +241,9 @@ constexpr int kWaitVm0 = 0x0F70;
 // element r of thread i at r * kThreads + i (one wave store covers 256
 // consecutive bytes).
 constexpr int kPartFloats = kThreads * 32;
+// Arrival counters sit one 128-byte line apart: counters sharing a line
+// serialize every workgroup's atomic on that line.
+constexpr int kCounterStride = 32;
 
 template <bool ID>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -469,11 +470,12 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     if (tid == 0)
-      last_arrival = __hip_atomic_fetch_add(cnt + tile, 1, __ATOMIC_RELAXED,
+      last_arrival = __hip_atomic_fetch_add(cnt + tile * kCounterStride, 1, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT) == ks - 1;
     __syncthreads();
     if (!last_arrival) return;  // workgroup-uniform
-    if (tid == 0) __hip_atomic_store(cnt + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0)
+      __hip_atomic_store(cnt + tile * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // The sum over splits in the fixed order 0..ks-1 (this split's own
     // values from registers).
     float4 sum[4][2];
@@ -534,43 +536,14 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
 // first split launch, kept until the process ends.
 constexpr int kSplitSlots = 512;   // tiles * ks stays within this
 constexpr int kSplitTiles = 256;   // above this many tiles, no split
-constexpr size_t kSplitBytes =
-    static_cast<size_t>(kSplitSlots) * kPartFloats * sizeof(float) + kSplitTiles * sizeof(int);
+constexpr size_t kSplitBytes = static_cast<size_t>(kSplitSlots) * kPartFloats * sizeof(float) +
+                               static_cast<size_t>(kSplitTiles) * kCounterStride * sizeof(int);
 
 // The grouped form's tile list: up to kIdMaxPairs pairs.
 constexpr int64_t kIdMaxPairs = int64_t{1} << 20;
 constexpr int kIdMaxExperts = 1024;
 constexpr int64_t kIdMaxTiles = kIdMaxPairs / BM + kIdMaxExperts + 1;
 constexpr size_t kIdBytes = kIdMaxPairs * sizeof(int32_t) + kIdMaxTiles * sizeof(int4) + 256;
-
-enum WorkspaceKind { kWsSplit = 0, kWsRoute = 1 };
-
-// Library-owned device memory, one buffer per (kind, device, stream) so that
-// calls on different streams never share one; allocated and zeroed on first
-// use, kept until the process ends.
-hipError_t stream_workspace(int kind, size_t bytes, hipStream_t stream, void** out) {
-  static std::mutex mu;
-  static std::unordered_map<uint64_t, void*> spaces;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  const uint64_t key = (static_cast<uint64_t>(dev) << 52) ^ (static_cast<uint64_t>(kind) << 48) ^
-                       reinterpret_cast<uintptr_t>(stream);
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = spaces.find(key);
-  if (it != spaces.end()) {
-    *out = it->second;
-    return hipSuccess;
-  }
-  void* p = nullptr;
-  if ((e = hipMalloc(&p, bytes)) != hipSuccess) return e;
-  if ((e = hipMemset(p, 0, bytes)) != hipSuccess || (e = hipDeviceSynchronize()) != hipSuccess) {
-    (void)hipFree(p);
-    return e;
-  }
-  *out = spaces[key] = p;
-  return hipSuccess;
-}
 
 }  // namespace
 

@@ -29,10 +29,15 @@
 #include <algorithm>
 
 #include "q4k_row.h"
+#include "q8k_block.h"
 #include "xq_launch.h"
 
 namespace xq {
 namespace {
+
+constexpr int kWaitVm0 = 0x0F70;             // s_waitcnt vmcnt(0), other counters not waited on
+constexpr int64_t kQuantTailBlocks = 16384;  // arrival counters: N <= 2^22 rows
+constexpr int kCounterStride = 32;           // ints: one 128-byte line per counter
 
 // Loads of the activation row into registers, issued before the weight
 // loads; the LDS stores follow them.
@@ -71,13 +76,25 @@ __device__ __forceinline__ void act_store(const uint4 (&a)[NA], uint8_t* lds, co
 // the slot's rows and reads nothing. Every row then runs the dense code
 // below unchanged, so the result is bit-identical to a dense launch on the
 // expert's rows.
-template <int R, int PF, int W, int NA, bool CLAMP, bool ID>
+// QOUT: the output is also quantized to q8_K ("25 — Writing XPU Kernels",
+// section 25.5: the FFN pair's fused tail, the up product handing the down
+// product its q8_K activation). N is a multiple of 256 and the R*W rows of a
+// workgroup divide 256, so 256/(R*W) workgroups make each q8_K block of y.
+// Each stores its rows with agent-scope atomic stores (coherent across XCDs),
+// waits for them, and counts its arrival on the block's counter; the last to
+// arrive resets the counter, reads the block's 256 values back with
+// agent-scope atomic loads and quantizes it with one wave, the quantize
+// kernel's own arithmetic (q8k_block_wave), so yq holds the bytes
+// xq_quantize_q8k gives for y.
+template <int R, int PF, int W, int NA, bool CLAMP, bool ID, bool QOUT>
 __global__ __launch_bounds__(W * kWave) void gemv_q4k_kernel(float* __restrict__ y,
                                                              const uint8_t* __restrict__ w,
                                                              const uint8_t* __restrict__ xq,
                                                              int N, int nb,
                                                              const int32_t* __restrict__ sel,
-                                                             int n_experts, int64_t x_stride) {
+                                                             int n_experts, int64_t x_stride,
+                                                             uint8_t* __restrict__ yq,
+                                                             int* __restrict__ qcnt) {
   extern __shared__ __align__(16) uint8_t act[];
   constexpr int kThreads = W * kWave;
   const int lane = threadIdx.x & (kWave - 1);
@@ -152,6 +169,35 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_kernel(float* __restrict__
     }
   }
 
+  if constexpr (QOUT) {
+    __shared__ int q_last;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float tot = wave_sum(acc[r]);
+      if (lane == 0)
+        __hip_atomic_store(y + row0 + r, tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this wave's row stores have completed
+    __syncthreads();
+    const int blk = (blockIdx.x * W * R) >> 8;
+    if (threadIdx.x == 0)
+      q_last = __hip_atomic_fetch_add(qcnt + blk * kCounterStride, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == 256 / (R * W) - 1;
+    __syncthreads();
+    if (!q_last) return;  // workgroup-uniform
+    if (threadIdx.x == 0)
+      __hip_atomic_store(qcnt + blk * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (wave == 0) {
+      const float* hb = y + 256 * blk + 4 * lane;
+      float4 v;
+      v.x = __hip_atomic_load(hb + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      v.y = __hip_atomic_load(hb + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      v.z = __hip_atomic_load(hb + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      v.w = __hip_atomic_load(hb + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      q8k_block_wave(v, yq + static_cast<int64_t>(blk) * kQ8KBytes, lane);
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const float tot = wave_sum(acc[r]);
@@ -262,6 +308,8 @@ struct IdArgs {
   int used;            // selection slots (grid.y)
   int n_experts;       // experts in the slab
   int64_t x_stride;    // bytes between the slots' activations (0: shared)
+  uint8_t* yq;         // fused q8_K output (null: none); excludes sel
+  int* qcnt;           // its per-block arrival counters
 };
 
 template <int R, int PF, int W, int NA, bool CLAMP>
@@ -271,12 +319,17 @@ hipError_t launch_cfg(float* y, const uint8_t* w, const uint8_t* xq, int N, int 
   const int grid = (waves + W - 1) / W;
   const size_t lds = static_cast<size_t>(nb) * kQ8KBytes;
   if (id.sel)
-    hipLaunchKernelGGL((gemv_q4k_kernel<R, PF, W, NA, CLAMP, true>), dim3(grid, id.used),
+    hipLaunchKernelGGL((gemv_q4k_kernel<R, PF, W, NA, CLAMP, true, false>), dim3(grid, id.used),
                        dim3(W * kWave), lds, stream, y, w, xq, N, nb, id.sel, id.n_experts,
-                       id.x_stride);
+                       id.x_stride, nullptr, nullptr);
+  else if (id.yq)
+    hipLaunchKernelGGL((gemv_q4k_kernel<R, PF, W, NA, CLAMP, false, true>), dim3(grid),
+                       dim3(W * kWave), lds, stream, y, w, xq, N, nb, nullptr, 0, int64_t{0}, id.yq,
+                       id.qcnt);
   else
-    hipLaunchKernelGGL((gemv_q4k_kernel<R, PF, W, NA, CLAMP, false>), dim3(grid),
-                       dim3(W * kWave), lds, stream, y, w, xq, N, nb, nullptr, 0, int64_t{0});
+    hipLaunchKernelGGL((gemv_q4k_kernel<R, PF, W, NA, CLAMP, false, false>), dim3(grid),
+                       dim3(W * kWave), lds, stream, y, w, xq, N, nb, nullptr, 0, int64_t{0},
+                       nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -367,14 +420,28 @@ hipError_t launch_gemv_q4k_multi(float* y, const void* w, const void* xq, int64_
 
 hipError_t launch_gemv_q4k(float* y, const void* w, const void* xq, int64_t N, int64_t K,
                            hipStream_t stream) {
-  return launch_rows(y, w, xq, N, K, IdArgs{nullptr, 1, 0, 0}, stream);
+  return launch_rows(y, w, xq, N, K, IdArgs{nullptr, 1, 0, 0, nullptr, nullptr}, stream);
+}
+
+hipError_t launch_gemv_q4k_q8k(float* y, void* yq, const void* w, const void* xq, int64_t N,
+                               int64_t K, hipStream_t stream) {
+  // Every launch shape of the table puts 4 or 8 rows in a workgroup, so the
+  // workgroups of a 256-row block never straddle two blocks.
+  if (N % 256 != 0 || N / 256 > kQuantTailBlocks) return hipErrorInvalidValue;
+  void* p = nullptr;
+  const hipError_t e =
+      stream_workspace(kWsQuantTail, kQuantTailBlocks * kCounterStride * sizeof(int), stream, &p);
+  if (e != hipSuccess) return e;
+  return launch_rows(y, w, xq, N, K,
+                     IdArgs{nullptr, 1, 0, 0, static_cast<uint8_t*>(yq), static_cast<int*>(p)},
+                     stream);
 }
 
 hipError_t launch_gemv_q4k_id(float* y, const void* slab, const void* xq, const int32_t* sel,
                               int64_t n_experts, int64_t used, int64_t rows, int64_t K,
                               int64_t x_stride_blocks, hipStream_t stream) {
   const IdArgs id{sel, static_cast<int>(used), static_cast<int>(n_experts),
-                  x_stride_blocks * kQ8KBytes};
+                  x_stride_blocks * kQ8KBytes, nullptr, nullptr};
   return launch_rows(y, slab, xq, rows, K, id, stream);
 }
 

@@ -108,6 +108,24 @@ xq_status xq_gemv_q4k(float* y, const void* w, const void* xq, int64_t N, int64_
                   "xq_gemv_q4k");
 }
 
+xq_status xq_gemv_q4k_q8k(float* y, void* yq, const void* w, const void* xq, int64_t N,
+                          int64_t K, void* stream) {
+  if (!y) return fail(XQ_E_NULL, "y is NULL");
+  if (!yq) return fail(XQ_E_NULL, "yq is NULL");
+  if (!w) return fail(XQ_E_NULL, "w is NULL");
+  if (!xq) return fail(XQ_E_NULL, "xq is NULL");
+  if (N < 256 || N % 256 != 0 || N > (1LL << 22))
+    return fail(XQ_E_SHAPE, "N=%lld not a multiple of 256 in 256..2^22", (long long)N);
+  if (xq_status s = check_k(K, XQ_MAX_K)) return s;
+  if (!aligned(y, 16)) return fail(XQ_E_ALIGN, "y not 16-byte aligned");
+  if (!aligned(yq, 16)) return fail(XQ_E_ALIGN, "yq not 16-byte aligned");
+  if (!aligned(w, 16)) return fail(XQ_E_ALIGN, "w not 16-byte aligned");
+  if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");
+  if (xq_status s = check_device()) return s;
+  return launched(xq::launch_gemv_q4k_q8k(y, yq, w, xq, N, K, static_cast<hipStream_t>(stream)),
+                  "xq_gemv_q4k_q8k");
+}
+
 xq_status xq_gemv_iq4nl(float* y, const void* w, const void* xq, int64_t N, int64_t K,
                         void* stream) {
   if (!y) return fail(XQ_E_NULL, "y is NULL");

@@ -7,6 +7,11 @@
 
 namespace xq {
 
+// Library-owned device workspaces (workspace.cpp): one zero-initialised
+// buffer per (kind, device, stream), allocated on first use and kept.
+enum WorkspaceKind { kWsSplit = 0, kWsRoute = 1, kWsQuantTail = 2 };
+hipError_t stream_workspace(int kind, size_t bytes, hipStream_t stream, void** out);
+
 hipError_t launch_quantize_q8k(void* xq, const float* x, int64_t rows, int64_t K,
                                hipStream_t stream);
 hipError_t launch_gemv_q4k(float* y, const void* w, const void* xq, int64_t N, int64_t K,
@@ -16,6 +21,10 @@ hipError_t launch_gemv_iq4nl(float* y, const void* w, const void* xq, int64_t N,
 // Expert-grouped mat-vecs: `used` slots, slot kk reads expert sel[kk] (rows
 // rows of the slab) and the activation x_stride_blocks q8_K blocks per slot
 // into xq; output slot-major.
+// y = W x as launch_gemv_q4k, and yq = q8_K(y) as launch_quantize_q8k(yq, y,
+// 1, N) would give, in the same launch (N a multiple of 256, N <= 2^24).
+hipError_t launch_gemv_q4k_q8k(float* y, void* yq, const void* w, const void* xq, int64_t N,
+                               int64_t K, hipStream_t stream);
 hipError_t launch_gemv_q4k_id(float* y, const void* slab, const void* xq, const int32_t* sel,
                               int64_t n_experts, int64_t used, int64_t rows, int64_t K,
                               int64_t x_stride_blocks, hipStream_t stream);

@@ -156,6 +156,26 @@ def test_gemm_id_refusals(args, status, text):
 
 
 @pytest.mark.parametrize("args,status,text", [
+    ((0, A16, A16, A16, 512, 4096, None), xq.XQ_E_NULL, "y is NULL"),
+    ((A16, 0, A16, A16, 512, 4096, None), xq.XQ_E_NULL, "yq is NULL"),
+    ((A16, A16, 0, A16, 512, 4096, None), xq.XQ_E_NULL, "w is NULL"),
+    ((A16, A16, A16, 0, 512, 4096, None), xq.XQ_E_NULL, "xq is NULL"),
+    ((A16, A16, A16, A16, 300, 4096, None), xq.XQ_E_SHAPE, "N=300"),
+    ((A16, A16, A16, A16, 0, 4096, None), xq.XQ_E_SHAPE, "N=0"),
+    ((A16, A16, A16, A16, 2 ** 22 + 256, 4096, None), xq.XQ_E_SHAPE, "N=4194560"),
+    ((A16, A16, A16, A16, 512, 4000, None), xq.XQ_E_SHAPE, "K=4000"),
+    ((A4, A16, A16, A16, 512, 4096, None), xq.XQ_E_ALIGN, "y not 16-byte"),
+    ((A16, A4, A16, A16, 512, 4096, None), xq.XQ_E_ALIGN, "yq not 16-byte"),
+    ((A16, A16, A4, A16, 512, 4096, None), xq.XQ_E_ALIGN, "w not 16-byte"),
+    ((A16, A16, A16, A4, 512, 4096, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
+])
+def test_gemv_q8k_refusals(args, status, text):
+    s, err = _call("xq_gemv_q4k_q8k", *args)
+    assert s == status and text in err, (s, err)
+
+
+
+@pytest.mark.parametrize("args,status,text", [
     ((0, A16, 10, 0, 9, None), xq.XQ_E_NULL, "resident is NULL"),
     ((A16, 0, 10, 0, 9, None), xq.XQ_E_NULL, "file_blocks is NULL"),
     ((A16, A16, 0, 0, 9, None), xq.XQ_E_SHAPE, "n_blocks=0"),

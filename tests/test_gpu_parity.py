@@ -242,6 +242,80 @@ def test_ffn_pair_chain():
     assert_close(y.cpu().numpy().astype(np.float64), ref2, T2, "down")
 
 
+# The mat-vec with its output quantized in the same launch (the FFN pair's
+# fused tail): y is xq_gemv_q4k's, bit for bit, and yq is what
+# xq_quantize_q8k writes for that y.
+GEMV_Q8K = [
+    ("up_14336x4096", 14336, 4096, wl.SEEDS["ffn_up"]),        # 8 rows per workgroup
+    ("down_4096x14336", 4096, 14336, wl.SEEDS["ffn_down"]),    # whole row in flight
+    ("n256_k1024", 256, 1024, 7601),                           # 4 rows per workgroup
+    ("n512_k20480", 512, 20480, 7602),                         # loads past the row skipped
+    ("n1280_k2304", 1280, 2304, 7603),                         # ragged unit tail
+]
+
+
+@pytest.mark.parametrize("name,N,K,seed", GEMV_Q8K, ids=[c[0] for c in GEMV_Q8K])
+def test_gemv_q4k_q8k(name, N, K, seed):
+    g = wl.rng(seed)
+    w = wl.q4k_weights(N, K, g)
+    xqb = oracle.quantize_q8k(wl.activations(1, K, g))
+    wd, xd = dev(w), dev(xqb)
+    _note("gemv q8k %s" % name)
+    nq = xq.xq_q8k_bytes(1, N)
+    outs = []
+    side = torch.cuda.Stream()
+    for call in range(3):  # repeated calls (counters reset), the last on a second stream
+        y = poisoned_f32(N)
+        yq = poisoned_u8(nq)
+        if call < 2:
+            xq.xq_gemv_q4k_q8k(y, yq, wd, xd, N, K)
+        else:
+            with torch.cuda.stream(side):
+                xq.xq_gemv_q4k_q8k(y, yq, wd, xd, N, K)
+            side.synchronize()
+        outs.append((take_f32(y, N), take_u8(yq, nq).reshape(N // 256, 320)))
+    y0 = poisoned_f32(N)
+    xq.xq_gemv_q4k(y0, wd, xd, N, K)
+    ref_y = take_f32(y0, N)
+    yq0 = poisoned_u8(nq)
+    xq.xq_quantize_q8k(yq0, y0[:N], 1, N)
+    ref_q = take_u8(yq0, nq).reshape(N // 256, 320)
+    oq = oracle.quantize_q8k(ref_y.astype(np.float32).reshape(1, N))[0]
+    for yy, qq in outs:
+        assert np.array_equal(yy, ref_y)
+        assert np.array_equal(qq[:, :292], ref_q[:, :292])
+        assert np.array_equal(qq[:, :292], oq[:, :292])
+        assert not qq[:, 292:].any()
+
+
+def test_ffn_pair_fused_tail_equals_four_launches():
+    """quantize x -> up with its q8_K tail -> down gives the four-launch
+    chain's h, q8_K(h) and y bit for bit."""
+    K, H = 4096, 14336
+    gu = wl.rng(wl.SEEDS["ffn_up"])
+    wu = dev(wl.q4k_weights(H, K, gu))
+    x = dev(wl.activations(1, K, gu))
+    wdn = dev(wl.q4k_weights(K, H, wl.rng(wl.SEEDS["ffn_down"])))
+    _note("ffn fused tail")
+    xq1 = torch.empty(xq.xq_q8k_bytes(1, K), dtype=torch.uint8, device="cuda")
+    outs = []
+    for fused in (False, True):
+        h = torch.empty(H, dtype=torch.float32, device="cuda")
+        xq2 = torch.zeros(xq.xq_q8k_bytes(1, H), dtype=torch.uint8, device="cuda")
+        y = torch.empty(K, dtype=torch.float32, device="cuda")
+        xq.xq_quantize_q8k(xq1, x, 1, K)
+        if fused:
+            xq.xq_gemv_q4k_q8k(h, xq2, wu, xq1, H, K)
+        else:
+            xq.xq_gemv_q4k(h, wu, xq1, H, K)
+            xq.xq_quantize_q8k(xq2, h, 1, H)
+        xq.xq_gemv_q4k(y, wdn, xq2, K, H)
+        torch.cuda.synchronize()
+        outs.append((h.cpu(), xq2.cpu(), y.cpu()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
 # ---------------------------------------------------------------------------
 # IQ4_NL mat-vec
 # ---------------------------------------------------------------------------
