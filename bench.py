@@ -822,10 +822,10 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
     del ws, w
     torch.cuda.empty_cache()
 
-    # The same product at other token counts: a 4-token batch on the up
-    # matrix (served by the batched mat-vec), 16 tokens on the up matrix and
-    # 64 and 512 tokens on the down matrix (int8 MFMA, K split over
-    # workgroups where the tile grid cannot fill the device).
+    # The same product at other token counts: 4 and 16 tokens on the up
+    # matrix (the 16-token MFMA tile), 64 and 512 tokens on the down matrix
+    # (the 64-token tile); K is split over workgroups where the tile grid
+    # cannot fill the device.
     for M, (N, K), seed in ((4, UP, wl.SEEDS["prefill"]), (16, UP, wl.SEEDS["prefill"]),
                             (64, DOWN, wl.SEEDS["ffn_down"]), (512, DOWN, wl.SEEDS["ffn_down"])):
         g = wl.rng(seed)

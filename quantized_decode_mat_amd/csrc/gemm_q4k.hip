@@ -44,10 +44,11 @@
 // (coherent without an L2 write-back); the last arrival resets the counter,
 // so counters are zero between launches.
 //
-// Short batches (M = 1, or up to the LDS token cap while M <= 6, or 8 on
+// Short batches (M = 1, or up to the LDS token cap while M <= 3, or 8 on
 // matrices of at most 2^25 weights) skip the MFMA tile: they are a weight
 // stream, and the dot4 mat-vec reads the weights once for all M tokens
-// (launch_gemv_q4k_multi; each token's row is the mat-vec's bits).
+// (launch_gemv_q4k_multi; each token's row is the mat-vec's bits). Up to 32
+// tokens (64 on matrices of at most 2^25 weights) use the 16-token tile.
 //
 // Grouped form (mul_mat_id, section 25.3: one launch over an expert map,
 // never one per expert): the same kernel over a device tile list built by
@@ -67,27 +68,35 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 64;           // tokens per workgroup tile
 constexpr int BN = 128;          // weight rows per workgroup tile
 constexpr int kWaves = BN / 32;  // waves side by side along the weight rows
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStages = 2;       // LDS ring: compute b while b+1 lands
+constexpr int kWInstr = BN * kQ4KBytes / 1024;     // 18 (BN * 9 chunks, 64 per load)
+static_assert(BN * 9 % 64 == 0, "weight chunks fill whole 64-lane loads");
 
-// One LDS stage holds one super-block of the tile:
+// The token tile: 64 tokens (4 MFMA tiles of 16 per wave), or 16 for short
+// batches (one MFMA tile per wave: the finest tile the MFMA has, section
+// 25.3's padding rule). One LDS stage holds one super-block of the tile:
 //  act  BM rows x 256 codes; row m's 16-byte chunk c sits in slot c ^ (m & 15)
 //       (the XOR spreads the 16 rows of an MFMA operand read over all banks);
 //  xs   BM f32 token scales;
 //  sums BM x 8 int32 sub-block sums of the token rows;
 //  w    BN raw 144-byte Q4_K blocks, back to back.
-constexpr int kActBytes = BM * 256;
-constexpr int kXsOff = kActBytes;
-constexpr int kSumOff = kXsOff + BM * 4;   // BM x 8 int32 sub-block sums
-constexpr int kWOff = kSumOff + BM * 32;
-constexpr int kStageBytes = kWOff + BN * kQ4KBytes;
-constexpr int kActInstr = kActBytes / 1024;        // 16 (64-lane x 16-byte loads)
-constexpr int kWInstr = BN * kQ4KBytes / 1024;     // 18 (BN * 9 chunks, 64 per load)
-static_assert(BN * 9 % 64 == 0, "weight chunks fill whole 64-lane loads");
-static_assert(2 * kStages * kStageBytes <= 160 * 1024, "two workgroups' rings exceed 160 KiB");
+template <int BMv>
+struct Tile {
+  static constexpr int BM = BMv;                   // tokens per workgroup tile
+  static constexpr int MT = BMv / 16;              // 16-token MFMA tiles per wave
+  static constexpr int kActBytes = BMv * 256;
+  static constexpr int kXsOff = kActBytes;
+  static constexpr int kSumOff = kXsOff + BMv * 4;
+  static constexpr int kWOff = kSumOff + BMv * 32;
+  static constexpr int kStageBytes = kWOff + BN * kQ4KBytes;
+  static constexpr int kActPerWave = BMv / 16;     // 64-lane act loads per wave
+  static constexpr int kPartFloats = kThreads * 8 * MT;  // split-K partial slot
+  static_assert(BMv == 16 || BMv == 64, "token tiles of 16 or 64");
+  static_assert(2 * kStages * kStageBytes <= 160 * 1024, "two workgroups' rings exceed 160 KiB");
+};
 
 __device__ __forceinline__ uint32_t mul_bytes(uint32_t nib, uint32_t f) {
   // Each byte of `nib` is 0..15 and f <= 7, so no product crosses its byte.
@@ -100,30 +109,31 @@ __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Stage loads per wave: wave w takes act rows 4j..4j+3 for j = w, w+4, w+8,
-// w+12; weight chunks 64j.. for j = w, w+4, w+8, w+12 (and w+16 < 18); wave 2
-// the sums of tokens 0..31, wave 3 those of tokens 32..63 and the 64 token
-// scales. A step waits for all of its wave's loads (vmcnt(0)) before the
-// barrier that publishes the stage.
-static_assert(kWaves == 4 && kActInstr == 16 && kWInstr == 18 && BM == 64,
-              "the load split below is written for this tile");
+// Stage loads per wave: wave w takes act rows 4j..4j+3 for j = w, w+4, ...
+// (BM/16 loads); weight chunks 64j.. for j = w, w+4, w+8, w+12 (and w+16 <
+// 18); wave 2 the sums of tokens 0..31 (lanes 0..31 when BM = 16), wave 3
+// those of tokens 32..63 (BM = 64) and the BM token scales. A step waits for
+// all of its wave's loads (vmcnt(0)) before the barrier that publishes the
+// stage.
+static_assert(kWaves == 4 && kWInstr == 18, "the load split below is written for this tile");
 
 // Per-lane byte offsets of this wave's stage loads relative to super-block
 // 0 (xq or w base); super-block b adds b*320 (codes, scales) or b*144
 // (weights). Offsets stay below 2^31 (the entry point refuses larger
 // inputs), so the loads use a scalar base plus a 32-bit lane offset.
+template <int BMv>
 struct StageOffsets {
-  uint32_t act[4];
+  uint32_t act[Tile<BMv>::kActPerWave];
   uint32_t wt[4];
   uint32_t extra;   // fifth weight load, sums (tokens 0..31), or token scales
-  uint32_t sums;    // wave 3: sums of tokens 32..63
+  uint32_t sums;    // wave 3 when BM = 64: sums of tokens 32..63
 };
 
 // ID: token rows come from xrow[m] (the gathered pairs' q8_K rows).
-template <bool ID>
-__device__ __forceinline__ StageOffsets stage_offsets(int M, int N, int nb, int m0, int n0,
-                                                      int wave, int lane, const int* xrow) {
-  StageOffsets o;
+template <int BMv, bool ID>
+__device__ __forceinline__ StageOffsets<BMv> stage_offsets(int M, int N, int nb, int m0, int n0,
+                                                           int wave, int lane, const int* xrow) {
+  StageOffsets<BMv> o;
   auto act_off = [&](int j) {
     const int m = 4 * j + (lane >> 4);
     const int c = (lane & 15) ^ (m & 15);      // source chunk of this lane's slot
@@ -137,14 +147,14 @@ __device__ __forceinline__ StageOffsets stage_offsets(int M, int N, int nb, int 
     return static_cast<uint32_t>(gn) * static_cast<uint32_t>(nb) * kQ4KBytes + 16u * c;
   };
 #pragma unroll
-  for (int k = 0; k < 4; ++k) o.act[k] = act_off(wave + 4 * k);
+  for (int k = 0; k < Tile<BMv>::kActPerWave; ++k) o.act[k] = act_off(wave + 4 * k);
 #pragma unroll
   for (int k = 0; k < 4; ++k) o.wt[k] = w_off(wave + 4 * k);
   if (wave < 2) {
     o.extra = w_off(wave + 16);
   }
   auto sum_off = [&](int h) {
-    const int m = 32 * h + (lane >> 1);
+    const int m = min(32 * h + (lane >> 1), BMv - 1);  // lanes past the tile: loads masked
     const int gm = ID ? xrow[m] : min(m0 + m, M - 1);
     return static_cast<uint32_t>(gm) * static_cast<uint32_t>(nb) * kQ8KBytes + 256u +
            16u * (lane & 1);
@@ -152,9 +162,10 @@ __device__ __forceinline__ StageOffsets stage_offsets(int M, int N, int nb, int 
   if (wave == 2) {
     o.extra = sum_off(0);
   } else if (wave == 3) {
-    const int gm = ID ? xrow[lane] : min(m0 + lane, M - 1);
+    const int m = min(lane, BMv - 1);
+    const int gm = ID ? xrow[m] : min(m0 + m, M - 1);
     o.extra = static_cast<uint32_t>(gm) * static_cast<uint32_t>(nb) * kQ8KBytes + 288u;
-    o.sums = sum_off(1);
+    o.sums = (BMv == 64) ? sum_off(1) : 0u;
   }
   return o;
 }
@@ -209,9 +220,11 @@ __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
+template <int BMv>
 __device__ __forceinline__ void issue_stage(uint8_t* base, const uint8_t* xq_in,
-                                            const uint8_t* w_in, const StageOffsets& o, int b,
-                                            int wave) {
+                                            const uint8_t* w_in, const StageOffsets<BMv>& o, int b,
+                                            int wave, int lane) {
+  using T = Tile<BMv>;
   const uint8_t* xq = uniform_ptr(xq_in);
   const uint8_t* w = uniform_ptr(w_in);
   const uint32_t xb = static_cast<uint32_t>(b) * kQ8KBytes;
@@ -220,16 +233,17 @@ __device__ __forceinline__ void issue_stage(uint8_t* base, const uint8_t* xq_in,
   const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_u32(base));
   const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) lds_dma16(xq, o.act[k] + xb, lb + 1024 * (wv + 4 * k));
+  for (int k = 0; k < T::kActPerWave; ++k) lds_dma16(xq, o.act[k] + xb, lb + 1024 * (wv + 4 * k));
 #pragma unroll
-  for (int k = 0; k < 4; ++k) lds_dma16(w, o.wt[k] + wb, lb + kWOff + 1024 * (wv + 4 * k));
+  for (int k = 0; k < 4; ++k) lds_dma16(w, o.wt[k] + wb, lb + T::kWOff + 1024 * (wv + 4 * k));
   if (wv < 2) {
-    lds_dma16(w, o.extra + wb, lb + kWOff + 1024 * (wv + 16));
+    lds_dma16(w, o.extra + wb, lb + T::kWOff + 1024 * (wv + 16));
   } else if (wv == 2) {
-    lds_dma16(xq, o.extra + xb, lb + kSumOff);
+    // BM = 16: 32 chunks of sums, lanes 0..31 (an inactive lane writes no LDS)
+    if (BMv == 64 || lane < 2 * BMv) lds_dma16(xq, o.extra + xb, lb + T::kSumOff);
   } else {
-    lds_dma4(xq, o.extra + xb, lb + kXsOff);
-    lds_dma16(xq, o.sums + xb, lb + kSumOff + 1024);
+    if (BMv == 64 || lane < BMv) lds_dma4(xq, o.extra + xb, lb + T::kXsOff);
+    if (BMv == 64) lds_dma16(xq, o.sums + xb, lb + T::kSumOff + 1024);
   }
 }
 
@@ -237,22 +251,24 @@ __device__ __forceinline__ void issue_stage(uint8_t* base, const uint8_t* xq_in,
 // [6:4] and lgkmcnt [11:8] left at their maxima, i.e. not waited on).
 constexpr int kWaitVm0 = 0x0F70;
 
-// A partial slot: the 32 f32 accumulators of each of the 256 threads,
+// A partial slot: the 8*MT f32 accumulators of each of the 256 threads,
 // element r of thread i at r * kThreads + i (one wave store covers 256
-// consecutive bytes).
-constexpr int kPartFloats = kThreads * 32;
+// consecutive bytes); Tile<BM>::kPartFloats floats.
 // Arrival counters sit one 128-byte line apart: counters sharing a line
 // serialize every workgroup's atomic on that line.
 constexpr int kCounterStride = 32;
 
-template <bool ID>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int BMv, bool ID>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
                      const uint8_t* __restrict__ xq, int M, int N, int nb, int mtiles,
                      int ntiles, int ks, float* __restrict__ part, int* __restrict__ cnt,
                      IdGemm id) {
-  __shared__ __align__(16) uint8_t stage0[kStageBytes];
-  __shared__ __align__(16) uint8_t stage1[kStageBytes];
+  using TL = Tile<BMv>;
+  constexpr int BM = BMv;
+  constexpr int MT = TL::MT;
+  __shared__ __align__(16) uint8_t stage0[TL::kStageBytes];
+  __shared__ __align__(16) uint8_t stage1[TL::kStageBytes];
   __shared__ int last_arrival;
   __shared__ int pair_s[ID ? BM : 1];
   __shared__ int xrow_s[ID ? BM : 1];
@@ -307,11 +323,11 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
   const int q = lane >> 4;         // k-quarter of an MFMA operand: k = 16q..16q+15
 
   typedef float v4f __attribute__((ext_vector_type(4)));
-  v4i sa[4][2], sb[4][2];
-  v4f cm[4][2];   // min term: sum_b xs * dmin * M_b, on f32 MFMA over sub-blocks
-  float4 acc[4][2];
+  v4i sa[MT][2], sb[MT][2];
+  v4f cm[MT][2];   // min term: sum_b xs * dmin * M_b, on f32 MFMA over sub-blocks
+  float4 acc[MT][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       acc[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -319,8 +335,8 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
     }
   const v4i zero = {0, 0, 0, 0};
 
-  const StageOffsets so = stage_offsets<ID>(M, N, nb, m0, n0, wave, lane, xrow_s);
-  issue_stage(stage0, xq, w, so, b_lo, wave);
+  const StageOffsets<BMv> so = stage_offsets<BMv, ID>(M, N, nb, m0, n0, wave, lane, xrow_s);
+  issue_stage<BMv>(stage0, xq, w, so, b_lo, wave, lane);
 
   // One super-block: wait for its stage, refill the other stage with
   // super-block b+1 (every wave finished reading it: it passed the barrier
@@ -328,7 +344,7 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
   auto step = [&](int b, const uint8_t* stg, uint8_t* refill) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    if (b + 1 < b_hi) issue_stage(refill, xq, w, so, b + 1, wave);
+    if (b + 1 < b_hi) issue_stage<BMv>(refill, xq, w, so, b + 1, wave, lane);
     // Wave priority: raised from here through the MFMA loop, lowered for the
     // epilogue, so that of the two waves sharing a SIMD the one feeding the
     // matrix core issues first and the other's VALU epilogue fills the gaps
@@ -336,9 +352,9 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
     __builtin_amdgcn_s_setprio(1);
 
     const uint8_t* act = stg;
-    const float* xs_s = reinterpret_cast<const float*>(stg + kXsOff);
-    const int* sum_s = reinterpret_cast<const int*>(stg + kSumOff);
-    const uint8_t* wblk = stg + kWOff;
+    const float* xs_s = reinterpret_cast<const float*>(stg + TL::kXsOff);
+    const int* sum_s = reinterpret_cast<const int*>(stg + TL::kSumOff);
+    const uint8_t* wblk = stg + TL::kWOff;
 
     // ---- this lane's weight rows: the sub-block scale of each (row, group)
     // for this lane's k-quarter, the block's d, and the min operands
@@ -366,7 +382,7 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
     }
     // ---- min term: A' = xs * s_j (token m = 16mt + l16, j = 4ks + q) ----
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
       const int r = 16 * mt + l16;
       const float xr = xs_s[r];
 #pragma unroll
@@ -381,9 +397,9 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       // A operands: token rows, codes k = 64g + 16q .. +15.
-      v4i a[4];
+      v4i a[MT];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
         const int r = 16 * mt + l16;
         a[mt] = *reinterpret_cast<const v4i*>(act + 256 * r + 16 * ((4 * g + q) ^ (r & 15)));
       }
@@ -405,7 +421,7 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
                        (int)mul_bytes(c3, fb)};
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           sa[mt][nt] = mfma(a[mt], ba[nt], g == 0 ? zero : sa[mt][nt]);
@@ -417,7 +433,7 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
     // ---- per-block epilogue: one float pass per output ----
     // C layout of a 16x16 tile: lane holds column l16, rows 4q..4q+3.
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
       const int mr = 16 * mt + 4 * q;
       const float x0 = xs_s[mr], x1 = xs_s[mr + 1], x2 = xs_s[mr + 2], x3 = xs_s[mr + 3];
 #pragma unroll
@@ -438,7 +454,7 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
     if (b + 1 < b_hi) step(b + 1, stage1, stage0);
   }
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       acc[mt][nt].x -= cm[mt][nt][0];
@@ -449,9 +465,9 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
 
   if (ks > 1) {
     // ---- split-K: publish this split's partial, count the arrival ----
-    float* mine = part + static_cast<int64_t>(tile * ks + split) * kPartFloats + tid;
+    float* mine = part + static_cast<int64_t>(tile * ks + split) * TL::kPartFloats + tid;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int r = 4 * (2 * mt + nt);
@@ -478,15 +494,15 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
       __hip_atomic_store(cnt + tile * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // The sum over splits in the fixed order 0..ks-1 (this split's own
     // values from registers).
-    float4 sum[4][2];
+    float4 sum[MT][2];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) sum[mt][nt] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < ks; ++j) {
-      const float* pj = part + static_cast<int64_t>(tile * ks + j) * kPartFloats + tid;
+      const float* pj = part + static_cast<int64_t>(tile * ks + j) * TL::kPartFloats + tid;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
           float4 v;
@@ -506,14 +522,14 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
         }
     }
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = sum[mt][nt];
   }
 
   // ---- store ----
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int n = n0 + 32 * wave + 16 * nt + l16;
@@ -536,32 +552,21 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
 // first split launch, kept until the process ends.
 constexpr int kSplitSlots = 512;   // tiles * ks stays within this
 constexpr int kSplitTiles = 256;   // above this many tiles, no split
-constexpr size_t kSplitBytes = static_cast<size_t>(kSplitSlots) * kPartFloats * sizeof(float) +
+constexpr size_t kSplitBytes = static_cast<size_t>(kSplitSlots) * Tile<64>::kPartFloats * sizeof(float) +
                                static_cast<size_t>(kSplitTiles) * kCounterStride * sizeof(int);
 
 // The grouped form's tile list: up to kIdMaxPairs pairs.
 constexpr int64_t kIdMaxPairs = int64_t{1} << 20;
 constexpr int kIdMaxExperts = 1024;
-constexpr int64_t kIdMaxTiles = kIdMaxPairs / BM + kIdMaxExperts + 1;
+constexpr int kIdBM = 64;  // the grouped form's token tile
+constexpr int64_t kIdMaxTiles = kIdMaxPairs / kIdBM + kIdMaxExperts + 1;
 constexpr size_t kIdBytes = kIdMaxPairs * sizeof(int32_t) + kIdMaxTiles * sizeof(int4) + 256;
 
-}  // namespace
-
-int gemm_q4k_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  const int64_t nb = K / 256;
-  if (tiles > kSplitTiles) return 1;
-  // Measured on MI355X (cold weights, 14336x4096 and 4096x14336): the best
-  // launches stay within one round of resident workgroups (two per CU, 512)
-  // and give each split at least ~7 super-blocks; more, shorter splits pay
-  // the per-workgroup prologue and the partial exchange.
-  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(kSplitSlots / tiles, nb / 7)));
-}
-
-hipError_t launch_gemm_q4k_split(float* y, const void* w, const void* xq, int64_t M, int64_t N,
-                                 int64_t K, int ks, hipStream_t stream) {
+template <int BMv>
+hipError_t launch_split(float* y, const void* w, const void* xq, int64_t M, int64_t N, int64_t K,
+                        int ks, hipStream_t stream) {
   const int nb = static_cast<int>(K / 256);
-  const int mtiles = static_cast<int>((M + BM - 1) / BM);
+  const int mtiles = static_cast<int>((M + BMv - 1) / BMv);
   const int ntiles = static_cast<int>((N + BN - 1) / BN);
   const int tiles = mtiles * ntiles;
   float* part = nullptr;
@@ -572,15 +577,36 @@ hipError_t launch_gemm_q4k_split(float* y, const void* w, const void* xq, int64_
     const hipError_t e = stream_workspace(kWsSplit, kSplitBytes, stream, &p);
     if (e != hipSuccess) return e;
     part = static_cast<float*>(p);
-    cnt = reinterpret_cast<int*>(part + static_cast<size_t>(kSplitSlots) * kPartFloats);
+    cnt = reinterpret_cast<int*>(part + static_cast<size_t>(kSplitSlots) * Tile<64>::kPartFloats);
   } else {
     ks = 1;
   }
-  hipLaunchKernelGGL(gemm_q4k_kernel<false>, dim3(tiles * ks), dim3(kThreads), 0, stream, y,
+  hipLaunchKernelGGL((gemm_q4k_kernel<BMv, false>), dim3(tiles * ks), dim3(kThreads), 0, stream, y,
                      static_cast<const uint8_t*>(w), static_cast<const uint8_t*>(xq),
                      static_cast<int>(M), static_cast<int>(N), nb, mtiles, ntiles, ks, part, cnt,
                      IdGemm{});
   return hipGetLastError();
+}
+
+}  // namespace
+
+int gemm_q4k_splits(int64_t M, int64_t N, int64_t K, int bm) {
+  const int64_t tiles = ((M + bm - 1) / bm) * ((N + BN - 1) / BN);
+  const int64_t nb = K / 256;
+  if (tiles > kSplitTiles) return 1;
+  // Measured on MI355X (cold weights; 14336x4096, 4096x14336 and 4096x4096
+  // at 7..512 tokens, both token tiles, ks = 1..8): the best launches stay
+  // within about one round of resident workgroups (512), give each split at
+  // least four super-blocks, and gain nothing past eight splits.
+  return static_cast<int>(
+      std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(kSplitSlots / tiles, nb / 4), 8)));
+}
+
+hipError_t launch_gemm_q4k_split(float* y, const void* w, const void* xq, int64_t M, int64_t N,
+                                 int64_t K, int ks, int bm, hipStream_t stream) {
+  if (bm == 16) return launch_split<16>(y, w, xq, M, N, K, ks, stream);
+  if (bm == 64) return launch_split<64>(y, w, xq, M, N, K, ks, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_q4k_id(float* y, const void* slab, const void* xq, const int32_t* ids,
@@ -594,36 +620,45 @@ hipError_t launch_gemm_q4k_id(float* y, const void* slab, const void* xq, const 
   int4* desc = static_cast<int4*>(p);
   int32_t* sorted = reinterpret_cast<int32_t*>(desc + kIdMaxTiles);
   int32_t* n_tiles = sorted + kIdMaxPairs;
-  if ((e = launch_route_experts(ids, n_pairs, n_experts, BM, sorted, desc, n_tiles, stream)) !=
+  if ((e = launch_route_experts(ids, n_pairs, n_experts, kIdBM, sorted, desc, n_tiles, stream)) !=
       hipSuccess)
     return e;
   const int nb = static_cast<int>(K / 256);
-  const int mtiles = static_cast<int>(route_max_tiles(n_pairs, n_experts, BM));
+  const int mtiles = static_cast<int>(route_max_tiles(n_pairs, n_experts, kIdBM));
   const int ntiles = static_cast<int>((rows + BN - 1) / BN);
   const IdGemm id{sorted, desc, n_tiles, static_cast<int>(n_experts), static_cast<int>(n_used),
                   per_slot_x, rows * nb * static_cast<int64_t>(kQ4KBytes)};
-  hipLaunchKernelGGL(gemm_q4k_kernel<true>, dim3(mtiles * ntiles), dim3(kThreads), 0, stream, y,
+  hipLaunchKernelGGL((gemm_q4k_kernel<kIdBM, true>), dim3(mtiles * ntiles), dim3(kThreads), 0, stream, y,
                      static_cast<const uint8_t*>(slab), static_cast<const uint8_t*>(xq),
                      static_cast<int>(n_pairs), static_cast<int>(rows), nb, mtiles, ntiles, 1,
                      nullptr, nullptr, id);
   return hipGetLastError();
 }
 
+int gemm_q4k_token_tile(int64_t M, int64_t N, int64_t K) {
+  // The 16-token tile (one MFMA tile per wave, a quarter of the accumulators,
+  // three workgroups per CU) against the 64-token one, measured: 14336x4096
+  // at 7..16 tokens 12.4-12.8 us against 19.3-21.2, at 48 tokens 24.4 against
+  // 21.0; 4096x4096 at 64 tokens 12.0 against 16.5.
+  return (M <= 32 || (M <= 64 && N * K <= (int64_t{1} << 25))) ? 16 : 64;
+}
+
 bool gemm_q4k_uses_matvec(int64_t M, int64_t N, int64_t K) {
-  // A short batch is a weight stream, not a dense contraction: one pass of
-  // the dot4 mat-vec over the weights for all M tokens costs less than the
-  // MFMA tile's fixed per-step latency. Measured on MI355X (cold weights):
-  // 14336x4096 at 6 tokens 20.2 us against 21.3 (7 tokens: 22.0 against 21.2),
-  // 4096x4096 at 8 tokens 9.7 us against 20.3.
+  // A very short batch is a weight stream, not a dense contraction: one pass
+  // of the dot4 mat-vec over the weights for all M tokens costs less than
+  // the 16-token MFMA tile. Measured on MI355X (cold weights): 14336x4096 at
+  // 3 tokens 11.7 us against 12.4 (4 tokens: 14.4 against 12.4); 4096x14336
+  // at 3 tokens 14.1 against 15.4; 4096x4096 at 8 tokens 9.6 against 9.5.
   return M == 1 ||
-         (M <= gemv_q4k_multi_max_tokens(K) && (M <= 6 || N * K <= (int64_t{1} << 25)));
+         (M <= gemv_q4k_multi_max_tokens(K) && (M <= 3 || N * K <= (int64_t{1} << 25)));
 }
 
 hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, int64_t N,
                            int64_t K, hipStream_t stream) {
   if (M == 1) return launch_gemv_q4k(y, w, xq, N, K, stream);
   if (gemm_q4k_uses_matvec(M, N, K)) return launch_gemv_q4k_multi(y, w, xq, M, N, K, stream);
-  return launch_gemm_q4k_split(y, w, xq, M, N, K, gemm_q4k_splits(M, N, K), stream);
+  const int bm = gemm_q4k_token_tile(M, N, K);
+  return launch_gemm_q4k_split(y, w, xq, M, N, K, gemm_q4k_splits(M, N, K, bm), bm, stream);
 }
 
 }  // namespace xq

@@ -433,7 +433,7 @@ def test_gemm_split_full_size(M, N, K):
 # M tokens, each token's row bit-identical to xq_gemv_q4k on that token.
 GEMM_SHORT = [
     (2, 14336, 4096, 7501),    # two rows per wave, clamped
-    (6, 14336, 4096, 7502),    # the longest batch on this shape
+    (3, 14336, 4096, 7502),    # the longest batch on this shape
     (3, 4096, 14336, 7503),    # seven units, three tokens fill the LDS cap
     (8, 4096, 4096, 7504),     # eight tokens on a 2^24-weight matrix
     (5, 300, 2304, 7505),      # ragged unit tail
@@ -457,6 +457,39 @@ def test_gemm_short_batch_rows_equal_matvec(M, N, K, seed):
     for m in sorted({0, M - 1}):
         ref, T = oracle.gemv_q4k(w, xqb[m], N, K)
         assert_close(Y[m], ref, T, "short batch row %d" % m)
+
+
+# The 16-token MFMA tile (M <= 32, or M <= 64 on matrices of at most 2^25
+# weights), split over K where the tile grid is short of the device.
+GEMM_TILE16 = [
+    (4, 14336, 4096, 7521),    # four tokens in one 16-token tile, four splits
+    (16, 14336, 4096, 7522),   # a full tile
+    (31, 4096, 14336, 7523),   # two tiles, the second ragged, eight splits
+    (17, 300, 2304, 7524),     # ragged tokens and rows, nine super-blocks
+    (64, 4096, 4096, 7525),    # four tiles on a 2^24-weight matrix
+]
+
+
+@pytest.mark.parametrize("M,N,K,seed", GEMM_TILE16)
+def test_gemm_token_tile_16(M, N, K, seed):
+    g = wl.rng(seed)
+    w = wl.q4k_weights(N, K, g)
+    xqb = oracle.quantize_q8k(wl.activations(M, K, g))
+    _note("gemm tile16 M=%d N=%d K=%d" % (M, N, K))
+    Y = gpu_gemm(w, xqb, M, N, K)
+    assert not np.isnan(Y).any()
+    if M * N * K <= 2 ** 28:
+        ref, T = oracle.gemm_q4k(w, xqb, M, N, K)
+        assert_close(Y.reshape(-1), ref.reshape(-1), T.reshape(-1), "tile16")
+    else:
+        s = wl.rng(seed + 1)
+        ms = np.concatenate([s.integers(0, M, 500), [0, M - 1, min(15, M - 1), min(16, M - 1)]])
+        ns = np.concatenate([s.integers(0, N, 500), [0, N - 1, 127, 128]])
+        ref, T = oracle.gemm_q4k(w, xqb, M, N, K, ms, ns)
+        assert_close(Y[ms, ns], ref, T, "tile16 sampled")
+        for m in sorted({0, M - 1}):
+            ref, T = oracle.gemv_q4k(w, xqb[m], N, K)
+            assert_close(Y[m], ref, T, "tile16 row %d" % m)
 
 
 def test_gemm_mfma_below_eight_tokens():
@@ -518,10 +551,10 @@ def test_gemm_prefill_512x14336x4096():
 
 
 @pytest.mark.parametrize("which", ["S", "M"])
-@pytest.mark.parametrize("M,K", [(3, 1024), (9, 1024), (9, 3584)])
+@pytest.mark.parametrize("M,K", [(3, 1024), (9, 1024), (9, 3584), (70, 1024)])
 def test_gemm_partials_bit_exact(which, M, K):
-    """M = 3 runs on the batched mat-vec, M = 9 on int8 MFMA (K = 3584: two
-    splits of 7 super-blocks)."""
+    """M = 3 runs on the batched mat-vec, M = 9 on the 16-token MFMA tile
+    (K = 3584: three splits), M = 70 on the 64-token tile."""
     N = 200
     g = wl.rng(7200)
     w = wl.q4k_isolation_weights(N, K, g, which)
