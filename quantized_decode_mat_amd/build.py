@@ -1,6 +1,7 @@
 """Build libxq.so in-tree with hipcc for gfx950.
 
     python -m quantized_decode_mat_amd.build
+    python -m quantized_decode_mat_amd.build --resource-usage   # compiler's per-kernel figures
 
 Every HIP translation unit is compiled with packed-FP32 instructions turned
 off (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the float code
@@ -70,6 +71,41 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def resource_usage() -> list:
+    """Per-kernel register, scratch, LDS and occupancy figures that the
+    compiler reports (-Rpass-analysis=kernel-resource-usage) for the device
+    code of every HIP source, as (kernel, fields) pairs."""
+    import re
+    out = []
+    with tempfile.TemporaryDirectory(prefix="xq_res_") as tmp:
+        for src in SOURCES:
+            if not src.endswith(".hip"):
+                continue
+            cmd = [HIPCC, "-x", "hip", *FLAGS, "--cuda-device-only", "-c", os.path.join(CSRC, src),
+                   "-o", os.path.join(tmp, src + ".o"), "-Rpass-analysis=kernel-resource-usage"]
+            r = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
+            if r.returncode != 0:
+                sys.stderr.write(r.stderr)
+                raise RuntimeError("hipcc failed on %s" % src)
+            for part in r.stderr.split("remark: Function Name: ")[1:]:
+                name = part.split("\n")[0].split(" [")[0].strip()
+                fields = {"source": src}
+                for key, pat in (("vgprs", r"VGPRs: (\d+)"), ("agprs", r"AGPRs: (\d+)"),
+                                 ("sgprs", r"SGPRs: (\d+)"),
+                                 ("scratch_bytes", r"ScratchSize \[bytes/lane\]: (\d+)"),
+                                 ("occupancy", r"Occupancy \[waves/SIMD\]: (\d+)"),
+                                 ("lds_bytes", r"LDS Size \[bytes/block\]: (\d+)")):
+                    m = re.search(pat, part)
+                    fields[key] = int(m.group(1)) if m else None
+                out.append((name, fields))
+    return out
+
+
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
-    print(LIB)
+    if "--resource-usage" in sys.argv:
+        import json
+        for name, fields in resource_usage():
+            print(json.dumps({"kernel": name, **fields}))
+    else:
+        build(verbose="-v" in sys.argv)
+        print(LIB)
