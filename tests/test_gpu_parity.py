@@ -331,6 +331,7 @@ IQ4_SHAPES = [
     ("n300_k8192_four_units", 300, 8192, 5006),
     ("n70_k10240_five_units", 70, 10240, 5007),
     ("n20000_k512_two_rows_per_wave", 20000, 512, 5008),
+    ("n64_kmax", 64, 49152, 5009),
 ]
 
 
@@ -599,3 +600,49 @@ def test_stream_read_probe_reads_every_chunk(nbytes):
     xq.xq_bench_stream_read(buf, nbytes, sink)
     torch.cuda.synchronize()
     assert np.array_equal(sink.cpu().numpy(), _stream_fold_model(words))
+
+
+# ---------------------------------------------------------------------------
+# Degenerate inputs
+# ---------------------------------------------------------------------------
+
+def test_zero_activations_give_exact_zeros():
+    """An all-zero activation quantizes to d = 0 and codes 0 (the quantizer's
+    zero-block case); every path then outputs exactly 0.0, with no NaN from
+    the zero scale. Zero token rows inside a batch stay exactly zero while
+    the other rows match the oracle."""
+    N, K = 300, 4096
+    g = wl.rng(7700)
+    wq = wl.q4k_weights(N, K, g)
+    wi = wl.iq4nl_weights(N, K, g)
+    zero = np.zeros((1, K), np.float32)
+    zq = oracle.quantize_q8k(zero)
+    assert not zq[:, :, :292].any()
+    _note("zero activations")
+    for name, fn, w in (("q4k", xq.xq_gemv_q4k, wq), ("iq4nl", xq.xq_gemv_iq4nl, wi),
+                        ("q4_0", xq.xq_gemv_q4_0, wi)):
+        y = poisoned_f32(N)
+        fn(y, dev(w), dev(zq), N, K)
+        got = take_f32(y, N)
+        assert np.array_equal(got, np.zeros(N)), name
+    for M in (3, 16, 70):  # batched mat-vec, 16-token tile, 64-token tile
+        x = wl.activations(M, K, g)
+        x[1::2] = 0.0
+        xqb = oracle.quantize_q8k(x)
+        Y = gpu_gemm(wq, xqb, M, N, K)
+        assert np.array_equal(Y[1::2], np.zeros_like(Y[1::2])), M
+        ref, T = oracle.gemm_q4k(wq, xqb, M, N, K)
+        assert_close(Y.reshape(-1), ref.reshape(-1), T.reshape(-1), "zero rows M=%d" % M)
+
+
+def test_gemm_max_k():
+    """The product at K = 49152 (192 super-blocks), the largest K the mat-vec
+    accepts, with ragged tokens and rows."""
+    M, N, K = 20, 130, 49152
+    g = wl.rng(7710)
+    w = wl.q4k_weights(N, K, g)
+    xqb = oracle.quantize_q8k(wl.activations(M, K, g))
+    _note("gemm max K")
+    Y = gpu_gemm(w, xqb, M, N, K)
+    ref, T = oracle.gemm_q4k(w, xqb, M, N, K)
+    assert_close(Y.reshape(-1), ref.reshape(-1), T.reshape(-1), "gemm max K")

@@ -37,6 +37,7 @@ Q40_SHAPES = [
     ("n300_k8192_four_units", 300, 8192, 8208),
     ("n70_k10240_five_units", 70, 10240, 8209),
     ("n20000_k512_two_rows_per_wave", 20000, 512, 8210),
+    ("n64_kmax", 64, 49152, 8211),
 ]
 
 
