@@ -10,7 +10,8 @@
 // Lane layout: a "unit" is 8 consecutive super-blocks of a row; lane l takes
 // block 8u + l/8 and its 16-byte nibble chunk c = l%8, which is half of nibble
 // group g = c/2 (h = c%2), plus the block's 16-byte header. Shared by the
-// mat-vec and the fused FFN-pair kernel, so both produce the same bits.
+// single-token and the batched mat-vec kernels, so a token's row comes out
+// with the same bits from either.
 #pragma once
 
 #include "xq_device.h"

@@ -6,7 +6,7 @@
 // is amax/127 and each code x/d, both IEEE f32 divisions (HIP's default
 // division is correctly rounded; nothing here is built with fast-math),
 // rounded to nearest-even by v_rndne_f32. Shared by the quantize kernel and
-// the fused FFN-pair kernel, so both produce the same bytes.
+// the mat-vec's fused q8_K tail, so both produce the same bytes.
 #pragma once
 
 #include "xq_device.h"

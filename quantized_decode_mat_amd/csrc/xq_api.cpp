@@ -156,10 +156,9 @@ xq_status xq_gemv_q4_0(float* y, const void* w, const void* xq, int64_t N, int64
                   "xq_gemv_q4_0");
 }
 
-static xq_status check_id(const char* fn, float* y, const void* slab, const void* xq,
+static xq_status check_id(float* y, const void* slab, const void* xq,
                    const int32_t* sel, int64_t n_experts, int64_t used, int64_t rows, int64_t K,
                    int64_t x_stride_blocks) {
-  (void)fn;
   if (!y) return fail(XQ_E_NULL, "y is NULL");
   if (!slab) return fail(XQ_E_NULL, "slab is NULL");
   if (!xq) return fail(XQ_E_NULL, "xq is NULL");
@@ -186,7 +185,7 @@ static xq_status check_id(const char* fn, float* y, const void* slab, const void
 xq_status xq_gemv_q4k_id(float* y, const void* slab, const void* xq, const int32_t* sel,
                          int64_t n_experts, int64_t used, int64_t rows, int64_t K,
                          int64_t x_stride_blocks, void* stream) {
-  if (xq_status s = check_id("xq_gemv_q4k_id", y, slab, xq, sel, n_experts, used, rows, K,
+  if (xq_status s = check_id(y, slab, xq, sel, n_experts, used, rows, K,
                              x_stride_blocks))
     return s;
   return launched(xq::launch_gemv_q4k_id(y, slab, xq, sel, n_experts, used, rows, K,
@@ -197,7 +196,7 @@ xq_status xq_gemv_q4k_id(float* y, const void* slab, const void* xq, const int32
 xq_status xq_gemv_iq4nl_id(float* y, const void* slab, const void* xq, const int32_t* sel,
                            int64_t n_experts, int64_t used, int64_t rows, int64_t K,
                            int64_t x_stride_blocks, void* stream) {
-  if (xq_status s = check_id("xq_gemv_iq4nl_id", y, slab, xq, sel, n_experts, used, rows, K,
+  if (xq_status s = check_id(y, slab, xq, sel, n_experts, used, rows, K,
                              x_stride_blocks))
     return s;
   return launched(xq::launch_gemv_iq4nl_id(y, slab, xq, sel, n_experts, used, rows, K,
