@@ -57,7 +57,7 @@ COUNTED = {
         "void xq::(anonymous namespace)::gemv_iq4nl_resident_kernel<2, false, 0>", 8,
         295501824 + 5120 + 4 * 128256, ("gemv_iq4nl.hip", "xq_device.h")),
     "gemm_q4k_512x14336x4096": (
-        "void xq::(anonymous namespace)::gemm_q4k_kernel<false>", 4,
+        "void xq::(anonymous namespace)::gemm_q4k_kernel<64, false>", 4,
         33030144 + 512 * 16 * 320 + 4 * 512 * 14336, ("gemm_q4k.hip", "xq_device.h")),
 }
 HEADLINE = "gemv_q4k_up_14336x4096"
