@@ -148,11 +148,13 @@ xq_status xq_gemv_iq4nl(float *y, const void *w, const void *xq, int64_t N, int6
  * tokens, and row m is then bit-identical to xq_gemv_q4k on token m. Larger
  * M runs on int8 MFMA, in tiles of 16 tokens up to M = 32 (64 when
  * N*K <= 2^25) and of 64 tokens beyond.
- * Shapes with at most 256 tiles of 16 or 64 tokens x 128 rows split K over several
- * workgroups (section 25.3: fill the device first); the partials go through
- * a workspace the library owns, one per (device, stream): 16 MiB allocated,
- * zeroed and synchronized on the first such call on a stream, kept until the
- * process ends. That first call therefore cannot be captured into a graph;
+ * Shapes with at most 256 tiles of 16 or 64 tokens x 128 rows split K over
+ * several workgroups (section 25.3: fill the device first); shapes with more
+ * tiles than one round of resident workgroups run whole rounds of whole
+ * tiles and may split the last, short round's tiles the same way. The
+ * partials go through a workspace the library owns, one per (device,
+ * stream): 64 MiB allocated, zeroed and synchronized on the first such call
+ * on a stream, kept until the process ends. That first call therefore cannot be captured into a graph;
  * later ones allocate nothing. Splits are summed in a fixed order, so
  * results are bit-identical from call to call. Calls on one stream are
  * ordered; calls on different streams use different workspaces.

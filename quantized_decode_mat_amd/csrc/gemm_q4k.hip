@@ -262,8 +262,8 @@ template <int BMv, bool ID>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
                      const uint8_t* __restrict__ xq, int M, int N, int nb, int mtiles,
-                     int ntiles, int ks, float* __restrict__ part, int* __restrict__ cnt,
-                     IdGemm id) {
+                     int ntiles, int n_full, int ks, float* __restrict__ part,
+                     int* __restrict__ cnt, IdGemm id) {
   using TL = Tile<BMv>;
   constexpr int BM = BMv;
   constexpr int MT = TL::MT;
@@ -273,21 +273,33 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
   __shared__ int pair_s[ID ? BM : 1];
   __shared__ int xrow_s[ID ? BM : 1];
 
-  // Workgroup -> (split, tile). When the workgroup count is a multiple of the
-  // 8 XCDs, XCD x (= id % 8) takes a contiguous run in which the token tiles
-  // of one weight tile (same split) are adjacent.
+  // Workgroup -> (tile, split). The first n_full workgroups take tiles
+  // 0..n_full-1 whole; the others split each remaining tile's K ks ways
+  // (split-major). When a region's workgroup count is a multiple of the 8
+  // XCDs, XCD x (= id % 8) takes a contiguous run of it, in which the token
+  // tiles of one weight tile (same split) are adjacent.
   const int tiles = mtiles * ntiles;
-  const int T = tiles * ks;
-  int t = blockIdx.x;
-  if (T % 8 == 0) t = (blockIdx.x % 8) * (T / 8) + blockIdx.x / 8;
-  const int split = t / tiles;
-  const int tile = t - split * tiles;
+  int tile, split = 0, kst = 1;
+  if (static_cast<int>(blockIdx.x) < n_full) {
+    const int t = (n_full % 8 == 0) ? (blockIdx.x % 8) * (n_full / 8) + blockIdx.x / 8
+                                    : static_cast<int>(blockIdx.x);
+    tile = t;
+  } else {
+    const int rest = tiles - n_full;
+    const int G = rest * ks;
+    const int v = blockIdx.x - n_full;
+    const int u = (G % 8 == 0) ? (v % 8) * (G / 8) + v / 8 : v;
+    split = u / rest;
+    tile = n_full + (u - split * rest);
+    kst = ks;
+  }
+  const int wt = tile - n_full;  // workspace slot of a split tile
   const int ntile = tile / mtiles;
   const int mtile = tile % mtiles;
   int m0 = mtile * BM;
   const int n0 = ntile * BN;
-  const int b_lo = static_cast<int>(static_cast<int64_t>(split) * nb / ks);
-  const int b_hi = static_cast<int>(static_cast<int64_t>(split + 1) * nb / ks);
+  const int b_lo = static_cast<int>(static_cast<int64_t>(split) * nb / kst);
+  const int b_hi = static_cast<int>(static_cast<int64_t>(split + 1) * nb / kst);
 
   const int tid = threadIdx.x;
   if constexpr (ID) {
@@ -463,9 +475,9 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
       acc[mt][nt].w -= cm[mt][nt][3];
     }
 
-  if (ks > 1) {
+  if (kst > 1) {
     // ---- split-K: publish this split's partial, count the arrival ----
-    float* mine = part + static_cast<int64_t>(tile * ks + split) * TL::kPartFloats + tid;
+    float* mine = part + static_cast<int64_t>(wt * kst + split) * TL::kPartFloats + tid;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -486,12 +498,12 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
     if (tid == 0)
-      last_arrival = __hip_atomic_fetch_add(cnt + tile * kCounterStride, 1, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT) == ks - 1;
+      last_arrival = __hip_atomic_fetch_add(cnt + wt * kCounterStride, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) == kst - 1;
     __syncthreads();
     if (!last_arrival) return;  // workgroup-uniform
     if (tid == 0)
-      __hip_atomic_store(cnt + tile * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(cnt + wt * kCounterStride, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // The sum over splits in the fixed order 0..ks-1 (this split's own
     // values from registers).
     float4 sum[MT][2];
@@ -499,8 +511,8 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) sum[mt][nt] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < ks; ++j) {
-      const float* pj = part + static_cast<int64_t>(tile * ks + j) * TL::kPartFloats + tid;
+    for (int j = 0; j < kst; ++j) {
+      const float* pj = part + static_cast<int64_t>(wt * kst + j) * TL::kPartFloats + tid;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -546,14 +558,21 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
     }
 }
 
-// Split-K workspace: kSplitSlots partial slots (16 MiB) and one counter per
-// tile for up to kSplitTiles tiles, one per (device, stream) so that calls on
-// different streams never share it; allocated and zeroed on a stream's
+// Split-K workspace: kSplitSlots partial slots of the 64-token tile (64 MiB)
+// and kSplitCounters arrival counters, one per (device, stream) so that calls
+// on different streams never share it; allocated and zeroed on a stream's
 // first split launch, kept until the process ends.
-constexpr int kSplitSlots = 512;   // tiles * ks stays within this
-constexpr int kSplitTiles = 256;   // above this many tiles, no split
-constexpr size_t kSplitBytes = static_cast<size_t>(kSplitSlots) * Tile<64>::kPartFloats * sizeof(float) +
-                               static_cast<size_t>(kSplitTiles) * kCounterStride * sizeof(int);
+constexpr int kSplitSlots = 2048;    // split workgroups of a launch
+constexpr int kSplitCounters = 768;  // split tiles of a launch
+constexpr int kSplitTiles = 256;     // up to this many tiles, every tile splits
+constexpr int kRound = 512;          // the all-split rule's one round of workgroups
+constexpr size_t kSplitBytes =
+    static_cast<size_t>(kSplitSlots) * Tile<64>::kPartFloats * sizeof(float) +
+    static_cast<size_t>(kSplitCounters) * kCounterStride * sizeof(int);
+
+// Workgroups resident at once over the 256 CUs: two 64-token tiles or three
+// 16-token tiles per CU (their LDS rings, 73 KB and 46 KB of the 160 KB).
+constexpr int64_t resident_tiles(int bm) { return bm == 16 ? 768 : 512; }
 
 // The grouped form's tile list: up to kIdMaxPairs pairs.
 constexpr int64_t kIdMaxPairs = int64_t{1} << 20;
@@ -564,48 +583,80 @@ constexpr size_t kIdBytes = kIdMaxPairs * sizeof(int32_t) + kIdMaxTiles * sizeof
 
 template <int BMv>
 hipError_t launch_split(float* y, const void* w, const void* xq, int64_t M, int64_t N, int64_t K,
-                        int ks, hipStream_t stream) {
+                        const GemmPlan& plan, hipStream_t stream) {
   const int nb = static_cast<int>(K / 256);
   const int mtiles = static_cast<int>((M + BMv - 1) / BMv);
   const int ntiles = static_cast<int>((N + BN - 1) / BN);
   const int tiles = mtiles * ntiles;
+  int n_full = tiles, ks = 1;
   float* part = nullptr;
   int* cnt = nullptr;
-  if (ks > 1) {
-    if (tiles > kSplitTiles || tiles * ks > kSplitSlots || ks > nb) return hipErrorInvalidValue;
+  if (plan.ks > 1) {
+    n_full = plan.n_full;
+    ks = plan.ks;
+    const int rest = tiles - n_full;
+    if (n_full < 0 || rest < 1 || rest > kSplitCounters || rest * ks > kSplitSlots || ks > nb)
+      return hipErrorInvalidValue;
     void* p = nullptr;
     const hipError_t e = stream_workspace(kWsSplit, kSplitBytes, stream, &p);
     if (e != hipSuccess) return e;
     part = static_cast<float*>(p);
     cnt = reinterpret_cast<int*>(part + static_cast<size_t>(kSplitSlots) * Tile<64>::kPartFloats);
-  } else {
-    ks = 1;
   }
-  hipLaunchKernelGGL((gemm_q4k_kernel<BMv, false>), dim3(tiles * ks), dim3(kThreads), 0, stream, y,
+  const int grid = n_full + (tiles - n_full) * ks;
+  hipLaunchKernelGGL((gemm_q4k_kernel<BMv, false>), dim3(grid), dim3(kThreads), 0, stream, y,
                      static_cast<const uint8_t*>(w), static_cast<const uint8_t*>(xq),
-                     static_cast<int>(M), static_cast<int>(N), nb, mtiles, ntiles, ks, part, cnt,
-                     IdGemm{});
+                     static_cast<int>(M), static_cast<int>(N), nb, mtiles, ntiles, n_full, ks,
+                     part, cnt, IdGemm{});
   return hipGetLastError();
 }
 
 }  // namespace
 
-int gemm_q4k_splits(int64_t M, int64_t N, int64_t K, int bm) {
+GemmPlan gemm_q4k_plan(int64_t M, int64_t N, int64_t K, int bm) {
   const int64_t tiles = ((M + bm - 1) / bm) * ((N + BN - 1) / BN);
   const int64_t nb = K / 256;
-  if (tiles > kSplitTiles) return 1;
-  // Measured on MI355X (cold weights; 14336x4096, 4096x14336 and 4096x4096
-  // at 7..512 tokens, both token tiles, ks = 1..8): the best launches stay
-  // within about one round of resident workgroups (512), give each split at
-  // least four super-blocks, and gain nothing past eight splits.
-  return static_cast<int>(
-      std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(kSplitSlots / tiles, nb / 4), 8)));
+  if (tiles <= kSplitTiles) {
+    // Measured on MI355X (cold weights; 14336x4096, 4096x14336 and 4096x4096
+    // at 7..512 tokens, both token tiles, ks = 1..8): the best launches stay
+    // within about one round of resident workgroups (512), give each split
+    // at least four super-blocks, and gain nothing past eight splits.
+    const int64_t ks = std::max<int64_t>(
+        1, std::min<int64_t>(std::min<int64_t>(kRound / tiles, nb / 4), 8));
+    return GemmPlan{0, static_cast<int>(ks)};
+  }
+  // More tiles than that: whole rounds of whole tiles, then the remainder,
+  // which leaves the device part-idle for a last round of nb super-blocks
+  // (section 25.3: fill the device). The remainder splits over K when the
+  // split workgroups fit one round and that round is shorter. Cost in tenths
+  // of a super-block step of a CU running two tiles, measured on MI355X
+  // (cold weights, 14336x4096 and 8192x4096): a CU with one tile runs a step
+  // in 0.7 of that, and a round of split workgroups pays about 2.5 steps
+  // more (the ring's first load, the partials and their sum). 320 x 14336 x
+  // 4096 (560 tiles = 512 whole + 48 in four splits): 59 us against 75;
+  // 576 x 8192 x 4096: 60 against 74. Remainders that would need several
+  // rounds of splits lose: 896 tiles with 384 in four splits, 100 us
+  // against 89.
+  const int64_t S = resident_tiles(bm);
+  const int64_t rest = tiles % S;
+  GemmPlan plan{static_cast<int>(tiles), 1};
+  if (rest == 0) return plan;
+  auto step_cost = [&](int64_t wgs) { return wgs <= S / 2 ? 7 : 10; };
+  int64_t best = nb * step_cost(rest);
+  for (int64_t ks = 2; ks <= 8 && nb / ks >= 4 && rest * ks <= S; ks *= 2) {
+    const int64_t cost = ((nb + ks - 1) / ks) * step_cost(rest * ks) + 25;
+    if (cost < best) {
+      best = cost;
+      plan = GemmPlan{static_cast<int>(tiles - rest), static_cast<int>(ks)};
+    }
+  }
+  return plan;
 }
 
 hipError_t launch_gemm_q4k_split(float* y, const void* w, const void* xq, int64_t M, int64_t N,
-                                 int64_t K, int ks, int bm, hipStream_t stream) {
-  if (bm == 16) return launch_split<16>(y, w, xq, M, N, K, ks, stream);
-  if (bm == 64) return launch_split<64>(y, w, xq, M, N, K, ks, stream);
+                                 int64_t K, const GemmPlan& plan, int bm, hipStream_t stream) {
+  if (bm == 16) return launch_split<16>(y, w, xq, M, N, K, plan, stream);
+  if (bm == 64) return launch_split<64>(y, w, xq, M, N, K, plan, stream);
   return hipErrorInvalidValue;
 }
 
@@ -630,8 +681,8 @@ hipError_t launch_gemm_q4k_id(float* y, const void* slab, const void* xq, const 
                   per_slot_x, rows * nb * static_cast<int64_t>(kQ4KBytes)};
   hipLaunchKernelGGL((gemm_q4k_kernel<kIdBM, true>), dim3(mtiles * ntiles), dim3(kThreads), 0, stream, y,
                      static_cast<const uint8_t*>(slab), static_cast<const uint8_t*>(xq),
-                     static_cast<int>(n_pairs), static_cast<int>(rows), nb, mtiles, ntiles, 1,
-                     nullptr, nullptr, id);
+                     static_cast<int>(n_pairs), static_cast<int>(rows), nb, mtiles, ntiles,
+                     mtiles * ntiles, 1, nullptr, nullptr, id);
   return hipGetLastError();
 }
 
@@ -658,7 +709,7 @@ hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, i
   if (M == 1) return launch_gemv_q4k(y, w, xq, N, K, stream);
   if (gemm_q4k_uses_matvec(M, N, K)) return launch_gemv_q4k_multi(y, w, xq, M, N, K, stream);
   const int bm = gemm_q4k_token_tile(M, N, K);
-  return launch_gemm_q4k_split(y, w, xq, M, N, K, gemm_q4k_splits(M, N, K, bm), bm, stream);
+  return launch_gemm_q4k_split(y, w, xq, M, N, K, gemm_q4k_plan(M, N, K, bm), bm, stream);
 }
 
 }  // namespace xq

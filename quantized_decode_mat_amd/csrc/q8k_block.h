@@ -6,7 +6,8 @@
 // is amax/127 and each code x/d, both IEEE f32 divisions (HIP's default
 // division is correctly rounded; nothing here is built with fast-math),
 // rounded to nearest-even by v_rndne_f32. Shared by the quantize kernel and
-// the mat-vec's fused q8_K tail, so both produce the same bytes.
+// the mat-vec's fused q8_K steps (quantizing its input in front, its output
+// in the tail), so all of them produce the same bytes.
 #pragma once
 
 #include "xq_device.h"
@@ -19,8 +20,15 @@ __device__ __forceinline__ int q8k_code(float x, float d) {
   return static_cast<int>(r);
 }
 
-// Writes the whole 320-byte block at `out` (global memory or LDS).
-__device__ __forceinline__ void q8k_block_wave(const float4 v, uint8_t* out, int lane) {
+// One lane's share of a block: its four packed codes, the sum of its
+// sub-block's 32 codes (valid on lanes 8j), and the block scale.
+struct Q8KLane {
+  uint32_t packed;
+  int32_t sum;
+  float d;
+};
+
+__device__ __forceinline__ Q8KLane q8k_block_lane(const float4 v) {
   const float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
   const float amax = wave_max(a);
   const float d = amax / 127.0f;
@@ -32,16 +40,38 @@ __device__ __forceinline__ void q8k_block_wave(const float4 v, uint8_t* out, int
     q2 = q8k_code(v.z, d);
     q3 = q8k_code(v.w, d);
   }
-  const uint32_t packed = (static_cast<uint32_t>(q0) & 0xFFu) |
-                          ((static_cast<uint32_t>(q1) & 0xFFu) << 8) |
-                          ((static_cast<uint32_t>(q2) & 0xFFu) << 16) |
-                          ((static_cast<uint32_t>(q3) & 0xFFu) << 24);
-  const int s = lane8_sum(q0 + q1 + q2 + q3);  // lanes 8j..8j+7 hold codes 32j..32j+31
+  Q8KLane o;
+  o.packed = (static_cast<uint32_t>(q0) & 0xFFu) | ((static_cast<uint32_t>(q1) & 0xFFu) << 8) |
+             ((static_cast<uint32_t>(q2) & 0xFFu) << 16) |
+             ((static_cast<uint32_t>(q3) & 0xFFu) << 24);
+  o.sum = lane8_sum(q0 + q1 + q2 + q3);  // lanes 8j..8j+7 hold codes 32j..32j+31
+  o.d = d;
+  return o;
+}
 
-  reinterpret_cast<uint32_t*>(out)[lane] = packed;
-  if ((lane & 7) == 0) reinterpret_cast<int32_t*>(out + 256)[lane >> 3] = s;
-  if (lane == 0) *reinterpret_cast<float*>(out + 288) = d;
+// Writes the whole 320-byte block at `out` (global memory or LDS).
+__device__ __forceinline__ void q8k_block_wave(const float4 v, uint8_t* out, int lane) {
+  const Q8KLane o = q8k_block_lane(v);
+  reinterpret_cast<uint32_t*>(out)[lane] = o.packed;
+  if ((lane & 7) == 0) reinterpret_cast<int32_t*>(out + 256)[lane >> 3] = o.sum;
+  if (lane == 0) *reinterpret_cast<float*>(out + 288) = o.d;
   if (lane >= 1 && lane < 8) reinterpret_cast<uint32_t*>(out + 288)[lane] = 0u;  // 292..319
+}
+
+// The same bytes written to global memory with agent-scope atomic stores,
+// which reach memory coherent across XCDs, for a block that workgroups on
+// other XCDs read while the kernel runs.
+__device__ __forceinline__ void q8k_block_wave_agent(const float4 v, uint8_t* out, int lane) {
+  const Q8KLane o = q8k_block_lane(v);
+  uint32_t* o32 = reinterpret_cast<uint32_t*>(out);
+  __hip_atomic_store(o32 + lane, o.packed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((lane & 7) == 0)
+    __hip_atomic_store(o32 + 64 + (lane >> 3), static_cast<uint32_t>(o.sum), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0)
+    __hip_atomic_store(o32 + 72, __float_as_uint(o.d), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane >= 1 && lane < 8)
+    __hip_atomic_store(o32 + 72 + lane, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace xq

@@ -47,14 +47,20 @@ hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, i
                            int64_t K, hipStream_t stream);
 // Whether launch_gemm_q4k serves this shape with the mat-vec kernels.
 bool gemm_q4k_uses_matvec(int64_t M, int64_t N, int64_t K);
-// The small-M product's token tile for a shape (16 or 64 tokens), the splits
-// of K it uses (1: none), and the product with an explicit tile and split
-// count (ks > 1 needs at most 256 tiles of bm x 128, tiles * ks <= 512 and
-// ks <= K/256).
+// The small-M product's launch plan: tiles 0..n_full-1 (of bm tokens x 128
+// rows, token tile fastest) run whole, the rest split K ks ways (ks = 1:
+// every tile whole). Needs, when ks > 1: 1 <= tiles - n_full <= 768,
+// (tiles - n_full) * ks <= 2048 and ks <= K/256.
+struct GemmPlan {
+  int n_full;
+  int ks;
+};
+// The token tile for a shape (16 or 64 tokens), the plan launch_gemm_q4k
+// uses, and the product with an explicit tile and plan.
 int gemm_q4k_token_tile(int64_t M, int64_t N, int64_t K);
-int gemm_q4k_splits(int64_t M, int64_t N, int64_t K, int bm);
+GemmPlan gemm_q4k_plan(int64_t M, int64_t N, int64_t K, int bm);
 hipError_t launch_gemm_q4k_split(float* y, const void* w, const void* xq, int64_t M, int64_t N,
-                                 int64_t K, int ks, int bm, hipStream_t stream);
+                                 int64_t K, const GemmPlan& plan, int bm, hipStream_t stream);
 // Grouped small-M product: route the (token, slot) pairs of ids by expert,
 // then one product launch over the tile list (at most 2^20 pairs and 1024
 // experts).

@@ -430,6 +430,31 @@ def test_gemm_split_full_size(M, N, K):
         assert_close(Y[m], ref, T, "split row %d" % m)
 
 
+@pytest.mark.parametrize("M,N,K,first_split_row", [(320, 14336, 4096, 13056), (576, 8192, 4096, 7168)])
+def test_gemm_whole_and_split_tiles(M, N, K, first_split_row):
+    """More tiles than one round of resident workgroups, with a short
+    remainder: 512 tiles run whole and the last ones split K four ways in
+    the same launch (320 tokens: 560 tiles, the split ones from weight tile
+    102 on; 576 tokens: 576 tiles, from weight tile 56 on). Sampled outputs
+    on both sides of that boundary, and whole rows against the mat-vec."""
+    g = wl.rng(7600 + M)
+    w = wl.q4k_weights(N, K, g)
+    xqb = oracle.quantize_q8k(wl.activations(M, K, g))
+    _note("gemm whole and split tiles M=%d N=%d K=%d" % (M, N, K))
+    Y = gpu_gemm(w, xqb, M, N, K)
+    assert not np.isnan(Y).any()
+    s = wl.rng(7610 + M)
+    ms = np.concatenate([s.integers(0, M, 1200), [0, M - 1, 63, 64, 127, 128, M - 1]])
+    ns = np.concatenate([s.integers(0, N, 600), s.integers(first_split_row, N, 600),
+                         [first_split_row - 1, first_split_row, N - 1, 0, 127, 128,
+                          first_split_row + 127]])
+    ref, T = oracle.gemm_q4k(w, xqb, M, N, K, ms, ns)
+    assert_close(Y[ms, ns], ref, T, "whole/split sampled")
+    for m in sorted({0, 130, M - 1}):
+        ref, T = oracle.gemv_q4k(w, xqb[m], N, K)
+        assert_close(Y[m], ref, T, "whole/split row %d" % m)
+
+
 # Short batches run on the mat-vec kernels: one pass over the weights for all
 # M tokens, each token's row bit-identical to xq_gemv_q4k on that token.
 GEMM_SHORT = [
