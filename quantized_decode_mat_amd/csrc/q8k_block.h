@@ -6,8 +6,7 @@
 // is amax/127 and each code x/d, both IEEE f32 divisions (HIP's default
 // division is correctly rounded; nothing here is built with fast-math),
 // rounded to nearest-even by v_rndne_f32. Shared by the quantize kernel and
-// the mat-vec's fused q8_K steps (quantizing its input in front, its output
-// in the tail), so all of them produce the same bytes.
+// the mat-vec's fused q8_K tail, so both produce the same bytes.
 #pragma once
 
 #include "xq_device.h"
@@ -56,22 +55,6 @@ __device__ __forceinline__ void q8k_block_wave(const float4 v, uint8_t* out, int
   if ((lane & 7) == 0) reinterpret_cast<int32_t*>(out + 256)[lane >> 3] = o.sum;
   if (lane == 0) *reinterpret_cast<float*>(out + 288) = o.d;
   if (lane >= 1 && lane < 8) reinterpret_cast<uint32_t*>(out + 288)[lane] = 0u;  // 292..319
-}
-
-// The same bytes written to global memory with agent-scope atomic stores,
-// which reach memory coherent across XCDs, for a block that workgroups on
-// other XCDs read while the kernel runs.
-__device__ __forceinline__ void q8k_block_wave_agent(const float4 v, uint8_t* out, int lane) {
-  const Q8KLane o = q8k_block_lane(v);
-  uint32_t* o32 = reinterpret_cast<uint32_t*>(out);
-  __hip_atomic_store(o32 + lane, o.packed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if ((lane & 7) == 0)
-    __hip_atomic_store(o32 + 64 + (lane >> 3), static_cast<uint32_t>(o.sum), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  if (lane == 0)
-    __hip_atomic_store(o32 + 72, __float_as_uint(o.d), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (lane >= 1 && lane < 8)
-    __hip_atomic_store(o32 + 72 + lane, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace xq
