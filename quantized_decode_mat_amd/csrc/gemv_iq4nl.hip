@@ -348,7 +348,14 @@ hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64
   const int n = static_cast<int>(N);
   // Launch shapes chosen by measurement on MI355X (cold weights; 128256 x
   // 4096: 76.4 us with one row-pair per wave and the activation read from LDS
-  // per row, 47.5 us resident).
+  // per row, 47.5 us resident). Grouped launches of single-unit rows over a
+  // few thousand rows per expert leave the resident kernel one row per wave
+  // and nothing to reuse its register copy of the activation for: 8 of 64
+  // experts of 1408 x 2048, 5.6 us staged against 6.2 resident (dense
+  // single-unit shapes: equal up to 8192 rows, resident ahead beyond). Both
+  // kernels give the same bits on single-unit rows.
+  if (units == 1 && id.sel && N <= 4096)
+    return launch_staged<1, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
   switch (units) {
     case 1: return launch_resident<1, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
     case 2: return launch_resident<2, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);

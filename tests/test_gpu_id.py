@@ -137,6 +137,8 @@ ID_SHAPES = [
     ("q4k", 3, 130, 20480, [1, 0]),         # loads past the row skipped (10 units)
     ("q4k", 3, 257, 6144, [1, 2, 0]),       # three units
     ("iq4nl", 3, 20000, 512, [2, 0]),       # persistent grid, waves take a second row
+    ("iq4nl", 3, 4096, 2048, [2, 0]),       # single-unit rows, the most a grouped staged launch takes
+    ("iq4nl", 3, 4097, 2048, [0, 1]),       # one row more: the persistent grid
     ("iq4nl", 3, 1000, 10240, [0, 2]),      # staged kernel (five units)
     ("iq4nl", 2, 130, 8192, [1, 0, 1]),     # four units
 ]
