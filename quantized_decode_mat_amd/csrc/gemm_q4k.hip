@@ -225,25 +225,25 @@ __device__ __forceinline__ void issue_stage(uint8_t* base, const uint8_t* xq_in,
                                             const uint8_t* w_in, const StageOffsets<BMv>& o, int b,
                                             int wave, int lane) {
   using T = Tile<BMv>;
-  const uint8_t* xq = uniform_ptr(xq_in);
-  const uint8_t* w = uniform_ptr(w_in);
-  const uint32_t xb = static_cast<uint32_t>(b) * kQ8KBytes;
-  const uint32_t wb = static_cast<uint32_t>(b) * kQ4KBytes;
+  // Super-block b's offset rides on the scalar base, so the per-lane
+  // offsets are the same every step (no vector address arithmetic per load).
+  const uint8_t* xq = uniform_ptr(xq_in + static_cast<size_t>(b) * kQ8KBytes);
+  const uint8_t* w = uniform_ptr(w_in + static_cast<size_t>(b) * kQ4KBytes);
   // The LDS destination of each load is wave-uniform.
   const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_u32(base));
   const int wv = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-  for (int k = 0; k < T::kActPerWave; ++k) lds_dma16(xq, o.act[k] + xb, lb + 1024 * (wv + 4 * k));
+  for (int k = 0; k < T::kActPerWave; ++k) lds_dma16(xq, o.act[k], lb + 1024 * (wv + 4 * k));
 #pragma unroll
-  for (int k = 0; k < 4; ++k) lds_dma16(w, o.wt[k] + wb, lb + T::kWOff + 1024 * (wv + 4 * k));
+  for (int k = 0; k < 4; ++k) lds_dma16(w, o.wt[k], lb + T::kWOff + 1024 * (wv + 4 * k));
   if (wv < 2) {
-    lds_dma16(w, o.extra + wb, lb + T::kWOff + 1024 * (wv + 16));
+    lds_dma16(w, o.extra, lb + T::kWOff + 1024 * (wv + 16));
   } else if (wv == 2) {
     // BM = 16: 32 chunks of sums, lanes 0..31 (an inactive lane writes no LDS)
-    if (BMv == 64 || lane < 2 * BMv) lds_dma16(xq, o.extra + xb, lb + T::kSumOff);
+    if (BMv == 64 || lane < 2 * BMv) lds_dma16(xq, o.extra, lb + T::kSumOff);
   } else {
-    if (BMv == 64 || lane < BMv) lds_dma4(xq, o.extra + xb, lb + T::kXsOff);
-    if (BMv == 64) lds_dma16(xq, o.sums + xb, lb + T::kSumOff + 1024);
+    if (BMv == 64 || lane < BMv) lds_dma4(xq, o.extra, lb + T::kXsOff);
+    if (BMv == 64) lds_dma16(xq, o.sums, lb + T::kSumOff + 1024);
   }
 }
 
