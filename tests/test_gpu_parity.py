@@ -430,13 +430,16 @@ def test_gemm_split_full_size(M, N, K):
         assert_close(Y[m], ref, T, "split row %d" % m)
 
 
-@pytest.mark.parametrize("M,N,K,first_split_row", [(320, 14336, 4096, 13056), (576, 8192, 4096, 7168)])
+@pytest.mark.parametrize("M,N,K,first_split_row", [(320, 14336, 4096, 13056), (576, 8192, 4096, 7168),
+                                                    (1024, 14336, 4096, 12288)])
 def test_gemm_whole_and_split_tiles(M, N, K, first_split_row):
-    """More tiles than one round of resident workgroups, with a short
-    remainder: 512 tiles run whole and the last ones split K four ways in
-    the same launch (320 tokens: 560 tiles, the split ones from weight tile
-    102 on; 576 tokens: 576 tiles, from weight tile 56 on). Sampled outputs
-    on both sides of that boundary, and whole rows against the mat-vec."""
+    """More tiles than whole rounds of resident workgroups, with a short
+    remainder: the whole rounds run whole tiles and the remainder splits K in
+    the same launch (320 tokens: 512 of 560 tiles whole, the rest in four
+    splits from weight tile 102 on; 576 tokens: 512 of 576 whole, four
+    splits from weight tile 56 on; 1024 tokens: 1536 of 1792 whole, two
+    splits from weight tile 96 on). Sampled outputs on both sides of that
+    boundary, and whole rows against the mat-vec."""
     g = wl.rng(7600 + M)
     w = wl.q4k_weights(N, K, g)
     xqb = oracle.quantize_q8k(wl.activations(M, K, g))
