@@ -35,11 +35,14 @@
 // token tiles sharing one weight tile land on one XCD (one L2).
 //
 // Split-K (section 25.3: a launch that cannot fill the device cannot be
-// fast). With few tiles (a short token batch, or few weight rows) the grid
-// is tiles x ks: split s of a tile takes super-blocks [s*nb/ks, (s+1)*nb/ks),
-// writes its f32 partial to a workspace slot and counts its arrival; the
-// split that arrives last sums the ks partials in the fixed order 0..ks-1
-// and writes Y, so the result does not depend on arrival order. Partials
+// fast). With few tiles (a short token batch, or few weight rows) every tile
+// splits: the grid is tiles x ks, split s of a tile takes super-blocks
+// [s*nb/ks, (s+1)*nb/ks), writes its f32 partial to a workspace slot and
+// counts its arrival; the split that arrives last sums the ks partials in
+// the fixed order 0..ks-1 and writes Y, so the result does not depend on
+// arrival order. With more tiles than whole rounds of resident workgroups,
+// the same launch runs the whole rounds of whole tiles and may split the
+// short remainder the same way (gemm_q4k_plan). Partials
 // and counters cross XCDs through agent-scope atomic loads and stores
 // (coherent without an L2 write-back); the last arrival resets the counter,
 // so counters are zero between launches.
