@@ -1,0 +1,108 @@
+"""Seeded random shapes through every dispatch regime, against the oracle.
+
+The fixed cases elsewhere pin each launch shape at chosen sizes; this sweep
+draws further shapes from a fixed seed so that ragged edges land in new
+places: mat-vecs of the three formats over ragged N and K, and the small-M
+product on the batched mat-vec, the 16-token tile, split K, and launches
+whose tiles run in whole rounds with a split remainder (the remainder and
+the whole rounds in one grid, for both token tiles). Outputs are compared to
+the oracle at the f32 bar (whole outputs where the oracle is quick, sampled
+outputs with tile corners and whole rows where not).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import quantized_decode_mat_amd as xq
+import workloads as wl
+from test_gpu_parity import _note, assert_close, dev, gpu_gemm, poisoned_f32, take_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _matvec_shapes():
+    g = wl.rng(8000)
+    out = []
+    for fmt in ("q4k", "iq4nl", "q4_0"):
+        for _ in range(5):
+            N = int(g.integers(1, 20001))
+            K = 256 * int(g.integers(1, 65))
+            out.append((fmt, N, K, int(g.integers(0, 2 ** 31))))
+    return out
+
+
+MATVEC = _matvec_shapes()
+
+
+@pytest.mark.parametrize("fmt,N,K,seed", MATVEC,
+                         ids=["%s_n%d_k%d" % (s[0], s[1], s[2]) for s in MATVEC])
+def test_sweep_matvec(fmt, N, K, seed):
+    g = wl.rng(seed)
+    xqb = oracle.quantize_q8k(wl.activations(1, K, g))
+    y = poisoned_f32(N)
+    _note("sweep mat-vec %s N=%d K=%d" % (fmt, N, K))
+    if fmt == "q4k":
+        w = wl.q4k_weights(N, K, g)
+        xq.xq_gemv_q4k(y, dev(w), dev(xqb), N, K)
+        ref, T = oracle.gemv_q4k(w, xqb, N, K)
+    elif fmt == "iq4nl":
+        w = wl.iq4nl_weights(N, K, g)
+        xq.xq_gemv_iq4nl(y, dev(w), dev(xqb), N, K)
+        ref, T = oracle.gemv_iq4nl(w, xqb, N, K)
+    else:
+        w = wl.iq4nl_weights(N, K, g)
+        xq.xq_gemv_q4_0(y, dev(w), dev(xqb), N, K)
+        ref, T = oracle.gemv_q4_0(w, xqb, N, K)
+    assert_close(take_f32(y, N), ref, T, "sweep %s" % fmt)
+
+
+def _product_shapes():
+    g = wl.rng(8100)
+    out = []
+    # (token range, rows range, K choices): short batches, the 16-token tile,
+    # the 64-token tile with split K, and grids past one round of workgroups.
+    regimes = [
+        ((2, 4), (1000, 16000), (2048, 4096, 14336)),
+        ((4, 33), (100, 16000), (1024, 4096, 7936)),
+        ((33, 129), (100, 4200), (4096, 8192, 14336)),
+        ((129, 320), (4000, 9000), (2048, 4096)),
+        ((320, 700), (7000, 15000), (2048, 4096, 8192)),
+    ]
+    for (m_lo, m_hi), (n_lo, n_hi), ks in regimes:
+        for _ in range(3):
+            M = int(g.integers(m_lo, m_hi))
+            N = int(g.integers(n_lo, n_hi))
+            K = int(ks[int(g.integers(0, len(ks)))])
+            out.append((M, N, K, int(g.integers(0, 2 ** 31))))
+    # Past whole rounds of the 16-token tile (768 resident): 20 tokens x
+    # 100000 rows is 1564 tiles, two whole rounds and a remainder of 28.
+    out.append((20, 100000, 4096, 8199))
+    return out
+
+
+PRODUCT = _product_shapes()
+
+
+@pytest.mark.parametrize("M,N,K,seed", PRODUCT,
+                         ids=["m%d_n%d_k%d" % s[:3] for s in PRODUCT])
+def test_sweep_product(M, N, K, seed):
+    g = wl.rng(seed)
+    w = wl.q4k_weights(N, K, g)
+    xqb = oracle.quantize_q8k(wl.activations(M, K, g))
+    _note("sweep product M=%d N=%d K=%d" % (M, N, K))
+    Y = gpu_gemm(w, xqb, M, N, K)
+    assert not np.isnan(Y).any()
+    if M * N * K <= 2 ** 27:
+        ref, T = oracle.gemm_q4k(w, xqb, M, N, K)
+        assert_close(Y.reshape(-1), ref.reshape(-1), T.reshape(-1), "sweep product")
+        return
+    s = wl.rng(seed + 1)
+    corners_m = [0, M - 1] + [t for t in (15, 16, 63, 64) if t < M]
+    corners_n = [0, N - 1] + [t for t in (127, 128) if t < N]
+    ms = np.concatenate([s.integers(0, M, 800), np.repeat(corners_m, len(corners_n))])
+    ns = np.concatenate([s.integers(0, N, 800), np.tile(corners_n, len(corners_m))])
+    ref, T = oracle.gemm_q4k(w, xqb, M, N, K, ms, ns)
+    assert_close(Y[ms, ns], ref, T, "sweep product sampled")
+    for m in sorted({0, M - 1}):
+        ref, T = oracle.gemv_q4k(w, xqb[m], N, K)
+        assert_close(Y[m], ref, T, "sweep product row %d" % m)
