@@ -124,6 +124,31 @@ def test_gemm_id_skewed_and_out_of_range():
     _check(Y, slab, xqb, ids, E, rows, K, 0, [(0, 0), (7, 1), (9, 1), (63, 1), (64, 0), (149, 1)])
 
 
+def test_gemm_id_ragged_tiles():
+    """Experts whose pairs leave ragged last tiles: 70 pairs (64 + 6), 20 (one
+    short tile), 100 (64 + 36), 96 (64 + 32), 33, and 5 out-of-range
+    selections in a NaN tile. Every pair against the oracle; permuting the
+    tokens moves pairs between tiles and must permute the outputs bit for
+    bit."""
+    E, rows, K = 6, 200, 2048
+    counts = {0: 70, 1: 20, 2: 100, 3: 96, 4: 33, -1: 5}
+    flat = np.concatenate([np.full(c, e, np.int32) for e, c in counts.items()])
+    flat = flat[wl.rng(9851).permutation(flat.size)]
+    U = 2
+    T = flat.size // U
+    ids = flat[: T * U].reshape(T, U)
+    slab = _slab(E, rows, K, 9850)
+    xqb = oracle.quantize_q8k(wl.activations(T, K, wl.rng(9852)))
+    _note("gemm id ragged tiles T=%d" % T)
+    Y = _run(slab, xqb, ids, E, rows, K, 0)
+    _check(Y, slab, xqb, ids, E, rows, K, 0)
+    perm = wl.rng(9853).permutation(T)
+    Yp = _run(slab, xqb[perm], ids[perm], E, rows, K, 0)
+    nan = np.isnan(Y[perm])
+    assert np.array_equal(np.isnan(Yp), nan)
+    assert np.array_equal(Yp[~nan], Y[perm][~nan])
+
+
 def test_gemm_id_permutation_is_bit_exact():
     E, rows, K, T, U = 8, 256, 2048, 97, 2
     slab = _slab(E, rows, K, 9800)
