@@ -300,6 +300,10 @@ def main():
     xq.xq_gemv_q4k(y, dns[0], xq2, DOWN[0], DOWN[1])
     torch.cuda.synchronize()
     assert bool(torch.isfinite(y).all())
+    # Kept for the CPU leg, which holds this pass against the oracle before
+    # any rate is printed.
+    first_pass = {"xq_x": xq1.cpu().numpy().copy(), "h": h.cpu().numpy().astype(np.float64),
+                  "xq_h": xq2.cpu().numpy().copy(), "y": y.cpu().numpy().astype(np.float64)}
 
     if args.counters:
         counters_run(torch, xq, L, dev, stream, ups, dns, xq1, xq2, h, y, x_d, pool)
@@ -381,10 +385,12 @@ def main():
     stream_gbps = stream_read(2 << 30, 100)
     log("streaming read, 2 GiB: %.1f GB/s" % stream_gbps)
     # Like-for-like: the probe over the same rotation pool as the up mat-vec,
-    # 33 MB per launch, so launch and ramp costs weigh the same.
+    # 33 MB per launch, so launch and ramp costs weigh the same; timed against
+    # the up mat-vec in interleaved ABBA rounds, whose median round of the
+    # mat-vec is also the roofline's launch duration.
     sink_s = torch.empty(xq.xq_bench_sink_words(w_up.nbytes), dtype=torch.int32, device=dev)
-    us_small = _time_loop(torch, stream, lambda k: L.xq_bench_stream_read(
-        ups[k % pool].data_ptr(), w_up.nbytes, sink_s.data_ptr(), s), 1000)
+    kern_us["gemv_up"], us_small = _abba(torch, stream, calls["gemv_up"], lambda k: L.xq_bench_stream_read(
+        ups[k % pool].data_ptr(), w_up.nbytes, sink_s.data_ptr(), s), 500)
     stream_small_gbps = w_up.nbytes / us_small / 1e3
     log("streaming read, 33 MB cold: %.3f us, %.1f GB/s" % (us_small, stream_small_gbps))
 
@@ -410,7 +416,10 @@ def main():
     # ---- CPU baseline: the oracle over whole FFN pairs ----
     cpu = cpu_all = None
     if not args.no_cpu:
-        cpu, cpu_all = cpu_legs(args, x, w_up, w_dn, pair_bytes)
+        cpu, cpu_all = cpu_legs(args, x, w_up, w_dn, pair_bytes, first_pass)
+        if not cpu["parity_gate"]["passed"]:
+            log("parity gate FAILED: %s" % cpu["parity_gate"])
+            sys.exit(1)
         log("cpu oracle: %s" % cpu)
         log("cpu oracle, all cores: %s" % cpu_all)
 
@@ -492,14 +501,37 @@ def graph_step(torch, step, pool, y, stream):
             "note": "replays checked equal to the eager step"}
 
 
-def cpu_legs(args, x, w_up, w_dn, pair_bytes):
+def _parity_gate(o, x, w_up, w_dn, fp):
+    """One step of the GPU (its first, checked pass) against the oracle on the
+    same bytes: q8_K(x) and q8_K(h) bytes 0..291 of every block equal, h and
+    y within 1e-5 of the sum of |terms| per output. The second quantization
+    is the oracle's of the GPU's own h, as in the parity tests."""
+    def q8k_equal(a, b):
+        return bool(np.array_equal(a.reshape(-1, 320)[:, :292], b.reshape(-1, 320)[:, :292]))
+
+    def within(got, ref, T):
+        return bool(np.all(np.abs(got - ref) <= 1e-5 * T)) and not np.isnan(got).any()
+
+    xq_x = o.quantize_q8k(x)
+    h_ref, Th = o.gemv_q4k(w_up, xq_x, *UP)
+    xq_h = o.quantize_q8k(fp["h"].astype(np.float32).reshape(1, -1))
+    y_ref, Ty = o.gemv_q4k(w_dn, xq_h, *DOWN)
+    checks = {"q8k_x_bytes": q8k_equal(fp["xq_x"], xq_x), "h": within(fp["h"], h_ref, Th),
+              "q8k_h_bytes": q8k_equal(fp["xq_h"], xq_h), "y": within(fp["y"], y_ref, Ty)}
+    return {"passed": all(checks.values()), **checks,
+            "checked": "one step (pool pair 0): q8_K bytes equal, h and y within 1e-5 T"}
+
+
+def cpu_legs(args, x, w_up, w_dn, pair_bytes, first_pass):
     """The oracle, as it stands, over whole FFN pairs: single-threaded, then
     row-split over the host's cores (the same C calls on row lists, one per
     thread; ctypes drops the GIL for the call). Each leg is the median of
-    three rounds that together take about args.cpu_seconds."""
+    three rounds that together take about args.cpu_seconds. Before the
+    timing, the GPU's first step is held against the oracle (_parity_gate)."""
     import concurrent.futures as cf
     import oracle
     o = oracle.default()
+    gate = _parity_gate(o, x, w_up, w_dn, first_pass)
     cores = min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16")), 16)
     model = "unknown"
     try:
@@ -552,7 +584,7 @@ def cpu_legs(args, x, w_up, w_dn, pair_bytes):
               "plain C oracle; median of 3 rounds")
     one = {"value": round(v1, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": "%d %s, single-threaded, %.0f s" % (n1, sample, args.cpu_seconds),
-           "rounds_GBps": [round(r, 4) for r in r1], "cpu": model}
+           "rounds_GBps": [round(r, 4) for r in r1], "cpu": model, "parity_gate": gate}
     alln = {"value": round(vn, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": "%d %s, rows split over %d threads, %.0f s" % (
                 nn, sample, cores, args.cpu_seconds / 2),
@@ -632,6 +664,27 @@ def _warm(torch, fn, start, ms=WARM_MS):
             return i
 
 
+def _abba(torch, stream, fa, fb, n, reps=2):
+    """fa and fb in interleaved rounds A B B A (`reps` times) of n calls each,
+    after one warm-up, so drift of clocks or temperature falls on both alike;
+    the rounds run back to back (one event between rounds, one synchronize at
+    the end). Returns the median round of each, in us per call."""
+    i = _warm(torch, fa, 0)
+    sides = [0, 1, 1, 0] * reps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sides) + 1)]
+    ev[0].record(stream)
+    for r, side in enumerate(sides):
+        f = fb if side else fa
+        for k in range(n):
+            f(i + k)
+        i += n
+        ev[r + 1].record(stream)
+    torch.cuda.synchronize()
+    ta = [ev[r].elapsed_time(ev[r + 1]) / n * 1e3 for r, sd in enumerate(sides) if sd == 0]
+    tb = [ev[r].elapsed_time(ev[r + 1]) / n * 1e3 for r, sd in enumerate(sides) if sd == 1]
+    return float(np.median(ta)), float(np.median(tb))
+
+
 def _time_loop(torch, stream, fn, n):
     warm = _warm(torch, fn, 0)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -656,12 +709,11 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
         log("suite: " + json.dumps(d))
 
     def matvec_line(name, ws, wb, call, n):
-        """Time `call` over the rotating pool `ws`, then the streaming read of
-        the same wb bytes over the same pool (like for like: same launch and
-        ramp costs), and emit both."""
-        us = _time_loop(torch, stream, call, n)
+        """Time `call` over the rotating pool `ws` against the streaming read
+        of the same wb bytes over the same pool (like for like: same launch and
+        ramp costs), in interleaved ABBA rounds, and emit both."""
         sink = torch.empty(xq.xq_bench_sink_words(wb), dtype=torch.int32, device=dev)
-        sus = _time_loop(torch, stream, lambda i: L.xq_bench_stream_read(
+        us, sus = _abba(torch, stream, call, lambda i: L.xq_bench_stream_read(
             ws[i % len(ws)].data_ptr(), wb, sink.data_ptr(), s), n)
         emit({"workload": name, "us": round(us, 3), "weight_GBps": round(wb / us / 1e3, 1),
               "frac_of_8TBps": round(wb / us / 1e3 / HBM_PEAK_GBPS, 4),
