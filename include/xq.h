@@ -153,7 +153,7 @@ xq_status xq_gemv_iq4nl(float *y, const void *w, const void *xq, int64_t N, int6
  * tiles than one round of resident workgroups run whole rounds of whole
  * tiles and may split the last, short round's tiles the same way. The
  * partials go through a workspace the library owns, one per (device,
- * stream): 64 MiB allocated, zeroed and synchronized on the first such call
+ * stream): 24 MiB allocated, zeroed and synchronized on the first such call
  * on a stream, kept until the process ends. That first call therefore cannot be captured into a graph;
  * later ones allocate nothing. Splits are summed in a fixed order, so
  * results are bit-identical from call to call. Calls on one stream are

@@ -561,11 +561,13 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
     }
 }
 
-// Split-K workspace: kSplitSlots partial slots of the 64-token tile (64 MiB)
+// Split-K workspace: kSplitSlots partial slots of the 64-token tile (24 MiB)
 // and kSplitCounters arrival counters, one per (device, stream) so that calls
 // on different streams never share it; allocated and zeroed on a stream's
-// first split launch, kept until the process ends.
-constexpr int kSplitSlots = 2048;    // split workgroups of a launch
+// first split launch, kept until the process ends. The planner keeps the
+// split workgroups of a launch within one round of resident workgroups
+// (512 for the all-split rule, at most 768 for a remainder).
+constexpr int kSplitSlots = 768;     // split workgroups of a launch
 constexpr int kSplitCounters = 768;  // split tiles of a launch
 constexpr int kSplitTiles = 256;     // up to this many tiles, every tile splits
 constexpr int kRound = 512;          // the all-split rule's one round of workgroups

@@ -50,7 +50,7 @@ bool gemm_q4k_uses_matvec(int64_t M, int64_t N, int64_t K);
 // The small-M product's launch plan: tiles 0..n_full-1 (of bm tokens x 128
 // rows, token tile fastest) run whole, the rest split K ks ways (ks = 1:
 // every tile whole). Needs, when ks > 1: 1 <= tiles - n_full <= 768,
-// (tiles - n_full) * ks <= 2048 and ks <= K/256.
+// (tiles - n_full) * ks <= 768 and ks <= K/256.
 struct GemmPlan {
   int n_full;
   int ks;
