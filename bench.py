@@ -249,7 +249,7 @@ def main():
         trace_summary(args.trace_summary)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d refused)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 

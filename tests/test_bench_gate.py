@@ -43,3 +43,12 @@ def test_bench_parity_gate():
     bad["y"][j] += 2e-5 * Ty[j]
     r = bench._parity_gate(o, x, w_up, w_dn, bad)
     assert not r["passed"] and not r["y"]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
