@@ -9,7 +9,12 @@
  *
  * Conventions shared by every entry point:
  *  - Pointers named as device buffers are device memory owned by the caller.
- *    The library allocates nothing, frees nothing and keeps no per-call state.
+ *    The library keeps no per-call state and allocates nothing, except the
+ *    device workspaces that three entry points document below (the split-K
+ *    partials of xq_gemm_q4k_small_m, the arrival counters of
+ *    xq_gemv_q4k_q8k, the expert map of xq_gemm_q4k_id): each is allocated
+ *    on the first call on a stream that needs it and kept until the process
+ *    ends.
  *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  *  - Outputs are fully overwritten, never accumulated into. Outputs must not
  *    alias inputs (documented, not checked).
@@ -79,7 +84,8 @@ xq_status xq_quantize_q8k(void *xq, const float *x, int64_t rows, int64_t K, voi
  * 25.2, and section 25.5 for the Q4_K mat-vec's 16-byte loads):
  *   y[r] = sum_b xs_b * (d_rb * S_rb - dmin_rb * M_rb),
  *   S_rb = sum_j sc_j * sum_{t<32} q * code   (exact int32),
- *   M_rb = sum_j m_j * sum_j(q8_K)            (exact int32, from the stored sums),
+ *   M_rb = sum_j m_j * s_j                    (exact int32; s_j the q8_K's stored
+ *                                              sum of sub-block j's 32 codes),
  * which is the dot of the dequantized row with the dequantized activation.
  *
  *  y   device, out: f32 [N], 4-byte aligned.
@@ -154,10 +160,11 @@ xq_status xq_gemv_iq4nl(float *y, const void *w, const void *xq, int64_t N, int6
  * tiles and may split the last, short round's tiles the same way. The
  * partials go through a workspace the library owns, one per (device,
  * stream): 24 MiB allocated, zeroed and synchronized on the first such call
- * on a stream, kept until the process ends. That first call therefore cannot be captured into a graph;
- * later ones allocate nothing. Splits are summed in a fixed order, so
- * results are bit-identical from call to call. Calls on one stream are
- * ordered; calls on different streams use different workspaces.
+ * on a stream, kept until the process ends. That first call therefore
+ * cannot be captured into a graph; later ones allocate nothing. Splits are
+ * summed in a fixed order, so results are bit-identical from call to call.
+ * Calls on one stream are ordered; calls on different streams use different
+ * workspaces.
  * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH (also
  * when the workspace cannot be allocated).
  */
@@ -167,8 +174,9 @@ xq_status xq_gemm_q4k_small_m(float *y, const void *w, const void *xq, int64_t M
 /*
  * Grouped Q4_K x q8_K small-M product over an expert slab (mul_mat_id; "25 —
  * Writing XPU Kernels", section 25.3: a mixture-of-experts prefill is one
- * launch over an expert map, padded only to the finest tile, never one
- * product per expert). Token t's slot k uses expert e = ids[t][k]:
+ * launch over an expert map, never one product per expert; here each
+ * expert's pairs are padded to tiles of 64). Token t's slot k uses expert
+ * e = ids[t][k]:
  *   y[t][k][n] = sum_b xs_b * (d_enb * S_b - dmin_enb * M_b)
  * with S, M the exact int32 block partials of expert e's row n against the
  * pair's q8_K row, which is row t of xq (x_per_slot = 0: the slots of a
