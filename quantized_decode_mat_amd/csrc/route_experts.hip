@@ -2,7 +2,7 @@
 //
 // "25 — Writing XPU Kernels", section 25.3: a mixture-of-experts prefill is
 // one launch over an expert map (mul_mat_id), never one GEMM per expert, and
-// a ragged expert batch is padded only to the finest tile. This kernel turns
+// a ragged expert batch is padded only to the tile. This kernel turns
 // the router's selections ids[t][k] (expert of token t's slot k) into that
 // map: the pairs p = t * n_used + k grouped by expert, and a list of tiles of
 // at most tile_m pairs of one expert each. Selections outside
