@@ -174,9 +174,8 @@ xq_status xq_gemm_q4k_small_m(float *y, const void *w, const void *xq, int64_t M
 /*
  * Grouped Q4_K x q8_K small-M product over an expert slab (mul_mat_id; "25 —
  * Writing XPU Kernels", section 25.3: a mixture-of-experts prefill is one
- * launch over an expert map, never one product per expert; here each
- * expert's pairs are padded to tiles of 64). Token t's slot k uses expert
- * e = ids[t][k]:
+ * launch over an expert map, padded only to the finest tile, never one
+ * product per expert). Token t's slot k uses expert e = ids[t][k]:
  *   y[t][k][n] = sum_b xs_b * (d_enb * S_b - dmin_enb * M_b)
  * with S, M the exact int32 block partials of expert e's row n against the
  * pair's q8_K row, which is row t of xq (x_per_slot = 0: the slots of a
@@ -192,12 +191,13 @@ xq_status xq_gemm_q4k_small_m(float *y, const void *w, const void *xq, int64_t M
  *  1 <= n_tokens * n_used <= 2^20.  1 <= n_experts <= 1024.  1 <= rows <= 2^30.
  *  K >= 256, a multiple of 256. One expert's weights and all of xq below
  *  2 GiB (32-bit offsets).
- * A first kernel groups the pairs by expert into a tile list of at most 64
- * pairs each, in a workspace the library owns (4.3 MB per (device, stream),
- * allocated, zeroed and synchronized on a stream's first call, kept until
- * the process ends; that first call cannot be captured into a graph). The
- * product then runs once over the list. Every output is computed from its
- * own pair alone, so results do not depend on how pairs fall into tiles.
+ * A first kernel groups the pairs by expert into tiles of at most 64 pairs
+ * (an expert's remainder of at most 32 pairs into tiles of at most 16), in a
+ * workspace the library owns (4.3 MB per (device, stream), allocated, zeroed
+ * and synchronized on a stream's first call, kept until the process ends;
+ * that first call cannot be captured into a graph). The product then runs
+ * once over both lists. Every output is computed from its own pair alone,
+ * so results do not depend on how pairs fall into tiles.
  * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH.
  */
 xq_status xq_gemm_q4k_id(float *y, const void *slab, const void *xq, const int32_t *ids,

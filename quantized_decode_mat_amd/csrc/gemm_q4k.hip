@@ -54,12 +54,14 @@
 // tokens (64 on matrices of at most 2^25 weights) use the 16-token tile.
 //
 // Grouped form (mul_mat_id, section 25.3: one launch over an expert map,
-// never one per expert): the same kernel over a device tile list built by
-// route_experts. A tile holds up to 64 (token, slot) pairs routed to one
-// expert; the workgroup gathers their q8_K rows, multiplies them by that
-// expert's weight tile and scatters the outputs to the pairs' rows. The grid
-// is sized by an upper bound on the tile count; workgroups past the list's
-// end return at once. Tiles of out-of-range selections write NaN.
+// never one per expert, padded only to the finest tile): the same tile code
+// over device tile lists built by route_experts. A tile holds up to 64
+// (token, slot) pairs routed to one expert, or up to 16 of an expert's
+// remainder (gemm_q4k_id_mixed_kernel runs both lists in one grid); the
+// workgroup gathers their q8_K rows, multiplies them by that expert's weight
+// tile and scatters the outputs to the pairs' rows. Each region of the grid
+// is sized by an upper bound on its list's length; workgroups past the end
+// return at once. Tiles of out-of-range selections write NaN.
 #include <algorithm>
 
 #include "xq_device.h"
@@ -261,20 +263,33 @@ constexpr int kWaitVm0 = 0x0F70;
 // serialize every workgroup's atomic on that line.
 constexpr int kCounterStride = 32;
 
+// LDS of one workgroup: the two stages of the ring, the last-arrival flag of
+// split-K, and the grouped form's pair and q8_K row of each token row.
+struct TileLds {
+  uint8_t* stage0;
+  uint8_t* stage1;
+  int* last_arrival;
+  int* pair_s;
+  int* xrow_s;
+};
+
+// One workgroup's tile: `wg` is its index in the launch's grid (or in its
+// region of a grid that runs two tile sizes).
 template <int BMv, bool ID>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
-                     const uint8_t* __restrict__ xq, int M, int N, int nb, int mtiles,
-                     int ntiles, int n_full, int ks, float* __restrict__ part,
-                     int* __restrict__ cnt, IdGemm id) {
+__device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __restrict__ y,
+                                          const uint8_t* __restrict__ w,
+                                          const uint8_t* __restrict__ xq, int M, int N, int nb,
+                                          int mtiles, int ntiles, int n_full, int ks,
+                                          float* __restrict__ part, int* __restrict__ cnt,
+                                          const IdGemm& id) {
   using TL = Tile<BMv>;
   constexpr int BM = BMv;
   constexpr int MT = TL::MT;
-  __shared__ __align__(16) uint8_t stage0[TL::kStageBytes];
-  __shared__ __align__(16) uint8_t stage1[TL::kStageBytes];
-  __shared__ int last_arrival;
-  __shared__ int pair_s[ID ? BM : 1];
-  __shared__ int xrow_s[ID ? BM : 1];
+  uint8_t* const stage0 = lds.stage0;
+  uint8_t* const stage1 = lds.stage1;
+  int& last_arrival = *lds.last_arrival;
+  int* const pair_s = lds.pair_s;
+  int* const xrow_s = lds.xrow_s;
 
   // Workgroup -> (tile, split). The first n_full workgroups take tiles
   // 0..n_full-1 whole; the others split each remaining tile's K ks ways
@@ -283,14 +298,13 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
   // tiles of one weight tile (same split) are adjacent.
   const int tiles = mtiles * ntiles;
   int tile, split = 0, kst = 1;
-  if (static_cast<int>(blockIdx.x) < n_full) {
-    const int t = (n_full % 8 == 0) ? (blockIdx.x % 8) * (n_full / 8) + blockIdx.x / 8
-                                    : static_cast<int>(blockIdx.x);
+  if (wg < n_full) {
+    const int t = (n_full % 8 == 0) ? (wg % 8) * (n_full / 8) + wg / 8 : wg;
     tile = t;
   } else {
     const int rest = tiles - n_full;
     const int G = rest * ks;
-    const int v = blockIdx.x - n_full;
+    const int v = wg - n_full;
     const int u = (G % 8 == 0) ? (v % 8) * (G / 8) + v / 8 : v;
     split = u / rest;
     tile = n_full + (u - split * rest);
@@ -561,6 +575,51 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
     }
 }
 
+template <int BMv, bool ID>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
+                     const uint8_t* __restrict__ xq, int M, int N, int nb, int mtiles,
+                     int ntiles, int n_full, int ks, float* __restrict__ part,
+                     int* __restrict__ cnt, IdGemm id) {
+  __shared__ __align__(16) uint8_t stage0[Tile<BMv>::kStageBytes];
+  __shared__ __align__(16) uint8_t stage1[Tile<BMv>::kStageBytes];
+  __shared__ int last_arrival;
+  __shared__ int pair_s[ID ? BMv : 1];
+  __shared__ int xrow_s[ID ? BMv : 1];
+  gemm_tile<BMv, ID>(TileLds{stage0, stage1, &last_arrival, pair_s, xrow_s},
+                     static_cast<int>(blockIdx.x), y, w, xq, M, N, nb, mtiles, ntiles, n_full, ks,
+                     part, cnt, id);
+}
+
+// The grouped form over two tile lists in one grid: the experts' whole tiles
+// of up to 64 pairs on the 64-token tile (workgroups 0 .. big_wgs-1), then
+// their remainders of at most 32 pairs in tiles of up to 16 on the 16-token
+// tile (workgroups from small_base on, a multiple of 8 so that each region
+// keeps its XCD layout). The small tiles run in the slots the whole tiles'
+// last round leaves free. Every output's arithmetic is the same on both
+// tiles.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_q4k_id_mixed_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
+                              const uint8_t* __restrict__ xq, int M, int N, int nb,
+                              int ntiles, int big_tiles, int small_tiles, int small_base,
+                              IdGemm big, IdGemm small) {
+  __shared__ __align__(16) uint8_t stage0[Tile<64>::kStageBytes];
+  __shared__ __align__(16) uint8_t stage1[Tile<64>::kStageBytes];
+  __shared__ int last_arrival;
+  __shared__ int pair_s[64];
+  __shared__ int xrow_s[64];
+  const TileLds lds{stage0, stage1, &last_arrival, pair_s, xrow_s};
+  const int b = static_cast<int>(blockIdx.x);
+  const int big_wgs = big_tiles * ntiles;
+  if (b < big_wgs) {
+    gemm_tile<64, true>(lds, b, y, w, xq, M, N, nb, big_tiles, ntiles, big_wgs, 1, nullptr,
+                        nullptr, big);
+  } else if (b >= small_base) {
+    gemm_tile<16, true>(lds, b - small_base, y, w, xq, M, N, nb, small_tiles, ntiles,
+                        small_tiles * ntiles, 1, nullptr, nullptr, small);
+  }
+}
+
 // Split-K workspace: kSplitSlots partial slots of the 64-token tile (24 MiB)
 // and kSplitCounters arrival counters, one per (device, stream) so that calls
 // on different streams never share it; allocated and zeroed on a stream's
@@ -582,9 +641,12 @@ constexpr int64_t resident_tiles(int bm) { return bm == 16 ? 768 : 512; }
 // The grouped form's tile list: up to kIdMaxPairs pairs.
 constexpr int64_t kIdMaxPairs = int64_t{1} << 20;
 constexpr int kIdMaxExperts = 1024;
-constexpr int kIdBM = 64;  // the grouped form's token tile
+constexpr int kIdBM = 64;  // the grouped form's whole tile
+constexpr int kIdBS = 16;  // its small tiles: an expert's remainder of at most 32 pairs
 constexpr int64_t kIdMaxTiles = kIdMaxPairs / kIdBM + kIdMaxExperts + 1;
-constexpr size_t kIdBytes = kIdMaxPairs * sizeof(int32_t) + kIdMaxTiles * sizeof(int4) + 256;
+constexpr int64_t kIdMaxSmall = 2 * (kIdMaxExperts + 1);
+constexpr size_t kIdBytes = kIdMaxPairs * sizeof(int32_t) +
+                            (kIdMaxTiles + kIdMaxSmall) * sizeof(int4) + 256;
 
 template <int BMv>
 hipError_t launch_split(float* y, const void* w, const void* xq, int64_t M, int64_t N, int64_t K,
@@ -674,20 +736,30 @@ hipError_t launch_gemm_q4k_id(float* y, const void* slab, const void* xq, const 
   hipError_t e = stream_workspace(kWsRoute, kIdBytes, stream, &p);
   if (e != hipSuccess) return e;
   int4* desc = static_cast<int4*>(p);
-  int32_t* sorted = reinterpret_cast<int32_t*>(desc + kIdMaxTiles);
+  int4* desc_s = desc + kIdMaxTiles;
+  int32_t* sorted = reinterpret_cast<int32_t*>(desc_s + kIdMaxSmall);
   int32_t* n_tiles = sorted + kIdMaxPairs;
-  if ((e = launch_route_experts(ids, n_pairs, n_experts, kIdBM, sorted, desc, n_tiles, stream)) !=
-      hipSuccess)
+  int32_t* n_small = n_tiles + 1;
+  if ((e = launch_route_experts(ids, n_pairs, n_experts, kIdBM, kIdBS, sorted, desc, n_tiles,
+                                desc_s, n_small, stream)) != hipSuccess)
     return e;
   const int nb = static_cast<int>(K / 256);
-  const int mtiles = static_cast<int>(route_max_tiles(n_pairs, n_experts, kIdBM));
   const int ntiles = static_cast<int>((rows + BN - 1) / BN);
-  const IdGemm id{sorted, desc, n_tiles, static_cast<int>(n_experts), static_cast<int>(n_used),
-                  per_slot_x, rows * nb * static_cast<int64_t>(kQ4KBytes)};
-  hipLaunchKernelGGL((gemm_q4k_kernel<kIdBM, true>), dim3(mtiles * ntiles), dim3(kThreads), 0, stream, y,
-                     static_cast<const uint8_t*>(slab), static_cast<const uint8_t*>(xq),
-                     static_cast<int>(n_pairs), static_cast<int>(rows), nb, mtiles, ntiles,
-                     mtiles * ntiles, 1, nullptr, nullptr, id);
+  const int64_t expert_bytes = rows * nb * static_cast<int64_t>(kQ4KBytes);
+  // One grid over both lists: whole tiles first, the small tiles from the
+  // next multiple of 8 workgroups on. Each region is sized by its list's
+  // bound; workgroups past a list's end return at once.
+  const int big = static_cast<int>(route_max_tiles(n_pairs, n_experts, kIdBM));
+  const int small = static_cast<int>(route_max_small_tiles(n_pairs, n_experts));
+  const int small_base = (big * ntiles + 7) / 8 * 8;
+  const IdGemm id_big{sorted, desc, n_tiles, static_cast<int>(n_experts),
+                      static_cast<int>(n_used), per_slot_x, expert_bytes};
+  const IdGemm id_small{sorted, desc_s, n_small, static_cast<int>(n_experts),
+                        static_cast<int>(n_used), per_slot_x, expert_bytes};
+  hipLaunchKernelGGL(gemm_q4k_id_mixed_kernel, dim3(small_base + small * ntiles), dim3(kThreads),
+                     0, stream, y, static_cast<const uint8_t*>(slab),
+                     static_cast<const uint8_t*>(xq), static_cast<int>(n_pairs),
+                     static_cast<int>(rows), nb, ntiles, big, small, small_base, id_big, id_small);
   return hipGetLastError();
 }
 

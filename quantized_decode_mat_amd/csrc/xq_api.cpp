@@ -256,7 +256,8 @@ xq_status xq_gemm_q4k_id(float* y, const void* slab, const void* xq, const int32
     return fail(XQ_E_SHAPE, "one expert of rows=%lld reaches 2 GiB", (long long)rows);
   if (xrows * (K / 256) * 320 >= (1LL << 31))
     return fail(XQ_E_SHAPE, "xq of %lld rows reaches 2 GiB", (long long)xrows);
-  if (xq::route_max_tiles(n_pairs, n_experts, 64) * ((rows + 127) / 128) > kMaxInt)
+  if ((xq::route_max_tiles(n_pairs, n_experts, 64) + xq::route_max_small_tiles(n_pairs, n_experts)) *
+              ((rows + 127) / 128) + 8 > kMaxInt)
     return fail(XQ_E_SHAPE, "too many tiles for one launch");
   if (!aligned(y, 4)) return fail(XQ_E_ALIGN, "y not 4-byte aligned");
   if (!aligned(slab, 16)) return fail(XQ_E_ALIGN, "slab not 16-byte aligned");

@@ -67,13 +67,17 @@ hipError_t launch_gemm_q4k_split(float* y, const void* w, const void* xq, int64_
 hipError_t launch_gemm_q4k_id(float* y, const void* slab, const void* xq, const int32_t* ids,
                               int64_t n_tokens, int64_t n_used, int64_t n_experts, int64_t rows,
                               int64_t K, int per_slot_x, hipStream_t stream);
-// The expert map: pairs grouped by expert into `sorted`, tiles of at most
+// The expert map: pairs grouped by expert into `sorted`; tiles of at most
 // tile_m pairs of one bucket into `desc` (int4: bucket, first, count, 0) and
-// their count into *n_tiles; route_max_tiles bounds that count.
+// their count into *n_tiles; a bucket's remainder of at most 2 * tile_s
+// pairs in tiles of at most tile_s pairs into `desc_s`, their count into
+// *n_small. route_max_tiles and route_max_small_tiles bound the counts.
 hipError_t launch_route_experts(const int32_t* ids, int64_t n_pairs, int64_t n_experts,
-                                int tile_m, int32_t* sorted, void* desc, int32_t* n_tiles,
+                                int tile_m, int tile_s, int32_t* sorted, void* desc,
+                                int32_t* n_tiles, void* desc_s, int32_t* n_small,
                                 hipStream_t stream);
 int64_t route_max_tiles(int64_t n_pairs, int64_t n_experts, int tile_m);
+int64_t route_max_small_tiles(int64_t n_pairs, int64_t n_experts);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink,
                               hipStream_t stream);
 int64_t stream_read_sink_words(int64_t bytes);
