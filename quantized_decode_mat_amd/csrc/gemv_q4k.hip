@@ -350,12 +350,15 @@ hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64
   //  * longer rows: batches of four units, eight waves per workgroup, loads
   //    past the row skipped (a whole row of eight or more units in flight
   //    is slower).
+  // Rows of the whole launch (all selected slots of a grouped launch) decide
+  // the rows per wave; a row's arithmetic is the same either way.
+  const int64_t rows_all = N * id.used;
   if (units == 1) {
-    if (N >= 8192) return launch_cfg<2, 1, 4, 2, true>(y, wb, xb, n, nb, id, stream);
+    if (rows_all >= 8192) return launch_cfg<2, 1, 4, 2, true>(y, wb, xb, n, nb, id, stream);
     return launch_cfg<1, 1, 4, 2, true>(y, wb, xb, n, nb, id, stream);
   }
   if (units == 2) {
-    if (N >= 8192) return launch_cfg<2, 2, 4, 2, true>(y, wb, xb, n, nb, id, stream);
+    if (rows_all >= 8192) return launch_cfg<2, 2, 4, 2, true>(y, wb, xb, n, nb, id, stream);
     return launch_cfg<1, 2, 4, 2, true>(y, wb, xb, n, nb, id, stream);
   }
   if (units == 3) return launch_cfg<1, 3, 8, 2, true>(y, wb, xb, n, nb, id, stream);
