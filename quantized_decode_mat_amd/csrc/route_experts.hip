@@ -11,12 +11,16 @@
 // expert's few leftover pairs are not padded to tile_m. Selections outside
 // 0..n_experts-1 form one more bucket, whose tiles the product fills with NaN.
 //
-// One workgroup of 1024 threads: a histogram of the buckets in LDS, three
-// block-wide exclusive scans (pair offsets and the two lists' tile offsets),
-// a scatter of the pairs, then the tile descriptors. The order of the pairs inside a
-// bucket follows LDS atomics and may differ from run to run; the product
-// computes every output from its own token row and expert alone, so the
-// result does not depend on it.
+// One workgroup of 1024 threads. The first kWindow pairs are read in one batch
+// of independent loads per thread, and the LDS atomic that counts a pair also
+// hands it its rank in its bucket, kept in registers for the scatter; pairs
+// past the window (up to 2^20) are counted after them and ranked by a second
+// atomic at the scatter, from where the window's counts end. One wave scans the
+// buckets (pair offsets and both lists' tile offsets at once), then the pairs
+// are scattered and the tile descriptors written. The order of the pairs inside
+// a bucket follows LDS atomics and may differ from run to run; the product
+// computes every output from its own token row and expert alone, so the result
+// does not depend on it.
 #include <algorithm>
 
 #include "xq_device.h"
@@ -26,37 +30,9 @@ namespace xq {
 namespace {
 
 constexpr int kRouteThreads = 1024;
-constexpr int kRouteBuckets = 2 * kRouteThreads;  // each thread owns two buckets
-
-// Exclusive scan over the workgroup of one value per thread; *total gets the
-// sum. Every thread must call it.
-__device__ int block_exclusive_scan(int v, int* wsum, int* total) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int u = __shfl_up(inc, d, kWave);
-    if (lane >= d) inc += u;
-  }
-  if (lane == kWave - 1) wsum[wave] = inc;
-  __syncthreads();
-  if (wave == 0) {
-    const int n = kRouteThreads / kWave;
-    int w = (lane < n) ? wsum[lane] : 0;
-#pragma unroll
-    for (int d = 1; d < n; d <<= 1) {
-      const int u = __shfl_up(w, d, kWave);
-      if (lane >= d) w += u;
-    }
-    if (lane < n) wsum[lane] = w;  // inclusive over waves
-  }
-  __syncthreads();
-  const int before = (wave > 0) ? wsum[wave - 1] : 0;
-  *total = wsum[kRouteThreads / kWave - 1];
-  __syncthreads();  // wsum is reused by the next scan
-  return before + inc - v;
-}
+constexpr int kRouteBuckets = 2048;
+constexpr int kWindowPerThread = 8;
+constexpr int kWindow = kRouteThreads * kWindowPerThread;
 
 // A bucket of c pairs: c / tile_m whole tiles; its remainder r in small
 // tiles when r <= 2 * tile_s, else in one more whole tile.
@@ -70,54 +46,93 @@ __device__ __forceinline__ BucketTiles bucket_tiles(int c, int tile_m, int tile_
   return BucketTiles{full, (r + tile_s - 1) / tile_s};
 }
 
+__device__ __forceinline__ int bucket_of(int e, int n_experts) {
+  return (e >= 0 && e < n_experts) ? e : n_experts;
+}
+
+// Inclusive scan of v over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int u = __shfl_up(v, d, kWave);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_experts_kernel(
     const int32_t* __restrict__ ids, int n_pairs, int n_experts, int tile_m, int tile_s,
     int32_t* __restrict__ sorted, int4* __restrict__ desc, int32_t* __restrict__ n_tiles,
     int4* __restrict__ desc_s, int32_t* __restrict__ n_small) {
   __shared__ int cnt[kRouteBuckets];
-  __shared__ int fill[kRouteBuckets];
+  __shared__ int fill[kRouteBuckets];  // next rank for pairs past the window
   __shared__ int off[kRouteBuckets];
   __shared__ int toff[kRouteBuckets];
   __shared__ int soff[kRouteBuckets];
-  __shared__ int wsum[kRouteThreads / kWave];
   const int tid = threadIdx.x;
   const int B = n_experts + 1;  // the last bucket holds out-of-range selections
 
-  for (int b = tid; b < kRouteBuckets; b += kRouteThreads) {
-    cnt[b] = 0;
-    fill[b] = 0;
-  }
+  for (int b = tid; b < B; b += kRouteThreads) cnt[b] = 0;
   __syncthreads();
-  for (int p = tid; p < n_pairs; p += kRouteThreads) {
-    const int e = ids[p];
-    atomicAdd(&cnt[(e >= 0 && e < n_experts) ? e : n_experts], 1);
+
+  // The window: pair j * kRouteThreads + tid for j < kWindowPerThread.
+  int bk[kWindowPerThread], rk[kWindowPerThread];
+#pragma unroll
+  for (int j = 0; j < kWindowPerThread; ++j) {
+    const int p = j * kRouteThreads + tid;
+    bk[j] = (p < n_pairs) ? bucket_of(ids[p], n_experts) : -1;
+  }
+#pragma unroll
+  for (int j = 0; j < kWindowPerThread; ++j)
+    if (bk[j] >= 0) rk[j] = atomicAdd(&cnt[bk[j]], 1);
+  __syncthreads();
+  if (n_pairs > kWindow) {
+    for (int b = tid; b < B; b += kRouteThreads) fill[b] = cnt[b];
+    __syncthreads();  // the snapshot is taken before the rest is counted
+    for (int p = kWindow + tid; p < n_pairs; p += kRouteThreads)
+      atomicAdd(&cnt[bucket_of(ids[p], n_experts)], 1);
+    __syncthreads();
+  }
+
+  // One wave scans the buckets, lane l taking a run of q consecutive ones.
+  if (tid < kWave) {
+    const int lane = tid;
+    const int q = (B + kWave - 1) / kWave;
+    const int lo = min(B, lane * q), hi = min(B, lo + q);
+    int sc = 0, sb = 0, ss = 0;
+    for (int b = lo; b < hi; ++b) {
+      const int c = cnt[b];
+      const BucketTiles t = bucket_tiles(c, tile_m, tile_s);
+      sc += c;
+      sb += t.big;
+      ss += t.small;
+    }
+    const int ic = wave_inclusive_scan(sc, lane);
+    const int ib = wave_inclusive_scan(sb, lane);
+    const int is = wave_inclusive_scan(ss, lane);
+    int oc = ic - sc, ob = ib - sb, os = is - ss;
+    for (int b = lo; b < hi; ++b) {
+      const int c = cnt[b];
+      const BucketTiles t = bucket_tiles(c, tile_m, tile_s);
+      off[b] = oc;
+      toff[b] = ob;
+      soff[b] = os;
+      oc += c;
+      ob += t.big;
+      os += t.small;
+    }
+    if (lane == kWave - 1) {
+      *n_tiles = ib;
+      *n_small = is;
+    }
   }
   __syncthreads();
 
-  const int b0 = 2 * tid, b1 = 2 * tid + 1;
-  const int c0 = (b0 < B) ? cnt[b0] : 0;
-  const int c1 = (b1 < B) ? cnt[b1] : 0;
-  const BucketTiles t0 = bucket_tiles(c0, tile_m, tile_s);
-  const BucketTiles t1 = bucket_tiles(c1, tile_m, tile_s);
-  int pairs_total = 0, tiles_total = 0, small_total = 0;
-  const int oc = block_exclusive_scan(c0 + c1, wsum, &pairs_total);
-  const int ot = block_exclusive_scan(t0.big + t1.big, wsum, &tiles_total);
-  const int os = block_exclusive_scan(t0.small + t1.small, wsum, &small_total);
-  off[b0] = oc;
-  off[b1] = oc + c0;
-  toff[b0] = ot;
-  toff[b1] = ot + t0.big;
-  soff[b0] = os;
-  soff[b1] = os + t0.small;
-  if (tid == 0) {
-    *n_tiles = tiles_total;
-    *n_small = small_total;
-  }
-  __syncthreads();
-
-  for (int p = tid; p < n_pairs; p += kRouteThreads) {
-    const int e = ids[p];
-    const int b = (e >= 0 && e < n_experts) ? e : n_experts;
+#pragma unroll
+  for (int j = 0; j < kWindowPerThread; ++j)
+    if (bk[j] >= 0) sorted[off[bk[j]] + rk[j]] = j * kRouteThreads + tid;
+  for (int p = kWindow + tid; p < n_pairs; p += kRouteThreads) {
+    const int b = bucket_of(ids[p], n_experts);
     sorted[off[b] + atomicAdd(&fill[b], 1)] = p;
   }
   for (int b = tid; b < B; b += kRouteThreads) {

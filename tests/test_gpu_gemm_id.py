@@ -186,3 +186,27 @@ def test_gemm_id_partials_bit_exact(which):
                 S, Mp = oracle.q4k_partials(slab[e * rows:(e + 1) * rows], xqb[t], rows, K)
                 want = S[:, b] if which == "S" else -Mp[:, b]
                 assert np.array_equal(Y[t, k], want.astype(np.float64)), (t, k, b)
+
+
+@pytest.mark.parametrize("T,U,E,rows,K,seed", [
+    (1100, 8, 64, 64, 256, 9950),    # 8800 pairs: past the routing kernel's 8192-pair window
+    (300, 8, 1024, 32, 256, 9960),   # the largest expert count: most experts hold a few pairs
+])
+def test_gemm_id_many_pairs_many_experts(T, U, E, rows, K, seed):
+    """Each expert's outputs against the oracle's product over that expert's
+    gathered token rows; no output is left unwritten."""
+    slab = _slab(E, rows, K, seed)
+    g = wl.rng(seed + 1)
+    xqb = oracle.quantize_q8k(wl.activations(T, K, g))
+    ids = _top_k(T, U, E, g)
+    _note("gemm id many pairs T=%d U=%d E=%d" % (T, U, E))
+    Y = _run(slab, xqb, ids, E, rows, K, 0)
+    assert not np.isnan(Y).any()
+    for e in range(E):
+        tk = np.argwhere(ids == e)
+        if len(tk) == 0:
+            continue
+        xr = xqb[tk[:, 0]]
+        ref, Tm = oracle.gemm_q4k(slab[e * rows:(e + 1) * rows], xr, len(tk), rows, K)
+        got = Y[tk[:, 0], tk[:, 1]]
+        assert_close(got.reshape(-1), ref.reshape(-1), Tm.reshape(-1), "expert %d" % e)
