@@ -64,6 +64,7 @@
 // return at once. Tiles of out-of-range selections write NaN.
 #include <algorithm>
 
+#include "lds_dma.h"
 #include "xq_device.h"
 #include "xq_launch.h"
 
@@ -185,45 +186,6 @@ struct IdGemm {
   int per_slot_x;         // 1: pair p reads q8_K row p; 0: row p / n_used
   int64_t expert_bytes;   // one expert's weights in the slab
 };
-
-// One direct global -> LDS load (gfx950 global_load_lds_dwordx4 /
-// global_load_lds_dword): lane l's bytes land at LDS address m0 + size*l.
-// Issued as inline assembly so the compiler's wait-count pass does not treat
-// the in-flight refill of one stage as a hazard for reads of the other; the
-// kernel waits for these loads itself (vmcnt) before the barrier that
-// publishes a stage.
-__device__ __forceinline__ void lds_dma16(const uint8_t* base, uint32_t off, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1\n\t"
-      :
-      : "v"(off), "s"(base), "s"(lds_addr)
-      : "memory", "m0");
-}
-
-__device__ __forceinline__ void lds_dma4(const uint8_t* base, uint32_t off, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %0, %1\n\t"
-      :
-      : "v"(off), "s"(base), "s"(lds_addr)
-      : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
-
-// A pointer every lane holds the same value of, as a scalar (the direct
-// loads take their base in scalar registers).
-__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
-  const uint64_t v = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-  return reinterpret_cast<const uint8_t*>((static_cast<uint64_t>(hi) << 32) | lo);
-}
 
 template <int BMv>
 __device__ __forceinline__ void issue_stage(uint8_t* base, const uint8_t* xq_in,
