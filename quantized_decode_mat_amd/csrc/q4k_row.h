@@ -110,13 +110,29 @@ __device__ __forceinline__ ChunkDecode chunk_decode(const uint4 nib, const uint4
   return c;
 }
 
-__device__ __forceinline__ float chunk_token(const ChunkDecode& c, const uint8_t* act, int b,
-                                             const LaneGeom& L) {
+// One token's share of a decoded chunk, from the lane's slice of that token's
+// q8_K block: its two 16-byte code pieces, the two sub-block sums and the
+// block scale.
+struct TokenSlice {
+  uint4 alo, ahi;
+  int2 sums;
+  float xs;
+};
+
+__device__ __forceinline__ TokenSlice token_slice(const uint8_t* act, int b, const LaneGeom& L) {
   const uint8_t* xb = act + b * kQ8KBytes;
-  const uint4 alo = *reinterpret_cast<const uint4*>(xb + 64 * L.g + 16 * L.h);
-  const uint4 ahi = *reinterpret_cast<const uint4*>(xb + 64 * L.g + 32 + 16 * L.h);
-  const int2 sums = *reinterpret_cast<const int2*>(xb + 256 + 8 * L.g);
-  const float xs = *reinterpret_cast<const float*>(xb + 288);
+  TokenSlice t;
+  t.alo = *reinterpret_cast<const uint4*>(xb + 64 * L.g + 16 * L.h);
+  t.ahi = *reinterpret_cast<const uint4*>(xb + 64 * L.g + 32 + 16 * L.h);
+  t.sums = *reinterpret_cast<const int2*>(xb + 256 + 8 * L.g);
+  t.xs = *reinterpret_cast<const float*>(xb + 288);
+  return t;
+}
+
+__device__ __forceinline__ float chunk_token_slice(const ChunkDecode& c, const TokenSlice& t) {
+  const uint4 alo = t.alo, ahi = t.ahi;
+  const int2 sums = t.sums;
+  const float xs = t.xs;
   const uint4 nib = c.nib;
   int dlo = sdot4(nib.x & 0x0F0F0F0Fu, alo.x, 0);
   dlo = sdot4(nib.y & 0x0F0F0F0Fu, alo.y, dlo);
@@ -129,6 +145,11 @@ __device__ __forceinline__ float chunk_token(const ChunkDecode& c, const uint8_t
   const int S = __mul24(c.sc0, dlo) + __mul24(c.sc1, dhi);
   const int M = __mul24(c.m0, sums.x) + __mul24(c.m1, sums.y);
   return xs * (c.d * static_cast<float>(S) - c.dmin * static_cast<float>(M));
+}
+
+__device__ __forceinline__ float chunk_token(const ChunkDecode& c, const uint8_t* act, int b,
+                                             const LaneGeom& L) {
+  return chunk_token_slice(c, token_slice(act, b, L));
 }
 
 }  // namespace xq

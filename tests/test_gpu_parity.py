@@ -468,6 +468,10 @@ GEMM_SHORT = [
     (5, 300, 2304, 7505),      # ragged unit tail
     (2, 130, 20480, 7506),     # ten units (two tokens fit): batches of four, loads past the row skipped
     (7, 8193, 2048, 7507),     # two rows per wave with an odd tail
+    (4, 4096, 4096, 7508),     # persistent grid, activation in registers, four tokens
+    (3, 3000, 1280, 7509),     # persistent grid, one ragged unit
+    (2, 20000, 3840, 7510),    # persistent grid, the second unit ragged, rows past one pass
+    (4, 100, 256, 7511),       # persistent grid smaller than a workgroup's waves allow
 ]
 
 
