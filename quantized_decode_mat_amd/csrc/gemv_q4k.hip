@@ -547,18 +547,22 @@ hipError_t launch_gemv_q4k_multi(float* y, const void* w, const void* xq, int64_
   const int nb = static_cast<int>(K / 256);
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   const uint8_t* xb = static_cast<const uint8_t*>(xq);
-  if (nb <= 16 && M <= 4 && (M <= 2 || N * K <= (int64_t{1} << 25))) {
+  if (nb <= 16 && M <= 4) {
     // Rows of one or two units: the persistent grid with the activation in
-    // registers. Measured on MI355X (cold weights), against the kernel
-    // below: 14336x4096 at 2 tokens 9.0 us against 9.9 (at 3 tokens 12.3
-    // against 12.0, so larger matrices keep the kernel below from 3 tokens
-    // on); 4096x4096 at 2, 3, 4 tokens 4.1, 4.8, 5.2 us against 4.4, 5.4, 6.2.
+    // registers, one instantiation per token count (registers, and so
+    // resident waves, grow with it). Measured on MI355X (cold weights),
+    // against the kernel below: 14336x4096 at 2 and 3 tokens 8.7 and 10.2 us
+    // against 9.9 and 12.2; 4096x4096 at 2, 3, 4 tokens 4.2, 4.6, 5.3 us
+    // against 4.4, 5.5, 6.1. (Four tokens on larger matrices take the MFMA
+    // tile: 12.4 us there against 13.1 on this grid.)
     const int n = static_cast<int>(N);
     if (nb <= 8) {
       if (M <= 2) return launch_multi_res<2, 1>(y, wb, xb, n, nb, t, stream);
+      if (M == 3) return launch_multi_res<3, 1>(y, wb, xb, n, nb, t, stream);
       return launch_multi_res<4, 1>(y, wb, xb, n, nb, t, stream);
     }
     if (M <= 2) return launch_multi_res<2, 2>(y, wb, xb, n, nb, t, stream);
+    if (M == 3) return launch_multi_res<3, 2>(y, wb, xb, n, nb, t, stream);
     return launch_multi_res<4, 2>(y, wb, xb, n, nb, t, stream);
   }
   if (M <= 2) return launch_multi_rows<2>(y, w, xq, N, K, t, stream);
