@@ -210,3 +210,52 @@ def test_gemm_id_many_pairs_many_experts(T, U, E, rows, K, seed):
         ref, Tm = oracle.gemm_q4k(slab[e * rows:(e + 1) * rows], xr, len(tk), rows, K)
         got = Y[tk[:, 0], tk[:, 1]]
         assert_close(got.reshape(-1), ref.reshape(-1), Tm.reshape(-1), "expert %d" % e)
+
+
+@pytest.mark.parametrize("T,U,E,seed", [
+    (1024, 8, 16, 9970),   # exactly the routing kernel's 8192-pair window
+    (1, 1, 1, 9971),       # one pair, one expert
+])
+def test_gemm_id_window_edges(T, U, E, seed):
+    """The routing window's edge (every pair ranked by the counting atomic)
+    and the smallest map; also one pair past the window with a single
+    expert, where every pair lands in one bucket."""
+    rows, K = 32, 256
+    slab = _slab(E, rows, K, seed)
+    g = wl.rng(seed + 1)
+    xqb = oracle.quantize_q8k(wl.activations(T, K, g))
+    ids = _top_k(T, U, E, g) if U <= E else g.integers(0, E, size=(T, U)).astype(np.int32)
+    _note("gemm id window edge T=%d U=%d E=%d" % (T, U, E))
+    Y = _run(slab, xqb, ids, E, rows, K, 0)
+    assert not np.isnan(Y).any()
+    for e in range(E):
+        tk = np.argwhere(ids == e)
+        if len(tk) == 0:
+            continue
+        ref, Tm = oracle.gemm_q4k(slab[e * rows:(e + 1) * rows], xqb[tk[:, 0]], len(tk), rows, K)
+        assert_close(Y[tk[:, 0], tk[:, 1]].reshape(-1), ref.reshape(-1), Tm.reshape(-1), "expert %d" % e)
+
+
+def test_gemm_id_one_expert_past_the_window():
+    """8193 pairs all routed to one expert: the first 8192 ranked in the
+    window, the last by the scatter's own atomic, every one in one bucket of
+    129 tiles (the last a small one)."""
+    E, rows, K, T, U = 1, 32, 256, 8193, 1
+    slab = _slab(E, rows, K, 9972)
+    xqb = oracle.quantize_q8k(wl.activations(T, K, wl.rng(9973)))
+    ids = np.zeros((T, U), dtype=np.int32)
+    _note("gemm id one expert past the window")
+    Y = _run(slab, xqb, ids, E, rows, K, 0)
+    ref, Tm = oracle.gemm_q4k(slab, xqb, T, rows, K)
+    assert_close(Y.reshape(T, rows).reshape(-1), ref.reshape(-1), Tm.reshape(-1), "one expert")
+
+
+def test_gemm_id_every_selection_out_of_range():
+    E, rows, K, T, U = 4, 40, 512, 30, 2
+    slab = _slab(E, rows, K, 9974)
+    xqb = oracle.quantize_q8k(wl.activations(T, K, wl.rng(9975)))
+    ids = np.full((T, U), -3, dtype=np.int32)
+    ids[::2, 1] = 1 << 20
+    _note("gemm id every selection out of range")
+    Y = _run(slab, xqb, ids, E, rows, K, 0)
+    assert np.isnan(Y).all()

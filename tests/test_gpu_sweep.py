@@ -83,6 +83,38 @@ def _product_shapes():
 PRODUCT = _product_shapes()
 
 
+def _short_shapes():
+    # Two to four tokens on rows of one or two units (K <= 4096): the batched
+    # mat-vec on its persistent grid; every token's row must be the mat-vec's.
+    g = wl.rng(8200)
+    out = []
+    for _ in range(8):
+        M = int(g.integers(2, 5))
+        N = int(g.integers(1, 30000))
+        K = 256 * int(g.integers(1, 17))
+        out.append((M, N, K, int(g.integers(0, 2 ** 31))))
+    return out
+
+
+SHORT = _short_shapes()
+
+
+@pytest.mark.parametrize("M,N,K,seed", SHORT, ids=["m%d_n%d_k%d" % s[:3] for s in SHORT])
+def test_sweep_short_batch_rows_equal_matvec(M, N, K, seed):
+    g = wl.rng(seed)
+    w = wl.q4k_weights(N, K, g)
+    xqb = oracle.quantize_q8k(wl.activations(M, K, g))
+    _note("sweep short batch M=%d N=%d K=%d" % (M, N, K))
+    Y = gpu_gemm(w, xqb, M, N, K)
+    wd = dev(w)
+    for m in range(M):
+        y = poisoned_f32(N)
+        xq.xq_gemv_q4k(y, wd, dev(xqb[m]), N, K)
+        assert np.array_equal(Y[m], take_f32(y, N)), m
+    ref, T = oracle.gemv_q4k(w, xqb[M - 1], N, K)
+    assert_close(Y[M - 1], ref, T, "sweep short batch last row")
+
+
 @pytest.mark.parametrize("M,N,K,seed", PRODUCT,
                          ids=["m%d_n%d_k%d" % s[:3] for s in PRODUCT])
 def test_sweep_product(M, N, K, seed):
