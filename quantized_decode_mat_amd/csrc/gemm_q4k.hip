@@ -218,6 +218,21 @@ __device__ __forceinline__ void issue_stage(uint8_t* base, const uint8_t* xq_in,
 // [6:4] and lgkmcnt [11:8] left at their maxima, i.e. not waited on).
 constexpr int kWaitVm0 = 0x0F70;
 
+// Waits until at most one stage's loads of this wave are in flight (the
+// three-stage ring, whose next stage is issued before this one is needed):
+// issue_stage makes 4 + BM/16 loads per wave (codes and weights), plus a
+// fifth weight load on waves 0 and 1, the sums on wave 2, and the token
+// scales (and, when BM = 64, the second half of the sums) on wave 3.
+template <int BMv>
+__device__ __forceinline__ void wait_stage_behind_one(int wave) {
+  constexpr int base = 4 + BMv / 16;
+  static_assert(base + 2 <= 15, "the wait count below is a 4-bit vmcnt");
+  if (BMv == 64 && wave == 3)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (base + 2));
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (base + 1));
+}
+
 // A partial slot: the 8*MT f32 accumulators of each of the 256 threads,
 // element r of thread i at r * kThreads + i (one wave store covers 256
 // consecutive bytes); Tile<BM>::kPartFloats floats.
@@ -230,6 +245,7 @@ constexpr int kCounterStride = 32;
 struct TileLds {
   uint8_t* stage0;
   uint8_t* stage1;
+  uint8_t* stage2;  // the third stage of a three-stage ring (else unused)
   int* last_arrival;
   int* pair_s;
   int* xrow_s;
@@ -237,7 +253,7 @@ struct TileLds {
 
 // One workgroup's tile: `wg` is its index in the launch's grid (or in its
 // region of a grid that runs two tile sizes).
-template <int BMv, bool ID>
+template <int BMv, bool ID, int NST = 2>
 __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __restrict__ y,
                                           const uint8_t* __restrict__ w,
                                           const uint8_t* __restrict__ xq, int M, int N, int nb,
@@ -247,8 +263,10 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
   using TL = Tile<BMv>;
   constexpr int BM = BMv;
   constexpr int MT = TL::MT;
+  static_assert(NST == 2 || NST == 3, "two- or three-stage ring");
   uint8_t* const stage0 = lds.stage0;
   uint8_t* const stage1 = lds.stage1;
+  uint8_t* const stage2 = lds.stage2;
   int& last_arrival = *lds.last_arrival;
   int* const pair_s = lds.pair_s;
   int* const xrow_s = lds.xrow_s;
@@ -328,14 +346,26 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
 
   const StageOffsets<BMv> so = stage_offsets<BMv, ID>(M, N, nb, m0, n0, wave, lane, xrow_s);
   issue_stage<BMv>(stage0, xq, w, so, b_lo, wave, lane);
+  if (NST == 3 && b_lo + 1 < b_hi) issue_stage<BMv>(stage1, xq, w, so, b_lo + 1, wave, lane);
 
-  // One super-block: wait for its stage, refill the other stage with
-  // super-block b+1 (every wave finished reading it: it passed the barrier
-  // below, which follows the compute of b-1), then compute from `stg`.
+  // One super-block: wait for its stage, refill the stage computed in the
+  // previous step (every wave finished reading it: it passed the barrier
+  // below, which follows the compute of b-1) with super-block b+1 (two
+  // stages) or b+2 (three stages, so b+1 stays in flight while b is
+  // computed), then compute from `stg`.
   auto step = [&](int b, const uint8_t* stg, uint8_t* refill) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    if (b + 1 < b_hi) issue_stage<BMv>(refill, xq, w, so, b + 1, wave, lane);
+    if constexpr (NST == 2) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      if (b + 1 < b_hi) issue_stage<BMv>(refill, xq, w, so, b + 1, wave, lane);
+    } else {
+      if (b + 1 < b_hi)
+        wait_stage_behind_one<BMv>(wave);
+      else
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      if (b + 2 < b_hi) issue_stage<BMv>(refill, xq, w, so, b + 2, wave, lane);
+    }
     // Wave priority: raised from here through the MFMA loop, lowered for the
     // epilogue, so that of the two waves sharing a SIMD the one feeding the
     // matrix core issues first and the other's VALU epilogue fills the gaps
@@ -439,10 +469,19 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
     }
   };
 
-  // The ring unrolled by two so each stage is a distinct LDS object.
-  for (int b = b_lo; b < b_hi; b += 2) {
-    step(b, stage0, stage1);
-    if (b + 1 < b_hi) step(b + 1, stage1, stage0);
+  // The ring unrolled by its depth so each stage is a distinct LDS object;
+  // super-block b uses stage (b - b_lo) % NST.
+  if constexpr (NST == 2) {
+    for (int b = b_lo; b < b_hi; b += 2) {
+      step(b, stage0, stage1);
+      if (b + 1 < b_hi) step(b + 1, stage1, stage0);
+    }
+  } else {
+    for (int b = b_lo; b < b_hi; b += 3) {
+      step(b, stage0, stage2);
+      if (b + 1 < b_hi) step(b + 1, stage1, stage0);
+      if (b + 2 < b_hi) step(b + 2, stage2, stage1);
+    }
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
@@ -548,9 +587,28 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
   __shared__ int last_arrival;
   __shared__ int pair_s[ID ? BMv : 1];
   __shared__ int xrow_s[ID ? BMv : 1];
-  gemm_tile<BMv, ID>(TileLds{stage0, stage1, &last_arrival, pair_s, xrow_s},
+  gemm_tile<BMv, ID>(TileLds{stage0, stage1, nullptr, &last_arrival, pair_s, xrow_s},
                      static_cast<int>(blockIdx.x), y, w, xq, M, N, nb, mtiles, ntiles, n_full, ks,
                      part, cnt, id);
+}
+
+// The 16-token tile with a three-stage ring: two super-blocks in flight
+// while one is computed (69 KB of LDS, two workgroups per CU).
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_q4k_deep_ring_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
+                               const uint8_t* __restrict__ xq, int M, int N, int nb, int mtiles,
+                               int ntiles, int n_full, int ks, float* __restrict__ part,
+                               int* __restrict__ cnt) {
+  static_assert(2 * 3 * Tile<16>::kStageBytes <= 160 * 1024, "two rings exceed 160 KiB");
+  __shared__ __align__(16) uint8_t stage0[Tile<16>::kStageBytes];
+  __shared__ __align__(16) uint8_t stage1[Tile<16>::kStageBytes];
+  __shared__ __align__(16) uint8_t stage2[Tile<16>::kStageBytes];
+  __shared__ int last_arrival;
+  __shared__ int pair_s[1];
+  __shared__ int xrow_s[1];
+  gemm_tile<16, false, 3>(TileLds{stage0, stage1, stage2, &last_arrival, pair_s, xrow_s},
+                          static_cast<int>(blockIdx.x), y, w, xq, M, N, nb, mtiles, ntiles, n_full,
+                          ks, part, cnt, IdGemm{});
 }
 
 // The grouped form over two tile lists in one grid: the experts' whole tiles
@@ -570,7 +628,7 @@ void gemm_q4k_id_mixed_kernel(float* __restrict__ y, const uint8_t* __restrict__
   __shared__ int last_arrival;
   __shared__ int pair_s[64];
   __shared__ int xrow_s[64];
-  const TileLds lds{stage0, stage1, &last_arrival, pair_s, xrow_s};
+  const TileLds lds{stage0, stage1, nullptr, &last_arrival, pair_s, xrow_s};
   const int b = static_cast<int>(blockIdx.x);
   const int big_wgs = big_tiles * ntiles;
   if (b < big_wgs) {
@@ -597,7 +655,8 @@ constexpr size_t kSplitBytes =
     static_cast<size_t>(kSplitCounters) * kCounterStride * sizeof(int);
 
 // Workgroups resident at once over the 256 CUs: two 64-token tiles or three
-// 16-token tiles per CU (their LDS rings, 73 KB and 46 KB of the 160 KB).
+// 16-token tiles per CU (their two-stage LDS rings, 73 KB and 46 KB of the
+// 160 KB).
 constexpr int64_t resident_tiles(int bm) { return bm == 16 ? 768 : 512; }
 
 // The grouped form's tile list: up to kIdMaxPairs pairs.
@@ -633,10 +692,23 @@ hipError_t launch_split(float* y, const void* w, const void* xq, int64_t M, int6
     cnt = reinterpret_cast<int*>(part + static_cast<size_t>(kSplitSlots) * Tile<64>::kPartFloats);
   }
   const int grid = n_full + (tiles - n_full) * ks;
-  hipLaunchKernelGGL((gemm_q4k_kernel<BMv, false>), dim3(grid), dim3(kThreads), 0, stream, y,
-                     static_cast<const uint8_t*>(w), static_cast<const uint8_t*>(xq),
-                     static_cast<int>(M), static_cast<int>(N), nb, mtiles, ntiles, n_full, ks,
-                     part, cnt, IdGemm{});
+  // The 16-token tile computes little per super-block. On a grid of at most
+  // one workgroup per CU (256), nothing else on the CU hides a super-block's
+  // load, so its ring goes three deep: 4096x14336 at 7 and 16 tokens 14.3
+  // us against 15.7. With more workgroups than CUs the second workgroup on a
+  // CU does that better (14336x4096 at 4-32 tokens: 12.5-16.9 us with two
+  // stages against 13.9-18.4 with three), and the two-stage ring keeps three
+  // per CU.
+  if (BMv == 16 && grid <= 256)
+    hipLaunchKernelGGL(gemm_q4k_deep_ring_kernel, dim3(grid), dim3(kThreads), 0, stream, y,
+                       static_cast<const uint8_t*>(w), static_cast<const uint8_t*>(xq),
+                       static_cast<int>(M), static_cast<int>(N), nb, mtiles, ntiles, n_full, ks,
+                       part, cnt);
+  else
+    hipLaunchKernelGGL((gemm_q4k_kernel<BMv, false>), dim3(grid), dim3(kThreads), 0, stream, y,
+                       static_cast<const uint8_t*>(w), static_cast<const uint8_t*>(xq),
+                       static_cast<int>(M), static_cast<int>(N), nb, mtiles, ntiles, n_full, ks,
+                       part, cnt, IdGemm{});
   return hipGetLastError();
 }
 

@@ -500,6 +500,9 @@ GEMM_TILE16 = [
     (31, 4096, 14336, 7523),   # two tiles, the second ragged, eight splits
     (17, 300, 2304, 7524),     # ragged tokens and rows, nine super-blocks
     (64, 4096, 4096, 7525),    # four tiles on a 2^24-weight matrix
+    (16, 4096, 14336, 7526),   # one workgroup per CU: the three-stage ring, 8 splits of 7 super-blocks
+    (10, 2000, 2816, 7527),    # the three-stage ring over uneven splits (5 and 6 super-blocks)
+    (9, 1000, 4096, 7528),     # the three-stage ring, 4 super-blocks per split
 ]
 
 
