@@ -593,22 +593,26 @@ void gemm_q4k_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
 }
 
 // The 16-token tile with a three-stage ring: two super-blocks in flight
-// while one is computed (69 KB of LDS, two workgroups per CU).
+// while one is computed (69 KB of LDS), for grids of at most one workgroup
+// per CU. (The 64-token tile's three-stage ring, 111 KB, measured slower on
+// such grids: 64 x 4096x14336 25.9 us against 25.0, 96 x 4096x4096 20.1
+// against 19.2; its compute per super-block covers the refill.)
+template <int BMv>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void gemm_q4k_deep_ring_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
                                const uint8_t* __restrict__ xq, int M, int N, int nb, int mtiles,
                                int ntiles, int n_full, int ks, float* __restrict__ part,
                                int* __restrict__ cnt) {
-  static_assert(2 * 3 * Tile<16>::kStageBytes <= 160 * 1024, "two rings exceed 160 KiB");
-  __shared__ __align__(16) uint8_t stage0[Tile<16>::kStageBytes];
-  __shared__ __align__(16) uint8_t stage1[Tile<16>::kStageBytes];
-  __shared__ __align__(16) uint8_t stage2[Tile<16>::kStageBytes];
+  static_assert(3 * Tile<BMv>::kStageBytes <= 160 * 1024, "the ring exceeds 160 KiB");
+  __shared__ __align__(16) uint8_t stage0[Tile<BMv>::kStageBytes];
+  __shared__ __align__(16) uint8_t stage1[Tile<BMv>::kStageBytes];
+  __shared__ __align__(16) uint8_t stage2[Tile<BMv>::kStageBytes];
   __shared__ int last_arrival;
   __shared__ int pair_s[1];
   __shared__ int xrow_s[1];
-  gemm_tile<16, false, 3>(TileLds{stage0, stage1, stage2, &last_arrival, pair_s, xrow_s},
-                          static_cast<int>(blockIdx.x), y, w, xq, M, N, nb, mtiles, ntiles, n_full,
-                          ks, part, cnt, IdGemm{});
+  gemm_tile<BMv, false, 3>(TileLds{stage0, stage1, stage2, &last_arrival, pair_s, xrow_s},
+                           static_cast<int>(blockIdx.x), y, w, xq, M, N, nb, mtiles, ntiles,
+                           n_full, ks, part, cnt, IdGemm{});
 }
 
 // The grouped form over two tile lists in one grid: the experts' whole tiles
@@ -700,7 +704,7 @@ hipError_t launch_split(float* y, const void* w, const void* xq, int64_t M, int6
   // stages against 13.9-18.4 with three), and the two-stage ring keeps three
   // per CU.
   if (BMv == 16 && grid <= 256)
-    hipLaunchKernelGGL(gemm_q4k_deep_ring_kernel, dim3(grid), dim3(kThreads), 0, stream, y,
+    hipLaunchKernelGGL((gemm_q4k_deep_ring_kernel<16>), dim3(grid), dim3(kThreads), 0, stream, y,
                        static_cast<const uint8_t*>(w), static_cast<const uint8_t*>(xq),
                        static_cast<int>(M), static_cast<int>(N), nb, mtiles, ntiles, n_full, ks,
                        part, cnt);
