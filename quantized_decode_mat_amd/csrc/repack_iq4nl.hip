@@ -37,39 +37,50 @@ __device__ __forceinline__ uint32_t src_half(const uint16_t* src, int64_t byte_o
   return src[byte_off >> 1];
 }
 
-template <bool DWORD_PREFIX>
+// I: the type of the block and item indices. 32-bit when every index of the
+// chunk fits (the host checks): a 64-bit division by bpr is a long software
+// sequence per work item, a 32-bit one a few instructions. Byte offsets stay
+// 64-bit either way.
+template <bool DWORD_PREFIX, typename I>
 __global__ __launch_bounds__(kRepackThreads) void repack_iq4nl_kernel(
-    uint8_t* __restrict__ out, const uint16_t* __restrict__ src, int64_t n, int64_t block_base,
-    int64_t bpr, int64_t prefix, int64_t row_bytes, int64_t prefix_items) {
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRepackThreads + threadIdx.x;
-  const int64_t pay_items = 4 * n;
+    uint8_t* __restrict__ out, const uint16_t* __restrict__ src, int64_t n64, int64_t base64,
+    int64_t bpr64, int64_t prefix, int64_t row_bytes, int64_t prefix_items64) {
+  const I n = static_cast<I>(n64);
+  const I block_base = static_cast<I>(base64);
+  const I bpr = static_cast<I>(bpr64);
+  const I prefix_items = static_cast<I>(prefix_items64);
+  const I t = static_cast<I>(blockIdx.x) * kRepackThreads + static_cast<I>(threadIdx.x);
+  const I pay_items = 4 * n;
   if (t < pay_items) {
-    const int64_t b = t >> 2;  // block within the chunk
+    const I b = t >> 2;  // block within the chunk
     const int k = static_cast<int>(t & 3);
-    const int64_t gb = block_base + b;
-    const int64_t row = gb / bpr;
-    const int64_t j = gb - row * bpr;
-    const int64_t so = b * kFileBlockBytes + 2 + 4 * k;
+    const I gb = block_base + b;
+    const I row = gb / bpr;
+    const I j = gb - row * bpr;
+    const int64_t so = static_cast<int64_t>(b) * kFileBlockBytes + 2 + 4 * k;
     const uint32_t w = src_half(src, so) | (src_half(src, so + 2) << 16);
-    uint8_t* orow = out + row * row_bytes;
-    *reinterpret_cast<uint32_t*>(orow + prefix + 16 * j + 4 * k) = w;
+    uint8_t* orow = out + static_cast<int64_t>(row) * row_bytes;
+    *reinterpret_cast<uint32_t*>(orow + prefix + 16 * static_cast<int64_t>(j) + 4 * k) = w;
     if (!DWORD_PREFIX && k == 0) {
-      reinterpret_cast<uint16_t*>(orow)[j] = static_cast<uint16_t>(src_half(src, b * kFileBlockBytes));
+      reinterpret_cast<uint16_t*>(orow)[j] =
+          static_cast<uint16_t>(src_half(src, static_cast<int64_t>(b) * kFileBlockBytes));
       if (j == bpr - 1 && (bpr & 1)) reinterpret_cast<uint16_t*>(orow)[j + 1] = 0;
     }
     return;
   }
   if (DWORD_PREFIX) {
-    const int64_t p = t - pay_items;  // prefix dword over the chunk's rows
+    const I p = t - pay_items;  // prefix dword over the chunk's rows
     if (p >= prefix_items) return;
-    const int64_t pw = prefix >> 2;
-    const int64_t r = p / pw;                 // row within the chunk
-    const int64_t i = p - r * pw;             // dword within the prefix
-    const int64_t b0 = r * bpr + 2 * i;       // block within the chunk
-    const uint32_t lo = src_half(src, b0 * kFileBlockBytes);
-    const uint32_t hi = (2 * i + 1 < bpr) ? src_half(src, (b0 + 1) * kFileBlockBytes) : 0u;
-    const int64_t row = block_base / bpr + r;
-    *reinterpret_cast<uint32_t*>(out + row * row_bytes + 4 * i) = lo | (hi << 16);
+    const I pw = static_cast<I>(prefix >> 2);
+    const I r = p / pw;                 // row within the chunk
+    const I i = p - r * pw;             // dword within the prefix
+    const I b0 = r * bpr + 2 * i;       // block within the chunk
+    const uint32_t lo = src_half(src, static_cast<int64_t>(b0) * kFileBlockBytes);
+    const uint32_t hi =
+        (2 * i + 1 < bpr) ? src_half(src, static_cast<int64_t>(b0 + 1) * kFileBlockBytes) : 0u;
+    const int64_t row = static_cast<int64_t>(block_base / bpr) + r;
+    *reinterpret_cast<uint32_t*>(out + row * row_bytes + 4 * static_cast<int64_t>(i)) =
+        lo | (hi << 16);
   }
 }
 
@@ -91,17 +102,31 @@ hipError_t launch_repack_iq4nl(void* resident, const void* file_blocks, int64_t 
   const int64_t grid = (items + kRepackThreads - 1) / kRepackThreads;
   uint8_t* out = static_cast<uint8_t*>(resident);
   const uint16_t* src = static_cast<const uint16_t*>(file_blocks);
+  // 32-bit indices when the largest of them (the grid's items, the last
+  // global block) fits below 2^32.
+  const int64_t kI32 = int64_t{1} << 32;
+  const bool idx32 = grid * kRepackThreads < kI32 && block_base + n < kI32;
   if (row_aligned) {
-    hipLaunchKernelGGL(repack_iq4nl_kernel<true>, dim3(static_cast<uint32_t>(grid)),
-                       dim3(kRepackThreads), 0, stream, out, src, n, block_base, bpr, prefix,
-                       row_bytes, prefix_items);
+    if (idx32)
+      hipLaunchKernelGGL((repack_iq4nl_kernel<true, uint32_t>), dim3(static_cast<uint32_t>(grid)),
+                         dim3(kRepackThreads), 0, stream, out, src, n, block_base, bpr, prefix,
+                         row_bytes, prefix_items);
+    else
+      hipLaunchKernelGGL((repack_iq4nl_kernel<true, int64_t>), dim3(static_cast<uint32_t>(grid)),
+                         dim3(kRepackThreads), 0, stream, out, src, n, block_base, bpr, prefix,
+                         row_bytes, prefix_items);
     const hipError_t e = hipGetLastError();
     if (e == hipSuccess) g_dword_prefix_launches.fetch_add(1, std::memory_order_relaxed);
     return e;
   }
-  hipLaunchKernelGGL(repack_iq4nl_kernel<false>, dim3(static_cast<uint32_t>(grid)),
-                     dim3(kRepackThreads), 0, stream, out, src, n, block_base, bpr, prefix,
-                     row_bytes, prefix_items);
+  if (idx32)
+    hipLaunchKernelGGL((repack_iq4nl_kernel<false, uint32_t>), dim3(static_cast<uint32_t>(grid)),
+                       dim3(kRepackThreads), 0, stream, out, src, n, block_base, bpr, prefix,
+                       row_bytes, prefix_items);
+  else
+    hipLaunchKernelGGL((repack_iq4nl_kernel<false, int64_t>), dim3(static_cast<uint32_t>(grid)),
+                       dim3(kRepackThreads), 0, stream, out, src, n, block_base, bpr, prefix,
+                       row_bytes, prefix_items);
   return hipGetLastError();
 }
 
