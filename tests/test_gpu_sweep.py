@@ -5,9 +5,11 @@ draws further shapes from a fixed seed so that ragged edges land in new
 places: mat-vecs of the three formats over ragged N and K, and the small-M
 product on the batched mat-vec, the 16-token tile, split K, and launches
 whose tiles run in whole rounds with a split remainder (the remainder and
-the whole rounds in one grid, for both token tiles). Outputs are compared to
-the oracle at the f32 bar (whole outputs where the oracle is quick, sampled
-outputs with tile corners and whole rows where not).
+the whole rounds in one grid, for both token tiles), and the grouped product
+over skewed routings with stray selections, some past the expert map's
+first batch of pairs. Outputs are compared to the oracle at the f32 bar
+(whole outputs where the oracle is quick, sampled outputs with tile corners
+and whole rows where not).
 """
 import numpy as np
 import pytest
@@ -15,6 +17,7 @@ import pytest
 import oracle
 import quantized_decode_mat_amd as xq
 import workloads as wl
+from test_gpu_gemm_id import _check, _run, _slab
 from test_gpu_parity import _note, assert_close, dev, gpu_gemm, poisoned_f32, take_f32
 
 pytestmark = pytest.mark.gpu
@@ -138,3 +141,48 @@ def test_sweep_product(M, N, K, seed):
     for m in sorted({0, M - 1}):
         ref, T = oracle.gemv_q4k(w, xqb[m], N, K)
         assert_close(Y[m], ref, T, "sweep product row %d" % m)
+
+
+def _grouped_shapes():
+    # (tokens, slots, experts, rows per expert, K, q8_K row per slot); the
+    # slab stays under 2^27 weights. The last regime passes 8192 pairs.
+    g = wl.rng(8300)
+    out = []
+    regimes = [((1, 64), (1, 4), (1, 9)), ((64, 700), (1, 9), (8, 129)),
+               ((1100, 1400), (8, 9), (16, 65))]
+    for (t_lo, t_hi), (u_lo, u_hi), (e_lo, e_hi) in regimes:
+        for _ in range(3):
+            E = int(g.integers(e_lo, e_hi))
+            U = min(E, int(g.integers(u_lo, u_hi)))
+            T = int(g.integers(t_lo, t_hi))
+            K = 256 * int(g.integers(1, 17))
+            rows = int(g.integers(1, max(2, min(3000, 2 ** 27 // (E * K)))))
+            out.append((T, U, E, rows, K, int(g.integers(0, 2)), int(g.integers(0, 2 ** 31))))
+    return out
+
+
+GROUPED = _grouped_shapes()
+
+
+@pytest.mark.parametrize("T,U,E,rows,K,per_slot,seed", GROUPED,
+                         ids=["t%d_u%d_e%d_r%d_k%d_s%d" % s[:6] for s in GROUPED])
+def test_sweep_grouped_product(T, U, E, rows, K, per_slot, seed):
+    g = wl.rng(seed)
+    slab = _slab(E, rows, K, seed)
+    xqb = oracle.quantize_q8k(wl.activations(T * U if per_slot else T, K, g))
+    # Each token's U distinct experts drawn with weights falling as 1/(e+1),
+    # so a few experts take most pairs; about 1 in 50 selections is replaced
+    # by an expert number outside 0..E-1.
+    w = 1.0 / np.arange(1, E + 1)
+    ids = np.stack([g.choice(E, size=U, replace=False, p=w / w.sum()) for _ in range(T)])
+    stray = g.random(ids.shape) < 0.02
+    ids = np.where(stray, g.choice([-1, E, E + 7], size=ids.shape), ids).astype(np.int32)
+    _note("sweep grouped T=%d U=%d E=%d rows=%d K=%d per_slot=%d" % (T, U, E, rows, K, per_slot))
+    Y = _run(slab, xqb, ids, E, rows, K, per_slot)
+    s = wl.rng(seed + 1)
+    pairs = sorted({(int(s.integers(T)), int(s.integers(U))) for _ in range(80)} |
+                   {(0, 0), (T - 1, U - 1)} | {tuple(int(v) for v in p) for p in np.argwhere(stray)[:8]})
+    _check(Y, slab, xqb, ids, E, rows, K, per_slot, pairs)
+    # Outputs outside the sample: NaN exactly where a selection is stray.
+    assert np.array_equal(np.isnan(Y).all(axis=2), (ids < 0) | (ids >= E))
+    assert not np.isnan(Y[(ids >= 0) & (ids < E)]).any()
