@@ -399,6 +399,66 @@ __global__ __launch_bounds__(kMresThreads) void gemv_q4k_multi_res_kernel(
   }
 }
 
+// Two or three tokens on rows of seven units (K in 12544..14336), a row's
+// units split across the waves of a workgroup: wave u takes unit u of R
+// consecutive rows. Each lane reads its slice of every token's q8_K block of
+// that unit from global memory into registers once (no LDS staging of the
+// activation row), then the R rows' weight chunks of its unit in one batch.
+// The per-lane partial of each (row, token, unit) goes to LDS; after one
+// barrier each (row, token) is summed over the units in unit order from 0.0f
+// and reduced across the wave, so the sequence of float additions, and so the
+// bits, are those of the clamped mat-vec (masked blocks add 0.0f there too).
+constexpr int kSplitMaxUnits = 7;
+
+template <int TM, int R>
+__global__ __launch_bounds__(kSplitMaxUnits * kWave) void gemv_q4k_unit_split_kernel(
+    float* __restrict__ y, const uint8_t* __restrict__ w, const uint8_t* __restrict__ xq, int N,
+    int nb, int tokens) {
+  __shared__ float part[R * TM][kSplitMaxUnits][kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int u = threadIdx.x >> 6;          // this wave's unit
+  const int units = blockDim.x >> 6;       // the row's units: (nb + 7) / 8
+  const int row0 = blockIdx.x * R;
+  const LaneGeom L = lane_geom(lane);
+  const int64_t row_bytes = static_cast<int64_t>(nb) * kQ4KBytes;
+  const int64_t xrow = static_cast<int64_t>(nb) * kQ8KBytes;
+  const int bb = u * 8 + L.bsub;
+  const int bc = min(bb, nb - 1);
+
+  TokenSlice ts[TM];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) ts[t] = token_slice(xq + min(t, tokens - 1) * xrow, bc, L);
+  uint4 nib[R], hdr[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = min(row0 + r, N - 1);  // rows past N reload the last (not stored)
+    const uint8_t* blk =
+        w + static_cast<int64_t>(row) * row_bytes + static_cast<int64_t>(bc) * kQ4KBytes;
+    nib[r] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (2 * L.g + L.h));
+    hdr[r] = *reinterpret_cast<const uint4*>(blk);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const ChunkDecode c = chunk_decode(nib[r], hdr[r], L);
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      if (t < tokens) {
+        const float v = chunk_token_slice(c, ts[t]);
+        part[r * TM + t][u][lane] = (bb < nb) ? v : 0.0f;
+      }
+    }
+  }
+  __syncthreads();
+  for (int k = u; k < R * TM; k += units) {
+    const int r = k / TM, t = k - r * TM;
+    if (t >= tokens || row0 + r >= N) continue;  // wave-uniform
+    float acc = 0.0f;
+    for (int v = 0; v < units; ++v) acc += part[k][v][lane];
+    const float tot = wave_sum(acc);
+    if (lane == 0) y[static_cast<int64_t>(t) * N + row0 + r] = tot;
+  }
+}
+
 struct IdArgs {
   const int32_t* sel;  // device selection buffer (null: dense launch)
   int used;            // selection slots (grid.y)
@@ -501,6 +561,17 @@ hipError_t launch_multi_rows(float* y, const void* w, const void* xq, int64_t N,
   return launch_multi_cfg<TM, 1, 4, 8, 3, false>(y, wb, xb, n, nb, tokens, stream);
 }
 
+template <int TM, int R>
+hipError_t launch_unit_split(float* y, const uint8_t* w, const uint8_t* xq, int N, int nb,
+                             int tokens, hipStream_t stream) {
+  const int units = (nb + 7) / 8;
+  if (units < 1 || units > kSplitMaxUnits || tokens < 1 || tokens > TM)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemv_q4k_unit_split_kernel<TM, R>), dim3((N + R - 1) / R),
+                     dim3(units * kWave), 0, stream, y, w, xq, N, nb, tokens);
+  return hipGetLastError();
+}
+
 // The persistent grid is the device's resident capacity for the kernel
 // (queried once per kernel and device), so each wave visits N / (grid's
 // waves) rows and the copy of the activation is paid once per wave.
@@ -564,6 +635,16 @@ hipError_t launch_gemv_q4k_multi(float* y, const void* w, const void* xq, int64_
     if (M <= 2) return launch_multi_res<2, 2>(y, wb, xb, n, nb, t, stream);
     if (M == 3) return launch_multi_res<3, 2>(y, wb, xb, n, nb, t, stream);
     return launch_multi_res<4, 2>(y, wb, xb, n, nb, t, stream);
+  }
+  if (nb > 48 && nb <= 56 && M <= 3) {
+    // Rows of seven units: the units split across a workgroup's waves.
+    // Measured on MI355X (cold weights), 4096x14336 at 2 and 3 tokens:
+    // 10.1 and 11.8 us against 11.2 and 14.1 for the kernel below. At four
+    // and five units it measured slower (4096x8192, 6000x5120), and for one
+    // token the mat-vec stays ahead (8.9 against 8.0 us).
+    const int n = static_cast<int>(N);
+    if (M <= 2) return launch_unit_split<2, 8>(y, wb, xb, n, nb, t, stream);
+    return launch_unit_split<3, 4>(y, wb, xb, n, nb, t, stream);
   }
   if (M <= 2) return launch_multi_rows<2>(y, w, xq, N, K, t, stream);
   if (M <= 4) return launch_multi_rows<4>(y, w, xq, N, K, t, stream);

@@ -472,6 +472,9 @@ GEMM_SHORT = [
     (3, 3000, 1280, 7509),     # persistent grid, one ragged unit
     (2, 20000, 3840, 7510),    # persistent grid, the second unit ragged, rows past one pass
     (4, 100, 256, 7511),       # persistent grid smaller than a workgroup's waves allow
+    (2, 4096, 14336, 7512),    # seven units split across a workgroup's waves
+    (2, 1001, 12544, 7513),    # the same, the last unit one block, rows past a workgroup's eight
+    (3, 4099, 13312, 7514),    # three tokens, four rows per workgroup and a ragged row tail
 ]
 
 
