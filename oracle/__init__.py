@@ -79,16 +79,16 @@ class Oracle:
         lib.xqo_q4k_code.restype = ctypes.c_int
         lib.xqo_dequant_q4k.argtypes = [P, I, I, P]
         lib.xqo_q4k_partials.argtypes = [P, P, I, I, P, I, P, P]
-        lib.xqo_gemv_q4k.argtypes = [P, P, I, I, P, I, P, P]
-        lib.xqo_gemm_q4k.argtypes = [P, P, I, I, I, P, P, I, P, P]
+        lib.xqo_gemv_q4k.argtypes = [P, P, I, I, P, I, P, P, P]
+        lib.xqo_gemm_q4k.argtypes = [P, P, I, I, I, P, P, I, P, P, P]
         lib.xqo_iq4nl_codebook.argtypes = [ctypes.c_int]
         lib.xqo_iq4nl_codebook.restype = ctypes.c_int
         lib.xqo_dequant_iq4nl.argtypes = [P, I, I, P]
         lib.xqo_iq4nl_partials.argtypes = [P, P, I, I, P, I, P]
-        lib.xqo_gemv_iq4nl.argtypes = [P, P, I, I, P, I, P, P]
+        lib.xqo_gemv_iq4nl.argtypes = [P, P, I, I, P, I, P, P, P]
         lib.xqo_dequant_q4_0.argtypes = [P, I, I, P]
         lib.xqo_q4_0_partials.argtypes = [P, P, I, I, P, I, P]
-        lib.xqo_gemv_q4_0.argtypes = [P, P, I, I, P, I, P, P]
+        lib.xqo_gemv_q4_0.argtypes = [P, P, I, I, P, I, P, P, P]
         self.lib = lib
         self.path = path
 
@@ -142,35 +142,37 @@ class Oracle:
         self.lib.xqo_q4k_partials(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(S), _ptr(M))
         return S, M
 
-    def gemv_q4k(self, w, xq, N: int, K: int, rows=None):
-        """(y, T), double [nrows]: y by the plain definition, T the sum of the
-        magnitudes of the products that make it up."""
+    def gemv_q4k(self, w, xq, N: int, K: int, rows=None, elem=False):
+        """(y, T), double [nrows]: y by the plain definition; T the sum of
+        |terms| of the f32 bar: over the row's blocks, |d*xs*S| + |dmin*xs*M|.
+        With elem=True: (y, T, Te), Te the sum over elements of
+        |d*sc*q*xhat| + |dmin*m*xhat| (Te >= T >= |y|)."""
         w = _u8(w)
         xq = _u8(xq)
         r, rp, n = _rows_arg(rows)
         nrows = N if r is None else n
-        y = np.empty(nrows, dtype=np.float64)
-        T = np.empty(nrows, dtype=np.float64)
-        self.lib.xqo_gemv_q4k(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(y), _ptr(T))
-        return y, T
+        y, T, Te = (np.empty(nrows, dtype=np.float64) for _ in range(3))
+        self.lib.xqo_gemv_q4k(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(y), _ptr(T), _ptr(Te))
+        return (y, T, Te) if elem else (y, T)
 
-    def gemm_q4k(self, w, xq, M: int, N: int, K: int, ms=None, ns=None):
-        """(Y, T): full [M, N] arrays, or values at the listed (m, n) pairs."""
+    def gemm_q4k(self, w, xq, M: int, N: int, K: int, ms=None, ns=None, elem=False):
+        """(Y, T) as gemv_q4k per (token, row): full [M, N] arrays, or values at
+        the listed (m, n) pairs; (Y, T, Te) with elem=True."""
         w = _u8(w)
         xq = _u8(xq)
         if ms is None:
-            Y = np.empty(M * N, dtype=np.float64)
-            T = np.empty(M * N, dtype=np.float64)
-            self.lib.xqo_gemm_q4k(_ptr(w), _ptr(xq), M, N, K, None, None, 0, _ptr(Y), _ptr(T))
-            return Y.reshape(M, N), T.reshape(M, N)
+            Y, T, Te = (np.empty(M * N, dtype=np.float64) for _ in range(3))
+            self.lib.xqo_gemm_q4k(_ptr(w), _ptr(xq), M, N, K, None, None, 0, _ptr(Y), _ptr(T),
+                                  _ptr(Te))
+            out = (Y.reshape(M, N), T.reshape(M, N), Te.reshape(M, N))
+            return out if elem else out[:2]
         ms = np.ascontiguousarray(np.asarray(ms, dtype=np.int64))
         ns = np.ascontiguousarray(np.asarray(ns, dtype=np.int64))
         assert ms.shape == ns.shape
-        Y = np.empty(ms.size, dtype=np.float64)
-        T = np.empty(ms.size, dtype=np.float64)
+        Y, T, Te = (np.empty(ms.size, dtype=np.float64) for _ in range(3))
         self.lib.xqo_gemm_q4k(_ptr(w), _ptr(xq), M, N, K, _ptr(ms), _ptr(ns), ms.size,
-                              _ptr(Y), _ptr(T))
-        return Y, T
+                              _ptr(Y), _ptr(T), _ptr(Te))
+        return (Y, T, Te) if elem else (Y, T)
 
     # ---- IQ4_NL ----------------------------------------------------------
     def iq4nl_codebook(self, nibble: int) -> int:
@@ -192,15 +194,16 @@ class Oracle:
         self.lib.xqo_iq4nl_partials(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(D))
         return D
 
-    def gemv_iq4nl(self, w, xq, N: int, K: int, rows=None):
+    def gemv_iq4nl(self, w, xq, N: int, K: int, rows=None, elem=False):
+        """(y, T): T the sum over 32-blocks of |d_c*xs*D_c|; with elem=True
+        (y, T, Te), Te the sum over elements of |d_c*kv*xhat|."""
         w = _u8(w)
         xq = _u8(xq)
         r, rp, n = _rows_arg(rows)
         nrows = N if r is None else n
-        y = np.empty(nrows, dtype=np.float64)
-        T = np.empty(nrows, dtype=np.float64)
-        self.lib.xqo_gemv_iq4nl(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(y), _ptr(T))
-        return y, T
+        y, T, Te = (np.empty(nrows, dtype=np.float64) for _ in range(3))
+        self.lib.xqo_gemv_iq4nl(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(y), _ptr(T), _ptr(Te))
+        return (y, T, Te) if elem else (y, T)
 
     def dequant_q4_0(self, w, N: int, K: int) -> np.ndarray:
         """Q4_0 resident rows (the IQ4_NL row shape) -> f64 weights d*(nibble-8)."""
@@ -219,15 +222,15 @@ class Oracle:
         self.lib.xqo_q4_0_partials(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(D))
         return D
 
-    def gemv_q4_0(self, w, xq, N: int, K: int, rows=None):
+    def gemv_q4_0(self, w, xq, N: int, K: int, rows=None, elem=False):
+        """(y, T) as gemv_iq4nl, weights d_c*(nibble-8)."""
         w = _u8(w)
         xq = _u8(xq)
         r, rp, n = _rows_arg(rows)
         nrows = N if r is None else n
-        y = np.empty(nrows, dtype=np.float64)
-        T = np.empty(nrows, dtype=np.float64)
-        self.lib.xqo_gemv_q4_0(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(y), _ptr(T))
-        return y, T
+        y, T, Te = (np.empty(nrows, dtype=np.float64) for _ in range(3))
+        self.lib.xqo_gemv_q4_0(_ptr(w), _ptr(xq), N, K, rp, n, _ptr(y), _ptr(T), _ptr(Te))
+        return (y, T, Te) if elem else (y, T)
 
 
 def repack_iq4nl(file_blocks, n_blocks: int, block_base: int, bpr: int, resident=None):

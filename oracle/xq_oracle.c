@@ -267,59 +267,93 @@ void xqo_q4k_partials(const uint8_t *w, const uint8_t *xq, int64_t N, int64_t K,
 }
 
 /* One output of the Q4_K mat-vec by the plain definition, against the q8_K
- * activation row xrow (K/256 blocks). *T receives the sum of the magnitudes
- * of the products that make it up, |d*sc*q*xhat| + |dmin*m*xhat| per element. */
-static void q4k_dot(const uint8_t *wrow, const uint8_t *xrow, int64_t nb, double *y, double *T)
+ * activation row xrow (K/256 blocks). Two magnitude sums come with it:
+ *  *Tb, the sum over blocks of the magnitudes of the two terms the integer
+ *      route adds per block, |d*xs*S| + |dmin*xs*M|, with S and M the block's
+ *      exact integer partials (the sum of |terms| of the f32 bar);
+ *  *Te, the sum over elements of |d*sc*q*xhat| + |dmin*m*xhat|.
+ * Te >= Tb >= |y| by the triangle inequality. Either may be NULL. */
+static void q4k_dot(const uint8_t *wrow, const uint8_t *xrow, int64_t nb, double *y, double *Tb,
+                    double *Te)
 {
-    double acc = 0.0, mag = 0.0;
+    double acc = 0.0, mag_b = 0.0, mag_e = 0.0;
     for (int64_t b = 0; b < nb; b++) {
         const uint8_t *blk = wrow + b * Q4K_BYTES;
         const uint8_t *xb = xrow + b * Q8K_BYTES;
         double d = xqo_f16_to_f64(rd_u16(blk));
         double dmin = xqo_f16_to_f64(rd_u16(blk + 2));
         double xs = (double)rd_f32(xb + 288);
+        int64_t S = 0, M = 0;
+#ifdef XQO_FAULT_TB_SUBBLOCK
+        double sub_mag = 0.0;
+        int64_t S_j = 0, M_j = 0;
+#endif
         for (int i = 0; i < QK; i++) {
             int j, q, sc, m;
             q4k_code(blk, i, &j, &q);
             xqo_q4k_scale_min(blk, j, &sc, &m);
-            double xhat = xs * (double)(int8_t)xb[i];
+            int code = (int8_t)xb[i];
+            double xhat = xs * (double)code;
             double wsc = d * (double)sc * (double)q;
             double wmin = dmin * (double)m;
 #ifdef XQO_FAULT_MIN_SIGN
             wmin = -wmin;
 #endif
             acc += (wsc - wmin) * xhat;
-            mag += fabs(wsc * xhat) + fabs(wmin * xhat);
+            mag_e += fabs(wsc * xhat) + fabs(wmin * xhat);
+#ifdef XQO_FAULT_T_DOUBLE
+            mag_e += fabs(wsc * xhat);
+#endif
+            S += (int64_t)sc * q * code;
+            M += (int64_t)m * code;
+#ifdef XQO_FAULT_TB_SUBBLOCK
+            S_j += (int64_t)sc * q * code;
+            M_j += (int64_t)m * code;
+            if (i % 32 == 31) {
+                sub_mag += fabs(d * xs * (double)S_j) + fabs(dmin * xs * (double)M_j);
+                S_j = 0;
+                M_j = 0;
+            }
+#endif
         }
+#ifdef XQO_FAULT_TB_SUBBLOCK
+        mag_b += sub_mag;
+#else
+        mag_b += fabs(d * xs * (double)S) + fabs(dmin * xs * (double)M);
+#endif
     }
     *y = acc;
-    *T = mag;
+    if (Tb) *Tb = mag_b;
+    if (Te) *Te = mag_e;
 }
 
 /* y = W * xhat for selected rows (all if rows is NULL); xq holds one q8_K
- * activation row. y, T: double [nrows]. */
+ * activation row. y, Tb, Te: double [nrows] (Tb, Te may be NULL). */
 void xqo_gemv_q4k(const uint8_t *w, const uint8_t *xq, int64_t N, int64_t K,
-                  const int64_t *rows, int64_t nrows, double *y, double *T)
+                  const int64_t *rows, int64_t nrows, double *y, double *Tb, double *Te)
 {
     int64_t nb = K / QK;
     if (!rows) nrows = N;
     for (int64_t k = 0; k < nrows; k++) {
         int64_t r = rows ? rows[k] : k;
-        q4k_dot(w + r * nb * Q4K_BYTES, xq, nb, &y[k], &T[k]);
+        q4k_dot(w + r * nb * Q4K_BYTES, xq, nb, &y[k], Tb ? &Tb[k] : NULL, Te ? &Te[k] : NULL);
     }
 }
 
 /* Y[m][n] = sum_i W[n][i] * xhat[m][i] for the listed (m, n) pairs (all
- * M*N pairs in row-major order if ms is NULL). y, T: double [count]. */
+ * M*N pairs in row-major order if ms is NULL). y, Tb, Te: double [count]
+ * (Tb, Te may be NULL). */
 void xqo_gemm_q4k(const uint8_t *w, const uint8_t *xq, int64_t Mrows, int64_t N, int64_t K,
-                  const int64_t *ms, const int64_t *ns, int64_t count, double *y, double *T)
+                  const int64_t *ms, const int64_t *ns, int64_t count, double *y, double *Tb,
+                  double *Te)
 {
     int64_t nb = K / QK;
     if (!ms) count = Mrows * N;
     for (int64_t k = 0; k < count; k++) {
         int64_t m = ms ? ms[k] : k / N;
         int64_t n = ms ? ns[k] : k % N;
-        q4k_dot(w + n * nb * Q4K_BYTES, xq + m * nb * Q8K_BYTES, nb, &y[k], &T[k]);
+        q4k_dot(w + n * nb * Q4K_BYTES, xq + m * nb * Q8K_BYTES, nb, &y[k], Tb ? &Tb[k] : NULL,
+                Te ? &Te[k] : NULL);
     }
 }
 
@@ -385,8 +419,12 @@ void xqo_iq4nl_partials(const uint8_t *w, const uint8_t *xq, int64_t N, int64_t 
     }
 }
 
+/* y = W * xhat for selected rows (all if rows is NULL). Tb is the sum over
+ * 32-blocks of |d_c*xs*D_c|, D_c the block's exact integer partial (the sum of
+ * |terms| of the f32 bar); Te the sum over elements of |d_c*kv*xhat|. y, Tb,
+ * Te: double [nrows] (Tb, Te may be NULL). */
 void xqo_gemv_iq4nl(const uint8_t *w, const uint8_t *xq, int64_t N, int64_t K,
-                    const int64_t *rows, int64_t nrows, double *y, double *T)
+                    const int64_t *rows, int64_t nrows, double *y, double *Tb, double *Te)
 {
     int64_t bpr, prefix, row_bytes;
     iq4nl_geometry(K, &bpr, &prefix, &row_bytes);
@@ -394,21 +432,32 @@ void xqo_gemv_iq4nl(const uint8_t *w, const uint8_t *xq, int64_t N, int64_t K,
     for (int64_t k = 0; k < nrows; k++) {
         int64_t r = rows ? rows[k] : k;
         const uint8_t *row = w + r * row_bytes;
-        double acc = 0.0, mag = 0.0;
+        double acc = 0.0, mag_b = 0.0, mag_e = 0.0;
         for (int64_t c = 0; c < bpr; c++) {
             double d = xqo_f16_to_f64(rd_u16(row + 2 * c));
             const uint8_t *pay = row + prefix + 16 * c;
+            const uint8_t *xb = xq + ((32 * c) / QK) * Q8K_BYTES;
+            double xs = (double)rd_f32(xb + 288);
+            int64_t D = 0;
             for (int t = 0; t < 32; t++) {
                 int64_t i = 32 * c + t;
-                const uint8_t *xb = xq + (i / QK) * Q8K_BYTES;
-                double xhat = (double)rd_f32(xb + 288) * (double)(int8_t)xb[i % QK];
-                double term = d * (double)IQ4NL_KV[iq4nl_nibble(pay, t)] * xhat;
+                int code = (int8_t)xb[i % QK];
+                int kv = IQ4NL_KV[iq4nl_nibble(pay, t)];
+                double term = d * (double)kv * (xs * (double)code);
                 acc += term;
-                mag += fabs(term);
+                mag_e += fabs(term);
+                D += (int64_t)kv * code;
             }
+#ifdef XQO_FAULT_TB_IQ4_ELEM
+            (void)D;
+            mag_b = mag_e;
+#else
+            mag_b += fabs(d * xs * (double)D);
+#endif
         }
         y[k] = acc;
-        T[k] = mag;
+        if (Tb) Tb[k] = mag_b;
+        if (Te) Te[k] = mag_e;
     }
 }
 
@@ -466,8 +515,9 @@ void xqo_q4_0_partials(const uint8_t *w, const uint8_t *xq, int64_t N, int64_t K
     }
 }
 
+/* As xqo_gemv_iq4nl, with weight d_c*(nibble-8) and D_c = sum (nibble-8)*code. */
 void xqo_gemv_q4_0(const uint8_t *w, const uint8_t *xq, int64_t N, int64_t K,
-                   const int64_t *rows, int64_t nrows, double *y, double *T)
+                   const int64_t *rows, int64_t nrows, double *y, double *Tb, double *Te)
 {
     int64_t bpr, prefix, row_bytes;
     iq4nl_geometry(K, &bpr, &prefix, &row_bytes);
@@ -475,20 +525,26 @@ void xqo_gemv_q4_0(const uint8_t *w, const uint8_t *xq, int64_t N, int64_t K,
     for (int64_t k = 0; k < nrows; k++) {
         int64_t r = rows ? rows[k] : k;
         const uint8_t *row = w + r * row_bytes;
-        double acc = 0.0, mag = 0.0;
+        double acc = 0.0, mag_b = 0.0, mag_e = 0.0;
         for (int64_t c = 0; c < bpr; c++) {
             double d = xqo_f16_to_f64(rd_u16(row + 2 * c));
             const uint8_t *pay = row + prefix + 16 * c;
+            const uint8_t *xb = xq + ((32 * c) / QK) * Q8K_BYTES;
+            double xs = (double)rd_f32(xb + 288);
+            int64_t D = 0;
             for (int t = 0; t < 32; t++) {
                 int64_t i = 32 * c + t;
-                const uint8_t *xb = xq + (i / QK) * Q8K_BYTES;
-                double xhat = (double)rd_f32(xb + 288) * (double)(int8_t)xb[i % QK];
-                double term = d * (double)q4_0_value(iq4nl_nibble(pay, t)) * xhat;
+                int code = (int8_t)xb[i % QK];
+                int v = q4_0_value(iq4nl_nibble(pay, t));
+                double term = d * (double)v * (xs * (double)code);
                 acc += term;
-                mag += fabs(term);
+                mag_e += fabs(term);
+                D += (int64_t)v * code;
             }
+            mag_b += fabs(d * xs * (double)D);
         }
         y[k] = acc;
-        T[k] = mag;
+        if (Tb) Tb[k] = mag_b;
+        if (Te) Te[k] = mag_e;
     }
 }

@@ -250,8 +250,6 @@ def pin_q4k_brute_force(o):
         y, T = o.gemv_q4k(w, xq, N, K)
         ref = o.dequant_q4k(w, N, K) @ o.dequant_q8k(xq, 1, K)[0]
         assert np.all(np.abs(y - ref) <= 1e-12 * T)
-        # T is the magnitude sum of the products d*sc*q*xhat and dmin*m*xhat
-        assert np.all(T >= np.abs(y))
 
 
 def pin_q4k_error_bound(o):
@@ -300,16 +298,146 @@ def pin_q4k_partials(o):
     assert S1[0, 0] == 15 * int((sc * s1).sum()) and M1[0, 0] == 0
 
 
+# ---------------------------------------------------------------------------
+# The magnitude sums that scale the f32 bar
+# ---------------------------------------------------------------------------
+# T: over the row's blocks, |d*xs*S| + |dmin*xs*M| (Q4_K) or |d_c*xs*D_c|
+# (IQ4_NL, Q4_0): the magnitudes of the terms the integer route adds.
+# Te: over the row's elements, |d*sc*q*xhat| + |dmin*m*xhat| (or |d_c*kv*xhat|).
+# Both are fixed here by construction, never by retyping them.
+
+def _q4k_parts(o, w, N, K):
+    """The scale part d*sc*q and the min part -dmin*m of every weight, each
+    through the oracle's dequantizer (pinned above) on a copy of the blocks
+    with the other f16 zeroed: dmin = 0 leaves d*sc*q, d = 0 leaves -dmin*m."""
+    w = np.array(w, dtype=np.uint8, copy=True).reshape(N, K // 256, 144)
+    ws = w.copy()
+    ws[:, :, 2:4] = 0
+    wm = w.copy()
+    wm[:, :, 0:2] = 0
+    return o.dequant_q4k(ws, N, K), o.dequant_q4k(wm, N, K)
+
+
+def pin_q4k_magnitudes_one_hot(o):
+    """x = 127*e_p: one element and one block contribute, xhat = 127, so
+    T = Te = 127*(|d*sc_j*q_p| + |dmin*m_j|) for every row, exactly."""
+    N, K = 3, 512
+    w, _ = _rand_q4k_case(17, N, K)
+    ws, wm = _q4k_parts(o, w, N, K)
+    for p in (0, 31, 32, 100, 255, 256, 300, 511):
+        x = np.zeros((1, K), np.float32)
+        x[0, p] = 127.0
+        y, T, Te = o.gemv_q4k(w, o.quantize_q8k(x), N, K, elem=True)
+        want = 127.0 * (np.abs(ws[:, p]) + np.abs(wm[:, p]))
+        assert np.array_equal(T, want), (p, T, want)
+        assert np.array_equal(Te, want), (p, Te, want)
+
+
+def pin_q4k_magnitudes_cancel(o):
+    """Codes +127 and -127 (scale 1) on two weights of one block whose scale
+    parts are equal and whose mins are equal: S = M = 0, so y = 0 and T = 0,
+    while Te = 2*127*(|d*sc*q| + |dmin*m|). Once within one sub-block (equal
+    nibbles), once across two sub-blocks of one block (sc_1*q_1 = sc_2*q_2,
+    m_1 = m_2): T is per block, not per sub-block. The same pair in two
+    different blocks does not cancel: T = Te. Unequal nibbles in one sub-block
+    leave S = 127*sc*(q1 - q2) and M = 0."""
+    sc = np.array([6, 3, 9, 2, 5, 7, 1, 4])
+    m = np.array([11, 11, 20, 8, 3, 63, 0, 17])
+    nib = np.zeros(128, np.uint8)
+    nib[0:32] = 4 | (8 << 4)       # sub-block 0: q = 4 (sc*q = 24); sub-block 1: q = 8 (24)
+    nib[32:64] = 9 | (2 << 4)      # sub-block 2: q = 9; sub-block 3: q = 2
+    nib[5] = 13 | (8 << 4)         # weight 5 of sub-block 0 gets q = 13
+    d, dmin = 0.5, 0.25
+    blk = wl.q4k_block(d, dmin, sc, m, nib)
+
+    def run(w, K, plus, minus):
+        x = np.zeros((1, K), np.float32)
+        x[0, plus] = 127.0
+        x[0, minus] = -127.0
+        return o.gemv_q4k(w, o.quantize_q8k(x), 1, K, elem=True)
+
+    one_pair = 2 * 127.0 * (d * 24 + dmin * 11)
+    y, T, Te = run(blk, 256, 0, 7)          # same sub-block, equal nibbles
+    assert y[0] == 0.0 and T[0] == 0.0 and Te[0] == one_pair, (y, T, Te)
+    y, T, Te = run(blk, 256, 1, 40)         # sub-blocks 0 and 1, 6*4 == 3*8, m equal
+    assert y[0] == 0.0 and T[0] == 0.0 and Te[0] == one_pair, (y, T, Te)
+    two = np.stack([blk, blk]).reshape(1, 2, 144)
+    y, T, Te = run(two, 512, 0, 256 + 7)    # the same weights in two blocks
+    assert y[0] == 0.0 and T[0] == one_pair and Te[0] == one_pair, (y, T, Te)
+    y, T, Te = run(blk, 256, 5, 0)          # q 13 against q 4 in sub-block 0
+    assert T[0] == 127.0 * d * 6 * (13 - 4), T
+    assert Te[0] == 127.0 * (d * 6 * (13 + 4) + 2 * dmin * 11), Te
+
+
+def pin_q4k_magnitudes_brute_force(o):
+    """Random rows: Te = |scale parts| . |xhat| + |min parts| . |xhat| and
+    T = sum over blocks of |scale parts . xhat| + |min parts . xhat|, from
+    the separately dequantized operands; |y| <= T <= Te; with every xhat >= 0
+    and no mins every term is non-negative, so y = T = Te."""
+    for seed, N, K in ((71, 4, 1024), (73, 3, 256)):
+        w, x = _rand_q4k_case(seed, N, K)
+        xq = o.quantize_q8k(x)
+        y, T, Te = o.gemv_q4k(w, xq, N, K, elem=True)
+        ws, wm = _q4k_parts(o, w, N, K)
+        xh = o.dequant_q8k(xq, 1, K)[0]
+        te = np.abs(ws) @ np.abs(xh) + np.abs(wm) @ np.abs(xh)
+        assert np.all(np.abs(Te - te) <= 1e-12 * te)
+        nb = K // 256
+        tb = (np.abs((ws * xh).reshape(N, nb, 256).sum(axis=2)).sum(axis=1) +
+              np.abs((wm * xh).reshape(N, nb, 256).sum(axis=2)).sum(axis=1))
+        assert np.all(np.abs(T - tb) <= 1e-12 * te)
+        assert np.all(np.abs(y) <= T * (1 + 1e-12)) and np.all(T <= Te * (1 + 1e-12))
+        # one sign everywhere: mins 0, activation >= 0
+        wz = np.array(w, copy=True).reshape(N, nb, 144)
+        wz[:, :, 2:4] = 0
+        xq_pos = o.quantize_q8k(np.abs(x))
+        y, T, Te = o.gemv_q4k(wz, xq_pos, N, K, elem=True)
+        assert np.all(np.abs(y - T) <= 1e-12 * T) and np.all(np.abs(T - Te) <= 1e-12 * T)
+
+
+def pin_iq4nl_magnitudes(o):
+    """A row of nibbles t with unit scales: each 32-block's D_c = kv[t]*s_c
+    (s_c the q8_K's stored sum of the block's 32 codes), so
+    T = sum_c |kv[t]|*xs*|s_c| and Te = |kv[t]| * sum |xhat|. A pair of codes
+    +127/-127 on equal nibbles of one 32-block cancels: T = 0, y = 0,
+    Te = 2*127*|d*kv|. The same for Q4_0, with kv[t] replaced by t - 8."""
+    kv = _codebook_golden()
+    K = 512
+    x = wl.activations(1, K, wl.rng(79))
+    xq = o.quantize_q8k(x)
+    xh = o.dequant_q8k(xq, 1, K)[0]
+    sums = np.concatenate([_q8k_fields(xq[0, b])[1] for b in range(K // 256)])
+    xs = np.repeat(np.array([_q8k_fields(xq[0, b])[2] for b in range(K // 256)], np.float64), 8)
+    for fmt, val, gemv in (("iq4nl", lambda t: kv[t], o.gemv_iq4nl),
+                           ("q4_0", lambda t: t - 8, o.gemv_q4_0)):
+        for t in range(16):
+            row = _iq4nl_row(K, np.ones(K // 32), np.full(16 * (K // 32), t | (t << 4), np.uint8))
+            y, T, Te = gemv(row, xq, 1, K, elem=True)
+            v = abs(val(t))
+            tb = float((v * xs * np.abs(sums)).sum())
+            te = float(v * np.abs(xh).sum())
+            assert abs(T[0] - tb) <= 1e-12 * te and abs(Te[0] - te) <= 1e-12 * te, (fmt, t)
+        scales = np.full(K // 32, 0.5)
+        pay = np.full(16 * (K // 32), 3 | (12 << 4), np.uint8)
+        row = _iq4nl_row(K, scales, pay)
+        xc = np.zeros((1, K), np.float32)
+        xc[0, 33] = 127.0                   # block 1, low nibble 3
+        xc[0, 40] = -127.0                  # block 1, low nibble 3
+        y, T, Te = gemv(row, o.quantize_q8k(xc), 1, K, elem=True)
+        assert y[0] == 0.0 and T[0] == 0.0, (fmt, y, T)
+        assert Te[0] == 2 * 127.0 * 0.5 * abs(val(3)), (fmt, Te)
+
+
 def pin_q4k_gemm_rows(o):
     """Each output of the small-M product equals the mat-vec of that token's
     activation row, and sampled pairs equal the full product."""
     M_, N, K = 3, 5, 512
     w, x = _rand_q4k_case(43, N, K, R=M_)
     xq = o.quantize_q8k(x)
-    Y, T = o.gemm_q4k(w, xq, M_, N, K)
+    Y, T, Te = o.gemm_q4k(w, xq, M_, N, K, elem=True)
     for m in range(M_):
-        y, t = o.gemv_q4k(w, xq[m], N, K)
-        assert np.array_equal(Y[m], y) and np.array_equal(T[m], t)
+        y, t, te = o.gemv_q4k(w, xq[m], N, K, elem=True)
+        assert np.array_equal(Y[m], y) and np.array_equal(T[m], t) and np.array_equal(Te[m], te)
     ms = np.array([2, 0, 1, 2])
     ns = np.array([4, 0, 3, 1])
     Ys, _ = o.gemm_q4k(w, xq, M_, N, K, ms, ns)

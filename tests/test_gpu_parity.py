@@ -9,10 +9,16 @@ section Comparing against it, and "25 — Writing XPU Kernels", section 25.7):
     against an activation whose only nonzero block has scale 1 make each
     output equal one block's S (or -M) exactly.
   * f32 outputs: |y - y_oracle| <= 1e-5 * T per output, T the sum of the
-    magnitudes of the products that make it up; T = 0 demands y = 0.
+    magnitudes of the terms the integer route adds for it: |d*xs*S| +
+    |dmin*xs*M| per Q4_K block, |d_c*xs*D_c| per IQ4_NL or Q4_0 32-block.
+    T = 0 demands y = 0. The largest |y - y_oracle| / T of each test is
+    recorded (HEADROOM) and, when XQ_HEADROOM_OUT names a file, written
+    there at the end of the session.
   * No NaN, and outputs written in full: every output buffer is poisoned with
     0xFF bytes first, and a canary tail past its end must stay untouched.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -65,9 +71,23 @@ def take_u8(buf: torch.Tensor, n: int) -> np.ndarray:
     return buf[:n].cpu().numpy()
 
 
+# Largest |y - y_oracle| / T seen per test (the bar's headroom).
+HEADROOM = {}
+
+
+def _record_headroom(err: np.ndarray, T: np.ndarray):
+    pos = T > 0
+    if not pos.any():
+        return
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    r = float((err[pos] / T[pos]).max())
+    HEADROOM[test] = max(HEADROOM.get(test, 0.0), r)
+
+
 def assert_close(y: np.ndarray, ref: np.ndarray, T: np.ndarray, what: str):
     assert not np.isnan(y).any(), "%s: %d NaN outputs" % (what, int(np.isnan(y).sum()))
     err = np.abs(y - ref)
+    _record_headroom(err, T)
     bad = err > REL * T
     assert not bad.any(), "%s: %d outputs outside 1e-5*T, first at %d: gpu %r oracle %r T %r" % (
         what, int(bad.sum()), int(np.argmax(bad)), y[bad][0], ref[bad][0], T[bad][0])

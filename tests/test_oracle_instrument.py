@@ -16,6 +16,9 @@ FAULTS = {
     "XQO_FAULT_SCALE_HIBITS": "pin_q4k_pack_roundtrip",
     "XQO_FAULT_IQ4_HALVES": "pin_iq4nl_layout",
     "XQO_FAULT_Q40_OFFSET": "pin_q4_0_layout",
+    "XQO_FAULT_T_DOUBLE": "pin_q4k_magnitudes_one_hot",
+    "XQO_FAULT_TB_SUBBLOCK": "pin_q4k_magnitudes_cancel",
+    "XQO_FAULT_TB_IQ4_ELEM": "pin_iq4nl_magnitudes",
 }
 
 
