@@ -10,13 +10,20 @@ the L2s, so the bytes come from HBM.
 
 Printed (one JSON line on stdout):
   value          weight bytes of a step (2 x 33,030,144) / step time, in GB/s
-  roofline       for the dominant kernel (the 14336 x 4096 up mat-vec):
-                 algorithmic bytes per launch / its mean duration (1000
-                 back-to-back launches on the step's stream, weights rotating,
-                 one HIP event pair around them, after WARM_MS of the same
-                 launches), against the 8 TB/s HBM peak;
+  roofline       for the metric's kernel (the 14336 x 4096 up mat-vec):
+                 algorithmic bytes per launch / its mean duration (the median
+                 of interleaved rounds of 500 back-to-back launches on the
+                 step's stream, weights rotating, after WARM_MS of the same
+                 launches), against the 8 TB/s HBM peak; beside it, its
+                 weight rate against the 2 GiB streaming read (the 75% bar)
+                 and against the streaming read of the same 33 MB;
                  traffic from the committed rocprofv3 counter summary when it
                  matches the current kernel source
+  roofline_down  the same for the 4096 x 14336 down mat-vec
+  configs        every workload config timed once on this machine: the tiny and
+                 4096 x 4096 Q4_K mat-vecs, the IQ4_NL 4096 x 4096 and
+                 128256 x 4096 mat-vecs, the 512-token prefill product, and
+                 the streaming read's fixed-cost fit t = b + bytes / rate
   cpu_baseline   the oracle on the host's cores over whole FFN pairs
   stream_read    the streaming-read ceiling measured by the library's probe
 """
@@ -331,11 +338,13 @@ def main():
 
     # ---- the same step in three launches: the up mat-vec quantizes its own
     # output (xq_gemv_q4k_q8k, the fused tail), beside the plain figure.
+    ws_tail = _workspace(torch, dev, xq.xq_gemv_q4k_q8k_workspace_bytes(UP[0]))
+
     def step_fused(i, s=s):
         k = i % pool
         L.xq_quantize_q8k(xq1.data_ptr(), x_d.data_ptr(), 1, UP[1], s)
         L.xq_gemv_q4k_q8k(h.data_ptr(), xq2.data_ptr(), ups[k].data_ptr(), xq1.data_ptr(), UP[0],
-                          UP[1], s)
+                          UP[1], ws_tail.data_ptr(), ws_tail.numel(), s)
         L.xq_gemv_q4k(y.data_ptr(), dns[k].data_ptr(), xq2.data_ptr(), DOWN[0], DOWN[1], s)
 
     fused_us = _time_loop(torch, stream, step_fused, args.steps)
@@ -394,24 +403,56 @@ def main():
     stream_small_gbps = w_up.nbytes / us_small / 1e3
     log("streaming read, 33 MB cold: %.3f us, %.1f GB/s" % (us_small, stream_small_gbps))
 
-    # ---- roofline of the up mat-vec ----
-    up_alg_bytes = w_up.nbytes + xq.xq_q8k_bytes(1, UP[1]) + 4 * UP[0]
-    achieved = up_alg_bytes / (kern_us["gemv_up"] * 1e-6) / 1e9
-    traffic, traffic_note = traffic_from_profile(HEADLINE)
-    roofline = {
-        "bound": "hbm",
-        "kernel": "gemv_q4k 14336x4096",
-        "achieved": round(achieved, 1),
-        "peak": HBM_PEAK_GBPS,
-        "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBPS, 4),
-        "traffic": traffic,
-        "traffic_note": traffic_note,
-        "alg_bytes_per_launch": up_alg_bytes,
-        "mean_launch_us": round(kern_us["gemv_up"], 3),
-        "frac_of_stream_read": round(achieved / stream_gbps, 4),
-        "frac_of_stream_read_same_size": round(achieved / stream_small_gbps, 4),
+    # The down mat-vec (the step's longest kernel) the same way, over its own
+    # pool, against the streaming read of its 33 MB.
+    sink_d = torch.empty(xq.xq_bench_sink_words(w_dn.nbytes), dtype=torch.int32, device=dev)
+    kern_us["gemv_down"], us_small_dn = _abba(torch, stream, calls["gemv_down"],
+                                              lambda k: L.xq_bench_stream_read(
+        dns[k % pool].data_ptr(), w_dn.nbytes, sink_d.data_ptr(), s), 500)
+    log("down mat-vec %.3f us; streaming read of its 33 MB %.3f us" % (kern_us["gemv_down"],
+                                                                      us_small_dn))
+    # The quantize kernels' GPU time: 64 launches replayed from one HIP graph
+    # (an eager loop of them measures the host's launch rate instead).
+    quant_graph_us = {
+        "quantize_x": _graph_us(torch, lambda sc: L.xq_quantize_q8k(
+            xq1.data_ptr(), x_d.data_ptr(), 1, UP[1], sc)),
+        "quantize_h": _graph_us(torch, lambda sc: L.xq_quantize_q8k(
+            xq2.data_ptr(), h.data_ptr(), 1, DOWN[1], sc)),
     }
+    log("quantize, graph-replayed: %s" % quant_graph_us)
+
+    # ---- rooflines of the two mat-vecs (the metric's kernel is the up) ----
+    def matvec_roofline(name, counted, alg_bytes, us, us_read_same, weight_bytes):
+        achieved = alg_bytes / (us * 1e-6) / 1e9
+        traffic, note = traffic_from_profile(counted)
+        return {
+            "bound": "hbm",
+            "kernel": name,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "traffic_note": note,
+            "alg_bytes_per_launch": alg_bytes,
+            "mean_launch_us": round(us, 3),
+            # the 75% bar: weight bytes per second against the 2 GiB
+            # streaming read, and against the same-size read of the same pool
+            "frac_of_stream_read": round(weight_bytes / us / 1e3 / stream_gbps, 4),
+            "frac_of_stream_read_same_size": round(us_read_same / us, 4),
+            "stream_read_same_size_us": round(us_read_same, 3),
+        }
+
+    up_alg_bytes = w_up.nbytes + xq.xq_q8k_bytes(1, UP[1]) + 4 * UP[0]
+    dn_alg_bytes = w_dn.nbytes + xq.xq_q8k_bytes(1, DOWN[1]) + 4 * DOWN[0]
+    roofline = matvec_roofline("gemv_q4k 14336x4096", HEADLINE, up_alg_bytes, kern_us["gemv_up"],
+                               us_small, w_up.nbytes)
+    roofline_down = matvec_roofline("gemv_q4k 4096x14336", "gemv_q4k_down_4096x14336",
+                                    dn_alg_bytes, kern_us["gemv_down"], us_small_dn, w_dn.nbytes)
+
+    # ---- every workload config, each timed once on this machine ----
+    del sink_s, sink_d
+    configs = config_block(args, torch, xq, wl, dev, stream, stream_gbps)
 
     # ---- CPU baseline: the oracle over whole FFN pairs ----
     cpu = cpu_all = None
@@ -448,8 +489,18 @@ def main():
             "step": "quantize x, up mat-vec, quantize h, down mat-vec",
         },
         "roofline": roofline,
+        "roofline_down": roofline_down,
         "cpu_baseline": cpu,
-        "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "configs": configs,
+        # mat-vecs: mean of back-to-back launches on the step's stream (GPU
+        # time, launches overlap their gaps); quantize: GPU time per launch
+        # replayed from a HIP graph, beside the eager loop's launch interval
+        "kernels_us": {"gemv_up": round(kern_us["gemv_up"], 3),
+                       "gemv_down": round(kern_us["gemv_down"], 3),
+                       "quantize_x_graph": round(quant_graph_us["quantize_x"], 3),
+                       "quantize_h_graph": round(quant_graph_us["quantize_h"], 3)},
+        "launch_interval_us": {"quantize_x": round(kern_us["quantize_x"], 3),
+                               "quantize_h": round(kern_us["quantize_h"], 3)},
         "stream_read_GBps": round(stream_gbps, 1),
         "stream_read_33MB_GBps": round(stream_small_gbps, 1),
         "frac_of_stream_read": round(value / stream_gbps, 4),
@@ -626,10 +677,11 @@ def counters_run(torch, xq, L, dev, stream, ups, dns, xq1, xq2, h, y, x_d, pool)
     xqm = torch.empty(xq.xq_q8k_bytes(M, UP[1]), dtype=torch.uint8, device=dev)
     L.xq_quantize_q8k(xqm.data_ptr(), xm.data_ptr(), M, UP[1], s)
     ym = torch.empty(M * UP[0], dtype=torch.float32, device=dev)
+    wsm = _workspace(torch, dev, xq.xq_gemm_q4k_small_m_workspace_bytes(M, UP[0], UP[1]))
     torch.cuda.synchronize()
     for i in range(4):
         L.xq_gemm_q4k_small_m(ym.data_ptr(), ups[(i + 11) % pool].data_ptr(), xqm.data_ptr(), M,
-                              UP[0], UP[1], s)
+                              UP[0], UP[1], wsm.data_ptr(), wsm.numel(), s)
     torch.cuda.synchronize()
     n = 64 << 20
     a = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -643,6 +695,169 @@ def counters_run(torch, xq, L, dev, stream, ups, dns, xq1, xq2, h, y, x_d, pool)
         L.xq_bench_stream_read(a.data_ptr(), n, sink.data_ptr(), s)
     torch.cuda.synchronize()
     log("counters run done")
+
+
+def _graph_us(torch, launch, n=64, reps=30):
+    """GPU time per launch: n launches of launch(stream_handle) captured in
+    one HIP graph on a side stream, replayed reps times after one checked
+    replay (one event pair around the replays)."""
+    launch(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    cs = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs, capture_error_mode="thread_local"):
+        sc = torch.cuda.current_stream().cuda_stream
+        for _ in range(n):
+            launch(sc)
+    g.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (reps * n) * 1e3
+
+
+def _matvec_entry(torch, xq, L, dev, stream, stream_gbps, call, pool, wbytes, alg_bytes, n):
+    """A mat-vec timed over its rotating weight pool against the streaming
+    read of the same bytes over the same pool, in interleaved ABBA rounds
+    (medians): us per launch, weight GB/s, the algorithmic-bytes roofline
+    fraction of 8 TB/s, and its fractions of the 2 GiB and the same-size
+    streaming reads."""
+    s = stream.cuda_stream
+    sink = torch.empty(xq.xq_bench_sink_words(wbytes), dtype=torch.int32, device=dev)
+    us, sus = _abba(torch, stream, call, lambda i: L.xq_bench_stream_read(
+        pool[i % len(pool)].data_ptr(), wbytes, sink.data_ptr(), s), n)
+    return {"us": round(us, 3), "weight_GBps": round(wbytes / us / 1e3, 1),
+            "alg_GBps": round(alg_bytes / us / 1e3, 1),
+            "frac_of_8TBps": round(alg_bytes / us / 1e3 / HBM_PEAK_GBPS, 4),
+            "frac_of_stream_read": round(wbytes / us / 1e3 / stream_gbps, 4),
+            "stream_read_same_size_us": round(sus, 3),
+            "frac_of_stream_read_same_size": round(sus / us, 4)}
+
+
+def _stream_fit(torch, xq, L, dev, stream, pool_mb):
+    """The streaming read over sizes, each cold (windows rotating through a
+    pool past the caches), and the fit t = b + bytes / rate that splits a
+    launch's fixed cost from the rate ("25 — Writing XPU Kernels", section
+    25.2: a bytes-per-second figure hides a fixed cost)."""
+    s = stream.cuda_stream
+    pool_bytes = (pool_mb * 1000 * 1000) // 4096 * 4096
+    big = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
+    big.fill_(1)
+    pts = []
+    for sz, n in ((9437184, 1000), (33030144, 1000), (132120576, 300), (295501824, 100),
+                  (1 << 30, 30)):
+        nwin = max(1, pool_bytes // sz)
+        sink = torch.empty(xq.xq_bench_sink_words(sz), dtype=torch.int32, device=dev)
+        us = _time_loop(torch, stream, lambda i: L.xq_bench_stream_read(
+            big.data_ptr() + (i % nwin) * sz, sz, sink.data_ptr(), s), n)
+        pts.append((sz, us))
+    del big
+    torch.cuda.empty_cache()
+    A = np.array([[1.0, b] for b, _ in pts])
+    coef, *_ = np.linalg.lstsq(A, np.array([u for _, u in pts]), rcond=None)
+    return {"points": [{"bytes": b, "us": round(u, 3), "GBps": round(b / u / 1e3, 1)}
+                       for b, u in pts],
+            "fit_fixed_us": round(float(coef[0]), 3),
+            "fit_rate_GBps": round(1e-3 / float(coef[1]), 1),
+            "windows": "rotating over %d MB" % (pool_bytes // 1000000)}
+
+
+def config_block(args, torch, xq, wl, dev, stream, stream_gbps):
+    """Every workload config on this machine, compactly: the tiny Q4_K mat-vec
+    (launch-bound, us only), the 4096x4096 Q4_K mat-vec, the IQ4_NL 4096x4096
+    and 128256x4096 mat-vecs (each against the 8 TB/s peak and the streaming
+    reads), the 512-token prefill product (TOPS against the int8 peak), and
+    the streaming read's fixed-cost fit. Weights are cold (rotating pools);
+    the FFN pair itself is the headline and its two rooflines."""
+    L = xq.lib()
+    s = stream.cuda_stream
+    out = {}
+    t0 = time.perf_counter()
+
+    def q4k_case(N, K, seed):
+        g = wl.rng(seed)
+        w = torch.from_numpy(wl.q4k_weights(N, K, g).reshape(-1)).to(dev)
+        xv = torch.from_numpy(wl.activations(1, K, g).reshape(-1)).to(dev)
+        return w, xv
+
+    # c0: 256 x 1024, 147 KB of weights: launch-bound, no roofline claim.
+    N, K = 256, 1024
+    w, xv = q4k_case(N, K, wl.SEEDS["q4k_tiny"])
+    xqb = torch.empty(xq.xq_q8k_bytes(1, K), dtype=torch.uint8, device=dev)
+    xq.xq_quantize_q8k(xqb, xv, 1, K)
+    pool = _pool_copies(w, 64)
+    yy = torch.empty(N, dtype=torch.float32, device=dev)
+    us = _time_loop(torch, stream, lambda i: L.xq_gemv_q4k(
+        yy.data_ptr(), pool[i % len(pool)].data_ptr(), xqb.data_ptr(), N, K, s), 2000)
+    out["c0_q4k_256x1024"] = {"us": round(us, 3), "bound": "launch"}
+    del pool, w
+
+    # c1: 4096 x 4096 Q4_K.
+    N, K = 4096, 4096
+    w, xv = q4k_case(N, K, wl.SEEDS["q4k_4096"])
+    xqb = torch.empty(xq.xq_q8k_bytes(1, K), dtype=torch.uint8, device=dev)
+    xq.xq_quantize_q8k(xqb, xv, 1, K)
+    pool = _pool_copies(w, args.pool_mb)
+    yy = torch.empty(N, dtype=torch.float32, device=dev)
+    out["c1_q4k_4096x4096"] = _matvec_entry(
+        torch, xq, L, dev, stream, stream_gbps, lambda i: L.xq_gemv_q4k(
+            yy.data_ptr(), pool[i % len(pool)].data_ptr(), xqb.data_ptr(), N, K, s),
+        pool, w.numel(), w.numel() + xq.xq_q8k_bytes(1, K) + 4 * N, 1000)
+    del pool, w
+    torch.cuda.empty_cache()
+
+    # c3: IQ4_NL 4096 x 4096 and the 128256 x 4096 head.
+    for key, (N, K), seed, n in (("c3_iq4nl_4096x4096", (4096, 4096), wl.SEEDS["iq4nl_4096"], 1000),
+                                 ("c3_iq4nl_128256x4096", (128256, 4096), wl.SEEDS["iq4nl_head"],
+                                  100)):
+        g = wl.rng(seed)
+        w = torch.from_numpy(wl.iq4nl_weights(N, K, g).reshape(-1)).to(dev)
+        xv = torch.from_numpy(wl.activations(1, K, g).reshape(-1)).to(dev)
+        xqb = torch.empty(xq.xq_q8k_bytes(1, K), dtype=torch.uint8, device=dev)
+        xq.xq_quantize_q8k(xqb, xv, 1, K)
+        pool = _pool_copies(w, args.pool_mb)
+        yy = torch.empty(N, dtype=torch.float32, device=dev)
+        out[key] = _matvec_entry(
+            torch, xq, L, dev, stream, stream_gbps, lambda i: L.xq_gemv_iq4nl(
+                yy.data_ptr(), pool[i % len(pool)].data_ptr(), xqb.data_ptr(), N, K, s),
+            pool, w.numel(), w.numel() + xq.xq_q8k_bytes(1, K) + 4 * N, n)
+        del pool, w
+        torch.cuda.empty_cache()
+
+    # c4: the 512-token prefill product on int8 MFMA.
+    M, (N, K) = 512, UP
+    g = wl.rng(wl.SEEDS["prefill"])
+    w = torch.from_numpy(wl.q4k_weights(N, K, g).reshape(-1)).to(dev)
+    xv = torch.from_numpy(wl.activations(M, K, g).reshape(-1)).to(dev)
+    xqb = torch.empty(xq.xq_q8k_bytes(M, K), dtype=torch.uint8, device=dev)
+    xq.xq_quantize_q8k(xqb, xv, M, K)
+    yy = torch.empty(M * N, dtype=torch.float32, device=dev)
+    pool = _pool_copies(w, args.pool_mb)
+    wsp = _workspace(torch, dev, xq.xq_gemm_q4k_small_m_workspace_bytes(M, N, K))
+    us = _time_loop(torch, stream, lambda i: L.xq_gemm_q4k_small_m(
+        yy.data_ptr(), pool[i % len(pool)].data_ptr(), xqb.data_ptr(), M, N, K, wsp.data_ptr(),
+        wsp.numel(), s), 200)
+    ops = 2.0 * M * N * K
+    out["c4_prefill_q4k_512x14336x4096"] = {
+        "us": round(us, 3), "TOPS": round(ops / us / 1e6, 1),
+        "frac_of_int8_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS, 4), "bound": "mfma"}
+    del pool, w, yy
+    torch.cuda.empty_cache()
+
+    out["stream_read_fit"] = _stream_fit(torch, xq, L, dev, stream, args.pool_mb)
+    log("configs (%.1f s): %s" % (time.perf_counter() - t0, json.dumps(out)))
+    return out
+
+
+def _workspace(torch, dev, nbytes):
+    """A caller-owned workspace for the library, zeroed before first use (at
+    least 256 bytes, so a call that needs none still gets a valid pointer)."""
+    return torch.zeros(max(256, nbytes), dtype=torch.uint8, device=dev)
 
 
 def _pool_copies(t, pool_mb):
@@ -721,26 +936,11 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
               "stream_read_same_size_us": round(sus, 3),
               "frac_of_stream_read_same_size": round(sus / us, 4)})
 
-    # The streaming read itself over sizes, each cold (windows rotate through
-    # a pool past the caches), and the fit t = b + bytes / rate that splits
-    # the fixed cost of a launch from the rate.
+    # The streaming read itself over sizes, and its fixed-cost fit.
+    emit({"workload": "stream_read_sizes", **_stream_fit(torch, xq, L, dev, stream, args.pool_mb)})
     pool_bytes = (args.pool_mb * 1000 * 1000) // 4096 * 4096
     big = torch.empty(pool_bytes, dtype=torch.uint8, device=dev)
     big.fill_(1)
-    pts = []
-    for sz, n in ((9437184, 1000), (33030144, 1000), (132120576, 300), (295501824, 100),
-                  (1 << 30, 30)):
-        nwin = max(1, pool_bytes // sz)
-        sink = torch.empty(xq.xq_bench_sink_words(sz), dtype=torch.int32, device=dev)
-        us = _time_loop(torch, stream, lambda i: L.xq_bench_stream_read(
-            big.data_ptr() + (i % nwin) * sz, sz, sink.data_ptr(), s), n)
-        pts.append((sz, us))
-    A = np.array([[1.0, b] for b, _ in pts])
-    coef, *_ = np.linalg.lstsq(A, np.array([u for _, u in pts]), rcond=None)
-    emit({"workload": "stream_read_sizes", "points": [
-        {"bytes": b, "us": round(u, 3), "GBps": round(b / u / 1e3, 1)} for b, u in pts],
-        "fit_fixed_us": round(float(coef[0]), 3), "fit_rate_GBps": round(1e-3 / float(coef[1]), 1),
-        "windows": "rotating over %d MB" % (pool_bytes // 1000000)})
     # A plain device-to-device copy of up to 1 GiB (torch's copy_, read + write).
     cb = min(1 << 30, pool_bytes)
     dst = torch.empty(cb, dtype=torch.uint8, device=dev)
@@ -864,8 +1064,10 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
         xqb.data_ptr(), xv.data_ptr(), M, K, s), 200)
     yy = torch.empty(M * N, dtype=torch.float32, device=dev)
     ws = _pool_copies(w, args.pool_mb)
+    wsp = _workspace(torch, dev, xq.xq_gemm_q4k_small_m_workspace_bytes(M, N, K))
     us = _time_loop(torch, stream, lambda i: L.xq_gemm_q4k_small_m(
-        yy.data_ptr(), ws[i % len(ws)].data_ptr(), xqb.data_ptr(), M, N, K, s), 200)
+        yy.data_ptr(), ws[i % len(ws)].data_ptr(), xqb.data_ptr(), M, N, K, wsp.data_ptr(),
+        wsp.numel(), s), 200)
     ops = 2.0 * M * N * K
     emit({"workload": "prefill_q4k_512x14336x4096", "us": round(us, 3),
           "TOPS": round(ops / us / 1e6, 1),
@@ -894,8 +1096,10 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
         xq.xq_quantize_q8k(xqb, xv, M, K)
         yy = torch.empty(M * N, dtype=torch.float32, device=dev)
         ws = _pool_copies(w, args.pool_mb)
+        wsp = _workspace(torch, dev, xq.xq_gemm_q4k_small_m_workspace_bytes(M, N, K))
         us = _time_loop(torch, stream, lambda i: L.xq_gemm_q4k_small_m(
-            yy.data_ptr(), ws[i % len(ws)].data_ptr(), xqb.data_ptr(), M, N, K, s), 200)
+            yy.data_ptr(), ws[i % len(ws)].data_ptr(), xqb.data_ptr(), M, N, K, wsp.data_ptr(),
+            wsp.numel(), s), 200)
         ops = 2.0 * M * N * K
         emit({"workload": "gemm_q4k_%dx%dx%d" % (M, N, K), "us": round(us, 3),
               "TOPS": round(ops / us / 1e6, 1),
@@ -920,9 +1124,10 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
     ids = torch.from_numpy(ids_np).to(dev)
     slabs = _pool_copies(slab, args.pool_mb)
     yy = torch.empty(T * U * rows, dtype=torch.float32, device=dev)
+    wsr = _workspace(torch, dev, xq.xq_gemm_q4k_id_workspace_bytes(T, U, E))
     us = _time_loop(torch, stream, lambda i: L.xq_gemm_q4k_id(
         yy.data_ptr(), slabs[i % len(slabs)].data_ptr(), xqb.data_ptr(), ids.data_ptr(), T, U, E,
-        rows, K, 0, s), 200)
+        rows, K, 0, wsr.data_ptr(), wsr.numel(), s), 200)
     nb8, rb = xq.xq_q8k_bytes(1, K), xq.xq_q4k_bytes(rows, K)
     xr = xqb.view(T, nb8)
     per = []
@@ -932,10 +1137,14 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
             per.append((e, len(toks), xr[toks].contiguous(),
                         torch.empty(len(toks) * rows, dtype=torch.float32, device=dev)))
 
+    wse = _workspace(torch, dev, max(xq.xq_gemm_q4k_small_m_workspace_bytes(m, rows, K)
+                                     for _, m, _, _ in per))
+
     def dense_all(i):
         base = slabs[i % len(slabs)].data_ptr()
         for e, m, xe, ye in per:
-            L.xq_gemm_q4k_small_m(ye.data_ptr(), base + e * rb, xe.data_ptr(), m, rows, K, s)
+            L.xq_gemm_q4k_small_m(ye.data_ptr(), base + e * rb, xe.data_ptr(), m, rows, K,
+                                  wse.data_ptr(), wse.numel(), s)
 
     dus = _time_loop(torch, stream, dense_all, 50)
     ops = 2.0 * T * U * rows * K

@@ -8,13 +8,23 @@
  * synchronisation.
  *
  * Conventions shared by every entry point:
- *  - Pointers named as device buffers are device memory owned by the caller.
- *    The library keeps no per-call state and allocates nothing, except the
- *    device workspaces that three entry points document below (the split-K
- *    partials of xq_gemm_q4k_small_m, the arrival counters of
- *    xq_gemv_q4k_q8k, the expert map of xq_gemm_q4k_id): each is allocated
- *    on the first call on a stream that needs it and kept until the process
- *    ends.
+ *  - Pointers named as device buffers are device memory owned by the caller
+ *    ("cajeta.xpu — one kernel, any device", section 2.2: buffers are the
+ *    caller's allocations). The library allocates no memory and keeps no
+ *    per-call state; it never synchronizes a stream or the device.
+ *  - Three entry points need device scratch beyond their inputs and outputs
+ *    (xq_gemm_q4k_small_m's split-K partials and arrival counters,
+ *    xq_gemv_q4k_q8k's arrival counters, xq_gemm_q4k_id's expert map). The
+ *    caller passes it as `workspace` (device memory, 256-byte aligned) and
+ *    `workspace_bytes`; the matching *_workspace_bytes query gives the exact
+ *    bytes a call needs (0: none, and then workspace may be NULL). The caller
+ *    zeroes a workspace once before its first use; every call that completes
+ *    leaves it ready for the next (its arrival counters back at zero), so one
+ *    workspace serves any sequence of calls on one stream whose needs it
+ *    covers. Calls that may run at the same time (different streams) need
+ *    different workspaces. A NULL workspace where one is needed is refused
+ *    with XQ_E_NULL, a short one with XQ_E_SHAPE, a misaligned one with
+ *    XQ_E_ALIGN.
  *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
  *  - Outputs are fully overwritten, never accumulated into. Outputs must not
  *    alias inputs (documented, not checked).
@@ -109,17 +119,15 @@ xq_status xq_gemv_q4k(float *y, const void *w, const void *xq, int64_t N, int64_
  *  y   device, out: f32 [N], 16-byte aligned.
  *  yq  device, out: q8_K [N/256] blocks (xq_q8k_bytes(1, N)), 16-byte aligned.
  *  w, xq, K as xq_gemv_q4k.
- *  N a multiple of 256, 256 <= N <= 2^24.
- * The arrival counters live in a 256 KB workspace the library owns, one per
- * (device, stream): allocated, zeroed and synchronized on a stream's first
- * call, kept until the process ends (that first call cannot be captured into
- * a graph). The last arrival resets its counter, so they are zero between
- * calls; calls on one stream are ordered, calls on different streams use
- * different counters.
+ *  N a multiple of 256, 256 <= N <= 2^22.
+ *  workspace  the block counters: xq_gemv_q4k_q8k_workspace_bytes(N) bytes
+ *      (one 128-byte line per q8_K block of y), zeroed before first use; the
+ *      last arrival at a counter resets it.
  * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH.
  */
 xq_status xq_gemv_q4k_q8k(float *y, void *yq, const void *w, const void *xq, int64_t N, int64_t K,
-                          void *stream);
+                          void *workspace, size_t workspace_bytes, void *stream);
+size_t xq_gemv_q4k_q8k_workspace_bytes(int64_t N);  /* N/256 * 128; 0 if N is invalid */
 
 /*
  * IQ4_NL x q8_K decode mat-vec, batch 1 ("25 — Writing XPU Kernels", section
@@ -157,19 +165,19 @@ xq_status xq_gemv_iq4nl(float *y, const void *w, const void *xq, int64_t N, int6
  * Shapes with at most 256 tiles of 16 or 64 tokens x 128 rows split K over
  * several workgroups (section 25.3: fill the device first); shapes with more
  * tiles than one round of resident workgroups run whole rounds of whole
- * tiles and may split the last, short round's tiles the same way. The
- * partials go through a workspace the library owns, one per (device,
- * stream): 24 MiB allocated, zeroed and synchronized on the first such call
- * on a stream, kept until the process ends. That first call therefore
- * cannot be captured into a graph; later ones allocate nothing. Splits are
- * summed in a fixed order, so results are bit-identical from call to call.
- * Calls on one stream are ordered; calls on different streams use different
- * workspaces.
- * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH (also
- * when the workspace cannot be allocated).
+ * tiles and may split the last, short round's tiles the same way. Splits
+ * are summed in a fixed order, so results are bit-identical from call to
+ * call and do not depend on the workspace's address.
+ *  workspace  96 KiB of arrival counters (one 128-byte line per split tile,
+ *      at the same place for every shape), then the split partials:
+ *      xq_gemm_q4k_small_m_workspace_bytes(M, N, K) bytes, 0 when the shape
+ *      splits no tile (at most 16 MiB + 96 KiB for any shape), zeroed
+ *      before first use.
+ * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH.
  */
 xq_status xq_gemm_q4k_small_m(float *y, const void *w, const void *xq, int64_t M, int64_t N,
-                              int64_t K, void *stream);
+                              int64_t K, void *workspace, size_t workspace_bytes, void *stream);
+size_t xq_gemm_q4k_small_m_workspace_bytes(int64_t M, int64_t N, int64_t K);  /* 0 if none */
 
 /*
  * Grouped Q4_K x q8_K small-M product over an expert slab (mul_mat_id; "25 —
@@ -192,17 +200,19 @@ xq_status xq_gemm_q4k_small_m(float *y, const void *w, const void *xq, int64_t M
  *  K >= 256, a multiple of 256. One expert's weights and all of xq below
  *  2 GiB (32-bit offsets).
  * A first kernel groups the pairs by expert into tiles of at most 64 pairs
- * (an expert's remainder of at most 32 pairs into tiles of at most 16), in a
- * workspace the library owns (4.3 MB per (device, stream), allocated, zeroed
- * and synchronized on a stream's first call, kept until the process ends;
- * that first call cannot be captured into a graph). The product then runs
- * once over both lists. Every output is computed from its own pair alone,
- * so results do not depend on how pairs fall into tiles.
+ * (an expert's remainder of at most 32 pairs into tiles of at most 16); the
+ * product then runs once over both lists. Every output is computed from its
+ * own pair alone, so results do not depend on how pairs fall into tiles.
+ *  workspace  the expert map (tile descriptors, the pairs grouped by
+ *      expert, the tile counts): xq_gemm_q4k_id_workspace_bytes(n_tokens,
+ *      n_used, n_experts) bytes (at most 4.3 MB), rewritten by every call.
  * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH.
  */
 xq_status xq_gemm_q4k_id(float *y, const void *slab, const void *xq, const int32_t *ids,
                          int64_t n_tokens, int64_t n_used, int64_t n_experts, int64_t rows,
-                         int64_t K, int64_t x_per_slot, void *stream);
+                         int64_t K, int64_t x_per_slot, void *workspace, size_t workspace_bytes,
+                         void *stream);
+size_t xq_gemm_q4k_id_workspace_bytes(int64_t n_tokens, int64_t n_used, int64_t n_experts);
 
 /* Largest K the mat-vecs accept: the q8_K activation row is staged whole in
  * the workgroup's LDS (XQ_MAX_K/256 * 320 bytes = 60 KiB). */

@@ -7,6 +7,11 @@ call, the binding checks that every tensor is a device tensor large enough for
 the layout the C function will read or write, so a wrong-sized buffer is
 refused on the host instead of being read out of bounds. Every step of the
 computation runs in the library's HIP kernels; there is no host path.
+
+Three calls take a caller-owned device workspace (``workspace=``, a device
+tensor of at least the bytes the matching ``*_workspace_bytes`` query gives,
+zeroed before its first use); the binding passes it through and allocates
+nothing.
 """
 
 from __future__ import annotations
@@ -29,7 +34,8 @@ EXPORTS = (
     "xq_q8k_bytes", "xq_q4k_bytes", "xq_iq4nl_bytes", "xq_status_name", "xq_last_error",
     "xq_bench_stream_read", "xq_bench_sink_words", "xq_gemv_q4k_id", "xq_gemv_iq4nl_id",
     "xq_repack_iq4nl", "xq_repack_dword_prefix_launches", "xq_gemv_q4_0", "xq_gemm_q4k_id",
-    "xq_gemv_q4k_q8k",
+    "xq_gemv_q4k_q8k", "xq_gemm_q4k_small_m_workspace_bytes", "xq_gemv_q4k_q8k_workspace_bytes",
+    "xq_gemm_q4k_id_workspace_bytes",
 )
 
 
@@ -53,13 +59,20 @@ def lib() -> ctypes.CDLL:
             L.xq_gemv_q4k.argtypes = [P, P, P, I, I, P]
             L.xq_gemv_iq4nl.argtypes = [P, P, P, I, I, P]
             L.xq_gemv_q4_0.argtypes = [P, P, P, I, I, P]
-            L.xq_gemm_q4k_small_m.argtypes = [P, P, P, I, I, I, P]
+            Z = ctypes.c_size_t
+            L.xq_gemm_q4k_small_m.argtypes = [P, P, P, I, I, I, P, Z, P]
             L.xq_bench_stream_read.argtypes = [P, I, P, P]
             L.xq_gemv_q4k_id.argtypes = [P, P, P, P, I, I, I, I, I, P]
             L.xq_gemv_iq4nl_id.argtypes = [P, P, P, P, I, I, I, I, I, P]
             L.xq_repack_iq4nl.argtypes = [P, P, I, I, I, P]
-            L.xq_gemm_q4k_id.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
-            L.xq_gemv_q4k_q8k.argtypes = [P, P, P, P, I, I, P]
+            L.xq_gemm_q4k_id.argtypes = [P, P, P, P, I, I, I, I, I, I, P, Z, P]
+            L.xq_gemv_q4k_q8k.argtypes = [P, P, P, P, I, I, P, Z, P]
+            L.xq_gemm_q4k_small_m_workspace_bytes.argtypes = [I, I, I]
+            L.xq_gemm_q4k_small_m_workspace_bytes.restype = Z
+            L.xq_gemv_q4k_q8k_workspace_bytes.argtypes = [I]
+            L.xq_gemv_q4k_q8k_workspace_bytes.restype = Z
+            L.xq_gemm_q4k_id_workspace_bytes.argtypes = [I, I, I]
+            L.xq_gemm_q4k_id_workspace_bytes.restype = Z
             L.xq_repack_dword_prefix_launches.argtypes = []
             L.xq_repack_dword_prefix_launches.restype = I
             for f in ("xq_quantize_q8k", "xq_gemv_q4k", "xq_gemv_iq4nl", "xq_gemm_q4k_small_m",
@@ -99,6 +112,15 @@ def _ptr(a, need_bytes: int, what: str):
     if have < need_bytes:
         raise ValueError("%s: holds %d bytes, the layout needs %d" % (what, have, need_bytes))
     return a.data_ptr()
+
+
+def _workspace(ws, need: int):
+    """(pointer, bytes) of a workspace tensor checked to hold `need` bytes;
+    (None, 0) for None (the library refuses it when the call needs one)."""
+    if ws is None:
+        return None, 0
+    p = _ptr(ws, need, "workspace")
+    return p, (ws.numel() * ws.element_size() if isinstance(ws, torch.Tensor) else need)
 
 
 def _stream(stream):
@@ -152,10 +174,15 @@ def xq_gemv_iq4nl(y, w, xq, N: int, K: int, stream=None) -> None:
            "xq_gemv_iq4nl")
 
 
-def xq_gemv_q4k_q8k(y, yq, w, xq, N: int, K: int, stream=None) -> None:
+def xq_gemv_q4k_q8k_workspace_bytes(N: int) -> int:
+    return lib().xq_gemv_q4k_q8k_workspace_bytes(N)
+
+
+def xq_gemv_q4k_q8k(y, yq, w, xq, N: int, K: int, workspace=None, stream=None) -> None:
+    wp, wb = _workspace(workspace, xq_gemv_q4k_q8k_workspace_bytes(N))
     _check(lib().xq_gemv_q4k_q8k(_ptr(y, 4 * N, "y"), _ptr(yq, xq_q8k_bytes(1, N), "yq"),
                                  _ptr(w, xq_q4k_bytes(N, K), "w"), _ptr(xq, xq_q8k_bytes(1, K), "xq"),
-                                 N, K, _stream(stream)),
+                                 N, K, wp, wb, _stream(stream)),
            "xq_gemv_q4k_q8k")
 
 
@@ -204,21 +231,31 @@ def iq4nl_row_bytes(bpr: int) -> int:
     return ((2 * bpr + 3) // 4) * 4 + 16 * bpr
 
 
-def xq_gemm_q4k_small_m(y, w, xq, M: int, N: int, K: int, stream=None) -> None:
+def xq_gemm_q4k_small_m_workspace_bytes(M: int, N: int, K: int) -> int:
+    return lib().xq_gemm_q4k_small_m_workspace_bytes(M, N, K)
+
+
+def xq_gemm_q4k_small_m(y, w, xq, M: int, N: int, K: int, workspace=None, stream=None) -> None:
+    wp, wb = _workspace(workspace, xq_gemm_q4k_small_m_workspace_bytes(M, N, K))
     _check(lib().xq_gemm_q4k_small_m(_ptr(y, 4 * M * N, "y"), _ptr(w, xq_q4k_bytes(N, K), "w"),
-                                     _ptr(xq, xq_q8k_bytes(M, K), "xq"), M, N, K,
+                                     _ptr(xq, xq_q8k_bytes(M, K), "xq"), M, N, K, wp, wb,
                                      _stream(stream)),
            "xq_gemm_q4k_small_m")
 
 
+def xq_gemm_q4k_id_workspace_bytes(n_tokens: int, n_used: int, n_experts: int) -> int:
+    return lib().xq_gemm_q4k_id_workspace_bytes(n_tokens, n_used, n_experts)
+
+
 def xq_gemm_q4k_id(y, slab, xq, ids, n_tokens: int, n_used: int, n_experts: int, rows: int,
-                   K: int, x_per_slot: int = 0, stream=None) -> None:
+                   K: int, x_per_slot: int = 0, workspace=None, stream=None) -> None:
     pairs = n_tokens * n_used
     xrows = pairs if x_per_slot else n_tokens
+    wp, wb = _workspace(workspace, xq_gemm_q4k_id_workspace_bytes(n_tokens, n_used, n_experts))
     _check(lib().xq_gemm_q4k_id(_ptr(y, 4 * pairs * rows, "y"),
                                 _ptr(slab, xq_q4k_bytes(n_experts * rows, K), "slab"),
                                 _ptr(xq, xq_q8k_bytes(xrows, K), "xq"), _ptr(ids, 4 * pairs, "ids"),
-                                n_tokens, n_used, n_experts, rows, K, x_per_slot,
+                                n_tokens, n_used, n_experts, rows, K, x_per_slot, wp, wb,
                                 _stream(stream)),
            "xq_gemm_q4k_id")
 

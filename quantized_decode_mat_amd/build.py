@@ -31,7 +31,6 @@ SOURCES = [
     "repack_iq4nl.hip",
     "route_experts.hip",
     "stream_read.hip",
-    "workspace.cpp",
     "xq_api.cpp",
 ]
 
@@ -47,11 +46,19 @@ FLAGS = [
 ]
 
 
+def _jobs() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(8, n, int(os.environ.get("MAX_JOBS", "8"))))
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libxq.so; returns its path."""
+    """Compile every source (in parallel) and link libxq.so; returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
     with tempfile.TemporaryDirectory(prefix="xq_build_") as tmp:
-        objs = []
-        for src in SOURCES:
+        def compile_one(src):
             obj = os.path.join(tmp, src + ".o")
             cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
             if src.endswith(".hip"):
@@ -59,6 +66,11 @@ def build(verbose: bool = False) -> str:
             if verbose:
                 print(" ".join(cmd), flush=True)
             r = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
+            return src, obj, r
+        with ThreadPoolExecutor(max_workers=_jobs()) as pool:
+            results = list(pool.map(compile_one, SOURCES))
+        objs = []
+        for src, obj, r in results:
             if r.returncode != 0:
                 sys.stderr.write(r.stderr)
                 raise RuntimeError("hipcc failed on %s" % src)

@@ -17,13 +17,15 @@
 // S is exact int32 (|S| <= 30.7M per block); f32 appears only in the
 // per-block epilogue xs * d * S.
 //
-// The min term sum_b xs_mb * dmin_nb * M_mnb = sum_(b,j) (xs_mb * s_mbj) *
-// (dmin_nb * m_nbj), with s_mbj the q8_K's stored sub-block sums, is a
-// contraction over the 8 sub-blocks of every block with the block scales
-// inside the operands, so it runs on f32 MFMA (v_mfma_f32_16x16x4f32) into
-// an accumulator that spans all blocks and is subtracted once at the end: no
-// min plane on the int8 MFMA and no min term in the per-block epilogue. Its
-// products are exact when the scales are 1 (isolation: y = -M exactly).
+// The min term's integer M_mnb = sum_j m_nbj * s_mbj, with s_mbj the q8_K's
+// stored sub-block sums, is a contraction over the block's 8 sub-blocks. It
+// runs on f32 MFMA (v_mfma_f32_16x16x4f32) with the integers themselves as
+// operands: |m * s| <= 63 * 4064 and |M| <= 2.05M < 2^24, so every product
+// and partial sum is an exact f32 integer and M comes out exact, whatever
+// the order. The block's float pass then applies both scales at once,
+// xs * (d * S - dmin * M), like the mat-vec: the per-block terms are exact
+// integers scaled once, so the f32 error stays a few units of 2^-24 of
+// |d*xs*S| + |dmin*xs*M| per block (no min plane on the int8 MFMA).
 //
 // Tile: 64 tokens x 128 weight rows per 256-thread workgroup, four waves side
 // by side along the rows, each wave 64 x 32 = 4 x 2 MFMA tiles of 16 x 16, so
@@ -43,9 +45,10 @@
 // arrival order. With more tiles than whole rounds of resident workgroups,
 // the same launch runs the whole rounds of whole tiles and may split the
 // short remainder the same way (gemm_q4k_plan). Partials
-// and counters cross XCDs through agent-scope atomic loads and stores
-// (coherent without an L2 write-back); the last arrival resets the counter,
-// so counters are zero between launches.
+// and counters live in the caller's workspace and cross XCDs through
+// agent-scope atomic loads and stores (coherent without an L2 write-back);
+// the last arrival resets the counter, so counters are zero again between
+// launches (the caller zeroes a workspace once, before its first use).
 //
 // Short batches (M = 1, or up to the LDS token cap while M <= 3, or 8 on
 // matrices of at most 2^25 weights) skip the MFMA tile: they are a weight
@@ -333,16 +336,13 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
 
   typedef float v4f __attribute__((ext_vector_type(4)));
   v4i sa[MT][2], sb[MT][2];
-  v4f cm[MT][2];   // min term: sum_b xs * dmin * M_b, on f32 MFMA over sub-blocks
   float4 acc[MT][2];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      acc[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      cm[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-    }
+    for (int j = 0; j < 2; ++j) acc[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
   const v4i zero = {0, 0, 0, 0};
+  const v4f zerof = {0.f, 0.f, 0.f, 0.f};
 
   const StageOffsets<BMv> so = stage_offsets<BMv, ID>(M, N, nb, m0, n0, wave, lane, xrow_s);
   issue_stage<BMv>(stage0, xq, w, so, b_lo, wave, lane);
@@ -378,10 +378,10 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
     const uint8_t* wblk = stg + TL::kWOff;
 
     // ---- this lane's weight rows: the sub-block scale of each (row, group)
-    // for this lane's k-quarter, the block's d, and the min operands
-    // dmin * m_j for j = q and 4 + q ----
+    // for this lane's k-quarter, the block's d and dmin, and the min
+    // operands m_j for j = q and 4 + q ----
     uint32_t scj[2][4];
-    float dn[2], mb[2][2];
+    float dn[2], dmn[2], mf[2][2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const uint8_t* blk = wblk + (32 * wave + 16 * nt + l16) * kQ4KBytes;
@@ -397,21 +397,23 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
         scj[nt][g] = (((g < 2) ? sc_lo : sc_hi) >> shift) & 0xFFu;
       }
       dn[nt] = half_bits_to_float(hdr.x & 0xFFFFu);
-      const float dmin = half_bits_to_float(hdr.x >> 16);
-      mb[nt][0] = dmin * static_cast<float>((m_lo >> (8 * q)) & 0xFFu);
-      mb[nt][1] = dmin * static_cast<float>((m_hi >> (8 * q)) & 0xFFu);
+      dmn[nt] = half_bits_to_float(hdr.x >> 16);
+      mf[nt][0] = static_cast<float>((m_lo >> (8 * q)) & 0xFFu);
+      mf[nt][1] = static_cast<float>((m_hi >> (8 * q)) & 0xFFu);
     }
-    // ---- min term: A' = xs * s_j (token m = 16mt + l16, j = 4ks + q) ----
+    // ---- this block's M = sum_j m_j * s_j, exact (A = s_j of token
+    // m = 16mt + l16, B = m_j of row n, j = 4ks + q) ----
+    v4f cm[MT][2];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int r = 16 * mt + l16;
-      const float xr = xs_s[r];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const float ma = xr * static_cast<float>(sum_s[8 * r + 4 * ks + q]);
+        const float ma = static_cast<float>(sum_s[8 * r + 4 * ks + q]);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
-          cm[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ma, mb[nt][ks], cm[mt][nt], 0, 0, 0);
+          cm[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ma, mf[nt][ks],
+                                                            ks == 0 ? zerof : cm[mt][nt], 0, 0, 0);
       }
     }
 
@@ -451,7 +453,8 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
     }
 
     __builtin_amdgcn_s_setprio(0);
-    // ---- per-block epilogue: one float pass per output ----
+    // ---- per-block epilogue: one float pass per output,
+    // xs * (d * S - dmin * M) ----
     // C layout of a 16x16 tile: lane holds column l16, rows 4q..4q+3.
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -460,11 +463,12 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const v4i sv = (sa[mt][nt] << 3) + sb[mt][nt];
-        const float d = dn[nt];
-        acc[mt][nt].x += x0 * (d * static_cast<float>(sv.x));
-        acc[mt][nt].y += x1 * (d * static_cast<float>(sv.y));
-        acc[mt][nt].z += x2 * (d * static_cast<float>(sv.z));
-        acc[mt][nt].w += x3 * (d * static_cast<float>(sv.w));
+        const float d = dn[nt], dm = -dmn[nt];
+        const v4f mv = cm[mt][nt];
+        acc[mt][nt].x += x0 * __builtin_fmaf(dm, mv[0], d * static_cast<float>(sv.x));
+        acc[mt][nt].y += x1 * __builtin_fmaf(dm, mv[1], d * static_cast<float>(sv.y));
+        acc[mt][nt].z += x2 * __builtin_fmaf(dm, mv[2], d * static_cast<float>(sv.z));
+        acc[mt][nt].w += x3 * __builtin_fmaf(dm, mv[3], d * static_cast<float>(sv.w));
       }
     }
   };
@@ -483,16 +487,6 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
       if (b + 2 < b_hi) step(b + 2, stage2, stage1);
     }
   }
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      acc[mt][nt].x -= cm[mt][nt][0];
-      acc[mt][nt].y -= cm[mt][nt][1];
-      acc[mt][nt].z -= cm[mt][nt][2];
-      acc[mt][nt].w -= cm[mt][nt][3];
-    }
-
   if (kst > 1) {
     // ---- split-K: publish this split's partial, count the arrival ----
     float* mine = part + static_cast<int64_t>(wt * kst + split) * TL::kPartFloats + tid;
@@ -644,19 +638,14 @@ void gemm_q4k_id_mixed_kernel(float* __restrict__ y, const uint8_t* __restrict__
   }
 }
 
-// Split-K workspace: kSplitSlots partial slots of the 64-token tile (24 MiB)
-// and kSplitCounters arrival counters, one per (device, stream) so that calls
-// on different streams never share it; allocated and zeroed on a stream's
-// first split launch, kept until the process ends. The planner keeps the
-// split workgroups of a launch within one round of resident workgroups
-// (512 for the all-split rule, at most 768 for a remainder).
+// Split-K: the planner keeps the split workgroups of a launch within one
+// round of resident workgroups (512 for the all-split rule, at most 768 for
+// a remainder); the caller's workspace holds one arrival counter per split
+// tile (one 128-byte line each) and one partial slot per split workgroup.
 constexpr int kSplitSlots = 768;     // split workgroups of a launch
 constexpr int kSplitCounters = 768;  // split tiles of a launch
 constexpr int kSplitTiles = 256;     // up to this many tiles, every tile splits
 constexpr int kRound = 512;          // the all-split rule's one round of workgroups
-constexpr size_t kSplitBytes =
-    static_cast<size_t>(kSplitSlots) * Tile<64>::kPartFloats * sizeof(float) +
-    static_cast<size_t>(kSplitCounters) * kCounterStride * sizeof(int);
 
 // Workgroups resident at once over the 256 CUs: two 64-token tiles or three
 // 16-token tiles per CU (their two-stage LDS rings, 73 KB and 46 KB of the
@@ -668,14 +657,38 @@ constexpr int64_t kIdMaxPairs = int64_t{1} << 20;
 constexpr int kIdMaxExperts = 1024;
 constexpr int kIdBM = 64;  // the grouped form's whole tile
 constexpr int kIdBS = 16;  // its small tiles: an expert's remainder of at most 32 pairs
-constexpr int64_t kIdMaxTiles = kIdMaxPairs / kIdBM + kIdMaxExperts + 1;
-constexpr int64_t kIdMaxSmall = 2 * (kIdMaxExperts + 1);
-constexpr size_t kIdBytes = kIdMaxPairs * sizeof(int32_t) +
-                            (kIdMaxTiles + kIdMaxSmall) * sizeof(int4) + 256;
+
+constexpr size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Split-K workspace of a plan: a fixed region of kSplitCounters arrival
+// counters (96 KiB; a plan uses the first `rest`), then the partial slots of
+// its split workgroups. The counters' region is the same for every plan, so
+// a workspace that served one shape serves the next: partials never land on
+// bytes another plan reads as counters.
+constexpr size_t kSplitCounterBytes = static_cast<size_t>(kSplitCounters) * kCounterStride * 4;
+size_t split_workspace_bytes(int rest, int ks, int bm) {
+  const size_t slot = (bm == 16 ? Tile<16>::kPartFloats : Tile<64>::kPartFloats) * sizeof(float);
+  return kSplitCounterBytes + static_cast<size_t>(rest) * ks * slot;
+}
+
+// The grouped product's workspace: whole-tile descriptors, small-tile
+// descriptors, the pairs grouped by expert, then the two tile counts.
+struct IdLayout {
+  size_t desc, desc_s, sorted, counts, bytes;
+};
+IdLayout id_layout(int64_t n_pairs, int64_t n_experts) {
+  IdLayout L;
+  L.desc = 0;
+  L.desc_s = L.desc + static_cast<size_t>(route_max_tiles(n_pairs, n_experts, kIdBM)) * 16;
+  L.sorted = L.desc_s + static_cast<size_t>(route_max_small_tiles(n_pairs, n_experts)) * 16;
+  L.counts = align_up(L.sorted + static_cast<size_t>(n_pairs) * sizeof(int32_t), 16);
+  L.bytes = L.counts + 16;
+  return L;
+}
 
 template <int BMv>
 hipError_t launch_split(float* y, const void* w, const void* xq, int64_t M, int64_t N, int64_t K,
-                        const GemmPlan& plan, hipStream_t stream) {
+                        const GemmPlan& plan, void* ws, size_t ws_bytes, hipStream_t stream) {
   const int nb = static_cast<int>(K / 256);
   const int mtiles = static_cast<int>((M + BMv - 1) / BMv);
   const int ntiles = static_cast<int>((N + BN - 1) / BN);
@@ -689,11 +702,9 @@ hipError_t launch_split(float* y, const void* w, const void* xq, int64_t M, int6
     const int rest = tiles - n_full;
     if (n_full < 0 || rest < 1 || rest > kSplitCounters || rest * ks > kSplitSlots || ks > nb)
       return hipErrorInvalidValue;
-    void* p = nullptr;
-    const hipError_t e = stream_workspace(kWsSplit, kSplitBytes, stream, &p);
-    if (e != hipSuccess) return e;
-    part = static_cast<float*>(p);
-    cnt = reinterpret_cast<int*>(part + static_cast<size_t>(kSplitSlots) * Tile<64>::kPartFloats);
+    if (!ws || ws_bytes < split_workspace_bytes(rest, ks, BMv)) return hipErrorInvalidValue;
+    cnt = static_cast<int*>(ws);
+    part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kSplitCounterBytes);
   }
   const int grid = n_full + (tiles - n_full) * ks;
   // The 16-token tile computes little per super-block. On a grid of at most
@@ -759,25 +770,33 @@ GemmPlan gemm_q4k_plan(int64_t M, int64_t N, int64_t K, int bm) {
 }
 
 hipError_t launch_gemm_q4k_split(float* y, const void* w, const void* xq, int64_t M, int64_t N,
-                                 int64_t K, const GemmPlan& plan, int bm, hipStream_t stream) {
-  if (bm == 16) return launch_split<16>(y, w, xq, M, N, K, plan, stream);
-  if (bm == 64) return launch_split<64>(y, w, xq, M, N, K, plan, stream);
+                                 int64_t K, const GemmPlan& plan, int bm, void* ws,
+                                 size_t ws_bytes, hipStream_t stream) {
+  if (bm == 16) return launch_split<16>(y, w, xq, M, N, K, plan, ws, ws_bytes, stream);
+  if (bm == 64) return launch_split<64>(y, w, xq, M, N, K, plan, ws, ws_bytes, stream);
   return hipErrorInvalidValue;
+}
+
+size_t gemm_q4k_id_workspace_bytes(int64_t n_pairs, int64_t n_experts) {
+  if (n_pairs < 1 || n_pairs > kIdMaxPairs || n_experts < 1 || n_experts > kIdMaxExperts) return 0;
+  return id_layout(n_pairs, n_experts).bytes;
 }
 
 hipError_t launch_gemm_q4k_id(float* y, const void* slab, const void* xq, const int32_t* ids,
                               int64_t n_tokens, int64_t n_used, int64_t n_experts, int64_t rows,
-                              int64_t K, int per_slot_x, hipStream_t stream) {
+                              int64_t K, int per_slot_x, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
   const int64_t n_pairs = n_tokens * n_used;
   if (n_pairs > kIdMaxPairs || n_experts > kIdMaxExperts) return hipErrorInvalidValue;
-  void* p = nullptr;
-  hipError_t e = stream_workspace(kWsRoute, kIdBytes, stream, &p);
-  if (e != hipSuccess) return e;
-  int4* desc = static_cast<int4*>(p);
-  int4* desc_s = desc + kIdMaxTiles;
-  int32_t* sorted = reinterpret_cast<int32_t*>(desc_s + kIdMaxSmall);
-  int32_t* n_tiles = sorted + kIdMaxPairs;
+  const IdLayout lay = id_layout(n_pairs, n_experts);
+  if (!ws || ws_bytes < lay.bytes) return hipErrorInvalidValue;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  int4* desc = reinterpret_cast<int4*>(base + lay.desc);
+  int4* desc_s = reinterpret_cast<int4*>(base + lay.desc_s);
+  int32_t* sorted = reinterpret_cast<int32_t*>(base + lay.sorted);
+  int32_t* n_tiles = reinterpret_cast<int32_t*>(base + lay.counts);
   int32_t* n_small = n_tiles + 1;
+  hipError_t e;
   if ((e = launch_route_experts(ids, n_pairs, n_experts, kIdBM, kIdBS, sorted, desc, n_tiles,
                                 desc_s, n_small, stream)) != hipSuccess)
     return e;
@@ -819,12 +838,23 @@ bool gemm_q4k_uses_matvec(int64_t M, int64_t N, int64_t K) {
          (M <= gemv_q4k_multi_max_tokens(K) && (M <= 3 || N * K <= (int64_t{1} << 25)));
 }
 
+size_t gemm_q4k_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 256 || K % 256) return 0;
+  if (M == 1 || gemm_q4k_uses_matvec(M, N, K)) return 0;
+  const int bm = gemm_q4k_token_tile(M, N, K);
+  const GemmPlan plan = gemm_q4k_plan(M, N, K, bm);
+  if (plan.ks <= 1) return 0;
+  const int64_t tiles = ((M + bm - 1) / bm) * ((N + BN - 1) / BN);
+  return split_workspace_bytes(static_cast<int>(tiles - plan.n_full), plan.ks, bm);
+}
+
 hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, int64_t N,
-                           int64_t K, hipStream_t stream) {
+                           int64_t K, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (M == 1) return launch_gemv_q4k(y, w, xq, N, K, stream);
   if (gemm_q4k_uses_matvec(M, N, K)) return launch_gemv_q4k_multi(y, w, xq, M, N, K, stream);
   const int bm = gemm_q4k_token_tile(M, N, K);
-  return launch_gemm_q4k_split(y, w, xq, M, N, K, gemm_q4k_plan(M, N, K, bm), bm, stream);
+  return launch_gemm_q4k_split(y, w, xq, M, N, K, gemm_q4k_plan(M, N, K, bm), bm, ws, ws_bytes,
+                               stream);
 }
 
 }  // namespace xq

@@ -656,17 +656,19 @@ hipError_t launch_gemv_q4k(float* y, const void* w, const void* xq, int64_t N, i
   return launch_rows(y, w, xq, N, K, IdArgs{nullptr, 1, 0, 0, nullptr, nullptr}, stream);
 }
 
+size_t gemv_q4k_q8k_workspace_bytes(int64_t N) {
+  if (N < 256 || N % 256 != 0 || N / 256 > kQuantTailBlocks) return 0;
+  return static_cast<size_t>(N / 256) * kCounterStride * sizeof(int);
+}
+
 hipError_t launch_gemv_q4k_q8k(float* y, void* yq, const void* w, const void* xq, int64_t N,
-                               int64_t K, hipStream_t stream) {
+                               int64_t K, void* ws, size_t ws_bytes, hipStream_t stream) {
   // Every launch shape of the table puts 4 or 8 rows in a workgroup, so the
   // workgroups of a 256-row block never straddle two blocks.
   if (N % 256 != 0 || N / 256 > kQuantTailBlocks) return hipErrorInvalidValue;
-  void* p = nullptr;
-  const hipError_t e =
-      stream_workspace(kWsQuantTail, kQuantTailBlocks * kCounterStride * sizeof(int), stream, &p);
-  if (e != hipSuccess) return e;
+  if (!ws || ws_bytes < gemv_q4k_q8k_workspace_bytes(N)) return hipErrorInvalidValue;
   return launch_rows(y, w, xq, N, K,
-                     IdArgs{nullptr, 1, 0, 0, static_cast<uint8_t*>(yq), static_cast<int*>(p)},
+                     IdArgs{nullptr, 1, 0, 0, static_cast<uint8_t*>(yq), static_cast<int*>(ws)},
                      stream);
 }
 

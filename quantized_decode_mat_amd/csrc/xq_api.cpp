@@ -69,6 +69,24 @@ constexpr int64_t kMaxRows = 1LL << 30;
 constexpr int64_t kIdMaxPairs = 1LL << 20;  // (token, slot) pairs of one grouped product
 constexpr int64_t kIdMaxExperts = 1024;
 
+// A call that needs `need` bytes of caller workspace: a null or short
+// workspace is refused by name (shape stage), a misaligned one at the
+// alignment stage (check_workspace_align).
+xq_status check_workspace(const void* ws, size_t ws_bytes, size_t need, const char* query) {
+  if (need == 0) return XQ_OK;
+  if (!ws)
+    return fail(XQ_E_NULL, "workspace is NULL; this call needs %zu bytes (%s)", need, query);
+  if (ws_bytes < need)
+    return fail(XQ_E_SHAPE, "workspace_bytes=%zu below the %zu bytes this call needs (%s)",
+                ws_bytes, need, query);
+  return XQ_OK;
+}
+
+xq_status check_workspace_align(const void* ws, size_t need) {
+  if (need > 0 && !aligned(ws, 256)) return fail(XQ_E_ALIGN, "workspace not 256-byte aligned");
+  return XQ_OK;
+}
+
 xq_status launched(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(XQ_E_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
   return ok();
@@ -109,7 +127,7 @@ xq_status xq_gemv_q4k(float* y, const void* w, const void* xq, int64_t N, int64_
 }
 
 xq_status xq_gemv_q4k_q8k(float* y, void* yq, const void* w, const void* xq, int64_t N,
-                          int64_t K, void* stream) {
+                          int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
   if (!y) return fail(XQ_E_NULL, "y is NULL");
   if (!yq) return fail(XQ_E_NULL, "yq is NULL");
   if (!w) return fail(XQ_E_NULL, "w is NULL");
@@ -117,14 +135,22 @@ xq_status xq_gemv_q4k_q8k(float* y, void* yq, const void* w, const void* xq, int
   if (N < 256 || N % 256 != 0 || N > (1LL << 22))
     return fail(XQ_E_SHAPE, "N=%lld not a multiple of 256 in 256..2^22", (long long)N);
   if (xq_status s = check_k(K, XQ_MAX_K)) return s;
+  const size_t need = xq::gemv_q4k_q8k_workspace_bytes(N);
+  if (xq_status s = check_workspace(workspace, workspace_bytes, need,
+                                    "xq_gemv_q4k_q8k_workspace_bytes"))
+    return s;
   if (!aligned(y, 16)) return fail(XQ_E_ALIGN, "y not 16-byte aligned");
   if (!aligned(yq, 16)) return fail(XQ_E_ALIGN, "yq not 16-byte aligned");
   if (!aligned(w, 16)) return fail(XQ_E_ALIGN, "w not 16-byte aligned");
   if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");
+  if (xq_status s = check_workspace_align(workspace, need)) return s;
   if (xq_status s = check_device()) return s;
-  return launched(xq::launch_gemv_q4k_q8k(y, yq, w, xq, N, K, static_cast<hipStream_t>(stream)),
+  return launched(xq::launch_gemv_q4k_q8k(y, yq, w, xq, N, K, workspace, workspace_bytes,
+                                          static_cast<hipStream_t>(stream)),
                   "xq_gemv_q4k_q8k");
 }
+
+size_t xq_gemv_q4k_q8k_workspace_bytes(int64_t N) { return xq::gemv_q4k_q8k_workspace_bytes(N); }
 
 xq_status xq_gemv_iq4nl(float* y, const void* w, const void* xq, int64_t N, int64_t K,
                         void* stream) {
@@ -205,7 +231,7 @@ xq_status xq_gemv_iq4nl_id(float* y, const void* slab, const void* xq, const int
 }
 
 xq_status xq_gemm_q4k_small_m(float* y, const void* w, const void* xq, int64_t M, int64_t N,
-                              int64_t K, void* stream) {
+                              int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
   if (!y) return fail(XQ_E_NULL, "y is NULL");
   if (!w) return fail(XQ_E_NULL, "w is NULL");
   if (!xq) return fail(XQ_E_NULL, "xq is NULL");
@@ -220,17 +246,28 @@ xq_status xq_gemm_q4k_small_m(float* y, const void* w, const void* xq, int64_t M
     return fail(XQ_E_SHAPE, "xq of M=%lld rows reaches 2 GiB", (long long)M);
   if (N * (K / 256) * 144 >= (1LL << 31))
     return fail(XQ_E_SHAPE, "w of N=%lld rows reaches 2 GiB", (long long)N);
+  const size_t need = xq::gemm_q4k_workspace_bytes(M, N, K);
+  if (xq_status s = check_workspace(workspace, workspace_bytes, need,
+                                    "xq_gemm_q4k_small_m_workspace_bytes"))
+    return s;
   if (!aligned(y, 4)) return fail(XQ_E_ALIGN, "y not 4-byte aligned");
   if (!aligned(w, 16)) return fail(XQ_E_ALIGN, "w not 16-byte aligned");
   if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");
+  if (xq_status s = check_workspace_align(workspace, need)) return s;
   if (xq_status s = check_device()) return s;
-  return launched(xq::launch_gemm_q4k(y, w, xq, M, N, K, static_cast<hipStream_t>(stream)),
+  return launched(xq::launch_gemm_q4k(y, w, xq, M, N, K, workspace, workspace_bytes,
+                                      static_cast<hipStream_t>(stream)),
                   "xq_gemm_q4k_small_m");
+}
+
+size_t xq_gemm_q4k_small_m_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  return xq::gemm_q4k_workspace_bytes(M, N, K);
 }
 
 xq_status xq_gemm_q4k_id(float* y, const void* slab, const void* xq, const int32_t* ids,
                          int64_t n_tokens, int64_t n_used, int64_t n_experts, int64_t rows,
-                         int64_t K, int64_t x_per_slot, void* stream) {
+                         int64_t K, int64_t x_per_slot, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   if (!y) return fail(XQ_E_NULL, "y is NULL");
   if (!slab) return fail(XQ_E_NULL, "slab is NULL");
   if (!xq) return fail(XQ_E_NULL, "xq is NULL");
@@ -259,15 +296,26 @@ xq_status xq_gemm_q4k_id(float* y, const void* slab, const void* xq, const int32
   if ((xq::route_max_tiles(n_pairs, n_experts, 64) + xq::route_max_small_tiles(n_pairs, n_experts)) *
               ((rows + 127) / 128) + 8 > kMaxInt)
     return fail(XQ_E_SHAPE, "too many tiles for one launch");
+  const size_t need = xq::gemm_q4k_id_workspace_bytes(n_pairs, n_experts);
+  if (xq_status s = check_workspace(workspace, workspace_bytes, need,
+                                    "xq_gemm_q4k_id_workspace_bytes"))
+    return s;
   if (!aligned(y, 4)) return fail(XQ_E_ALIGN, "y not 4-byte aligned");
   if (!aligned(slab, 16)) return fail(XQ_E_ALIGN, "slab not 16-byte aligned");
   if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");
   if (!aligned(ids, 4)) return fail(XQ_E_ALIGN, "ids not 4-byte aligned");
+  if (xq_status s = check_workspace_align(workspace, need)) return s;
   if (xq_status s = check_device()) return s;
   return launched(xq::launch_gemm_q4k_id(y, slab, xq, ids, n_tokens, n_used, n_experts, rows, K,
-                                         static_cast<int>(x_per_slot),
-                                         static_cast<hipStream_t>(stream)),
+                                         static_cast<int>(x_per_slot), workspace,
+                                         workspace_bytes, static_cast<hipStream_t>(stream)),
                   "xq_gemm_q4k_id");
+}
+
+size_t xq_gemm_q4k_id_workspace_bytes(int64_t n_tokens, int64_t n_used, int64_t n_experts) {
+  if (n_used < 1 || n_used > kIdMaxPairs || n_tokens < 1 || n_tokens > kIdMaxPairs / n_used)
+    return 0;
+  return xq::gemm_q4k_id_workspace_bytes(n_tokens * n_used, n_experts);
 }
 
 xq_status xq_repack_iq4nl(void* resident, const void* file_blocks, int64_t n_blocks,

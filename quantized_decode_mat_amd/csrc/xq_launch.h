@@ -7,11 +7,12 @@
 
 namespace xq {
 
-// Library-owned device workspaces (workspace.cpp): one zero-initialised
-// buffer per (kind, device, stream), allocated on first use and kept.
-enum WorkspaceKind { kWsSplit = 0, kWsRoute = 1, kWsQuantTail = 2 };
-hipError_t stream_workspace(int kind, size_t bytes, hipStream_t stream, void** out);
-
+// Three launchers take a caller-owned device workspace (`ws`, `ws_bytes`):
+// the split-K partials and arrival counters of the small-M product, the
+// arrival counters of the fused quantizing mat-vec, and the grouped
+// product's expert map. The *_workspace_bytes functions give the bytes a
+// call needs (0: none). Arrival counters must be zero before a workspace's
+// first use; every completed call leaves them at zero again.
 hipError_t launch_quantize_q8k(void* xq, const float* x, int64_t rows, int64_t K,
                                hipStream_t stream);
 hipError_t launch_gemv_q4k(float* y, const void* w, const void* xq, int64_t N, int64_t K,
@@ -22,9 +23,10 @@ hipError_t launch_gemv_iq4nl(float* y, const void* w, const void* xq, int64_t N,
 // rows of the slab) and the activation x_stride_blocks q8_K blocks per slot
 // into xq; output slot-major.
 // y = W x as launch_gemv_q4k, and yq = q8_K(y) as launch_quantize_q8k(yq, y,
-// 1, N) would give, in the same launch (N a multiple of 256, N <= 2^24).
+// 1, N) would give, in the same launch (N a multiple of 256, N <= 2^22).
+size_t gemv_q4k_q8k_workspace_bytes(int64_t N);
 hipError_t launch_gemv_q4k_q8k(float* y, void* yq, const void* w, const void* xq, int64_t N,
-                               int64_t K, hipStream_t stream);
+                               int64_t K, void* ws, size_t ws_bytes, hipStream_t stream);
 hipError_t launch_gemv_q4k_id(float* y, const void* slab, const void* xq, const int32_t* sel,
                               int64_t n_experts, int64_t used, int64_t rows, int64_t K,
                               int64_t x_stride_blocks, hipStream_t stream);
@@ -43,8 +45,9 @@ hipError_t launch_gemv_q4_0(float* y, const void* w, const void* xq, int64_t N, 
 int64_t gemv_q4k_multi_max_tokens(int64_t K);
 hipError_t launch_gemv_q4k_multi(float* y, const void* w, const void* xq, int64_t M, int64_t N,
                                  int64_t K, hipStream_t stream);
+size_t gemm_q4k_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, int64_t N,
-                           int64_t K, hipStream_t stream);
+                           int64_t K, void* ws, size_t ws_bytes, hipStream_t stream);
 // Whether launch_gemm_q4k serves this shape with the mat-vec kernels.
 bool gemm_q4k_uses_matvec(int64_t M, int64_t N, int64_t K);
 // The small-M product's launch plan: tiles 0..n_full-1 (of bm tokens x 128
@@ -60,13 +63,16 @@ struct GemmPlan {
 int gemm_q4k_token_tile(int64_t M, int64_t N, int64_t K);
 GemmPlan gemm_q4k_plan(int64_t M, int64_t N, int64_t K, int bm);
 hipError_t launch_gemm_q4k_split(float* y, const void* w, const void* xq, int64_t M, int64_t N,
-                                 int64_t K, const GemmPlan& plan, int bm, hipStream_t stream);
+                                 int64_t K, const GemmPlan& plan, int bm, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
 // Grouped small-M product: route the (token, slot) pairs of ids by expert,
 // then one product launch over the tile list (at most 2^20 pairs and 1024
 // experts).
+size_t gemm_q4k_id_workspace_bytes(int64_t n_pairs, int64_t n_experts);
 hipError_t launch_gemm_q4k_id(float* y, const void* slab, const void* xq, const int32_t* ids,
                               int64_t n_tokens, int64_t n_used, int64_t n_experts, int64_t rows,
-                              int64_t K, int per_slot_x, hipStream_t stream);
+                              int64_t K, int per_slot_x, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
 // The expert map: pairs grouped by expert into `sorted`; tiles of at most
 // tile_m pairs of one bucket into `desc` (int4: bucket, first, count, 0) and
 // their count into *n_tiles; a bucket's remainder of at most 2 * tile_s

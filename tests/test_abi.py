@@ -37,6 +37,35 @@ def test_layout_sizes():
     assert xq.xq_q8k_bytes(1, 1000) == 0 and xq.xq_q4k_bytes(0, 256) == 0
 
 
+def test_workspace_sizes():
+    """The bytes each workspace query gives, worked out from the plans they
+    describe: a fixed region of 768 counter lines of 128 bytes (96 KiB, the
+    same for every plan, so a reused workspace never reads another plan's
+    partials as counters) then one partial slot per split workgroup (8 KiB on
+    the 16-token tile, 32 KiB on the 64-token one); one counter line per q8_K
+    block of the fused tail; the expert map's descriptors, pairs and two
+    counts."""
+    ws = xq.xq_gemm_q4k_small_m_workspace_bytes
+    assert ws(1, 14336, 4096) == 0                 # the mat-vec
+    assert ws(3, 14336, 4096) == 0                 # the batched mat-vec
+    assert ws(512, 14336, 4096) == 0               # whole tiles only
+    # 16 tokens x 4096 rows x 56 blocks: 32 tiles of 16 x 128, 8 splits each
+    assert ws(16, 4096, 14336) == 768 * 128 + 32 * 8 * 8192
+    # 320 tokens x 14336 rows x 16 blocks: 560 tiles, 512 whole + 48 in 4 splits
+    assert ws(320, 14336, 4096) == 768 * 128 + 48 * 4 * 32768
+    assert ws(0, 8, 256) == 0 and ws(16, 4096, 1000) == 0
+    assert xq.xq_gemv_q4k_q8k_workspace_bytes(14336) == 56 * 128
+    assert xq.xq_gemv_q4k_q8k_workspace_bytes(300) == 0
+    # 16 pairs over 6 experts: 7 whole-tile and 14 small-tile descriptors of
+    # 16 B, 16 pair indices, then two counts in a 16-byte slot
+    assert xq.xq_gemm_q4k_id_workspace_bytes(8, 2, 6) == 7 * 16 + 14 * 16 + 64 + 16
+    assert xq.xq_gemm_q4k_id_workspace_bytes(0, 2, 6) == 0
+    # the largest split plan stays within 16 MiB + 96 KiB
+    worst = max(ws(M, N, K) for M in (17, 33, 48, 64, 100, 200, 320, 400, 700)
+                for N in (128, 1000, 4096, 14336, 30000) for K in (1024, 4096, 14336))
+    assert 0 < worst <= (16 << 20) + (96 << 10)
+
+
 def test_status_names():
     assert [xq.xq_status_name(s) for s in range(6)] == [
         "XQ_OK", "XQ_E_NULL", "XQ_E_SHAPE", "XQ_E_ALIGN", "XQ_E_DEVICE", "XQ_E_LAUNCH"]
@@ -47,6 +76,8 @@ def test_status_names():
 A16 = 0x7F0000000000
 A4 = A16 + 4
 A1 = A16 + 1
+W256 = 0x7F0000100000   # a 256-byte-aligned fake workspace
+BIG = 1 << 30           # its claimed size
 
 
 def _call(name, *args):
@@ -89,18 +120,46 @@ def test_gemv_refusals(fn, args, status, text):
 
 
 @pytest.mark.parametrize("args,status,text", [
-    ((0, A16, A16, 4, 8, 256, None), xq.XQ_E_NULL, "y is NULL"),
-    ((A16, A16, A16, 0, 8, 256, None), xq.XQ_E_SHAPE, "M=0"),
-    ((A16, A16, A16, 4, 0, 256, None), xq.XQ_E_SHAPE, "N=0"),
-    ((A16, A16, A16, 4, 8, 257, None), xq.XQ_E_SHAPE, "K=257"),
-    ((A16, A4, A16, 4, 8, 256, None), xq.XQ_E_ALIGN, "w not 16-byte"),
-    ((A16, A16, A1, 4, 8, 256, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
-    ((A16, A16, A16, 2 ** 20, 8, 2048, None), xq.XQ_E_SHAPE, "reaches 2 GiB"),
-    ((A16, A16, A16, 4, 2 ** 21, 2048, None), xq.XQ_E_SHAPE, "reaches 2 GiB"),
+    ((0, A16, A16, 4, 8, 256, None, 0, None), xq.XQ_E_NULL, "y is NULL"),
+    ((A16, A16, A16, 0, 8, 256, None, 0, None), xq.XQ_E_SHAPE, "M=0"),
+    ((A16, A16, A16, 4, 0, 256, None, 0, None), xq.XQ_E_SHAPE, "N=0"),
+    ((A16, A16, A16, 4, 8, 257, None, 0, None), xq.XQ_E_SHAPE, "K=257"),
+    ((A16, A4, A16, 4, 8, 256, None, 0, None), xq.XQ_E_ALIGN, "w not 16-byte"),
+    ((A16, A16, A1, 4, 8, 256, None, 0, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
+    ((A16, A16, A16, 2 ** 20, 8, 2048, None, 0, None), xq.XQ_E_SHAPE, "reaches 2 GiB"),
+    ((A16, A16, A16, 4, 2 ** 21, 2048, None, 0, None), xq.XQ_E_SHAPE, "reaches 2 GiB"),
 ])
 def test_gemm_refusals(args, status, text):
     s, err = _call("xq_gemm_q4k_small_m", *args)
     assert s == status and text in err
+
+
+# 16 tokens x 4096 x 14336 splits K: it needs a workspace.
+_SPLIT = (A16, A16, A16, 16, 4096, 14336)
+_SPLIT_NEED = 768 * 128 + 32 * 8 * 8192
+
+
+@pytest.mark.parametrize("ws,nbytes,status,text", [
+    (None, 0, xq.XQ_E_NULL, "workspace is NULL"),
+    (None, BIG, xq.XQ_E_NULL, "workspace is NULL"),
+    (W256, _SPLIT_NEED - 1, xq.XQ_E_SHAPE, "below the %d bytes" % _SPLIT_NEED),
+    (W256 + 128, BIG, xq.XQ_E_ALIGN, "workspace not 256-byte"),
+])
+def test_gemm_workspace_refusals(ws, nbytes, status, text):
+    s, err = _call("xq_gemm_q4k_small_m", *_SPLIT, ws, nbytes, None)
+    assert s == status and text in err, (s, err)
+
+
+def test_gemm_workspace_not_needed_may_be_null():
+    """A shape that splits nothing passes the workspace gates with NULL and
+    stops only at the device gate (no GPU here) or runs (GPU)."""
+    import torch
+    if torch.cuda.device_count() != 0:
+        pytest.skip("a GPU is visible; this gate is exercised only where none is")
+    s, err = _call("xq_gemm_q4k_small_m", A16, A16, A16, 512, 14336, 4096, None, 0, None)
+    assert s == xq.XQ_E_DEVICE, err
+    s, err = _call("xq_gemm_q4k_small_m", *_SPLIT, W256, _SPLIT_NEED, None)
+    assert s == xq.XQ_E_DEVICE, err
 
 
 @pytest.mark.parametrize("fn", ["xq_gemv_q4k_id", "xq_gemv_iq4nl_id"])
@@ -130,47 +189,67 @@ def test_id_refusals(fn, args, status, text):
 
 
 @pytest.mark.parametrize("args,status,text", [
-    ((0, A16, A16, A16, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_NULL, "y is NULL"),
-    ((A16, 0, A16, A16, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_NULL, "slab is NULL"),
-    ((A16, A16, 0, A16, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_NULL, "xq is NULL"),
-    ((A16, A16, A16, 0, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_NULL, "ids is NULL"),
-    ((A16, A16, A16, A16, 8, 0, 6, 64, 2048, 0, None), xq.XQ_E_SHAPE, "n_used=0"),
-    ((A16, A16, A16, A16, 0, 2, 6, 64, 2048, 0, None), xq.XQ_E_SHAPE, "n_tokens*n_used"),
-    ((A16, A16, A16, A16, 2 ** 19 + 1, 2, 6, 64, 2048, 0, None), xq.XQ_E_SHAPE,
+    ((0, A16, A16, A16, 8, 2, 6, 64, 2048, 0, W256, BIG, None), xq.XQ_E_NULL, "y is NULL"),
+    ((A16, 0, A16, A16, 8, 2, 6, 64, 2048, 0, W256, BIG, None), xq.XQ_E_NULL, "slab is NULL"),
+    ((A16, A16, 0, A16, 8, 2, 6, 64, 2048, 0, W256, BIG, None), xq.XQ_E_NULL, "xq is NULL"),
+    ((A16, A16, A16, 0, 8, 2, 6, 64, 2048, 0, W256, BIG, None), xq.XQ_E_NULL, "ids is NULL"),
+    ((A16, A16, A16, A16, 8, 0, 6, 64, 2048, 0, W256, BIG, None), xq.XQ_E_SHAPE, "n_used=0"),
+    ((A16, A16, A16, A16, 0, 2, 6, 64, 2048, 0, W256, BIG, None), xq.XQ_E_SHAPE, "n_tokens*n_used"),
+    ((A16, A16, A16, A16, 2 ** 19 + 1, 2, 6, 64, 2048, 0, W256, BIG, None), xq.XQ_E_SHAPE,
      "n_tokens*n_used"),
-    ((A16, A16, A16, A16, 8, 2, 0, 64, 2048, 0, None), xq.XQ_E_SHAPE, "n_experts=0"),
-    ((A16, A16, A16, A16, 8, 2, 1025, 64, 2048, 0, None), xq.XQ_E_SHAPE, "n_experts=1025"),
-    ((A16, A16, A16, A16, 8, 2, 6, 0, 2048, 0, None), xq.XQ_E_SHAPE, "rows=0"),
-    ((A16, A16, A16, A16, 8, 2, 6, 64, 2000, 0, None), xq.XQ_E_SHAPE, "K=2000"),
-    ((A16, A16, A16, A16, 8, 2, 6, 64, 2048, 2, None), xq.XQ_E_SHAPE, "x_per_slot=2"),
-    ((A16, A16, A16, A16, 8, 2, 6, 2 ** 21, 2048, 0, None), xq.XQ_E_SHAPE, "reaches 2 GiB"),
-    ((A16, A16, A16, A16, 2 ** 19, 2, 6, 64, 4096, 1, None), xq.XQ_E_SHAPE, "reaches 2 GiB"),
-    ((A16 + 2, A16, A16, A16, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_ALIGN, "y not 4-byte"),
-    ((A16, A4, A16, A16, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_ALIGN, "slab not 16-byte"),
-    ((A16, A16, A4, A16, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
-    ((A16, A16, A16, A1, 8, 2, 6, 64, 2048, 0, None), xq.XQ_E_ALIGN, "ids not 4-byte"),
+    ((A16, A16, A16, A16, 8, 2, 0, 64, 2048, 0, W256, BIG, None), xq.XQ_E_SHAPE, "n_experts=0"),
+    ((A16, A16, A16, A16, 8, 2, 1025, 64, 2048, 0, W256, BIG, None), xq.XQ_E_SHAPE, "n_experts=1025"),
+    ((A16, A16, A16, A16, 8, 2, 6, 0, 2048, 0, W256, BIG, None), xq.XQ_E_SHAPE, "rows=0"),
+    ((A16, A16, A16, A16, 8, 2, 6, 64, 2000, 0, W256, BIG, None), xq.XQ_E_SHAPE, "K=2000"),
+    ((A16, A16, A16, A16, 8, 2, 6, 64, 2048, 2, W256, BIG, None), xq.XQ_E_SHAPE, "x_per_slot=2"),
+    ((A16, A16, A16, A16, 8, 2, 6, 2 ** 21, 2048, 0, W256, BIG, None), xq.XQ_E_SHAPE, "reaches 2 GiB"),
+    ((A16, A16, A16, A16, 2 ** 19, 2, 6, 64, 4096, 1, W256, BIG, None), xq.XQ_E_SHAPE, "reaches 2 GiB"),
+    ((A16 + 2, A16, A16, A16, 8, 2, 6, 64, 2048, 0, W256, BIG, None), xq.XQ_E_ALIGN, "y not 4-byte"),
+    ((A16, A4, A16, A16, 8, 2, 6, 64, 2048, 0, W256, BIG, None), xq.XQ_E_ALIGN, "slab not 16-byte"),
+    ((A16, A16, A4, A16, 8, 2, 6, 64, 2048, 0, W256, BIG, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
+    ((A16, A16, A16, A1, 8, 2, 6, 64, 2048, 0, W256, BIG, None), xq.XQ_E_ALIGN, "ids not 4-byte"),
 ])
 def test_gemm_id_refusals(args, status, text):
     s, err = _call("xq_gemm_q4k_id", *args)
     assert s == status and text in err, (s, err)
 
 
+@pytest.mark.parametrize("ws,nbytes,status,text", [
+    (None, BIG, xq.XQ_E_NULL, "workspace is NULL"),
+    (W256, 7 * 16 + 14 * 16 + 64 + 15, xq.XQ_E_SHAPE, "below the 416 bytes"),
+    (W256 + 16, BIG, xq.XQ_E_ALIGN, "workspace not 256-byte"),
+])
+def test_gemm_id_workspace_refusals(ws, nbytes, status, text):
+    s, err = _call("xq_gemm_q4k_id", A16, A16, A16, A16, 8, 2, 6, 64, 2048, 0, ws, nbytes, None)
+    assert s == status and text in err, (s, err)
+
+
 @pytest.mark.parametrize("args,status,text", [
-    ((0, A16, A16, A16, 512, 4096, None), xq.XQ_E_NULL, "y is NULL"),
-    ((A16, 0, A16, A16, 512, 4096, None), xq.XQ_E_NULL, "yq is NULL"),
-    ((A16, A16, 0, A16, 512, 4096, None), xq.XQ_E_NULL, "w is NULL"),
-    ((A16, A16, A16, 0, 512, 4096, None), xq.XQ_E_NULL, "xq is NULL"),
-    ((A16, A16, A16, A16, 300, 4096, None), xq.XQ_E_SHAPE, "N=300"),
-    ((A16, A16, A16, A16, 0, 4096, None), xq.XQ_E_SHAPE, "N=0"),
-    ((A16, A16, A16, A16, 2 ** 22 + 256, 4096, None), xq.XQ_E_SHAPE, "N=4194560"),
-    ((A16, A16, A16, A16, 512, 4000, None), xq.XQ_E_SHAPE, "K=4000"),
-    ((A4, A16, A16, A16, 512, 4096, None), xq.XQ_E_ALIGN, "y not 16-byte"),
-    ((A16, A4, A16, A16, 512, 4096, None), xq.XQ_E_ALIGN, "yq not 16-byte"),
-    ((A16, A16, A4, A16, 512, 4096, None), xq.XQ_E_ALIGN, "w not 16-byte"),
-    ((A16, A16, A16, A4, 512, 4096, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
+    ((0, A16, A16, A16, 512, 4096, W256, BIG, None), xq.XQ_E_NULL, "y is NULL"),
+    ((A16, 0, A16, A16, 512, 4096, W256, BIG, None), xq.XQ_E_NULL, "yq is NULL"),
+    ((A16, A16, 0, A16, 512, 4096, W256, BIG, None), xq.XQ_E_NULL, "w is NULL"),
+    ((A16, A16, A16, 0, 512, 4096, W256, BIG, None), xq.XQ_E_NULL, "xq is NULL"),
+    ((A16, A16, A16, A16, 300, 4096, W256, BIG, None), xq.XQ_E_SHAPE, "N=300"),
+    ((A16, A16, A16, A16, 0, 4096, W256, BIG, None), xq.XQ_E_SHAPE, "N=0"),
+    ((A16, A16, A16, A16, 2 ** 22 + 256, 4096, W256, BIG, None), xq.XQ_E_SHAPE, "N=4194560"),
+    ((A16, A16, A16, A16, 512, 4000, W256, BIG, None), xq.XQ_E_SHAPE, "K=4000"),
+    ((A4, A16, A16, A16, 512, 4096, W256, BIG, None), xq.XQ_E_ALIGN, "y not 16-byte"),
+    ((A16, A4, A16, A16, 512, 4096, W256, BIG, None), xq.XQ_E_ALIGN, "yq not 16-byte"),
+    ((A16, A16, A4, A16, 512, 4096, W256, BIG, None), xq.XQ_E_ALIGN, "w not 16-byte"),
+    ((A16, A16, A16, A4, 512, 4096, W256, BIG, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
 ])
 def test_gemv_q8k_refusals(args, status, text):
     s, err = _call("xq_gemv_q4k_q8k", *args)
+    assert s == status and text in err, (s, err)
+
+
+@pytest.mark.parametrize("ws,nbytes,status,text", [
+    (None, BIG, xq.XQ_E_NULL, "workspace is NULL"),
+    (W256, 255, xq.XQ_E_SHAPE, "below the 256 bytes"),
+    (W256 + 64, BIG, xq.XQ_E_ALIGN, "workspace not 256-byte"),
+])
+def test_gemv_q8k_workspace_refusals(ws, nbytes, status, text):
+    s, err = _call("xq_gemv_q4k_q8k", A16, A16, A16, A16, 512, 4096, ws, nbytes, None)
     assert s == status and text in err, (s, err)
 
 

@@ -14,7 +14,7 @@ import torch
 import oracle
 import quantized_decode_mat_amd as xq
 import workloads as wl
-from test_gpu_parity import _note, assert_close, dev, poisoned_f32, take_f32
+from test_gpu_parity import _note, assert_close, dev, poisoned_f32, take_f32, zeroed_workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -36,8 +36,9 @@ def _slab(E, rows, K, seed):
 def _run(slab, xqb, ids, E, rows, K, per_slot):
     T, U = ids.shape
     y = poisoned_f32(T * U * rows)
+    ws = zeroed_workspace(xq.xq_gemm_q4k_id_workspace_bytes(T, U, E))
     xq.xq_gemm_q4k_id(y, dev(slab), dev(xqb), dev(ids.astype(np.int32)), T, U, E, rows, K,
-                      per_slot)
+                      per_slot, workspace=ws)
     return take_f32(y, T * U * rows).reshape(T, U, rows)
 
 

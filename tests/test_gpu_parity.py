@@ -115,9 +115,21 @@ def gpu_gemv_iq4nl(w: np.ndarray, xqb: np.ndarray, N: int, K: int) -> np.ndarray
     return take_f32(y, N)
 
 
+def zeroed_workspace(nbytes: int):
+    """A caller-owned device workspace of nbytes, zeroed before its first use
+    (None when a call needs none)."""
+    if nbytes == 0:
+        return None
+    return torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+
+
+def gemm_workspace(M: int, N: int, K: int):
+    return zeroed_workspace(xq.xq_gemm_q4k_small_m_workspace_bytes(M, N, K))
+
+
 def gpu_gemm(w: np.ndarray, xqb: np.ndarray, M: int, N: int, K: int) -> np.ndarray:
     y = poisoned_f32(M * N)
-    xq.xq_gemm_q4k_small_m(y, dev(w), dev(xqb), M, N, K)
+    xq.xq_gemm_q4k_small_m(y, dev(w), dev(xqb), M, N, K, workspace=gemm_workspace(M, N, K))
     return take_f32(y, M * N).reshape(M, N)
 
 
@@ -284,14 +296,16 @@ def test_gemv_q4k_q8k(name, N, K, seed):
     nq = xq.xq_q8k_bytes(1, N)
     outs = []
     side = torch.cuda.Stream()
+    ws = zeroed_workspace(xq.xq_gemv_q4k_q8k_workspace_bytes(N))
+    ws_side = zeroed_workspace(xq.xq_gemv_q4k_q8k_workspace_bytes(N))
     for call in range(3):  # repeated calls (counters reset), the last on a second stream
         y = poisoned_f32(N)
         yq = poisoned_u8(nq)
         if call < 2:
-            xq.xq_gemv_q4k_q8k(y, yq, wd, xd, N, K)
+            xq.xq_gemv_q4k_q8k(y, yq, wd, xd, N, K, workspace=ws)
         else:
             with torch.cuda.stream(side):
-                xq.xq_gemv_q4k_q8k(y, yq, wd, xd, N, K)
+                xq.xq_gemv_q4k_q8k(y, yq, wd, xd, N, K, workspace=ws_side)
             side.synchronize()
         outs.append((take_f32(y, N), take_u8(yq, nq).reshape(N // 256, 320)))
     y0 = poisoned_f32(N)
@@ -318,6 +332,7 @@ def test_ffn_pair_fused_tail_equals_four_launches():
     wdn = dev(wl.q4k_weights(K, H, wl.rng(wl.SEEDS["ffn_down"])))
     _note("ffn fused tail")
     xq1 = torch.empty(xq.xq_q8k_bytes(1, K), dtype=torch.uint8, device="cuda")
+    ws = zeroed_workspace(xq.xq_gemv_q4k_q8k_workspace_bytes(H))
     outs = []
     for fused in (False, True):
         h = torch.empty(H, dtype=torch.float32, device="cuda")
@@ -325,7 +340,7 @@ def test_ffn_pair_fused_tail_equals_four_launches():
         y = torch.empty(K, dtype=torch.float32, device="cuda")
         xq.xq_quantize_q8k(xq1, x, 1, K)
         if fused:
-            xq.xq_gemv_q4k_q8k(h, xq2, wu, xq1, H, K)
+            xq.xq_gemv_q4k_q8k(h, xq2, wu, xq1, H, K, workspace=ws)
         else:
             xq.xq_gemv_q4k(h, wu, xq1, H, K)
             xq.xq_quantize_q8k(xq2, h, 1, H)
@@ -565,27 +580,76 @@ def test_gemm_mfma_below_eight_tokens():
 
 
 def test_gemm_split_repeatable_across_calls_and_streams():
-    """Bit-identical results on repeated calls (the arrival counters reset
-    themselves) and on a second stream (its own workspace)."""
+    """Bit-identical results on repeated calls through one workspace (the
+    arrival counters reset themselves), through a workspace at another
+    address, on a second stream with its own workspace, and after the
+    workspace served a call of another shape."""
     M, N, K = 40, 640, 8192
     g = wl.rng(7400)
     wd = dev(wl.q4k_weights(N, K, g))
     xd = dev(oracle.quantize_q8k(wl.activations(M, K, g)))
+    need = xq.xq_gemm_q4k_small_m_workspace_bytes(M, N, K)
+    assert need > 0
     _note("gemm split repeat")
+    ws = zeroed_workspace(need + 4096)
     outs = []
     for _ in range(3):
         y = poisoned_f32(M * N)
-        xq.xq_gemm_q4k_small_m(y, wd, xd, M, N, K)
+        xq.xq_gemm_q4k_small_m(y, wd, xd, M, N, K, workspace=ws)
         outs.append(take_f32(y, M * N))
+    other = zeroed_workspace(need + 4096)[1024:]          # another address, 256-aligned
+    y = poisoned_f32(M * N)
+    xq.xq_gemm_q4k_small_m(y, wd, xd, M, N, K, workspace=other)
+    outs.append(take_f32(y, M * N))
     side = torch.cuda.Stream()
+    ws_side = zeroed_workspace(need)
     with torch.cuda.stream(side):
         y = poisoned_f32(M * N)
-        xq.xq_gemm_q4k_small_m(y, wd, xd, M, N, K)
+        xq.xq_gemm_q4k_small_m(y, wd, xd, M, N, K, workspace=ws_side)
     side.synchronize()
+    outs.append(take_f32(y, M * N))
+    # the first workspace serves a smaller split shape, then this one again
+    M2, K2 = 20, 4096
+    assert 0 < xq.xq_gemm_q4k_small_m_workspace_bytes(M2, N, K2) <= need + 4096
+    y2 = poisoned_f32(M2 * N)
+    xq.xq_gemm_q4k_small_m(y2, wd, dev(oracle.quantize_q8k(wl.activations(M2, K2, g))), M2, N,
+                           K2, workspace=ws)
+    take_f32(y2, M2 * N)
+    y = poisoned_f32(M * N)
+    xq.xq_gemm_q4k_small_m(y, wd, xd, M, N, K, workspace=ws)
     outs.append(take_f32(y, M * N))
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
     assert not np.isnan(outs[0]).any()
+
+
+def test_gemm_split_graph_capture_first_use():
+    """A split call captured into a HIP graph on its workspace's first use
+    (the caller zeroed it before the capture) replays to the eager result bit
+    for bit, three times, with eager work between the replays."""
+    M, N, K = 16, 4096, 14336
+    g = wl.rng(7410)
+    wd = dev(wl.q4k_weights(N, K, g))
+    xd = dev(oracle.quantize_q8k(wl.activations(M, K, g)))
+    need = xq.xq_gemm_q4k_small_m_workspace_bytes(M, N, K)
+    assert need > 0
+    _note("gemm split graph capture")
+    y_eager = poisoned_f32(M * N)
+    xq.xq_gemm_q4k_small_m(y_eager, wd, xd, M, N, K, workspace=zeroed_workspace(need))
+    want = take_f32(y_eager, M * N)
+    ws = zeroed_workspace(need)
+    y = poisoned_f32(M * N)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        xq.xq_gemm_q4k_small_m(y, wd, xd, M, N, K, workspace=ws)
+    for r in range(3):
+        y[:M * N].fill_(float("nan"))
+        graph.replay()
+        assert np.array_equal(take_f32(y, M * N), want), "replay %d" % r
+        y_e = poisoned_f32(M * N)                            # eager work between replays
+        xq.xq_gemm_q4k_small_m(y_e, wd, xd, M, N, K, workspace=zeroed_workspace(need))
+        assert np.array_equal(take_f32(y_e, M * N), want)
 
 
 def test_gemm_prefill_512x14336x4096():
@@ -623,7 +687,7 @@ def test_gemm_partials_bit_exact(which, M, K):
         xqb = oracle.quantize_q8k(x)
         _note("gemm partial %s block %d" % (which, b))
         y = poisoned_f32(M * N)
-        xq.xq_gemm_q4k_small_m(y, wd, dev(xqb), M, N, K)
+        xq.xq_gemm_q4k_small_m(y, wd, dev(xqb), M, N, K, workspace=gemm_workspace(M, N, K))
         got = take_f32(y, M * N).reshape(M, N)
         for m in range(M):
             S, Mp = oracle.q4k_partials(w, xqb[m], N, K)
