@@ -180,6 +180,26 @@ xq_status xq_gemm_q4k_small_m(float *y, const void *w, const void *xq, int64_t M
 size_t xq_gemm_q4k_small_m_workspace_bytes(int64_t M, int64_t N, int64_t K);  /* 0 if none */
 
 /*
+ * xq_gemm_q4k_small_m without a workspace and without any allocation, for
+ * callers that cannot allocate device memory or pass a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results (bit for bit), gates and errors as
+ * xq_gemm_q4k_small_m, except the workspace: the split-K partials and
+ * arrival counters live in the library's own device array of
+ * XQ_NOALLOC_SCRATCH_BYTES, one per GPU, held until the process ends. A shape
+ * whose plan needs more scratch than that (xq_gemm_q4k_small_m_workspace_bytes
+ * above it: some 64-token-tile shapes with split K) is refused with
+ * XQ_E_SHAPE; every shape of up to 32 tokens fits. The first call on a GPU
+ * looks the array up and clears its counters on the caller's stream; every
+ * completed call leaves them at zero. All calls on one GPU share the array:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * and must not be issued.
+ */
+#define XQ_NOALLOC_SCRATCH_BYTES (8u * 1024u * 1024u)
+xq_status xq_gemm_q4k_small_m_noalloc(float *y, const void *w, const void *xq, int64_t M,
+                                      int64_t N, int64_t K, void *stream);
+
+/*
  * Grouped Q4_K x q8_K small-M product over an expert slab (mul_mat_id; "25 —
  * Writing XPU Kernels", section 25.3: a mixture-of-experts prefill is one
  * launch over an expert map, padded only to the finest tile, never one

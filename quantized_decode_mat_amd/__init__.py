@@ -35,8 +35,9 @@ EXPORTS = (
     "xq_bench_stream_read", "xq_bench_sink_words", "xq_gemv_q4k_id", "xq_gemv_iq4nl_id",
     "xq_repack_iq4nl", "xq_repack_dword_prefix_launches", "xq_gemv_q4_0", "xq_gemm_q4k_id",
     "xq_gemv_q4k_q8k", "xq_gemm_q4k_small_m_workspace_bytes", "xq_gemv_q4k_q8k_workspace_bytes",
-    "xq_gemm_q4k_id_workspace_bytes",
+    "xq_gemm_q4k_id_workspace_bytes", "xq_gemm_q4k_small_m_noalloc",
 )
+XQ_NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024
 
 
 class XQError(RuntimeError):
@@ -61,6 +62,7 @@ def lib() -> ctypes.CDLL:
             L.xq_gemv_q4_0.argtypes = [P, P, P, I, I, P]
             Z = ctypes.c_size_t
             L.xq_gemm_q4k_small_m.argtypes = [P, P, P, I, I, I, P, Z, P]
+            L.xq_gemm_q4k_small_m_noalloc.argtypes = [P, P, P, I, I, I, P]
             L.xq_bench_stream_read.argtypes = [P, I, P, P]
             L.xq_gemv_q4k_id.argtypes = [P, P, P, P, I, I, I, I, I, P]
             L.xq_gemv_iq4nl_id.argtypes = [P, P, P, P, I, I, I, I, I, P]
@@ -77,7 +79,8 @@ def lib() -> ctypes.CDLL:
             L.xq_repack_dword_prefix_launches.restype = I
             for f in ("xq_quantize_q8k", "xq_gemv_q4k", "xq_gemv_iq4nl", "xq_gemm_q4k_small_m",
                       "xq_bench_stream_read", "xq_gemv_q4k_id", "xq_gemv_iq4nl_id", "xq_repack_iq4nl",
-                      "xq_gemv_q4_0", "xq_gemm_q4k_id", "xq_gemv_q4k_q8k"):
+                      "xq_gemv_q4_0", "xq_gemm_q4k_id", "xq_gemv_q4k_q8k",
+                      "xq_gemm_q4k_small_m_noalloc"):
                 getattr(L, f).restype = S
             for f in ("xq_q8k_bytes", "xq_q4k_bytes", "xq_iq4nl_bytes"):
                 getattr(L, f).argtypes = [I, I]
@@ -241,6 +244,14 @@ def xq_gemm_q4k_small_m(y, w, xq, M: int, N: int, K: int, workspace=None, stream
                                      _ptr(xq, xq_q8k_bytes(M, K), "xq"), M, N, K, wp, wb,
                                      _stream(stream)),
            "xq_gemm_q4k_small_m")
+
+
+def xq_gemm_q4k_small_m_noalloc(y, w, xq, M: int, N: int, K: int, stream=None) -> None:
+    _check(lib().xq_gemm_q4k_small_m_noalloc(_ptr(y, 4 * M * N, "y"),
+                                             _ptr(w, xq_q4k_bytes(N, K), "w"),
+                                             _ptr(xq, xq_q8k_bytes(M, K), "xq"), M, N, K,
+                                             _stream(stream)),
+           "xq_gemm_q4k_small_m_noalloc")
 
 
 def xq_gemm_q4k_id_workspace_bytes(n_tokens: int, n_used: int, n_experts: int) -> int:

@@ -66,6 +66,7 @@
 // is sized by an upper bound on its list's length; workgroups past the end
 // return at once. Tiles of out-of-range selections write NaN.
 #include <algorithm>
+#include <mutex>
 
 #include "lds_dma.h"
 #include "xq_device.h"
@@ -838,6 +839,53 @@ bool gemm_q4k_uses_matvec(int64_t M, int64_t N, int64_t K) {
          (M <= gemv_q4k_multi_max_tokens(K) && (M <= 3 || N * K <= (int64_t{1} << 25)));
 }
 
+// ---- the product for callers that cannot allocate ----
+// Split-K scratch of xq_gemm_q4k_small_m_noalloc: every GPU the library runs
+// on holds one copy until the process ends, and every call on that GPU shares
+// it. In host code `scratch` names a host-side stand-in, not the device
+// array: host code uses only the address hipGetSymbolAddress returns for the
+// current device (noalloc_scratch below).
+constexpr size_t kNoAllocScratchBytes = size_t{8} << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+__global__ void clear_words_kernel(int* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// The device address of `scratch` on the current device, looked up once per
+// device. The first call on a device also clears the arrival counters (on
+// the caller's stream, ahead of the product); every completed call leaves
+// them at zero again.
+hipError_t noalloc_scratch(hipStream_t stream, void** out) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    constexpr int words = static_cast<int>(kSplitCounterBytes / 4);
+    hipLaunchKernelGGL(clear_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream,
+                       static_cast<int*>(p), words);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t gemm_q4k_noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
 size_t gemm_q4k_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 256 || K % 256) return 0;
   if (M == 1 || gemm_q4k_uses_matvec(M, N, K)) return 0;
@@ -855,6 +903,18 @@ hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, i
   const int bm = gemm_q4k_token_tile(M, N, K);
   return launch_gemm_q4k_split(y, w, xq, M, N, K, gemm_q4k_plan(M, N, K, bm), bm, ws, ws_bytes,
                                stream);
+}
+
+hipError_t launch_gemm_q4k_noalloc(float* y, const void* w, const void* xq, int64_t M, int64_t N,
+                                   int64_t K, hipStream_t stream) {
+  const size_t need = gemm_q4k_workspace_bytes(M, N, K);
+  if (need > kNoAllocScratchBytes) return hipErrorInvalidValue;
+  void* p = nullptr;
+  if (need > 0) {
+    const hipError_t e = noalloc_scratch(stream, &p);
+    if (e != hipSuccess) return e;
+  }
+  return launch_gemm_q4k(y, w, xq, M, N, K, p, kNoAllocScratchBytes, stream);
 }
 
 }  // namespace xq

@@ -230,8 +230,9 @@ xq_status xq_gemv_iq4nl_id(float* y, const void* slab, const void* xq, const int
                   "xq_gemv_iq4nl_id");
 }
 
-xq_status xq_gemm_q4k_small_m(float* y, const void* w, const void* xq, int64_t M, int64_t N,
-                              int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+// The small-M product's gates up to the workspace: null pointers, shape.
+static xq_status check_gemm(const float* y, const void* w, const void* xq, int64_t M, int64_t N,
+                            int64_t K) {
   if (!y) return fail(XQ_E_NULL, "y is NULL");
   if (!w) return fail(XQ_E_NULL, "w is NULL");
   if (!xq) return fail(XQ_E_NULL, "xq is NULL");
@@ -246,18 +247,46 @@ xq_status xq_gemm_q4k_small_m(float* y, const void* w, const void* xq, int64_t M
     return fail(XQ_E_SHAPE, "xq of M=%lld rows reaches 2 GiB", (long long)M);
   if (N * (K / 256) * 144 >= (1LL << 31))
     return fail(XQ_E_SHAPE, "w of N=%lld rows reaches 2 GiB", (long long)N);
+  return XQ_OK;
+}
+
+static xq_status check_gemm_align(const float* y, const void* w, const void* xq) {
+  if (!aligned(y, 4)) return fail(XQ_E_ALIGN, "y not 4-byte aligned");
+  if (!aligned(w, 16)) return fail(XQ_E_ALIGN, "w not 16-byte aligned");
+  if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");
+  return XQ_OK;
+}
+
+xq_status xq_gemm_q4k_small_m(float* y, const void* w, const void* xq, int64_t M, int64_t N,
+                              int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  if (xq_status s = check_gemm(y, w, xq, M, N, K)) return s;
   const size_t need = xq::gemm_q4k_workspace_bytes(M, N, K);
   if (xq_status s = check_workspace(workspace, workspace_bytes, need,
                                     "xq_gemm_q4k_small_m_workspace_bytes"))
     return s;
-  if (!aligned(y, 4)) return fail(XQ_E_ALIGN, "y not 4-byte aligned");
-  if (!aligned(w, 16)) return fail(XQ_E_ALIGN, "w not 16-byte aligned");
-  if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");
+  if (xq_status s = check_gemm_align(y, w, xq)) return s;
   if (xq_status s = check_workspace_align(workspace, need)) return s;
   if (xq_status s = check_device()) return s;
   return launched(xq::launch_gemm_q4k(y, w, xq, M, N, K, workspace, workspace_bytes,
                                       static_cast<hipStream_t>(stream)),
                   "xq_gemm_q4k_small_m");
+}
+
+xq_status xq_gemm_q4k_small_m_noalloc(float* y, const void* w, const void* xq, int64_t M,
+                                      int64_t N, int64_t K, void* stream) {
+  if (xq_status s = check_gemm(y, w, xq, M, N, K)) return s;
+  const size_t need = xq::gemm_q4k_workspace_bytes(M, N, K);
+  if (need > xq::gemm_q4k_noalloc_scratch_bytes())
+    return fail(XQ_E_SHAPE,
+                "M=%lld N=%lld K=%lld needs %zu bytes of split-K scratch, above the %zu bytes "
+                "xq_gemm_q4k_small_m_noalloc holds (xq_gemm_q4k_small_m with a caller workspace "
+                "takes any shape)",
+                (long long)M, (long long)N, (long long)K, need,
+                xq::gemm_q4k_noalloc_scratch_bytes());
+  if (xq_status s = check_gemm_align(y, w, xq)) return s;
+  if (xq_status s = check_device()) return s;
+  return launched(xq::launch_gemm_q4k_noalloc(y, w, xq, M, N, K, static_cast<hipStream_t>(stream)),
+                  "xq_gemm_q4k_small_m_noalloc");
 }
 
 size_t xq_gemm_q4k_small_m_workspace_bytes(int64_t M, int64_t N, int64_t K) {

@@ -46,6 +46,12 @@ int64_t gemv_q4k_multi_max_tokens(int64_t K);
 hipError_t launch_gemv_q4k_multi(float* y, const void* w, const void* xq, int64_t M, int64_t N,
                                  int64_t K, hipStream_t stream);
 size_t gemm_q4k_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// The same product with its split-K scratch in the library's per-device
+// static array (gemm_q4k_noalloc_scratch_bytes of it): no allocation and no
+// workspace argument; shapes needing more scratch are refused.
+size_t gemm_q4k_noalloc_scratch_bytes();
+hipError_t launch_gemm_q4k_noalloc(float* y, const void* w, const void* xq, int64_t M, int64_t N,
+                                   int64_t K, hipStream_t stream);
 hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, int64_t N,
                            int64_t K, void* ws, size_t ws_bytes, hipStream_t stream);
 // Whether launch_gemm_q4k serves this shape with the mat-vec kernels.

@@ -150,6 +150,25 @@ def test_gemm_workspace_refusals(ws, nbytes, status, text):
     assert s == status and text in err, (s, err)
 
 
+def test_noalloc_scratch_limit():
+    """The no-allocation product holds 8 MiB of split-K scratch: every plan of
+    up to 32 tokens fits, and a shape that needs more is refused by name
+    before the device gate (48 tokens x 14336 x 4096: 112 tiles of 64 x 128
+    split four ways, 448 slots of 32 KiB after the 96 KiB of counters)."""
+    ws = xq.xq_gemm_q4k_small_m_workspace_bytes
+    assert xq.XQ_NOALLOC_SCRATCH_BYTES == 8 << 20
+    assert max(ws(M, N, K) for M in range(2, 33) for N in (100, 1000, 4096, 14336, 100000)
+               for K in (256, 1024, 4096, 14336, 49152)) <= xq.XQ_NOALLOC_SCRATCH_BYTES
+    need = ws(48, 14336, 4096)
+    assert need == 768 * 128 + 448 * 32768 > xq.XQ_NOALLOC_SCRATCH_BYTES
+    s, err = _call("xq_gemm_q4k_small_m_noalloc", A16, A16, A16, 48, 14336, 4096, None)
+    assert s == xq.XQ_E_SHAPE and "above the 8388608 bytes" in err, err
+    s, err = _call("xq_gemm_q4k_small_m_noalloc", 0, A16, A16, 48, 14336, 4096, None)
+    assert s == xq.XQ_E_NULL and "y is NULL" in err
+    s, err = _call("xq_gemm_q4k_small_m_noalloc", A16, A4, A16, 32, 4096, 14336, None)
+    assert s == xq.XQ_E_ALIGN and "w not 16-byte" in err
+
+
 def test_gemm_workspace_not_needed_may_be_null():
     """A shape that splits nothing passes the workspace gates with NULL and
     stops only at the device gate (no GPU here) or runs (GPU)."""
