@@ -234,9 +234,11 @@ xq_status xq_gemm_q4k_id(float *y, const void *slab, const void *xq, const int32
                          void *stream);
 size_t xq_gemm_q4k_id_workspace_bytes(int64_t n_tokens, int64_t n_used, int64_t n_experts);
 
-/* Largest K the mat-vecs accept: the q8_K activation row is staged whole in
- * the workgroup's LDS (XQ_MAX_K/256 * 320 bytes = 60 KiB). */
-#define XQ_MAX_K 49152
+/* Largest K the mat-vecs accept (the q8_K row is then 1.25 MiB). Rows of up
+ * to 49152 columns stage the row in the workgroup's LDS (60 KiB at most);
+ * longer rows read it from global memory, where every workgroup finds it in
+ * L2. The small-M product (xq_gemm_q4k_small_m) takes any K. */
+#define XQ_MAX_K 1048576
 
 /* Byte sizes of the layouts above; 0 when the shape is invalid. */
 size_t xq_q8k_bytes(int64_t rows, int64_t K);   /* rows*(K/256)*320 */
@@ -293,8 +295,8 @@ xq_status xq_gemv_iq4nl_id(float *y, const void *slab, const void *xq, const int
 /*
  * Bind-time repack of IQ4_NL file blocks into resident rows ("25 — Writing XPU
  * Kernels", section 25.4: weights are converted once, at upload, into the one
- * resident layout the kernels read; section 25.4.1: one work item per payload
- * dword). A file block is 18 bytes: the f16 scale, then the 16 payload bytes
+ * resident layout the kernels read; section 25.4.1: each work item moves one
+ * payload dword). A file block is 18 bytes: the f16 scale, then the 16 payload bytes
  * (byte t: weight t in the low nibble, weight t+16 in the high nibble).
  *  file_blocks  the chunk: n_blocks blocks back to back, global blocks
  *               block_base .. block_base + n_blocks - 1 of a matrix of bpr

@@ -28,7 +28,7 @@ _lock = threading.Lock()
 _lib = None
 
 XQ_OK, XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH = range(6)
-XQ_MAX_K = 49152
+XQ_MAX_K = 1048576
 EXPORTS = (
     "xq_quantize_q8k", "xq_gemv_q4k", "xq_gemv_iq4nl", "xq_gemm_q4k_small_m",
     "xq_q8k_bytes", "xq_q4k_bytes", "xq_iq4nl_bytes", "xq_status_name", "xq_last_error",

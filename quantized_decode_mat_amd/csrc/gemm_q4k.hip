@@ -840,8 +840,9 @@ bool gemm_q4k_uses_matvec(int64_t M, int64_t N, int64_t K) {
   // A very short batch is a weight stream, not a dense contraction: one pass
   // of the dot4 mat-vec over the weights for all M tokens costs less than
   // the 16-token MFMA tile. Measured on MI355X (cold weights): 14336x4096 at
-  // 3 tokens 11.7 us against 12.4 (4 tokens: 14.4 against 12.4); 4096x14336
-  // at 3 tokens 14.1 against 15.4; 4096x4096 at 8 tokens 9.6 against 9.5.
+  // 3 tokens 9.6-10.2 us on the persistent grid against 12.4 (4 tokens: 13.1
+  // against 12.4); 4096x14336 at 3 tokens 11.8-12.0 with a row's units split
+  // across waves against 15.4; 4096x4096 at 8 tokens 9.6 against 9.5.
   return M == 1 ||
          (M <= gemv_q4k_multi_max_tokens(K) && (M <= 3 || N * K <= (int64_t{1} << 25)));
 }

@@ -137,14 +137,17 @@ __device__ __forceinline__ bool select_slot(YPtr& y, BPtr& w, BPtr& xq, int N, i
   return true;
 }
 
-template <int R, int PF, bool ID, int FMT>
+// GACT: rows too long to stage (K > kMaxStagedK) read the q8_K row from
+// global memory (served from L2: every workgroup reads the same row), with
+// the same arithmetic.
+template <int R, int PF, bool ID, int FMT, bool GACT = false>
 __global__ __launch_bounds__(kThreads) void gemv_iq4nl_kernel(float* __restrict__ y,
                                                               const uint8_t* __restrict__ w,
                                                               const uint8_t* __restrict__ xq,
                                                               int N, int bpr, int prefix,
                                                               int64_t row_bytes, int nq8,
                                                               IdArgs id) {
-  extern __shared__ __align__(16) uint8_t act[];
+  extern __shared__ __align__(16) uint8_t act_lds[];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * kWavesPerGroup + wave) * R;
@@ -174,13 +177,14 @@ __global__ __launch_bounds__(kThreads) void gemv_iq4nl_kernel(float* __restrict_
   };
 
   load_batch(0);
-  {
+  const uint8_t* act = GACT ? xq : act_lds;
+  if constexpr (!GACT) {
     const uint4* src = reinterpret_cast<const uint4*>(xq);
-    uint4* dst = reinterpret_cast<uint4*>(act);
+    uint4* dst = reinterpret_cast<uint4*>(act_lds);
     const int n16 = nq8 * (kQ8KBytes / 16);
     for (int i = threadIdx.x; i < n16; i += kThreads) dst[i] = src[i];
+    __syncthreads();
   }
-  __syncthreads();
 
   float acc[R];
 #pragma unroll
@@ -320,17 +324,17 @@ hipError_t launch_resident(float* y, const uint8_t* w, const uint8_t* xq, int N,
   return hipGetLastError();
 }
 
-template <int PF, int FMT>
+template <int PF, int FMT, bool GACT = false>
 hipError_t launch_staged(float* y, const uint8_t* w, const uint8_t* xq, int N, int bpr, int prefix,
                          int64_t row_bytes, int nq8, const IdArgs& id, hipStream_t stream) {
   const int grid = (N + kWavesPerGroup - 1) / kWavesPerGroup;
-  const size_t lds = static_cast<size_t>(nq8) * kQ8KBytes;
+  const size_t lds = GACT ? 0 : static_cast<size_t>(nq8) * kQ8KBytes;
   if (id.sel)
-    hipLaunchKernelGGL((gemv_iq4nl_kernel<1, PF, true, FMT>), dim3(grid, id.used), dim3(kThreads), lds,
-                       stream, y, w, xq, N, bpr, prefix, row_bytes, nq8, id);
+    hipLaunchKernelGGL((gemv_iq4nl_kernel<1, PF, true, FMT, GACT>), dim3(grid, id.used),
+                       dim3(kThreads), lds, stream, y, w, xq, N, bpr, prefix, row_bytes, nq8, id);
   else
-    hipLaunchKernelGGL((gemv_iq4nl_kernel<1, PF, false, FMT>), dim3(grid), dim3(kThreads), lds, stream,
-                       y, w, xq, N, bpr, prefix, row_bytes, nq8, id);
+    hipLaunchKernelGGL((gemv_iq4nl_kernel<1, PF, false, FMT, GACT>), dim3(grid), dim3(kThreads),
+                       lds, stream, y, w, xq, N, bpr, prefix, row_bytes, nq8, id);
   return hipGetLastError();
 }
 
@@ -364,7 +368,11 @@ hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64
     case 5: return launch_staged<5, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
     case 6: return launch_staged<6, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
     case 7: return launch_staged<7, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
-    default: return launch_staged<8, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+    default:
+      if (K <= kMaxStagedK)
+        return launch_staged<8, FMT>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
+      // Rows too long to stage: the activation from global memory.
+      return launch_staged<8, FMT, true>(y, wb, xb, n, bpr, prefix, row_bytes, nq8, id, stream);
   }
 }
 

@@ -6,15 +6,16 @@
 // signed bytes); the sub-block scales multiply the integer sub-block dots in
 // 24-bit integer multiplies; the min term is paid from the q8_K's stored
 // sub-block sums; the f16/f32 scales are applied once per block after the
-// integer work ("reduce first, scale once", section 25.2.1).
+// integer work: the sums are reduced in integers and the float scales are
+// applied once per block afterwards (section 25.2.1).
 //
 // Mapping (MI355X-first, not the pages' wave32 one-lane-per-block design):
 //  * One wave owns R rows. A "unit" is 8 consecutive super-blocks of one row;
 //    lane l takes block 8u + l/8 and its 16-byte nibble chunk c = l%8, which
 //    is half of nibble group g = c/2 (h = c%2). A wave's nibble load covers
 //    8 x 128 B of the 8 x 144 B span, the header load the other 8 x 16 B:
-//    every byte the wave touches is a byte it needs ("count lines touched,
-//    not loads issued", section 25.2).
+//    every byte the wave touches is a byte it needs (section 25.2: the
+//    cache lines a wave touches are what costs, not its load count).
 //  * Each lane also loads its block's 16-byte header; the eight lanes of a
 //    block load the same 16 bytes, which the cache serves once per line.
 //  * All of a lane's loads for a batch of PF units are issued before any is
@@ -87,7 +88,11 @@ __device__ __forceinline__ void act_store(const uint4 (&a)[NA], uint8_t* lds, co
 // agent-scope atomic loads and quantizes it with one wave, the quantize
 // kernel's own arithmetic (q8k_block_wave), so yq holds the bytes
 // xq_quantize_q8k gives for y.
-template <int R, int PF, int W, int NA, bool CLAMP, bool ID, bool QOUT>
+// GACT: rows longer than the LDS can stage (K > kMaxStagedK): no staging,
+// every lane reads its slices of the q8_K row from global memory (the row is
+// shared by every workgroup, so it is served from L2), with the same
+// arithmetic, so the bits are those of the staged form.
+template <int R, int PF, int W, int NA, bool CLAMP, bool ID, bool QOUT, bool GACT = false>
 __global__ __launch_bounds__(W * kWave) void gemv_q4k_kernel(float* __restrict__ y,
                                                              const uint8_t* __restrict__ w,
                                                              const uint8_t* __restrict__ xq,
@@ -96,7 +101,7 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_kernel(float* __restrict__
                                                              int n_experts, int64_t x_stride,
                                                              uint8_t* __restrict__ yq,
                                                              int* __restrict__ qcnt) {
-  extern __shared__ __align__(16) uint8_t act[];
+  extern __shared__ __align__(16) uint8_t act_lds[];
   constexpr int kThreads = W * kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
@@ -141,11 +146,16 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_kernel(float* __restrict__
       }
   };
 
-  uint4 areg[NA];
-  act_load<NA, kThreads>(areg, xq, n16);
-  load_batch(0);
-  act_store<NA, kThreads>(areg, act, xq, n16);
-  __syncthreads();
+  const uint8_t* act = GACT ? xq : act_lds;
+  if constexpr (GACT) {
+    load_batch(0);
+  } else {
+    uint4 areg[NA];
+    act_load<NA, kThreads>(areg, xq, n16);
+    load_batch(0);
+    act_store<NA, kThreads>(areg, act_lds, xq, n16);
+    __syncthreads();
+  }
 
   float acc[R];
 #pragma unroll
@@ -474,22 +484,22 @@ struct IdArgs {
   int* qcnt;           // its per-block arrival counters
 };
 
-template <int R, int PF, int W, int NA, bool CLAMP>
+template <int R, int PF, int W, int NA, bool CLAMP, bool GACT = false>
 hipError_t launch_cfg(float* y, const uint8_t* w, const uint8_t* xq, int N, int nb,
                       const IdArgs& id, hipStream_t stream) {
   const int waves = (N + R - 1) / R;
   const int grid = (waves + W - 1) / W;
-  const size_t lds = static_cast<size_t>(nb) * kQ8KBytes;
+  const size_t lds = GACT ? 0 : static_cast<size_t>(nb) * kQ8KBytes;
   if (id.sel)
-    hipLaunchKernelGGL((gemv_q4k_kernel<R, PF, W, NA, CLAMP, true, false>), dim3(grid, id.used),
-                       dim3(W * kWave), lds, stream, y, w, xq, N, nb, id.sel, id.n_experts,
-                       id.x_stride, nullptr, nullptr);
+    hipLaunchKernelGGL((gemv_q4k_kernel<R, PF, W, NA, CLAMP, true, false, GACT>),
+                       dim3(grid, id.used), dim3(W * kWave), lds, stream, y, w, xq, N, nb, id.sel,
+                       id.n_experts, id.x_stride, nullptr, nullptr);
   else if (id.yq)
-    hipLaunchKernelGGL((gemv_q4k_kernel<R, PF, W, NA, CLAMP, false, true>), dim3(grid),
+    hipLaunchKernelGGL((gemv_q4k_kernel<R, PF, W, NA, CLAMP, false, true, GACT>), dim3(grid),
                        dim3(W * kWave), lds, stream, y, w, xq, N, nb, nullptr, 0, int64_t{0}, id.yq,
                        id.qcnt);
   else
-    hipLaunchKernelGGL((gemv_q4k_kernel<R, PF, W, NA, CLAMP, false, false>), dim3(grid),
+    hipLaunchKernelGGL((gemv_q4k_kernel<R, PF, W, NA, CLAMP, false, false, GACT>), dim3(grid),
                        dim3(W * kWave), lds, stream, y, w, xq, N, nb, nullptr, 0, int64_t{0},
                        nullptr, nullptr);
   return hipGetLastError();
@@ -528,7 +538,9 @@ hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64
   if (units == 5) return launch_cfg<1, 5, 8, 3, true>(y, wb, xb, n, nb, id, stream);
   if (units == 6) return launch_cfg<1, 6, 8, 3, true>(y, wb, xb, n, nb, id, stream);
   if (units == 7) return launch_cfg<1, 7, 8, 3, true>(y, wb, xb, n, nb, id, stream);
-  return launch_cfg<1, 4, 8, 3, false>(y, wb, xb, n, nb, id, stream);
+  if (K <= kMaxStagedK) return launch_cfg<1, 4, 8, 3, false>(y, wb, xb, n, nb, id, stream);
+  // Rows too long to stage: the activation from global memory.
+  return launch_cfg<1, 4, 8, 3, false, true>(y, wb, xb, n, nb, id, stream);
 }
 
 template <int TM, int R, int PF, int W, int NA, bool CLAMP>

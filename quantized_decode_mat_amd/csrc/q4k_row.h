@@ -5,7 +5,8 @@
 // valid signed bytes); the sub-block scales multiply the integer sub-block dots
 // in 24-bit integer multiplies; the min term is paid from the q8_K's stored
 // sub-block sums; the f16/f32 scales are applied once per block after the
-// integer work ("reduce first, scale once", section 25.2.1).
+// integer work: the sums are reduced in integers and the float scales are
+// applied once per block afterwards (section 25.2.1).
 //
 // Lane layout: a "unit" is 8 consecutive super-blocks of a row; lane l takes
 // block 8u + l/8 and its 16-byte nibble chunk c = l%8, which is half of nibble

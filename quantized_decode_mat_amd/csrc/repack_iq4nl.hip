@@ -3,10 +3,11 @@
 // "25 — Writing XPU Kernels", section 25.4: weights are converted once when
 // they are bound, into the one resident layout every kernel reads (a row is
 // its f16 block scales padded to a dword, then its 16-byte payloads), and the
-// copy follows the decode rules: one work item per payload dword, not one
-// wave per block; a separate pass over the scattered scale bytes pulls a
-// cache line per block for two useful bytes, so the scale goes with the pass
-// that already reads those lines (section 25.4.1 leaves that fold open).
+// copy is mapped like the decode kernels: each work item moves one dword of
+// payload rather than a wave taking a whole block. A separate pass over the
+// scattered scale bytes would pull a cache line per block for two useful
+// bytes, so the scale goes with the pass that already reads those lines
+// (section 25.4.1 leaves that fold open).
 //
 // Source: a chunk of the file's 18-byte blocks (f16 scale at +0, then the 16
 // payload bytes), global blocks block_base .. block_base + n - 1 of a matrix

@@ -7,6 +7,11 @@
 
 namespace xq {
 
+// The longest row whose q8_K activation the mat-vecs stage whole in a
+// workgroup's LDS (192 blocks = 60 KiB); longer rows (up to XQ_MAX_K) read it
+// from global memory instead.
+constexpr int64_t kMaxStagedK = 49152;
+
 // Three launchers take a caller-owned device workspace (`ws`, `ws_bytes`):
 // the split-K partials and arrival counters of the small-M product, the
 // arrival counters of the fused quantizing mat-vec, and the grouped

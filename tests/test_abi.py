@@ -109,7 +109,7 @@ def test_quantize_refusals(args, status, text):
     ((A16, A16, A16, 0, 256, None), xq.XQ_E_SHAPE, "N=0"),
     ((A16, A16, A16, 2 ** 30 + 1, 256, None), xq.XQ_E_SHAPE, "N=1073741825"),
     ((A16, A16, A16, 8, 300, None), xq.XQ_E_SHAPE, "K=300"),
-    ((A16, A16, A16, 8, 49152 + 256, None), xq.XQ_E_SHAPE, "above the largest"),
+    ((A16, A16, A16, 8, 1048576 + 256, None), xq.XQ_E_SHAPE, "above the largest"),
     ((A1, A16, A16, 8, 256, None), xq.XQ_E_ALIGN, "y not 4-byte"),
     ((A16, A4, A16, 8, 256, None), xq.XQ_E_ALIGN, "w not 16-byte"),
     ((A16, A16, A4, 8, 256, None), xq.XQ_E_ALIGN, "xq not 16-byte"),

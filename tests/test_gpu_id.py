@@ -141,6 +141,8 @@ ID_SHAPES = [
     ("iq4nl", 3, 4097, 2048, [0, 1]),       # one row more: the persistent grid
     ("iq4nl", 3, 1000, 10240, [0, 2]),      # staged kernel (five units)
     ("iq4nl", 2, 130, 8192, [1, 0, 1]),     # four units
+    ("q4k", 3, 70, 53248, [2, 0]),          # rows past the staged limit
+    ("iq4nl", 3, 70, 53248, [1, 2]),        # rows past the staged limit
 ]
 
 

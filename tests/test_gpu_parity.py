@@ -199,6 +199,9 @@ Q4K_SHAPES = [
     ("n33_k11264_six_units_ragged", 33, 11264, 3010),
     ("n1000_k14080_seven_units_ragged", 1000, 14080, 3011),
     ("n50_k16384_eight_units", 50, 16384, 3012),
+    ("n64_k49408_unstaged", 64, 49408, 3013),          # one block past the staged limit
+    ("n40_k53248_unstaged", 40, 53248, 3014),
+    ("n3_k1048576_max", 3, 1048576, 3015),             # the largest K accepted
 ]
 
 
@@ -283,6 +286,7 @@ GEMV_Q8K = [
     ("n256_k1024", 256, 1024, 7601),                           # 4 rows per workgroup
     ("n512_k20480", 512, 20480, 7602),                         # loads past the row skipped
     ("n1280_k2304", 1280, 2304, 7603),                         # ragged unit tail
+    ("n512_k53248", 512, 53248, 7604),                         # activation from global memory
 ]
 
 
@@ -366,7 +370,9 @@ IQ4_SHAPES = [
     ("n300_k8192_four_units", 300, 8192, 5006),
     ("n70_k10240_five_units", 70, 10240, 5007),
     ("n20000_k512_two_rows_per_wave", 20000, 512, 5008),
-    ("n64_kmax", 64, 49152, 5009),
+    ("n64_k49152_staged_max", 64, 49152, 5009),
+    ("n40_k53248_unstaged", 40, 53248, 5010),
+    ("n3_k1048576_max", 3, 1048576, 5011),
 ]
 
 
@@ -757,14 +763,15 @@ def test_zero_activations_give_exact_zeros():
         assert_close(Y.reshape(-1), ref.reshape(-1), T.reshape(-1), "zero rows M=%d" % M)
 
 
-def test_gemm_max_k():
-    """The product at K = 49152 (192 super-blocks), the largest K the mat-vec
-    accepts, with ragged tokens and rows."""
-    M, N, K = 20, 130, 49152
+@pytest.mark.parametrize("K", [49152, 53248])
+def test_gemm_max_k(K):
+    """The product at K = 49152 (192 super-blocks, the longest row the
+    mat-vecs stage in LDS) and past it, with ragged tokens and rows."""
+    M, N = 20, 130
     g = wl.rng(7710)
     w = wl.q4k_weights(N, K, g)
     xqb = oracle.quantize_q8k(wl.activations(M, K, g))
-    _note("gemm max K")
+    _note("gemm max K %d" % K)
     Y = gpu_gemm(w, xqb, M, N, K)
     ref, T = oracle.gemm_q4k(w, xqb, M, N, K)
     assert_close(Y.reshape(-1), ref.reshape(-1), T.reshape(-1), "gemm max K")

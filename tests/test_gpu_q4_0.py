@@ -37,7 +37,8 @@ Q40_SHAPES = [
     ("n300_k8192_four_units", 300, 8192, 8208),
     ("n70_k10240_five_units", 70, 10240, 8209),
     ("n20000_k512_two_rows_per_wave", 20000, 512, 8210),
-    ("n64_kmax", 64, 49152, 8211),
+    ("n64_k49152_staged_max", 64, 49152, 8211),
+    ("n40_k53248_unstaged", 40, 53248, 8212),
 ]
 
 

@@ -114,3 +114,32 @@ def test_repack_head_round_trip():
     torch.cuda.synchronize()
     assert xq.xq_repack_dword_prefix_launches() - before == 1
     assert np.array_equal(res.cpu().numpy().reshape(N, row_bytes), w)
+
+
+@pytest.mark.parametrize("bpr,first,n,route", [
+    (1 << 16, 1 << 32, 1 << 16, 1),           # one whole row at global block 2^32: dword route
+    ((1 << 16) + 1, (1 << 32) + 7, 1000, 0),  # mid-row, odd bpr (row 65535, blocks 8..1007)
+], ids=["whole_row", "mid_row"])
+def test_repack_past_2_32_blocks(bpr, first, n, route):
+    """A chunk whose global block indices pass 2^32 takes the 64-bit-index
+    kernel. The resident base the library takes is row 0 of the matrix and it
+    writes only the chunk's rows, so only those rows are allocated here and
+    the base passed is that allocation shifted back by its first row. The
+    bytes equal the oracle's repack of the same blocks in a frame that starts
+    at that row, and nothing outside the chunk's blocks is written."""
+    row0 = first // bpr
+    rows = (first + n + bpr - 1) // bpr - row0
+    rb = xq.iq4nl_row_bytes(bpr)
+    blocks = wl.iq4nl_file_blocks(n, wl.rng(9520 + route))
+    res = dev(_poisoned(rows, bpr))
+    src = dev(blocks)
+    _note("repack past 2^32 blocks first=%d n=%d bpr=%d" % (first, n, bpr))
+    before = xq.xq_repack_dword_prefix_launches()
+    st = xq.lib().xq_repack_iq4nl(res.data_ptr() - row0 * rb, src.data_ptr(), n, first, bpr,
+                                  torch.cuda.current_stream().cuda_stream)
+    assert st == xq.XQ_OK, xq.xq_last_error()
+    torch.cuda.synchronize()
+    assert xq.xq_repack_dword_prefix_launches() - before == route
+    got = res.cpu().numpy().reshape(rows, rb)
+    want = oracle.repack_iq4nl(blocks, n, first - row0 * bpr, bpr, resident=_poisoned(rows, bpr))
+    assert np.array_equal(got, want)
