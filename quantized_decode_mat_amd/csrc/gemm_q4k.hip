@@ -19,13 +19,15 @@
 //
 // The min term's integer M_mnb = sum_j m_nbj * s_mbj, with s_mbj the q8_K's
 // stored sub-block sums, is a contraction over the block's 8 sub-blocks. It
-// runs on f32 MFMA (v_mfma_f32_16x16x4f32) with the integers themselves as
-// operands: |m * s| <= 63 * 4064 and |M| <= 2.05M < 2^24, so every product
-// and partial sum is an exact f32 integer and M comes out exact, whatever
-// the order. The block's float pass then applies both scales at once,
-// xs * (d * S - dmin * M), like the mat-vec: the per-block terms are exact
-// integers scaled once, so the f32 error stays a few units of 2^-24 of
-// |d*xs*S| + |dmin*xs*M| per block (no min plane on the int8 MFMA).
+// runs on one f16 MFMA per tile and block (v_mfma_f32_16x16x16_f16, K = 16)
+// with the integers split so every operand is exact in f16: s = 128*sh + sl
+// with sl in 0..127 and sh in -32..31, A = [sl_0..7, sh_0..7] for the token,
+// B = [m_0..7, 128*m_0..7] for the row. Every product (at most 127*63 or
+// 32*8064) and partial sum (|M| <= 2.05M < 2^24) is an exact f32 integer, so
+// M comes out exact whatever the order. The block's float pass then applies
+// both scales at once, xs * (d * S - dmin * M), like the mat-vec: the
+// per-block terms are exact integers scaled once, so the f32 error stays a
+// few units of 2^-24 of |d*xs*S| + |dmin*xs*M| per block.
 //
 // Tile: 64 tokens x 128 weight rows per 256-thread workgroup, four waves side
 // by side along the rows, each wave 64 x 32 = 4 x 2 MFMA tiles of 16 x 16, so
@@ -76,6 +78,7 @@ namespace xq {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BN = 128;          // weight rows per workgroup tile
@@ -344,6 +347,11 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
     for (int j = 0; j < 2; ++j) acc[i][j] = make_float4(0.f, 0.f, 0.f, 0.f);
   const v4i zero = {0, 0, 0, 0};
   const v4f zerof = {0.f, 0.f, 0.f, 0.f};
+  // The min term's operand split by lane quarter: q < 2 carry the low 7 bits
+  // of each sum (and m_j), q >= 2 the sum shifted down by 7 (and 128*m_j).
+  const int a_shift = (q >> 1) ? 7 : 0;
+  const int a_mask = (q >> 1) ? -1 : 127;
+  const _Float16 b_scale = static_cast<_Float16>((q >> 1) ? 128.0f : 1.0f);
 
   const StageOffsets<BMv> so = stage_offsets<BMv, ID>(M, N, nb, m0, n0, wave, lane, xrow_s);
   issue_stage<BMv>(stage0, xq, w, so, b_lo, wave, lane);
@@ -379,10 +387,11 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
     const uint8_t* wblk = stg + TL::kWOff;
 
     // ---- this lane's weight rows: the sub-block scale of each (row, group)
-    // for this lane's k-quarter, the block's d and dmin, and the min
-    // operands m_j for j = q and 4 + q ----
+    // for this lane's k-quarter, the block's d and dmin, and the min term's
+    // B operand (m_j or 128*m_j for k = 4q..4q+3) ----
     uint32_t scj[2][4];
-    float dn[2], dmn[2], mf[2][2];
+    float dn[2], dmn[2];
+    h4 mbh[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const uint8_t* blk = wblk + (32 * wave + 16 * nt + l16) * kQ4KBytes;
@@ -399,23 +408,27 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
       }
       dn[nt] = half_bits_to_float(hdr.x & 0xFFFFu);
       dmn[nt] = half_bits_to_float(hdr.x >> 16);
-      mf[nt][0] = static_cast<float>((m_lo >> (8 * q)) & 0xFFu);
-      mf[nt][1] = static_cast<float>((m_hi >> (8 * q)) & 0xFFu);
+      const uint32_t mw4 = (q & 1) ? m_hi : m_lo;  // mins 4(q&1) .. 4(q&1)+3
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        mbh[nt][i] =
+            static_cast<_Float16>(static_cast<unsigned short>((mw4 >> (8 * i)) & 0xFFu)) * b_scale;
     }
-    // ---- this block's M = sum_j m_j * s_j, exact (A = s_j of token
-    // m = 16mt + l16, B = m_j of row n, j = 4ks + q) ----
+    // ---- this block's M = sum_j m_j * s_j, exact: A = sl_j (lanes q < 2)
+    // or sh_j (q >= 2) of token m = 16mt + l16 for j = 4(q&1) .. +3 ----
     v4f cm[MT][2];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int r = 16 * mt + l16;
+      const int4 s4 = *reinterpret_cast<const int4*>(sum_s + 8 * r + 4 * (q & 1));
+      h4 ah;
+      ah[0] = static_cast<_Float16>(static_cast<short>((s4.x >> a_shift) & a_mask));
+      ah[1] = static_cast<_Float16>(static_cast<short>((s4.y >> a_shift) & a_mask));
+      ah[2] = static_cast<_Float16>(static_cast<short>((s4.z >> a_shift) & a_mask));
+      ah[3] = static_cast<_Float16>(static_cast<short>((s4.w >> a_shift) & a_mask));
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const float ma = static_cast<float>(sum_s[8 * r + 4 * ks + q]);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          cm[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(ma, mf[nt][ks],
-                                                            ks == 0 ? zerof : cm[mt][nt], 0, 0, 0);
-      }
+      for (int nt = 0; nt < 2; ++nt)
+        cm[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, mbh[nt], zerof, 0, 0, 0);
     }
 
 #pragma unroll
