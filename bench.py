@@ -49,16 +49,17 @@ INT8_PEAK_TOPS = 5000.0
 UP = (14336, 4096)
 DOWN = (4096, 14336)
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
+COUNTERS_MD = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 CSRC = os.path.join(ROOT, "quantized_decode_mat_amd", "csrc")
 # Each counted kernel: the name rocprofv3 reports (a prefix), the launches of a
 # --counters run, its algorithmic bytes per launch, and the sources its code
 # comes from (the summary is void once any of them changes).
 COUNTED = {
     "gemv_q4k_up_14336x4096": (
-        "void xq::(anonymous namespace)::gemv_q4k_kernel<2, 2, 4, 2, true, false, false>", 20,
+        "void xq::(anonymous namespace)::gemv_q4k_kernel<2, 2, 4, 2, true, false, false, false>", 20,
         33030144 + 5120 + 4 * 14336, ("gemv_q4k.hip", "q4k_row.h", "xq_device.h")),
     "gemv_q4k_down_4096x14336": (
-        "void xq::(anonymous namespace)::gemv_q4k_kernel<1, 7, 8, 3, true, false, false>", 20,
+        "void xq::(anonymous namespace)::gemv_q4k_kernel<1, 7, 8, 3, true, false, false, false>", 20,
         33030144 + 17920 + 4 * 4096, ("gemv_q4k.hip", "q4k_row.h", "xq_device.h")),
     "gemv_iq4nl_head_128256x4096": (
         "void xq::(anonymous namespace)::gemv_iq4nl_resident_kernel<2, false, 0>", 8,
@@ -116,6 +117,9 @@ def parse():
                    help="read the *_kernel_trace.csv of a rocprofv3 --kernel-trace run under "
                         "TRACE_DIR and print one JSON line per kernel (calls, mean/min/max us, "
                         "mean of the last 1000 launches), then exit (no GPU needed)")
+    p.add_argument("--pmc-table", nargs="+", metavar="DIR",
+                   help="print a markdown table of every counter in the rocprofv3 counter CSVs under "
+                        "the DIRs, per counted kernel of a --counters run, then exit (no GPU needed)")
     p.add_argument("--counters-summary", nargs="+", metavar="DIR",
                    help="FETCH_DIR WRITE_DIR [MFMA_DIR]: read the rocprofv3 CSVs of the "
                         "--counters runs (FETCH_SIZE; WRITE_SIZE; optionally " +
@@ -227,7 +231,7 @@ def counters_summary(fetch_dir, write_dir, mfma_dir=None):
             # GRBM_GUI_ACTIVE sums the eight XCDs' busy cycles; MFMA busy
             # cycles sum over the 1024 SIMDs (256 CUs x 4).
             "cycles_per_xcd": round(raw["GRBM_GUI_ACTIVE"] / XCDS, 1),
-            # every MFMA (int8 and the f32 min term) over the SIMD cycles
+            # every MFMA (int8 and the f16 min term) over the SIMD cycles
             "mfma_busy_frac": round(raw["SQ_VALU_MFMA_BUSY_CYCLES"] /
                                     (SIMDS * raw["GRBM_GUI_ACTIVE"] / XCDS), 4),
             # the int8 MFMA share, at 2048 int8 ops per cycle per SIMD
@@ -242,7 +246,102 @@ def counters_summary(fetch_dir, write_dir, mfma_dir=None):
     with open(COUNTERS, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
+    with open(COUNTERS_MD, "w") as f:
+        f.write(counters_markdown(out))
     print(json.dumps(out, indent=1))
+
+
+def counters_markdown(out):
+    """profiles/hbm_traffic_counters.md, written from the same numbers as the
+    JSON next to it."""
+    ks = out["kernels"]
+    lines = [
+        "# HBM traffic and MFMA counters: mat-vecs, IQ4_NL head and small-M product (cold weights)",
+        "",
+        "Generated by `bench.py --counters-summary` from the rocprofv3 counter runs below, over the committed "
+        "launch sequence of `bench.py --counters` (20 up and 20 down Q4_K mat-vecs over the 1.1 GB cold pool, 8 "
+        "IQ4_NL 128256x4096 mat-vecs over four rotating copies, 4 small-M products 512x14336x4096, then 5 device "
+        "copies and 5 streaming reads of 64 MiB). The same numbers are in "
+        "`profiles/hbm_traffic_counters.json`, which `bench.py` reads for the roofline's `traffic`.",
+        "",
+        "```",
+        "cd /tmp && TMPDIR=/tmp timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --output-format csv \\",
+        "    -d $OUT/pmc_1 -o pmc -- python3 $REPO/bench.py --counters --no-cpu",
+        "cd /tmp && TMPDIR=/tmp timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --output-format csv \\",
+        "    -d $OUT/pmc_2 -o pmc -- python3 $REPO/bench.py --counters --no-cpu",
+        "cd /tmp && TMPDIR=/tmp timeout -s KILL 120 rocprofv3 --pmc " + " ".join(MFMA_COUNTERS) + " \\",
+        "    --output-format csv -d $OUT/pmc_3 -o pmc -- python3 $REPO/bench.py --counters --no-cpu",
+        "python3 $REPO/bench.py --counters-summary $OUT/pmc_1 $OUT/pmc_2 $OUT/pmc_3",
+        "```",
+        "",
+        "Calibration against the plain device copy of known size (64 MiB read and 64 MiB written per copy): "
+        "FETCH_SIZE x %.5f, WRITE_SIZE x %.5f." % (out["fetch_calibration"], out["write_calibration"]),
+        "",
+        "| kernel | FETCH_SIZE KiB/launch | WRITE_SIZE KiB/launch | calibrated HBM bytes | algorithmic bytes "
+        "| ratio |",
+        "|---|---|---|---|---|---|",
+    ]
+    for name, k in ks.items():
+        lines.append("| %s `%s` | %.1f | %.1f | %d | %d | %.4f |" % (
+            name, k["kernel"].split("::")[-1], k["fetch_size_kib_per_launch"],
+            k["write_size_kib_per_launch"], k["hbm_bytes_per_launch"], k["alg_bytes_per_launch"],
+            k["traffic_over_alg"]))
+    lines += ["", "Algorithmic bytes: every weight byte, the q8_K activation and the f32 output once (the "
+              "product: W once, the 512-token q8_K once, Y once). Where the ratio sits above 1: the Q4_K "
+              "mat-vecs' lanes each load their block's 16-byte header (the cache serves the repeats); each "
+              "of the IQ4_NL head's workgroups stages the q8_K row from L2, which the non-temporal weight "
+              "stream evicts; the small-M product's weight tiles re-read the 2.6 MB of activations, and the "
+              "token tiles of one weight tile re-read its stage when they do not share an L2 in time."]
+    pre = ks.get(PREFILL[0], {}).get("mfma")
+    if pre:
+        pl = pre["per_launch"]
+        lines += ["", "**MFMA pass (small-M product, per launch).** SQ_INSTS_VALU_MFMA_MOPS_I8 = %d (units of "
+                  "512 ops): %d int8 ops executed, %.2fx the %d algorithmic ops (the two scale planes; the "
+                  "min term runs on f16 MFMA and is not counted there). SQ_VALU_MFMA_BUSY_CYCLES = %d. "
+                  "GRBM_GUI_ACTIVE = %d, the eight XCDs' busy cycles summed (%.0f per XCD). All MFMA busy "
+                  "%.1f%% of the SIMD cycles; int8 MFMA busy %.1f%% (at 2048 int8 ops per cycle per SIMD); "
+                  "algorithmic work %.1f%% of the int8 capacity of the run." % (
+                      pl["SQ_INSTS_VALU_MFMA_MOPS_I8"], pre["int8_ops_executed"],
+                      pre["executed_over_algorithmic"], PREFILL[1], pl["SQ_VALU_MFMA_BUSY_CYCLES"],
+                      pl["GRBM_GUI_ACTIVE"], pre["cycles_per_xcd"], 100 * pre["mfma_busy_frac"],
+                      100 * pre["int8_busy_frac"], 100 * pre["useful_int8_frac"])]
+    lines += ["", "Each entry carries the sha256 (first 16 hex digits) of the sources its kernel is built "
+              "from; `bench.py` reports `traffic: null` once they differ from the committed files.", ""]
+    return "\n".join(lines)
+
+
+def pmc_table(dirs):
+    """A markdown table of every counter found in the rocprofv3 counter CSVs
+    under `dirs`, per counted kernel: the counter's value per dispatch (summed
+    over the CSV's rows for that dispatch), averaged over the kernel's last n
+    dispatches of the `bench.py --counters` sequence; a counter collected in
+    several runs is averaged over them."""
+    import csv
+    import glob
+    found = {}
+    for d in dirs:
+        per = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    key = (r["Counter_Name"], int(r["Dispatch_Id"]), r["Kernel_Name"])
+                    per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for cn in {k[0] for k in per}:
+            for name, spec in COUNTED.items():
+                kname, n = spec[0], spec[1]
+                v = sorted((disp, val) for (c, disp, kn), val in per.items()
+                           if c == cn and kn.startswith(kname))[-n:]
+                if len(v) == n:
+                    found.setdefault((cn, name), []).append(sum(x for _, x in v) / n)
+    names = list(COUNTED)
+    rows = ["| counter | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    for cn in sorted({c for c, _ in found}):
+        vals = []
+        for name in names:
+            v = found.get((cn, name))
+            vals.append("{:,.0f}".format(sum(v) / len(v)) if v else "-")
+        rows.append("| `%s` | %s |" % (cn, " | ".join(vals)))
+    print("\n".join(rows))
 
 
 def main():
@@ -254,6 +353,9 @@ def main():
         return
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.pmc_table:
+        pmc_table(args.pmc_table)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
