@@ -515,10 +515,13 @@ hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64
   const int n = static_cast<int>(N);
   // Launch shapes chosen by measurement on MI355X (cold weights):
   //  * rows of one or two units: every load of a row in flight at once,
-  //    two rows per wave when there are enough rows to fill the device;
+  //    two rows per wave when there are enough rows to fill the device
+  //    (14336x4096: 7.31 us against 7.63-8.90 for one row per wave or eight
+  //    and sixteen waves per workgroup);
   //  * rows of five to seven units: the whole row in flight at once (clamped
   //    loads, static wait counts), eight waves per workgroup (the activation
-  //    row is staged half as often): 3-15% faster than two batches;
+  //    row is staged half as often): 3-15% faster than two batches
+  //    (4096x14336: 7.83 us; four, twelve or sixteen waves 8.8-10.8);
   //  * longer rows: batches of four units, eight waves per workgroup, loads
   //    past the row skipped (a whole row of eight or more units in flight
   //    is slower).
@@ -531,7 +534,9 @@ hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64
   }
   if (units == 2) {
     if (rows_all >= 8192) return launch_cfg<2, 2, 4, 2, true>(y, wb, xb, n, nb, id, stream);
-    return launch_cfg<1, 2, 4, 2, true>(y, wb, xb, n, nb, id, stream);
+    // 4096x4096: 3.75 us with eight waves per workgroup against 3.88 with
+    // four (the activation row staged half as often).
+    return launch_cfg<1, 2, 8, 2, true>(y, wb, xb, n, nb, id, stream);
   }
   if (units == 3) return launch_cfg<1, 3, 8, 2, true>(y, wb, xb, n, nb, id, stream);
   if (units == 4) return launch_cfg<1, 4, 8, 3, true>(y, wb, xb, n, nb, id, stream);
