@@ -7,8 +7,8 @@
 // "25 — Writing XPU Kernels", section 25.3: fill the device first, then feed
 // the tile; a GEMM that reuses the weight tile across the token block is the
 // point of the prefill path. Here the integer products are a dense
-// contraction, so they run on int8 MFMA (v_mfma_i32_16x16x64_i8, K = 64 = one
-// nibble group = sub-blocks 2g and 2g+1).
+// contraction, so they run on int8 MFMA (v_mfma_i32_16x16x64_i8, K = 64: two
+// sub-blocks' worth of weights per MFMA).
 //
 // One MFMA's K spans two sub-blocks with different 6-bit scales, so the
 // scale cannot be applied after the MFMA without splitting K. Instead the
@@ -386,9 +386,10 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
     const int* sum_s = reinterpret_cast<const int*>(stg + TL::kSumOff);
     const uint8_t* wblk = stg + TL::kWOff;
 
-    // ---- this lane's weight rows: the sub-block scale of each (row, group)
-    // for this lane's k-quarter, the block's d and dmin, and the min term's
-    // B operand (m_j or 128*m_j for k = 4q..4q+3) ----
+    // ---- this lane's weight rows: the sub-block scale of each (row, MFMA t)
+    // for this lane (sub-block 2*(q>>1) + (t&1) + 4*(t>>1), below), the
+    // block's d and dmin, and the min term's B operand (m_j or 128*m_j for
+    // k = 4q..4q+3) ----
     uint32_t scj[2][4];
     float dn[2], dmn[2];
     h4 mbh[2];
@@ -402,9 +403,9 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
       const uint32_t sc_hi = (h3 & 0x0F0F0F0Fu) | ((h1 >> 2) & 0x30303030u);
       const uint32_t m_hi = ((h3 >> 4) & 0x0F0F0F0Fu) | ((h2 >> 2) & 0x30303030u);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int shift = 8 * (2 * (g & 1) + (q >> 1));
-        scj[nt][g] = (((g < 2) ? sc_lo : sc_hi) >> shift) & 0xFFu;
+      for (int t = 0; t < 4; ++t) {
+        const int shift = 8 * (2 * (q >> 1) + (t & 1));
+        scj[nt][t] = (((t < 2) ? sc_lo : sc_hi) >> shift) & 0xFFu;
       }
       dn[nt] = half_bits_to_float(hdr.x & 0xFFFFu);
       dmn[nt] = half_bits_to_float(hdr.x >> 16);
@@ -431,27 +432,40 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
         cm[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ah, mbh[nt], zerof, 0, 0, 0);
     }
 
+    // ---- the four MFMAs of a tile: MFMA t takes, in lane q, one nibble half
+    // of a 16-byte chunk of the row's nibbles: chunk q (bytes 16q..16q+15)
+    // for t = 0, 1 and chunk q + 4 for t = 2, 3, low nibbles for even t and
+    // high nibbles for odd t. Chunk c holds the low (sub-block 2*(c/2)) and
+    // high (sub-block 2*(c/2)+1) nibbles of weights 64*(c/2) + 16*(c%2) + i,
+    // so every loaded byte feeds two MFMAs, and lane q's sub-block in MFMA t
+    // is j = 2*(q>>1) + (t&1) + 4*(t>>1). The A operand reads the codes of
+    // the same weights: 16-byte code chunk 4*(q>>1) + (q&1) + 2*(t&1) +
+    // 8*(t>>1). (Any assignment of the 64 k of an MFMA to lanes is the same
+    // contraction as long as A and B agree on it.) ----
+    uint4 rw[2][2];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      // A operands: token rows, codes k = 64g + 16q .. +15.
+    for (int nt = 0; nt < 2; ++nt) {
+      const uint8_t* blk = wblk + (32 * wave + 16 * nt + l16) * kQ4KBytes;
+      rw[nt][0] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * q);
+      rw[nt][1] = *reinterpret_cast<const uint4*>(blk + 16 + 64 + 16 * q);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int ct = 4 * (q >> 1) + (q & 1) + 2 * (t & 1) + 8 * (t >> 1);
       v4i a[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int r = 16 * mt + l16;
-        a[mt] = *reinterpret_cast<const v4i*>(act + 256 * r + 16 * ((4 * g + q) ^ (r & 15)));
+        a[mt] = *reinterpret_cast<const v4i*>(act + 256 * r + 16 * (ct ^ (r & 15)));
       }
-      // B operands (weight row n, k = 16q..16q+15 of group g): q = 0, 1
-      // take the low nibbles of group bytes 0..15 / 16..31 (sub-block 2g),
-      // q = 2, 3 the high nibbles of the same bytes (sub-block 2g+1).
       v4i ba[2], bb[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const uint8_t* blk = wblk + (32 * wave + 16 * nt + l16) * kQ4KBytes;
-        const uint4 raw = *reinterpret_cast<const uint4*>(blk + 16 + 32 * g + 16 * (q & 1));
-        const uint32_t hs = (q >> 1) ? 4u : 0u;
+        const uint4 raw = rw[nt][t >> 1];
+        const uint32_t hs = (t & 1) ? 4u : 0u;
         const uint32_t c0 = (raw.x >> hs) & 0x0F0F0F0Fu, c1 = (raw.y >> hs) & 0x0F0F0F0Fu;
         const uint32_t c2 = (raw.z >> hs) & 0x0F0F0F0Fu, c3 = (raw.w >> hs) & 0x0F0F0F0Fu;
-        const uint32_t fa = scj[nt][g] >> 3, fb = scj[nt][g] & 7u;
+        const uint32_t fa = scj[nt][t] >> 3, fb = scj[nt][t] & 7u;
         ba[nt] = (v4i){(int)mul_bytes(c0, fa), (int)mul_bytes(c1, fa), (int)mul_bytes(c2, fa),
                        (int)mul_bytes(c3, fa)};
         bb[nt] = (v4i){(int)mul_bytes(c0, fb), (int)mul_bytes(c1, fb), (int)mul_bytes(c2, fb),
@@ -461,8 +475,8 @@ __device__ __forceinline__ void gemm_tile(const TileLds& lds, int wg, float* __r
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          sa[mt][nt] = mfma(a[mt], ba[nt], g == 0 ? zero : sa[mt][nt]);
-          sb[mt][nt] = mfma(a[mt], bb[nt], g == 0 ? zero : sb[mt][nt]);
+          sa[mt][nt] = mfma(a[mt], ba[nt], t == 0 ? zero : sa[mt][nt]);
+          sb[mt][nt] = mfma(a[mt], bb[nt], t == 0 ? zero : sb[mt][nt]);
         }
     }
 
