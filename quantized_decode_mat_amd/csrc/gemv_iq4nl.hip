@@ -24,6 +24,9 @@
 //    barrier per row; the activation leaves L2 once per workgroup.
 //  * longer rows: one row per wave, up to eight units of loads in flight,
 //    the activation read from the LDS copy per row.
+#include <algorithm>
+#include <atomic>
+
 #include "xq_device.h"
 #include "xq_launch.h"
 
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void gemv_iq4nl_kernel(float* __restrict_
 constexpr int kResidentUnits = 4;
 constexpr int kResWaves = 8;
 constexpr int kResThreads = kResWaves * kWave;
-constexpr int kResMaxGroups = 2048;
+constexpr int kResMaxGroups = 2048;  // grouped launches: workgroups per slot
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -307,12 +310,50 @@ __global__ __launch_bounds__(kResThreads) void gemv_iq4nl_resident_kernel(
   }
 }
 
+// Workgroups of gemv_iq4nl_resident_kernel<U, false, FMT> resident at once on
+// the current device (queried once per instance and device).
+template <int U, int FMT>
+hipError_t resident_capacity(int* cap_out) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> resident[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  int cap = resident[dev].load(std::memory_order_relaxed);
+  if (cap == 0) {
+    int per_cu = 0, cus = 0;
+    // The largest staging a row of U units asks for: 8*U q8_K blocks.
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void*>(&gemv_iq4nl_resident_kernel<U, false, FMT>),
+        kResThreads, static_cast<size_t>(8 * U) * kQ8KBytes);
+    if (e != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+      return e;
+    cap = std::max(1, per_cu) * std::max(1, cus);
+    resident[dev].store(cap, std::memory_order_relaxed);
+  }
+  *cap_out = cap;
+  return hipSuccess;
+}
+
 template <int U, int FMT>
 hipError_t launch_resident(float* y, const uint8_t* w, const uint8_t* xq, int N, int bpr,
                            int prefix, int64_t row_bytes, int nq8, const IdArgs& id,
                            hipStream_t stream) {
   int grid = (N + kResWaves - 1) / kResWaves;
-  if (grid > kResMaxGroups) grid = kResMaxGroups;
+  if (!id.sel) {
+    // Dense launches: at most two rounds of resident workgroups fit one
+    // resident round (14336 x 4096: 1792 workgroups in 1.75 rounds 9.89 us,
+    // 1024 in one 8.12); longer launches take two rounds (the 128256 x 4096
+    // head: 47.0 us against 47.5 in one round and 48.1 in three).
+    int cap = 0;
+    const hipError_t e = resident_capacity<U, FMT>(&cap);
+    if (e != hipSuccess) return e;
+    grid = (grid > 2 * cap) ? 2 * cap : std::min(grid, cap);
+  } else if (grid > kResMaxGroups) {
+    grid = kResMaxGroups;
+  }
   const size_t lds = static_cast<size_t>(nq8) * kQ8KBytes;
   if (id.sel)
     hipLaunchKernelGGL((gemv_iq4nl_resident_kernel<U, true, FMT>), dim3(grid, id.used),
