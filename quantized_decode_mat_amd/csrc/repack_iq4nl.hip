@@ -85,6 +85,72 @@ __global__ __launch_bounds__(kRepackThreads) void repack_iq4nl_kernel(
   }
 }
 
+// The tiled form, for a 16-byte aligned source: a workgroup stages 256 file
+// blocks (4608 bytes, a whole number of 16-byte chunks) into LDS with 16-byte
+// loads, then each item moves one whole block from LDS: its 16 payload bytes
+// as one 16-byte store where the destination is 16-byte aligned (four dword
+// stores otherwise), and its scale. The 2-byte loads of the direct form bring
+// a wave 128 bytes per load instruction; the staging brings 1 KiB, and one
+// row division per block replaces four. Both routes as above: the scale goes
+// as a half (and the pad after an odd row's last scale), or, in the
+// dword-prefix route when the block starts a scale pair (even index within
+// its row), as the pair's dword; the pair's second scale comes from the tile,
+// or from global memory when the pair straddles the tile's end.
+constexpr int kTileBlocks = 256;
+constexpr int kTileBytes = kTileBlocks * kFileBlockBytes;
+static_assert(kTileBytes % 16 == 0, "a tile is whole 16-byte chunks");
+
+template <bool DWORD_PREFIX, typename I>
+__global__ __launch_bounds__(kRepackThreads) void repack_iq4nl_tiled_kernel(
+    uint8_t* __restrict__ out, const uint8_t* __restrict__ src, int64_t n64, int64_t base64,
+    int64_t bpr64, int64_t prefix, int64_t row_bytes) {
+  __shared__ __align__(16) uint16_t tile[kTileBytes / 2];
+  const I n = static_cast<I>(n64);
+  const I block_base = static_cast<I>(base64);
+  const I bpr = static_cast<I>(bpr64);
+  const I b0 = static_cast<I>(blockIdx.x) * kTileBlocks;  // the tile's first block in the chunk
+  const int nb = static_cast<int>(min(n - b0, static_cast<I>(kTileBlocks)));
+  const uint8_t* tsrc = src + static_cast<int64_t>(b0) * kFileBlockBytes;
+  const int bytes = nb * kFileBlockBytes;  // even
+  const int full = bytes >> 4;             // whole 16-byte chunks inside the chunk
+  for (int c = threadIdx.x; c < full; c += kRepackThreads)
+    reinterpret_cast<uint4*>(tile)[c] = reinterpret_cast<const uint4*>(tsrc)[c];
+  for (int h = 8 * full + threadIdx.x; h < (bytes >> 1); h += kRepackThreads)
+    tile[h] = reinterpret_cast<const uint16_t*>(tsrc)[h];
+  __syncthreads();
+
+  for (int b = threadIdx.x; b < nb; b += kRepackThreads) {
+    const I gb = block_base + b0 + static_cast<I>(b);
+    const I row = gb / bpr;
+    const I j = gb - row * bpr;
+    const int hb = (b * kFileBlockBytes) >> 1;  // the block's first half in the tile
+    uint4 p;
+    p.x = static_cast<uint32_t>(tile[hb + 1]) | (static_cast<uint32_t>(tile[hb + 2]) << 16);
+    p.y = static_cast<uint32_t>(tile[hb + 3]) | (static_cast<uint32_t>(tile[hb + 4]) << 16);
+    p.z = static_cast<uint32_t>(tile[hb + 5]) | (static_cast<uint32_t>(tile[hb + 6]) << 16);
+    p.w = static_cast<uint32_t>(tile[hb + 7]) | (static_cast<uint32_t>(tile[hb + 8]) << 16);
+    uint8_t* orow = out + static_cast<int64_t>(row) * row_bytes;
+    uint8_t* dst = orow + prefix + 16 * static_cast<int64_t>(j);
+    if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      *reinterpret_cast<uint4*>(dst) = p;
+    } else {
+      uint32_t* d4 = reinterpret_cast<uint32_t*>(dst);
+      d4[0] = p.x; d4[1] = p.y; d4[2] = p.z; d4[3] = p.w;
+    }
+    const uint32_t sc = tile[hb];
+    if (!DWORD_PREFIX) {
+      reinterpret_cast<uint16_t*>(orow)[j] = static_cast<uint16_t>(sc);
+      if (j == bpr - 1 && (bpr & 1)) reinterpret_cast<uint16_t*>(orow)[j + 1] = 0;
+    } else if ((j & 1) == 0) {
+      uint32_t hi = 0;
+      if (j + 1 < bpr)
+        hi = (b + 1 < nb) ? tile[((b + 1) * kFileBlockBytes) >> 1]
+                          : reinterpret_cast<const uint16_t*>(tsrc)[((b + 1) * kFileBlockBytes) >> 1];
+      *reinterpret_cast<uint32_t*>(orow + 2 * static_cast<int64_t>(j)) = sc | (hi << 16);
+    }
+  }
+}
+
 std::atomic<int64_t> g_dword_prefix_launches{0};
 
 }  // namespace
@@ -103,6 +169,35 @@ hipError_t launch_repack_iq4nl(void* resident, const void* file_blocks, int64_t 
   const int64_t grid = (items + kRepackThreads - 1) / kRepackThreads;
   uint8_t* out = static_cast<uint8_t*>(resident);
   const uint16_t* src = static_cast<const uint16_t*>(file_blocks);
+  if ((reinterpret_cast<uintptr_t>(file_blocks) & 15) == 0) {
+    // The tiled form (16-byte aligned source). Its indices: block and row
+    // indices below block_base + n, tile indices below n / 256.
+    const int64_t tiles = (n + kTileBlocks - 1) / kTileBlocks;
+    const bool t32 = block_base + n < (int64_t{1} << 32);
+    const uint8_t* s8 = static_cast<const uint8_t*>(file_blocks);
+    if (row_aligned) {
+      if (t32)
+        hipLaunchKernelGGL((repack_iq4nl_tiled_kernel<true, uint32_t>),
+                           dim3(static_cast<uint32_t>(tiles)), dim3(kRepackThreads), 0, stream, out,
+                           s8, n, block_base, bpr, prefix, row_bytes);
+      else
+        hipLaunchKernelGGL((repack_iq4nl_tiled_kernel<true, int64_t>),
+                           dim3(static_cast<uint32_t>(tiles)), dim3(kRepackThreads), 0, stream, out,
+                           s8, n, block_base, bpr, prefix, row_bytes);
+      const hipError_t e = hipGetLastError();
+      if (e == hipSuccess) g_dword_prefix_launches.fetch_add(1, std::memory_order_relaxed);
+      return e;
+    }
+    if (t32)
+      hipLaunchKernelGGL((repack_iq4nl_tiled_kernel<false, uint32_t>),
+                         dim3(static_cast<uint32_t>(tiles)), dim3(kRepackThreads), 0, stream, out,
+                         s8, n, block_base, bpr, prefix, row_bytes);
+    else
+      hipLaunchKernelGGL((repack_iq4nl_tiled_kernel<false, int64_t>),
+                         dim3(static_cast<uint32_t>(tiles)), dim3(kRepackThreads), 0, stream, out,
+                         s8, n, block_base, bpr, prefix, row_bytes);
+    return hipGetLastError();
+  }
   // 32-bit indices when the largest of them (the grid's items, the last
   // global block) fits below 2^32.
   const int64_t kI32 = int64_t{1} << 32;

@@ -143,3 +143,24 @@ def test_repack_past_2_32_blocks(bpr, first, n, route):
     got = res.cpu().numpy().reshape(rows, rb)
     want = oracle.repack_iq4nl(blocks, n, first - row0 * bpr, bpr, resident=_poisoned(rows, bpr))
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("rows,bpr,cuts", [
+    (7, 9, [0, 5, 9, 27, 40, 63]),            # odd bpr: pads, chunks on and off rows
+    (3, 1100, [0, 1100, 1700, 3300]),         # tiles of 512 blocks inside and across rows
+])
+def test_repack_unaligned_source_takes_the_direct_route(rows, bpr, cuts):
+    # A 16-byte aligned source is staged through LDS in tiles of 512 blocks;
+    # any other source (2-byte aligned at least) is read directly as halves.
+    # Both must write the oracle's bytes.
+    blocks = wl.iq4nl_file_blocks(rows * bpr, wl.rng(9540 + bpr))
+    _note("repack unaligned source rows=%d bpr=%d" % (rows, bpr))
+    for offset in (2, 0):
+        res = dev(_poisoned(rows, bpr))
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            buf = torch.zeros(18 * (b - a) + 16, dtype=torch.uint8, device="cuda")
+            buf[offset:offset + 18 * (b - a)] = dev(blocks[a:b].reshape(-1))
+            xq.xq_repack_iq4nl(res, buf.data_ptr() + offset, b - a, a, bpr)
+            torch.cuda.synchronize()
+        got = res.cpu().numpy().reshape(rows, -1)
+        assert np.array_equal(got, oracle.repack_iq4nl(blocks, rows * bpr, 0, bpr)), offset
