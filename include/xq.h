@@ -301,7 +301,9 @@ xq_status xq_gemv_iq4nl_id(float *y, const void *slab, const void *xq, const int
  *  file_blocks  the chunk: n_blocks blocks back to back, global blocks
  *               block_base .. block_base + n_blocks - 1 of a matrix of bpr
  *               blocks per row (block g is block g % bpr of row g / bpr);
- *               2-byte aligned.
+ *               2-byte aligned (16-byte aligned chunks are staged through LDS
+ *               with 16-byte loads, the faster route; the bytes written are
+ *               the same).
  *  resident     row 0 of the matrix in resident rows (xq_iq4nl_bytes per row
  *               for K = 32*bpr: bpr f16 scales, zero-padded to a multiple of
  *               4 bytes, then bpr payloads of 16 B); 4-byte aligned; must hold
