@@ -310,19 +310,21 @@ __global__ __launch_bounds__(kResThreads) void gemv_iq4nl_resident_kernel(
   }
 }
 
-// Workgroups of gemv_iq4nl_resident_kernel<U, false, FMT> resident at once on
-// the current device (queried once per instance and device).
+// The device's CU count and the workgroups of gemv_iq4nl_resident_kernel<U,
+// false, FMT> resident at once on it (queried once per instance and device).
 template <int U, int FMT>
-hipError_t resident_capacity(int* cap_out) {
+hipError_t resident_shape(int* cus_out, int* cap_out) {
   constexpr int kMaxDev = 64;
   static std::atomic<int> resident[kMaxDev];
+  static std::atomic<int> cu_count[kMaxDev];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
   int cap = resident[dev].load(std::memory_order_relaxed);
-  if (cap == 0) {
-    int per_cu = 0, cus = 0;
+  int cus = cu_count[dev].load(std::memory_order_relaxed);
+  if (cap == 0 || cus == 0) {
+    int per_cu = 0;
     // The largest staging a row of U units asks for: 8*U q8_K blocks.
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
         &per_cu, reinterpret_cast<const void*>(&gemv_iq4nl_resident_kernel<U, false, FMT>),
@@ -330,9 +332,12 @@ hipError_t resident_capacity(int* cap_out) {
     if (e != hipSuccess) return e;
     if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
       return e;
-    cap = std::max(1, per_cu) * std::max(1, cus);
+    cus = std::max(1, cus);
+    cap = std::max(1, per_cu) * cus;
+    cu_count[dev].store(cus, std::memory_order_relaxed);
     resident[dev].store(cap, std::memory_order_relaxed);
   }
+  *cus_out = cus;
   *cap_out = cap;
   return hipSuccess;
 }
@@ -343,14 +348,19 @@ hipError_t launch_resident(float* y, const uint8_t* w, const uint8_t* xq, int N,
                            hipStream_t stream) {
   int grid = (N + kResWaves - 1) / kResWaves;
   if (!id.sel) {
-    // Dense launches: at most two rounds of resident workgroups fit one
-    // resident round (14336 x 4096: 1792 workgroups in 1.75 rounds 9.89 us,
-    // 1024 in one 8.12); longer launches take two rounds (the 128256 x 4096
-    // head: 47.0 us against 47.5 in one round and 48.1 in three).
-    int cap = 0;
-    const hipError_t e = resident_capacity<U, FMT>(&cap);
+    // Dense launches, by rows (measured on MI355X, cold weights, K = 4096 and
+    // 8192): up to 16384 rows one workgroup per CU, each wave walking two to
+    // eight rows (4096x4096 4.09 -> 3.99 us, 8192x4096 6.53 -> 5.51,
+    // 14336x4096 8.15 -> 7.72, 16384x8192 16.5 -> 14.0); up to 65536 rows two
+    // per CU (24576x4096 13.2 -> 11.2, 49152x4096 21.3 -> 19.7); longer, two
+    // rounds of resident workgroups (the 128256x4096 head: 47.1 us against
+    // 47.4 at two per CU and 49.1 at one). Grids that are not whole multiples
+    // of the CUs measured slower (384 workgroups: 4.5 us on 4096x4096).
+    int cus = 0, cap = 0;
+    const hipError_t e = resident_shape<U, FMT>(&cus, &cap);
     if (e != hipSuccess) return e;
-    grid = (grid > 2 * cap) ? 2 * cap : std::min(grid, cap);
+    const int target = (N <= 16384) ? cus : (N <= 65536) ? 2 * cus : 2 * cap;
+    grid = std::min(grid, target);
   } else if (grid > kResMaxGroups) {
     grid = kResMaxGroups;
   }
