@@ -370,6 +370,9 @@ IQ4_SHAPES = [
     ("n300_k8192_four_units", 300, 8192, 5006),
     ("n70_k10240_five_units", 70, 10240, 5007),
     ("n20000_k512_two_rows_per_wave", 20000, 512, 5008),
+    ("n16384_k4096_grid_one_per_cu", 16384, 4096, 5012),
+    ("n16385_k2048_grid_two_per_cu", 16385, 2048, 5013),
+    ("n65537_k2048_grid_two_rounds", 65537, 2048, 5014),
     ("n64_k49152_staged_max", 64, 49152, 5009),
     ("n40_k53248_unstaged", 40, 53248, 5010),
     ("n3_k1048576_max", 3, 1048576, 5011),
