@@ -186,3 +186,38 @@ def test_sweep_grouped_product(T, U, E, rows, K, per_slot, seed):
     # Outputs outside the sample: NaN exactly where a selection is stray.
     assert np.array_equal(np.isnan(Y).all(axis=2), (ids < 0) | (ids >= E))
     assert not np.isnan(Y[(ids >= 0) & (ids < E)]).any()
+
+
+def _repack_cases():
+    g = wl.rng(8400)
+    out = []
+    for i in range(8):
+        bpr = int(g.integers(1, 1200))
+        rows = int(g.integers(1, 9))
+        n = rows * bpr
+        cuts = sorted(set([0, n] + [int(c) for c in g.integers(1, max(2, n), size=int(g.integers(0, 5)))]))
+        out.append((rows, bpr, cuts, 0 if i % 2 == 0 else 2, int(g.integers(0, 2 ** 31))))
+    return out
+
+
+REPACK = _repack_cases()
+
+
+@pytest.mark.parametrize("rows,bpr,cuts,offset,seed", REPACK,
+                         ids=["r%d_bpr%d_c%d_off%d" % (s[0], s[1], len(s[2]) - 1, s[3]) for s in REPACK])
+def test_sweep_repack(rows, bpr, cuts, offset, seed):
+    # Random chunkings of a matrix's file blocks, each chunk from a 16-byte
+    # aligned source (staged through LDS) or a 2-byte aligned one (read as
+    # halves): the resident rows equal the oracle's byte for byte, and no
+    # byte of the poisoned buffer is left unwritten.
+    import torch
+    blocks = wl.iq4nl_file_blocks(rows * bpr, wl.rng(seed))
+    res = dev(np.full((rows, xq.iq4nl_row_bytes(bpr)), 0xAB, dtype=np.uint8))
+    _note("sweep repack rows=%d bpr=%d cuts=%s offset=%d" % (rows, bpr, cuts, offset))
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        buf = torch.zeros(18 * (b - a) + 16, dtype=torch.uint8, device="cuda")
+        buf[offset:offset + 18 * (b - a)] = dev(blocks[a:b].reshape(-1))
+        xq.xq_repack_iq4nl(res, buf.data_ptr() + offset, b - a, a, bpr)
+        torch.cuda.synchronize()
+    got = res.cpu().numpy().reshape(rows, -1)
+    assert np.array_equal(got, oracle.repack_iq4nl(blocks, rows * bpr, 0, bpr))
