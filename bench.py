@@ -51,6 +51,7 @@ DOWN = (4096, 14336)
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_traffic_counters.json")
 COUNTERS_MD = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 CSRC = os.path.join(ROOT, "quantized_decode_mat_amd", "csrc")
+BUILD_SCRIPT = os.path.join(ROOT, "quantized_decode_mat_amd", "build.py")
 # Each counted kernel: the name rocprofv3 reports (a prefix), the launches of a
 # --counters run, its algorithmic bytes per launch, and the sources its code
 # comes from (the summary is void once any of them changes).
@@ -134,9 +135,11 @@ def sha_of(path):
 
 
 def sources_sha(files):
+    """Hash of a kernel's sources and of the build script that sets its
+    compiler flags: either changes the machine code the counters measured."""
     h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(CSRC, f), "rb") as fh:
+    for path in [os.path.join(CSRC, f) for f in files] + [BUILD_SCRIPT]:
+        with open(path, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -306,7 +309,8 @@ def counters_markdown(out):
                       pl["GRBM_GUI_ACTIVE"], pre["cycles_per_xcd"], 100 * pre["mfma_busy_frac"],
                       100 * pre["int8_busy_frac"], 100 * pre["useful_int8_frac"])]
     lines += ["", "Each entry carries the sha256 (first 16 hex digits) of the sources its kernel is built "
-              "from; `bench.py` reports `traffic: null` once they differ from the committed files.", ""]
+              "from and of the build script that sets the compiler flags; `bench.py` reports "
+              "`traffic: null` once they differ from the committed files.", ""]
     return "\n".join(lines)
 
 

@@ -5,7 +5,14 @@
 
 Every HIP translation unit is compiled with packed-FP32 instructions turned
 off (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the float code
-here is plain scalar code. Code objects are emitted as version 5, which the
+here is plain scalar code. Kernel arguments are preloaded: the first 16
+dwords of every kernel's argument segment arrive in SGPRs when a wave starts
+(``-mllvm -amdgpu-kernarg-preload-count=16``, a gfx950 feature), so no
+workgroup waits on a scalar load of its pointers before its first memory
+access. Each kernel keeps a 256-byte prologue that loads the same registers
+for firmware without the feature. Measured against the same sources without
+it, in one process with the two builds interleaved: the FFN step 19.65 ->
+19.28 us, the 16-token 14336x4096 product 12.94 -> 12.40 us. Code objects are emitted as version 5, which the
 HIP runtime bundled with the PyTorch wheel (the runtime libxq shares with
 torch in one process) loads.
 """
@@ -42,6 +49,7 @@ FLAGS = [
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"),
 ]
 
