@@ -83,7 +83,9 @@ enum {
  * d == 0); sum_j = sum of codes 32j..32j+31.
  *
  *  xq    device, out: rows*(K/256) q8_K blocks, 16-byte aligned.
- *  x     device, in: f32 [rows][K] row-major, 16-byte aligned.
+ *  x     device, in: f32 [rows][K] row-major, 4-byte aligned (a 16-byte
+ *        aligned x is read with 16-byte loads, any other with 4-byte loads;
+ *        the bytes written are the same).
  *  rows  >= 1.  K >= 256, a multiple of 256.
  * Errors: XQ_E_NULL, XQ_E_SHAPE, XQ_E_ALIGN, XQ_E_DEVICE, XQ_E_LAUNCH.
  */
@@ -116,7 +118,7 @@ xq_status xq_gemv_q4k(float *y, const void *w, const void *xq, int64_t N, int64_
  * The 256/(rows per workgroup) workgroups of each q8_K block of y count
  * their arrival on a counter; the last quantizes the block.
  *
- *  y   device, out: f32 [N], 16-byte aligned.
+ *  y   device, out: f32 [N], 4-byte aligned.
  *  yq  device, out: q8_K [N/256] blocks (xq_q8k_bytes(1, N)), 16-byte aligned.
  *  w, xq, K as xq_gemv_q4k.
  *  N a multiple of 256, 256 <= N <= 2^22.

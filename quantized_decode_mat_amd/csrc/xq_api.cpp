@@ -105,7 +105,7 @@ xq_status xq_quantize_q8k(void* xq, const float* x, int64_t rows, int64_t K, voi
     return fail(XQ_E_SHAPE, "rows*K/256 = %lld*%lld exceeds 2^31-1 blocks", (long long)rows,
                 (long long)(K / 256));
   if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");
-  if (!aligned(x, 16)) return fail(XQ_E_ALIGN, "x not 16-byte aligned");
+  if (!aligned(x, 4)) return fail(XQ_E_ALIGN, "x not 4-byte aligned");
   if (xq_status s = check_device()) return s;
   return launched(xq::launch_quantize_q8k(xq, x, rows, K, static_cast<hipStream_t>(stream)),
                   "xq_quantize_q8k");
@@ -139,7 +139,7 @@ xq_status xq_gemv_q4k_q8k(float* y, void* yq, const void* w, const void* xq, int
   if (xq_status s = check_workspace(workspace, workspace_bytes, need,
                                     "xq_gemv_q4k_q8k_workspace_bytes"))
     return s;
-  if (!aligned(y, 16)) return fail(XQ_E_ALIGN, "y not 16-byte aligned");
+  if (!aligned(y, 4)) return fail(XQ_E_ALIGN, "y not 4-byte aligned");
   if (!aligned(yq, 16)) return fail(XQ_E_ALIGN, "yq not 16-byte aligned");
   if (!aligned(w, 16)) return fail(XQ_E_ALIGN, "w not 16-byte aligned");
   if (!aligned(xq, 16)) return fail(XQ_E_ALIGN, "xq not 16-byte aligned");

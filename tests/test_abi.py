@@ -94,7 +94,7 @@ def _call(name, *args):
     ((A16, A16, 1, 0, None), xq.XQ_E_SHAPE, "K=0"),
     ((A16, A16, 2 ** 40, 256, None), xq.XQ_E_SHAPE, "exceeds"),
     ((A4, A16, 1, 256, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
-    ((A16, A4, 1, 256, None), xq.XQ_E_ALIGN, "x not 16-byte"),
+    ((A16, A1, 1, 256, None), xq.XQ_E_ALIGN, "x not 4-byte"),
 ])
 def test_quantize_refusals(args, status, text):
     s, err = _call("xq_quantize_q8k", *args)
@@ -252,7 +252,7 @@ def test_gemm_id_workspace_refusals(ws, nbytes, status, text):
     ((A16, A16, A16, A16, 0, 4096, W256, BIG, None), xq.XQ_E_SHAPE, "N=0"),
     ((A16, A16, A16, A16, 2 ** 22 + 256, 4096, W256, BIG, None), xq.XQ_E_SHAPE, "N=4194560"),
     ((A16, A16, A16, A16, 512, 4000, W256, BIG, None), xq.XQ_E_SHAPE, "K=4000"),
-    ((A4, A16, A16, A16, 512, 4096, W256, BIG, None), xq.XQ_E_ALIGN, "y not 16-byte"),
+    ((A1, A16, A16, A16, 512, 4096, W256, BIG, None), xq.XQ_E_ALIGN, "y not 4-byte"),
     ((A16, A4, A16, A16, 512, 4096, W256, BIG, None), xq.XQ_E_ALIGN, "yq not 16-byte"),
     ((A16, A16, A4, A16, 512, 4096, W256, BIG, None), xq.XQ_E_ALIGN, "w not 16-byte"),
     ((A16, A16, A16, A4, 512, 4096, W256, BIG, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
@@ -308,4 +308,9 @@ def test_device_gate_without_gpu():
     if torch.cuda.device_count() != 0:
         pytest.skip("a GPU is visible; this gate is exercised only where none is")
     s, err = _call("xq_gemv_q4k", A16, A16, A16, 8, 256, None)
+    assert s == xq.XQ_E_DEVICE, err
+    # 4-byte alignment is enough for the quantizer's x and the fused tail's y
+    s, err = _call("xq_quantize_q8k", A16, A4, 1, 256, None)
+    assert s == xq.XQ_E_DEVICE, err
+    s, err = _call("xq_gemv_q4k_q8k", A4, A16, A16, A16, 512, 4096, W256, BIG, None)
     assert s == xq.XQ_E_DEVICE, err

@@ -178,6 +178,27 @@ def test_quantize_q8k_bit_exact(name):
     assert np.all(got[:, :, 292:] == 0)
 
 
+@pytest.mark.parametrize("offset", [1, 2, 3])
+def test_quantize_q8k_rows_4_byte_aligned(offset):
+    """x needs only 4-byte alignment: rows that start 4, 8 or 12 bytes past a
+    16-byte boundary take the 4-byte loads and give the same bytes."""
+    rows, K = 3, 4096
+    x = wl.activations(rows, K, wl.rng(2100 + offset)).astype(np.float32)
+    x[1, 7] = 0.5 * np.abs(x[1]).max() / 127 * 3  # a tie one half past a code
+    _note("quantize 4-byte aligned x, offset %d floats" % offset)
+    buf = torch.full((rows * K + 4,), float("nan"), dtype=torch.float32, device="cuda")
+    buf[offset:offset + rows * K] = torch.from_numpy(x.reshape(-1)).cuda()
+    xv = buf[offset:offset + rows * K]
+    assert xv.data_ptr() % 16 == 4 * offset
+    n = xq.xq_q8k_bytes(rows, K)
+    out = poisoned_u8(n)
+    xq.xq_quantize_q8k(out, xv, rows, K)
+    got = take_u8(out, n).reshape(rows, K // 256, 320)
+    want = oracle.quantize_q8k(x)
+    assert np.array_equal(got[:, :, :292], want[:, :, :292])
+    assert np.array_equal(got, gpu_quantize(x))
+
+
 # ---------------------------------------------------------------------------
 # Q4_K mat-vec
 # ---------------------------------------------------------------------------
@@ -324,6 +345,29 @@ def test_gemv_q4k_q8k(name, N, K, seed):
         assert np.array_equal(qq[:, :292], ref_q[:, :292])
         assert np.array_equal(qq[:, :292], oq[:, :292])
         assert not qq[:, 292:].any()
+
+
+def test_gemv_q4k_q8k_y_4_byte_aligned():
+    """The fused tail's y needs only 4-byte alignment: y 4 bytes past a
+    16-byte boundary gets the bits of the aligned call, and yq the same bytes."""
+    N, K = 14336, 4096
+    g = wl.rng(7611)
+    w = wl.q4k_weights(N, K, g)
+    xqb = oracle.quantize_q8k(wl.activations(1, K, g))
+    wd, xd = dev(w), dev(xqb)
+    _note("gemv q8k with y at +4 bytes")
+    nq = xq.xq_q8k_bytes(1, N)
+    ws = zeroed_workspace(xq.xq_gemv_q4k_q8k_workspace_bytes(N))
+    ya, yqa = poisoned_f32(N), poisoned_u8(nq)
+    xq.xq_gemv_q4k_q8k(ya, yqa, wd, xd, N, K, workspace=ws)
+    buf, yqb = poisoned_f32(N + 1), poisoned_u8(nq)
+    yv = buf[1:1 + N]
+    assert yv.data_ptr() % 16 == 4
+    xq.xq_gemv_q4k_q8k(yv, yqb, wd, xd, N, K, workspace=ws)
+    yb = take_f32(buf, N + 1)
+    assert bool((buf[:1].view(torch.int32) == -1).all()), "the word before y was written"
+    assert np.array_equal(yb[1:], take_f32(ya, N))
+    assert np.array_equal(take_u8(yqb, nq), take_u8(yqa, nq))
 
 
 def test_ffn_pair_fused_tail_equals_four_launches():
