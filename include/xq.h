@@ -179,7 +179,8 @@ xq_status xq_gemv_iq4nl(float *y, const void *w, const void *xq, int64_t N, int6
  */
 xq_status xq_gemm_q4k_small_m(float *y, const void *w, const void *xq, int64_t M, int64_t N,
                               int64_t K, void *workspace, size_t workspace_bytes, void *stream);
-size_t xq_gemm_q4k_small_m_workspace_bytes(int64_t M, int64_t N, int64_t K);  /* 0 if none */
+size_t xq_gemm_q4k_small_m_workspace_bytes(int64_t M, int64_t N, int64_t K);  /* 0 if none, or
+                                                                              if the shape is refused */
 
 /*
  * xq_gemm_q4k_small_m without a workspace and without any allocation, for

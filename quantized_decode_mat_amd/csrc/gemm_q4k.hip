@@ -960,7 +960,11 @@ hipError_t noalloc_scratch(hipStream_t stream, void** out) {
 size_t gemm_q4k_noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
 
 size_t gemm_q4k_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || N < 1 || K < 256 || K % 256) return 0;
+  // Shapes the entry point refuses need nothing (and this keeps every
+  // product below in range: M, N <= 2^30, N*K/256*144 < 2^31).
+  constexpr int64_t kRows = int64_t{1} << 30, kInt = 2147483647;
+  if (M < 1 || N < 1 || M > kRows || N > kRows || K < 256 || K % 256 || K / 256 > kInt) return 0;
+  if (M > (kInt / 320) / (K / 256) || N > (kInt / 144) / (K / 256)) return 0;
   if (M == 1 || gemm_q4k_uses_matvec(M, N, K)) return 0;
   const int bm = gemm_q4k_token_tile(M, N, K);
   const GemmPlan plan = gemm_q4k_plan(M, N, K, bm);

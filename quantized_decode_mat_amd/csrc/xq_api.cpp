@@ -242,10 +242,12 @@ static xq_status check_gemm(const float* y, const void* w, const void* xq, int64
   if (K / 256 > kMaxInt) return fail(XQ_E_SHAPE, "K=%lld too large", (long long)K);
   if (((M + 63) / 64) * ((N + 127) / 128) > kMaxInt)
     return fail(XQ_E_SHAPE, "M*N too large for one launch");
-  // The kernel addresses its inputs with 32-bit byte offsets.
-  if (M * (K / 256) * 320 >= (1LL << 31))
+  // The kernel addresses its inputs with 32-bit byte offsets. (Compared by
+  // division: a row's bytes fit in int64, a matrix's need not.)
+  const int64_t nb = K / 256;
+  if (M > ((1LL << 31) - 1) / (nb * 320))
     return fail(XQ_E_SHAPE, "xq of M=%lld rows reaches 2 GiB", (long long)M);
-  if (N * (K / 256) * 144 >= (1LL << 31))
+  if (N > ((1LL << 31) - 1) / (nb * 144))
     return fail(XQ_E_SHAPE, "w of N=%lld rows reaches 2 GiB", (long long)N);
   return XQ_OK;
 }
@@ -317,10 +319,10 @@ xq_status xq_gemm_q4k_id(float* y, const void* slab, const void* xq, const int32
   const int64_t n_pairs = n_tokens * n_used;
   const int64_t xrows = x_per_slot ? n_pairs : n_tokens;
   // The kernel addresses one expert's weights and all of xq with 32-bit byte
-  // offsets.
-  if (rows * (K / 256) * 144 >= (1LL << 31))
+  // offsets (compared by division, as in the dense product).
+  if (rows > ((1LL << 31) - 1) / ((K / 256) * 144))
     return fail(XQ_E_SHAPE, "one expert of rows=%lld reaches 2 GiB", (long long)rows);
-  if (xrows * (K / 256) * 320 >= (1LL << 31))
+  if (xrows > ((1LL << 31) - 1) / ((K / 256) * 320))
     return fail(XQ_E_SHAPE, "xq of %lld rows reaches 2 GiB", (long long)xrows);
   if ((xq::route_max_tiles(n_pairs, n_experts, 64) + xq::route_max_small_tiles(n_pairs, n_experts)) *
               ((rows + 127) / 128) + 8 > kMaxInt)

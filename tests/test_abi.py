@@ -54,6 +54,9 @@ def test_workspace_sizes():
     # 320 tokens x 14336 rows x 16 blocks: 560 tiles, 512 whole + 48 in 4 splits
     assert ws(320, 14336, 4096) == 768 * 128 + 48 * 4 * 32768
     assert ws(0, 8, 256) == 0 and ws(16, 4096, 1000) == 0
+    # shapes the entry point refuses (sizes past 2^30 rows or 2 GiB) need nothing
+    assert ws(2 ** 40, 4096, 4096) == 0 and ws(16, 2 ** 40, 4096) == 0
+    assert ws(16, 2 ** 30, 2 ** 38) == 0 and ws(2 ** 30, 2 ** 30, 2 ** 62) == 0
     assert xq.xq_gemv_q4k_q8k_workspace_bytes(14336) == 56 * 128
     assert xq.xq_gemv_q4k_q8k_workspace_bytes(300) == 0
     # 16 pairs over 6 experts: 7 whole-tile and 14 small-tile descriptors of
@@ -128,6 +131,10 @@ def test_gemv_refusals(fn, args, status, text):
     ((A16, A16, A1, 4, 8, 256, None, 0, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
     ((A16, A16, A16, 2 ** 20, 8, 2048, None, 0, None), xq.XQ_E_SHAPE, "reaches 2 GiB"),
     ((A16, A16, A16, 4, 2 ** 21, 2048, None, 0, None), xq.XQ_E_SHAPE, "reaches 2 GiB"),
+    # rows x bytes per row past int64: refused by the size gate, not wrapped past it
+    ((A16, A16, A16, 2 ** 30, 1, 2 ** 38, None, 0, None), xq.XQ_E_SHAPE,
+     "xq of M=1073741824 rows reaches 2 GiB"),
+    ((A16, A16, A16, 1, 2 ** 30, 2 ** 38, None, 0, None), xq.XQ_E_SHAPE, "reaches 2 GiB"),
 ])
 def test_gemm_refusals(args, status, text):
     s, err = _call("xq_gemm_q4k_small_m", *args)
@@ -227,6 +234,8 @@ def test_id_refusals(fn, args, status, text):
     ((A16, A4, A16, A16, 8, 2, 6, 64, 2048, 0, W256, BIG, None), xq.XQ_E_ALIGN, "slab not 16-byte"),
     ((A16, A16, A4, A16, 8, 2, 6, 64, 2048, 0, W256, BIG, None), xq.XQ_E_ALIGN, "xq not 16-byte"),
     ((A16, A16, A16, A1, 8, 2, 6, 64, 2048, 0, W256, BIG, None), xq.XQ_E_ALIGN, "ids not 4-byte"),
+    ((A16, A16, A16, A16, 8, 2, 6, 2 ** 30, 2 ** 38, 0, W256, BIG, None), xq.XQ_E_SHAPE,
+     "one expert of rows=1073741824 reaches 2 GiB"),
 ])
 def test_gemm_id_refusals(args, status, text):
     s, err = _call("xq_gemm_q4k_id", *args)
