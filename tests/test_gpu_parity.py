@@ -781,6 +781,47 @@ def test_stream_read_probe_reads_every_chunk(nbytes):
 # Degenerate inputs
 # ---------------------------------------------------------------------------
 
+def _subnormal_scales(g, shape):
+    """f16 bit patterns: a random half subnormal (0x0001..0x03FF), the rest
+    small normals (0x0400..0x2400, up to about 0.0156)."""
+    sub = g.integers(1, 0x400, size=shape, dtype=np.uint16)
+    nor = g.integers(0x400, 0x2401, size=shape, dtype=np.uint16)
+    return np.where(g.random(shape) < 0.5, sub, nor).astype("<u2")
+
+
+def test_subnormal_block_scales():
+    """f16 block scales that are subnormal (valid f16 numbers the weights'
+    scales can take) decode as the oracle's f16 decoder does, on the Q4_K
+    mat-vec, the batched mat-vec, the MFMA tile, and the IQ4_NL and Q4_0
+    mat-vecs."""
+    g = wl.rng(7700)
+    N, K = 1000, 2048
+    nb = K // 256
+    w = wl.q4k_weights(N, K, g)
+    w[:, :, 0:2] = _subnormal_scales(g, (N, nb)).view(np.uint8).reshape(N, nb, 2)
+    w[:, :, 2:4] = _subnormal_scales(g, (N, nb)).view(np.uint8).reshape(N, nb, 2)
+    _note("subnormal scales: Q4_K mat-vec")
+    xqb = oracle.quantize_q8k(wl.activations(1, K, g))
+    ref, T = oracle.gemv_q4k(w, xqb, N, K)
+    assert_close(gpu_gemv_q4k(w, xqb, N, K), ref, T, "q4k subnormal")
+    for M in (3, 70):
+        _note("subnormal scales: Q4_K product M=%d" % M)
+        xqm = oracle.quantize_q8k(wl.activations(M, K, g))
+        ref, T = oracle.gemm_q4k(w, xqm, M, N, K)
+        Y = gpu_gemm(w, xqm, M, N, K)
+        assert_close(Y.reshape(-1), ref.reshape(-1), T.reshape(-1), "gemm subnormal M=%d" % M)
+    wi = wl.iq4nl_weights(N, K, g)
+    bpr = K // 32
+    wi[:, 0:2 * bpr] = _subnormal_scales(g, (N, bpr)).view(np.uint8).reshape(N, 2 * bpr)
+    _note("subnormal scales: IQ4_NL and Q4_0 mat-vecs")
+    ref, T = oracle.gemv_iq4nl(wi, xqb, N, K)
+    assert_close(gpu_gemv_iq4nl(wi, xqb, N, K), ref, T, "iq4nl subnormal")
+    y = poisoned_f32(N)
+    xq.xq_gemv_q4_0(y, dev(wi), dev(xqb), N, K)
+    ref, T = oracle.gemv_q4_0(wi, xqb, N, K)
+    assert_close(take_f32(y, N), ref, T, "q4_0 subnormal")
+
+
 def test_zero_activations_give_exact_zeros():
     """An all-zero activation quantizes to d = 0 and codes 0 (the quantizer's
     zero-block case); every path then outputs exactly 0.0, with no NaN from
