@@ -783,15 +783,18 @@ def test_stream_read_probe_reads_every_chunk(nbytes):
 
 def _subnormal_scales(g, shape):
     """f16 bit patterns: a random half subnormal (0x0001..0x03FF), the rest
-    small normals (0x0400..0x2400, up to about 0.0156)."""
+    small normals (0x0400..0x2400, up to about 0.0156); a random quarter of
+    either kind negative (the formats store signed f16 scales)."""
     sub = g.integers(1, 0x400, size=shape, dtype=np.uint16)
     nor = g.integers(0x400, 0x2401, size=shape, dtype=np.uint16)
-    return np.where(g.random(shape) < 0.5, sub, nor).astype("<u2")
+    bits = np.where(g.random(shape) < 0.5, sub, nor)
+    bits = np.where(g.random(shape) < 0.25, bits | 0x8000, bits)
+    return bits.astype("<u2")
 
 
 def test_subnormal_block_scales():
-    """f16 block scales that are subnormal (valid f16 numbers the weights'
-    scales can take) decode as the oracle's f16 decoder does, on the Q4_K
+    """f16 block scales that are subnormal or negative (valid f16 numbers the
+    weights' scales can take) decode as the oracle's f16 decoder does, on the Q4_K
     mat-vec, the batched mat-vec, the MFMA tile, and the IQ4_NL and Q4_0
     mat-vecs."""
     g = wl.rng(7700)
