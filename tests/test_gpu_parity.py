@@ -619,6 +619,39 @@ def test_gemm_token_tile_16(M, N, K, seed):
             assert_close(Y[m], ref, T, "tile16 row %d" % m)
 
 
+# Both sides of every dispatch boundary of the small-M product: the batched
+# mat-vec against the 16-token tile (3|4 tokens on a large matrix, 8|9 on a
+# matrix of 2^24 weights), the 16-token tile against the 64-token tile (32|33 on
+# a large matrix, 64|65 on matrices of 2^24 and 2^25 weights).
+GEMM_BOUNDARY = [
+    (4, 14336, 4096, 7531),
+    (9, 4096, 4096, 7532),
+    (32, 14336, 4096, 7533),
+    (33, 14336, 4096, 7534),
+    (65, 4096, 4096, 7535),
+    (64, 8192, 4096, 7536),
+    (65, 8192, 4096, 7537),
+]
+
+
+@pytest.mark.parametrize("M,N,K,seed", GEMM_BOUNDARY, ids=["m%d_n%d_k%d" % c[:3] for c in GEMM_BOUNDARY])
+def test_gemm_dispatch_boundaries(M, N, K, seed):
+    g = wl.rng(seed)
+    w = wl.q4k_weights(N, K, g)
+    xqb = oracle.quantize_q8k(wl.activations(M, K, g))
+    _note("gemm dispatch boundary M=%d N=%d K=%d" % (M, N, K))
+    Y = gpu_gemm(w, xqb, M, N, K)
+    s = wl.rng(seed + 1)
+    corners_m = sorted({0, 15, 16, 31, 32, M - 1} & set(range(M)))
+    corners_n = [0, 127, 128, N - 1]
+    ms = np.concatenate([s.integers(0, M, 600), np.repeat(corners_m, len(corners_n))])
+    ns = np.concatenate([s.integers(0, N, 600), np.tile(corners_n, len(corners_m))])
+    ref, T = oracle.gemm_q4k(w, xqb, M, N, K, ms, ns)
+    assert_close(Y[ms, ns], ref, T, "boundary sampled")
+    ref, T = oracle.gemv_q4k(w, xqb[M - 1], N, K)
+    assert_close(Y[M - 1], ref, T, "boundary last row")
+
+
 def test_gemm_mfma_below_eight_tokens():
     """Five tokens whose q8_K rows exceed the mat-vec's LDS cap (K = 14336
     holds three): the MFMA product, split over K."""
