@@ -214,6 +214,8 @@ Q4K_SHAPES = [
     ("n9000_k4352", 9000, 4352, 3004),
     ("n8193_k2048_tworow", 8193, 2048, 3005),
     ("n64_kmax", 64, 49152, 3006),
+    ("n300_k8192_four_units", 300, 8192, 3016),
+    ("n100_k7424_four_units_ragged", 100, 7424, 3017),  # 29 super-blocks: a last unit of five
     ("n77_k10240_five_units", 77, 10240, 3007),
     ("n300_k9472_five_units_ragged", 300, 9472, 3008),
     ("n257_k12288_six_units", 257, 12288, 3009),
@@ -307,6 +309,7 @@ GEMV_Q8K = [
     ("n256_k1024", 256, 1024, 7601),                           # 4 rows per workgroup
     ("n512_k20480", 512, 20480, 7602),                         # loads past the row skipped
     ("n1280_k2304", 1280, 2304, 7603),                         # ragged unit tail
+    ("n512_k7424", 512, 7424, 7605),                           # four units, the last ragged
     ("n512_k53248", 512, 53248, 7604),                         # activation from global memory
 ]
 
@@ -561,6 +564,7 @@ GEMM_SHORT = [
     (2, 20000, 3840, 7510),    # persistent grid, the second unit ragged, rows past one pass
     (4, 100, 256, 7511),       # persistent grid smaller than a workgroup's waves allow
     (2, 4096, 14336, 7512),    # seven units split across a workgroup's waves
+    (2, 1000, 7424, 7519),     # four units (the last ragged) on the LDS form
     (2, 1001, 12544, 7513),    # the same, the last unit one block, rows past a workgroup's eight
     (3, 4099, 13312, 7514),    # three tokens, four rows per workgroup and a ragged row tail
 ]
