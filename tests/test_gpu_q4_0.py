@@ -39,6 +39,9 @@ Q40_SHAPES = [
     ("n20000_k512_two_rows_per_wave", 20000, 512, 8210),
     ("n64_k49152_staged_max", 64, 49152, 8211),
     ("n40_k53248_unstaged", 40, 53248, 8212),
+    ("n500_k6144_three_units", 500, 6144, 8213),
+    ("n90_k12288_six_units", 90, 12288, 8214),
+    ("n50_k16384_eight_units", 50, 16384, 8215),
 ]
 
 
