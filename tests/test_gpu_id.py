@@ -143,6 +143,15 @@ ID_SHAPES = [
     ("iq4nl", 2, 130, 8192, [1, 0, 1]),     # four units
     ("q4k", 3, 70, 53248, [2, 0]),          # rows past the staged limit
     ("iq4nl", 3, 70, 53248, [1, 2]),        # rows past the staged limit
+    ("q4k", 3, 1000, 4096, [2, 1]),         # two units, one row per wave (under 8192 rows in all)
+    ("q4k", 2, 200, 8192, [1, 0]),          # four units
+    ("q4k", 2, 100, 10240, [0, 1]),         # five units
+    ("q4k", 2, 100, 12288, [1, 0]),         # six units
+    ("iq4nl", 3, 3000, 4096, [2, 0]),       # persistent grid, two units
+    ("iq4nl", 2, 500, 6144, [1, 0]),        # persistent grid, three units
+    ("iq4nl", 2, 100, 12288, [0, 1]),       # staged kernel, six units
+    ("iq4nl", 3, 200, 14336, [0, 2]),       # staged kernel, seven units
+    ("iq4nl", 2, 64, 20480, [1, 0]),        # staged kernel, batches of eight units
 ]
 
 
