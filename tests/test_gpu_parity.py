@@ -565,6 +565,11 @@ GEMM_SHORT = [
     (4, 100, 256, 7511),       # persistent grid smaller than a workgroup's waves allow
     (2, 4096, 14336, 7512),    # seven units split across a workgroup's waves
     (2, 1000, 7424, 7519),     # four units (the last ragged) on the LDS form
+    (4, 3000, 8192, 7541),     # four tokens, four units (a 2^25-weight matrix)
+    (6, 2000, 8192, 7542),     # six tokens fill the LDS at four units
+    (6, 2000, 6144, 7543),     # three units, the eight-token instance
+    (3, 2500, 10240, 7544),    # five units, the four-token instance
+    (2, 1500, 12288, 7545),    # six units, below the unit split's row lengths
     (2, 1001, 12544, 7513),    # the same, the last unit one block, rows past a workgroup's eight
     (3, 4099, 13312, 7514),    # three tokens, four rows per workgroup and a ragged row tail
 ]
