@@ -311,6 +311,10 @@ GEMV_Q8K = [
     ("n1280_k2304", 1280, 2304, 7603),                         # ragged unit tail
     ("n512_k7424", 512, 7424, 7605),                           # four units, the last ragged
     ("n512_k53248", 512, 53248, 7604),                         # activation from global memory
+    ("n8192_k2048", 8192, 2048, 7606),                         # one unit, two rows per wave
+    ("n768_k6144", 768, 6144, 7607),                           # three units
+    ("n256_k10240", 256, 10240, 7608),                         # five units
+    ("n512_k12288", 512, 12288, 7609),                         # six units
 ]
 
 
