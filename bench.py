@@ -1184,7 +1184,7 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
 
     # The same product at other token counts: 2 and 3 tokens on the up
     # matrix (the batched mat-vec on its persistent grid), 4 and 16 (the
-    # 16-token MFMA tile); 2 and 3 tokens on the down matrix (the batched
+    # wave-split MFMA tile); 2 and 3 tokens on the down matrix (the batched
     # mat-vec with the tokens' rows in LDS), 16 (the 16-token tile on its
     # three-stage ring: 256 workgroups), 64 and 512 (the 64-token tile); K is split over workgroups where the tile grid cannot fill the
     # device. 320 tokens on the up matrix: 512 of its 560 tiles whole, the

@@ -52,10 +52,13 @@
 // the last arrival resets the counter, so counters are zero again between
 // launches (the caller zeroes a workspace once, before its first use).
 //
-// Short batches (M = 1, or up to the LDS token cap while M <= 3, or 8 on
-// matrices of at most 2^25 weights) skip the MFMA tile: they are a weight
-// stream, and the dot4 mat-vec reads the weights once for all M tokens
-// (launch_gemv_q4k_multi; each token's row is the mat-vec's bits). Up to 32
+// Short batches (M = 1, or up to the LDS token cap while M <= 3, M = 4 on
+// matrices of at most 2^25 weights or M <= 6 on at most 2^24; see
+// gemm_q4k_uses_matvec) skip the MFMA tile: they are a weight stream, and the
+// dot4 mat-vec reads the weights once for all M tokens
+// (launch_gemv_q4k_multi; each token's row is the mat-vec's bits). 4 to 16
+// tokens on tall matrices of 8 to 16 super-blocks per row use the
+// wave-split tile (gemm_q4k_wave_split_kernel); other batches of up to 32
 // tokens (64 on matrices of at most 2^25 weights) use the 16-token tile.
 //
 // Grouped form (mul_mat_id, section 25.3: one launch over an expert map,
@@ -682,6 +685,171 @@ void gemm_q4k_deep_ring_kernel(float* __restrict__ y, const uint8_t* __restrict_
                            n_full, ks, part, cnt, IdGemm{});
 }
 
+// ---- short batches on tall matrices: K split across a workgroup's waves ----
+// Tile: up to 16 tokens x 32 weight rows per 256-thread workgroup. Wave g
+// takes super-blocks [g*nb/4, (g+1)*nb/4) of all 32 rows through a two-stage
+// LDS ring of its own (its own loads, its own waits: no barrier between the
+// waves until the end), with the 16-token tile's arithmetic per super-block.
+// The four partial tiles are summed in LDS in the fixed order 0..3, so a
+// grid of one workgroup per 32 rows fills the device without the split-K
+// workspace and its cross-workgroup hand-off (section 25.3: fill the device;
+// the hand-off costs about 2 us at 16 x 14336 x 4096). The price is four
+// copies of the tokens' q8_K rows per workgroup, read from L2.
+struct WsStage {
+  static constexpr int kRows = 32;
+  static constexpr int kActBytes = 16 * 256;              // codes, chunks XOR-swizzled
+  static constexpr int kXsOff = kActBytes;                 // 16 f32 token scales
+  static constexpr int kSumOff = kXsOff + 16 * 4;          // 16 x 8 int32 sub-block sums
+  static constexpr int kWOff = kSumOff + 16 * 32;          // 32 raw Q4_K blocks
+  static constexpr int kBytes = kWOff + kRows * kQ4KBytes;  // 9280
+  static constexpr int kLoads = 4 + 5 + 1 + 1;              // DMA instructions per stage
+};
+static_assert(WsStage::kBytes % 16 == 0 && WsStage::kWOff % 16 == 0, "16-byte LDS slots");
+static_assert(8 * WsStage::kBytes * 2 <= 160 * 1024, "two workgroups' rings exceed 160 KiB");
+static_assert(WsStage::kLoads == 11, "the wait count below assumes 11 loads per stage");
+
+// This lane's byte offsets of one stage's loads relative to super-block 0.
+struct WsOffsets {
+  uint32_t act[4];
+  uint32_t wt[5];
+  uint32_t sums, xs;
+};
+
+__device__ __forceinline__ WsOffsets ws_offsets(int M, int N, int nb, int m0, int n0, int lane) {
+  WsOffsets o;
+  const uint32_t xrow = static_cast<uint32_t>(nb) * kQ8KBytes;
+  const uint32_t wrow = static_cast<uint32_t>(nb) * kQ4KBytes;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = 4 * j + (lane >> 4);
+    const int c = (lane & 15) ^ (m & 15);  // source chunk of this lane's slot
+    o.act[j] = static_cast<uint32_t>(min(m0 + m, M - 1)) * xrow + 16u * c;
+  }
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const int i = min(64 * j + lane, WsStage::kRows * 9 - 1);  // lanes past 288: masked
+    const int n = i / 9, c = i - 9 * (i / 9);
+    o.wt[j] = static_cast<uint32_t>(min(n0 + n, N - 1)) * wrow + 16u * c;
+  }
+  const int ms = min(lane >> 1, 15);  // lanes 0..31: the sums, two chunks per token
+  o.sums = static_cast<uint32_t>(min(m0 + ms, M - 1)) * xrow + 256u + 16u * (lane & 1);
+  o.xs = static_cast<uint32_t>(min(m0 + min(lane, 15), M - 1)) * xrow + 288u;
+  return o;
+}
+
+// Eleven loads, every one issued with at least one active lane (so each
+// counts once in vmcnt): codes 4, weights 5 (the fifth on lanes 0..31),
+// sums (lanes 0..31) and token scales (lanes 0..15). Token rows past the
+// batch (m0 + m >= M) are not loaded, except lane 0 of a code load that
+// would have none (it keeps the count): their LDS rows hold stale bytes,
+// which reach only the MFMA rows of outputs that are never stored (an
+// output row reads its own token row of each operand and nothing else).
+__device__ __forceinline__ void ws_issue(uint8_t* stage, const uint8_t* xq_in,
+                                         const uint8_t* w_in, const WsOffsets& o, int b,
+                                         int lane, int rows) {
+  const uint8_t* xq = uniform_ptr(xq_in + static_cast<size_t>(b) * kQ8KBytes);
+  const uint8_t* w = uniform_ptr(w_in + static_cast<size_t>(b) * kQ4KBytes);
+  const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_u32(stage));
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    if (4 * j + (lane >> 4) < rows || lane == 0) lds_dma16(xq, o.act[j], lb + 1024 * j);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lds_dma16(w, o.wt[j], lb + WsStage::kWOff + 1024 * j);
+  if (lane < 32) lds_dma16(w, o.wt[4], lb + WsStage::kWOff + 4096);
+  if (lane < 32 && (lane >> 1) < rows) lds_dma16(xq, o.sums, lb + WsStage::kSumOff);
+  if (lane < 16 && lane < rows) lds_dma4(xq, o.xs, lb + WsStage::kXsOff);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_q4k_wave_split_kernel(float* __restrict__ y, const uint8_t* __restrict__ w,
+                                const uint8_t* __restrict__ xq, int M, int N, int nb,
+                                int mtiles) {
+  static_assert(kThreads == 256, "four waves, one K quarter each");
+  __shared__ __align__(16) uint8_t ring[4][2][WsStage::kBytes];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;
+  const int q = lane >> 4;
+  const int wg = static_cast<int>(blockIdx.x);
+  const int m0 = 16 * (wg % mtiles);
+  const int n0 = WsStage::kRows * (wg / mtiles);
+  const int b_lo = static_cast<int>(static_cast<int64_t>(wave) * nb / 4);
+  const int b_hi = static_cast<int>(static_cast<int64_t>(wave + 1) * nb / 4);
+  uint8_t* const st0 = ring[wave][0];
+  uint8_t* const st1 = ring[wave][1];
+
+  float4 acc[1][2];
+  acc[0][0] = make_float4(0.f, 0.f, 0.f, 0.f);
+  acc[0][1] = acc[0][0];
+  const WsOffsets so = ws_offsets(M, N, nb, m0, n0, lane);
+  const int rows = min(M - m0, 16);  // token rows of this tile, >= 1
+  if (b_lo < b_hi) ws_issue(st0, xq, w, so, b_lo, lane, rows);
+  if (b_lo + 1 < b_hi) ws_issue(st1, xq, w, so, b_lo + 1, lane, rows);
+
+  // Super-block b from `stg`: wait until its eleven loads have landed (the
+  // next stage's eleven may still be in flight; loads complete in order),
+  // compute, then refill `stg` with b + 2 once every read of it is done.
+  auto step = [&](int b, uint8_t* stg) {
+    if (b + 1 < b_hi)
+      __builtin_amdgcn_s_waitcnt(kWaitVm0 | WsStage::kLoads);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_s_setprio(1);
+    uint4 hdr[2], rw[2][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const uint8_t* blk = stg + WsStage::kWOff + (16 * nt + l16) * kQ4KBytes;
+      hdr[nt] = *reinterpret_cast<const uint4*>(blk);
+      rw[nt][0] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * q);
+      rw[nt][1] = *reinterpret_cast<const uint4*>(blk + 16 + 64 + 16 * q);
+    }
+    block_product<1>(stg, WsStage::kXsOff, WsStage::kSumOff, hdr, rw, lane, acc);
+    if (b + 2 < b_hi) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of stg are done
+      ws_issue(stg, xq, w, so, b + 2, lane, rows);
+    }
+  };
+  for (int b = b_lo; b < b_hi; b += 2) {
+    step(b, st0);
+    if (b + 1 < b_hi) step(b + 1, st1);
+  }
+
+  // ---- the four partial tiles, summed in the order 0, 1, 2, 3 ----
+  // Waves 1..3 leave theirs in their own first stage (all their loads have
+  // landed and their reads are done); wave 0 adds them to its own.
+  float4* red = reinterpret_cast<float4*>(st0) + 2 * lane;
+  if (wave > 0) {
+    red[0] = acc[0][0];
+    red[1] = acc[0][1];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int g = 1; g < 4; ++g) {
+    const float4* pg = reinterpret_cast<const float4*>(ring[g][0]) + 2 * lane;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float4 v = pg[nt];
+      acc[0][nt].x += v.x;
+      acc[0][nt].y += v.y;
+      acc[0][nt].z += v.z;
+      acc[0][nt].w += v.w;
+    }
+  }
+  // C layout of a 16x16 tile: lane holds row column l16, tokens 4q..4q+3.
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int n = n0 + 16 * nt + l16;
+    const int mr = m0 + 4 * q;
+    if (n >= N) continue;
+    const float v[4] = {acc[0][nt].x, acc[0][nt].y, acc[0][nt].z, acc[0][nt].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (mr + i < M) y[static_cast<int64_t>(mr + i) * N + n] = v[i];
+  }
+}
+
 // The grouped form over two tile lists in one grid: the experts' whole tiles
 // of up to 64 pairs on the 64-token tile (workgroups 0 .. big_wgs-1), then
 // their remainders of at most 32 pairs in tiles of up to 16 on the 16-token
@@ -901,15 +1069,59 @@ int gemm_q4k_token_tile(int64_t M, int64_t N, int64_t K) {
   return (M <= 32 || (M <= 64 && N * K <= (int64_t{1} << 25))) ? 16 : 64;
 }
 
+namespace {
+// The wave-split tile's shapes: 256 to 512 row tiles of 32 (one round of two
+// workgroups per CU) and 8 to 16 super-blocks (two to four per wave).
+bool wave_split_shape(int64_t N, int64_t K) {
+  const int64_t rt = (N + WsStage::kRows - 1) / WsStage::kRows, nb = K / 256;
+  return rt >= 256 && rt <= 512 && nb >= 8 && nb <= 16;
+}
+}  // namespace
+
+bool gemm_q4k_uses_wave_split(int64_t M, int64_t N, int64_t K) {
+  // Measured on MI355X (cold weights), against the 16-token tile split four
+  // ways over K through the workspace: 14336x4096 at 4, 8, 12, 16 tokens
+  // 11.0, 11.7, 12.1, 12.5 us against 11.8, 12.0, 12.2, 12.4; 16 x 8192x4096
+  // 7.8 against 9.6; 16 x 14336x3072 10.0 against 11.7; 16384x4096 at 4 and
+  // 16 tokens 11.4 and 12.8 against 12.3 and 13.0. Rows of 32 super-blocks
+  // lose (8 x 14336x8192: 19.1 against 18.5): each wave reads its own copy of
+  // the tokens' rows, and that grows with K while the hand-off it saves does
+  // not.
+  return M >= 4 && M <= 16 && !gemm_q4k_uses_matvec(M, N, K) && wave_split_shape(N, K);
+}
+
+hipError_t launch_gemm_q4k_wave_split(float* y, const void* w, const void* xq, int64_t M,
+                                      int64_t N, int64_t K, hipStream_t stream) {
+  const int mtiles = static_cast<int>((M + 15) / 16);
+  const int64_t grid = (N + WsStage::kRows - 1) / WsStage::kRows * mtiles;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemm_q4k_wave_split_kernel, dim3(static_cast<unsigned>(grid)),
+                     dim3(kThreads), 0, stream, y, static_cast<const uint8_t*>(w),
+                     static_cast<const uint8_t*>(xq), static_cast<int>(M), static_cast<int>(N),
+                     static_cast<int>(K / 256), mtiles);
+  return hipGetLastError();
+}
+
 bool gemm_q4k_uses_matvec(int64_t M, int64_t N, int64_t K) {
   // A very short batch is a weight stream, not a dense contraction: one pass
   // of the dot4 mat-vec over the weights for all M tokens costs less than
-  // the 16-token MFMA tile. Measured on MI355X (cold weights): 14336x4096 at
-  // 3 tokens 9.6-10.2 us on the persistent grid against 12.4 (4 tokens: 13.1
-  // against 12.4); 4096x14336 at 3 tokens 11.8-12.0 with a row's units split
-  // across waves against 15.4; 4096x4096 at 8 tokens 9.6 against 9.5.
-  return M == 1 ||
-         (M <= gemv_q4k_multi_max_tokens(K) && (M <= 3 || N * K <= (int64_t{1} << 25)));
+  // an MFMA tile while M is small, and its cost grows with M. Measured on
+  // MI355X (cold weights), batched mat-vec against the MFMA tiles:
+  // 14336x4096 at 3 tokens 9.6-10.2 us on the persistent grid against 12.4;
+  // 4096x14336 at 3 tokens 11.8-12.0 with a row's units split across waves
+  // against 15.4; 4 tokens on 4096x4096, 6144x4096, 4096x8192 and 11008x2048
+  // 5.2, 6.8, 9.6, 6.0 against 8.5, 9.0, 11.2, 6.5, but on 8192x4096 (the
+  // wave-split tile) 8.2 against 7.1; 6 tokens on 4096x4096 7.8 against 8.5,
+  // on 8192x4096 and 14336x2048 12.8 and 11.5 against 7.2 and 7.0; 5 tokens
+  // on 5120x5120 10.4 against 9.4; 8 tokens on 4096x4096, 6144x4096 and
+  // 5120x6144 9.3, 13.7, 15.7 against 8.5, 9.0, 10.1.
+  if (M == 1) return true;
+  if (M > gemv_q4k_multi_max_tokens(K)) return false;
+  const int64_t nk = N * K;
+  if (M <= 3) return true;
+  if (M == 4)
+    return nk <= (int64_t{1} << 25) && !(wave_split_shape(N, K) && K / 256 >= 16);
+  return M <= 6 && nk <= (int64_t{1} << 24);
 }
 
 // ---- the product for callers that cannot allocate ----
@@ -965,7 +1177,7 @@ size_t gemm_q4k_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   constexpr int64_t kRows = int64_t{1} << 30, kInt = 2147483647;
   if (M < 1 || N < 1 || M > kRows || N > kRows || K < 256 || K % 256 || K / 256 > kInt) return 0;
   if (M > (kInt / 320) / (K / 256) || N > (kInt / 144) / (K / 256)) return 0;
-  if (M == 1 || gemm_q4k_uses_matvec(M, N, K)) return 0;
+  if (M == 1 || gemm_q4k_uses_matvec(M, N, K) || gemm_q4k_uses_wave_split(M, N, K)) return 0;
   const int bm = gemm_q4k_token_tile(M, N, K);
   const GemmPlan plan = gemm_q4k_plan(M, N, K, bm);
   if (plan.ks <= 1) return 0;
@@ -977,6 +1189,8 @@ hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, i
                            int64_t K, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (M == 1) return launch_gemv_q4k(y, w, xq, N, K, stream);
   if (gemm_q4k_uses_matvec(M, N, K)) return launch_gemv_q4k_multi(y, w, xq, M, N, K, stream);
+  if (gemm_q4k_uses_wave_split(M, N, K))
+    return launch_gemm_q4k_wave_split(y, w, xq, M, N, K, stream);
   const int bm = gemm_q4k_token_tile(M, N, K);
   return launch_gemm_q4k_split(y, w, xq, M, N, K, gemm_q4k_plan(M, N, K, bm), bm, ws, ws_bytes,
                                stream);

@@ -61,6 +61,8 @@ hipError_t launch_gemm_q4k(float* y, const void* w, const void* xq, int64_t M, i
                            int64_t K, void* ws, size_t ws_bytes, hipStream_t stream);
 // Whether launch_gemm_q4k serves this shape with the mat-vec kernels.
 bool gemm_q4k_uses_matvec(int64_t M, int64_t N, int64_t K);
+// Whether it serves it with the wave-split short-batch tile (no workspace).
+bool gemm_q4k_uses_wave_split(int64_t M, int64_t N, int64_t K);
 // The small-M product's launch plan: tiles 0..n_full-1 (of bm tokens x 128
 // rows, token tile fastest) run whole, the rest split K ks ways (ks = 1:
 // every tile whole). Needs, when ks > 1: 1 <= tiles - n_full <= 768,

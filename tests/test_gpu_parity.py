@@ -559,10 +559,10 @@ GEMM_SHORT = [
     (2, 14336, 4096, 7501),    # two rows per wave, clamped
     (3, 14336, 4096, 7502),    # the longest batch on this shape
     (3, 4096, 14336, 7503),    # seven units, three tokens fill the LDS cap
-    (8, 4096, 4096, 7504),     # eight tokens on a 2^24-weight matrix
+    (6, 4096, 4096, 7504),     # six tokens on a 2^24-weight matrix (the eight-token instance)
     (5, 300, 2304, 7505),      # ragged unit tail
     (2, 130, 20480, 7506),     # ten units (two tokens fit): batches of four, loads past the row skipped
-    (7, 8193, 2048, 7507),     # two rows per wave with an odd tail
+    (6, 8191, 2048, 7507),     # two rows per wave with an odd tail
     (4, 4096, 4096, 7508),     # persistent grid, activation in registers, four tokens
     (3, 3000, 1280, 7509),     # persistent grid, one ragged unit
     (2, 20000, 3840, 7510),    # persistent grid, the second unit ragged, rows past one pass
@@ -599,8 +599,8 @@ def test_gemm_short_batch_rows_equal_matvec(M, N, K, seed):
 # The 16-token MFMA tile (M <= 32, or M <= 64 on matrices of at most 2^25
 # weights), split over K where the tile grid is short of the device.
 GEMM_TILE16 = [
-    (4, 14336, 4096, 7521),    # four tokens in one 16-token tile, four splits
-    (16, 14336, 4096, 7522),   # a full tile
+    (4, 14336, 8192, 7521),    # four tokens in one 16-token tile, four splits of 8 super-blocks
+    (16, 14336, 6144, 7522),   # a full tile, four splits of 6 super-blocks
     (31, 4096, 14336, 7523),   # two tiles, the second ragged, eight splits
     (17, 300, 2304, 7524),     # ragged tokens and rows, nine super-blocks
     (64, 4096, 4096, 7525),    # four tiles on a 2^24-weight matrix
@@ -632,13 +632,61 @@ def test_gemm_token_tile_16(M, N, K, seed):
             assert_close(Y[m], ref, T, "tile16 row %d" % m)
 
 
+# Short batches on tall matrices: the wave-split tile (four waves split K,
+# their partial tiles summed in LDS; no workspace).
+GEMM_WAVE_SPLIT = [
+    (4, 14336, 4096, 7551),    # 448 workgroups, four super-blocks per wave
+    (16, 14336, 4096, 7552),   # a full token tile
+    (7, 8192, 4096, 7553),     # one workgroup per CU
+    (16, 8200, 2304, 7554),    # a last row tile of 8 rows; 9 super-blocks (2, 2, 2, 3 per wave)
+    (12, 16384, 3840, 7555),   # 512 workgroups; 15 super-blocks (3, 4, 4, 4)
+    (5, 11008, 2048, 7556),    # two super-blocks per wave
+]
+
+
+@pytest.mark.parametrize("M,N,K,seed", GEMM_WAVE_SPLIT, ids=["m%d_n%d_k%d" % c[:3] for c in GEMM_WAVE_SPLIT])
+def test_gemm_wave_split(M, N, K, seed):
+    g = wl.rng(seed)
+    w = wl.q4k_weights(N, K, g)
+    xqb = oracle.quantize_q8k(wl.activations(M, K, g))
+    assert xq.xq_gemm_q4k_small_m_workspace_bytes(M, N, K) == 0
+    _note("gemm wave split M=%d N=%d K=%d" % (M, N, K))
+    wd, xd = dev(w), dev(xqb)
+    outs = []
+    for _ in range(2):
+        y = poisoned_f32(M * N)
+        xq.xq_gemm_q4k_small_m(y, wd, xd, M, N, K)
+        outs.append(take_f32(y, M * N).reshape(M, N))
+    Y = outs[0]
+    assert np.array_equal(outs[1], Y)
+    assert not np.isnan(Y).any()
+    s = wl.rng(seed + 1)
+    corners_m = sorted({0, 3, 4, M - 1} & set(range(M)))
+    corners_n = [0, 31, 32, N - 32, N - 1]
+    ms = np.concatenate([s.integers(0, M, 800), np.repeat(corners_m, len(corners_n))])
+    ns = np.concatenate([s.integers(0, N, 800), np.tile(corners_n, len(corners_m))])
+    ref, T = oracle.gemm_q4k(w, xqb, M, N, K, ms, ns)
+    assert_close(Y[ms, ns], ref, T, "wave split sampled")
+    for m in sorted({0, M - 1}):
+        ref, T = oracle.gemv_q4k(w, xqb[m], N, K)
+        assert_close(Y[m], ref, T, "wave split row %d" % m)
+
+
 # Both sides of every dispatch boundary of the small-M product: the batched
-# mat-vec against the 16-token tile (3|4 tokens on a large matrix, 8|9 on a
-# matrix of 2^24 weights), the 16-token tile against the 64-token tile (32|33 on
-# a large matrix, 64|65 on matrices of 2^24 and 2^25 weights).
+# mat-vec against the MFMA tiles (3|4 tokens on a large matrix, 4|5 on 2^25
+# weights, 6|7 on 2^24, and 4 tokens on the wave-split tile's shapes: 16 and 8
+# super-blocks), the wave-split tile against the 16-token tile (16|17 tokens),
+# the 16-token tile against the 64-token tile (32|33 on a large matrix, 64|65
+# on matrices of 2^24 and 2^25 weights).
 GEMM_BOUNDARY = [
     (4, 14336, 4096, 7531),
-    (9, 4096, 4096, 7532),
+    (4, 4096, 8192, 7538),
+    (5, 4096, 8192, 7539),
+    (6, 4096, 4096, 7540),
+    (7, 4096, 4096, 7532),
+    (4, 8192, 4096, 7546),
+    (4, 11008, 2048, 7547),
+    (17, 14336, 4096, 7548),
     (32, 14336, 4096, 7533),
     (33, 14336, 4096, 7534),
     (65, 4096, 4096, 7535),
@@ -773,11 +821,12 @@ def test_gemm_prefill_512x14336x4096():
 
 
 @pytest.mark.parametrize("which", ["S", "M"])
-@pytest.mark.parametrize("M,K", [(3, 1024), (9, 1024), (9, 3584), (70, 1024)])
-def test_gemm_partials_bit_exact(which, M, K):
+@pytest.mark.parametrize("M,N,K", [(3, 200, 1024), (9, 200, 1024), (9, 200, 3584), (70, 200, 1024),
+                                   (9, 8192, 2048)])
+def test_gemm_partials_bit_exact(which, M, N, K):
     """M = 3 runs on the batched mat-vec, M = 9 on the 16-token MFMA tile
-    (K = 3584: three splits), M = 70 on the 64-token tile."""
-    N = 200
+    (K = 3584: three splits) or, on 8192 rows, the wave-split tile (two
+    super-blocks per wave), M = 70 on the 64-token tile."""
     g = wl.rng(7200)
     w = wl.q4k_isolation_weights(N, K, g, which)
     wd = dev(w)
