@@ -1186,7 +1186,8 @@ def suite(args, torch, xq, wl, dev, stream, stream_gbps):
     # matrix (the batched mat-vec on its persistent grid), 4 and 16 (the
     # wave-split MFMA tile); 2 and 3 tokens on the down matrix (the batched
     # mat-vec with the tokens' rows in LDS), 16 (the 16-token tile on its
-    # three-stage ring: 256 workgroups), 64 and 512 (the 64-token tile); K is split over workgroups where the tile grid cannot fill the
+    # three-stage ring: 256 workgroups), 64 (the 16-token tile, four token
+    # tiles) and 512 (the 64-token tile); K is split over workgroups where the tile grid cannot fill the
     # device. 320 tokens on the up matrix: 512 of its 560 tiles whole, the
     # rest split four ways in the same launch.
     for M, (N, K), seed in ((2, UP, wl.SEEDS["prefill"]), (3, UP, wl.SEEDS["prefill"]),

@@ -53,13 +53,14 @@
 // launches (the caller zeroes a workspace once, before its first use).
 //
 // Short batches (M = 1, or up to the LDS token cap while M <= 3, M = 4 on
-// matrices of at most 2^25 weights or M <= 6 on at most 2^24; see
-// gemm_q4k_uses_matvec) skip the MFMA tile: they are a weight stream, and the
+// matrices of at most 2^25 weights, M <= 6 on at most 2^24 or M <= 8 on at
+// most 2^23; see gemm_q4k_uses_matvec) skip the MFMA tile: they are a weight stream, and the
 // dot4 mat-vec reads the weights once for all M tokens
 // (launch_gemv_q4k_multi; each token's row is the mat-vec's bits). 4 to 16
 // tokens on tall matrices of 8 to 16 super-blocks per row use the
 // wave-split tile (gemm_q4k_wave_split_kernel); other batches of up to 32
-// tokens (64 on matrices of at most 2^25 weights) use the 16-token tile.
+// tokens (up to 128 on matrices with few weight tiles; see
+// gemm_q4k_token_tile) use the 16-token tile.
 //
 // Grouped form (mul_mat_id, section 25.3: one launch over an expert map,
 // never one per expert, padded only to the finest tile): the same tile code
@@ -1065,8 +1066,20 @@ int gemm_q4k_token_tile(int64_t M, int64_t N, int64_t K) {
   // The 16-token tile (one MFMA tile per wave, a quarter of the accumulators,
   // three workgroups per CU) against the 64-token one, measured: 14336x4096
   // at 7..16 tokens 12.4-12.8 us against 19.3-21.2, at 48 tokens 24.4 against
-  // 21.0; 4096x4096 at 64 tokens 12.0 against 16.5.
-  return (M <= 32 || (M <= 64 && N * K <= (int64_t{1} << 25))) ? 16 : 64;
+  // 21.0; 4096x4096 at 64 tokens 12.0 against 16.5. Where the weight tiles
+  // are few (short matrices) the finer token tile fills the device at more
+  // tokens: 4096x4096 at 96 and 128 tokens 14.4 and 15.0 us against 17.7 and
+  // 17.6, 2048x2048 8.7 and 9.1 against 12.7 and 12.8; 5120x5120 and
+  // 8192x4096 at 96 tokens 17.1 and 20.5 against 19.9 and 22.3 (at 128 the
+  // 64-token tile is ahead again: 20.3 and 22.7 against 22.8 and 23.1);
+  // 4096 rows of 11008 and 14336 at 48 tokens 17.2 and 21.2 against 20.8 and
+  // 22.5.
+  const int64_t nk = N * K;
+  if (M <= 32) return 16;
+  if (M <= 64 && (nk <= (int64_t{1} << 25) || N <= 4096)) return 16;
+  if (M <= 96 && nk <= (int64_t{1} << 25)) return 16;
+  if (M <= 128 && nk <= (int64_t{1} << 24)) return 16;
+  return 64;
 }
 
 namespace {
@@ -1114,11 +1127,12 @@ bool gemm_q4k_uses_matvec(int64_t M, int64_t N, int64_t K) {
   // wave-split tile) 8.2 against 7.1; 6 tokens on 4096x4096 7.8 against 8.5,
   // on 8192x4096 and 14336x2048 12.8 and 11.5 against 7.2 and 7.0; 5 tokens
   // on 5120x5120 10.4 against 9.4; 8 tokens on 4096x4096, 6144x4096 and
-  // 5120x6144 9.3, 13.7, 15.7 against 8.5, 9.0, 10.1.
+  // 5120x6144 9.3, 13.7, 15.7 against 8.5, 9.0, 10.1; but on 2048x2048
+  // (launch-bound on both paths) 8 tokens 4.4 against 7.5.
   if (M == 1) return true;
   if (M > gemv_q4k_multi_max_tokens(K)) return false;
   const int64_t nk = N * K;
-  if (M <= 3) return true;
+  if (M <= 3 || nk <= (int64_t{1} << 23)) return true;
   if (M == 4)
     return nk <= (int64_t{1} << 25) && !(wave_split_shape(N, K) && K / 256 >= 16);
   return M <= 6 && nk <= (int64_t{1} << 24);

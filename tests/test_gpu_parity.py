@@ -486,9 +486,11 @@ def test_gemm_full_compare(M, N, K, seed):
 # Split-K shapes (few tiles: the grid is tiles x splits; the last split of a
 # tile to arrive sums the partials in split order).
 GEMM_SPLIT = [
-    (37, 1000, 4352, 7011),    # 17 super-blocks in two splits of 8 and 9
+    (37, 1000, 4352, 7011),    # 16-token tile: 17 super-blocks in four splits
     (16, 300, 14336, 7012),    # eight splits of seven super-blocks
-    (70, 129, 7936, 7013),     # 31 super-blocks, four splits, ragged M and N
+    (70, 129, 7936, 7013),     # 31 super-blocks, seven splits, ragged M and N
+    (150, 129, 7936, 7014),    # 64-token tile: 31 super-blocks, seven splits, ragged M and N
+    (137, 1000, 4352, 7015),   # 64-token tile: 17 super-blocks in four splits (4, 4, 4, 5)
 ]
 
 
@@ -504,7 +506,8 @@ def test_gemm_split_full_compare(M, N, K, seed):
     assert_close(Y.reshape(-1), ref.reshape(-1), T.reshape(-1), "gemm split")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 14336, 4096), (64, 4096, 14336), (256, 4096, 14336)])
+@pytest.mark.parametrize("M,N,K", [(1, 14336, 4096), (64, 4096, 14336), (65, 4096, 14336),
+                                   (256, 4096, 14336)])
 def test_gemm_split_full_size(M, N, K):
     """The FFN shapes at token counts that split K: sampled outputs with the
     tile corners, plus whole rows against the mat-vec oracle."""
@@ -674,10 +677,11 @@ def test_gemm_wave_split(M, N, K, seed):
 
 # Both sides of every dispatch boundary of the small-M product: the batched
 # mat-vec against the MFMA tiles (3|4 tokens on a large matrix, 4|5 on 2^25
-# weights, 6|7 on 2^24, and 4 tokens on the wave-split tile's shapes: 16 and 8
-# super-blocks), the wave-split tile against the 16-token tile (16|17 tokens),
-# the 16-token tile against the 64-token tile (32|33 on a large matrix, 64|65
-# on matrices of 2^24 and 2^25 weights).
+# weights, 6|7 on 2^24, 8|9 on 2^23, and 4 tokens on the wave-split tile's
+# shapes: 16 and 8 super-blocks), the wave-split tile against the 16-token
+# tile (16|17 tokens), the 16-token tile against the 64-token tile (32|33 on a
+# large matrix, 64|65 on 4096 rows of a long K, 96|97 on 2^25 weights, 128|129
+# on 2^24).
 GEMM_BOUNDARY = [
     (4, 14336, 4096, 7531),
     (4, 4096, 8192, 7538),
@@ -689,9 +693,13 @@ GEMM_BOUNDARY = [
     (17, 14336, 4096, 7548),
     (32, 14336, 4096, 7533),
     (33, 14336, 4096, 7534),
-    (65, 4096, 4096, 7535),
-    (64, 8192, 4096, 7536),
-    (65, 8192, 4096, 7537),
+    (8, 4096, 2048, 7549),
+    (64, 4096, 14336, 7550),
+    (65, 4096, 14336, 7557),
+    (96, 8192, 4096, 7536),
+    (97, 8192, 4096, 7537),
+    (128, 4096, 4096, 7535),
+    (129, 4096, 4096, 7558),
 ]
 
 
@@ -821,12 +829,12 @@ def test_gemm_prefill_512x14336x4096():
 
 
 @pytest.mark.parametrize("which", ["S", "M"])
-@pytest.mark.parametrize("M,N,K", [(3, 200, 1024), (9, 200, 1024), (9, 200, 3584), (70, 200, 1024),
+@pytest.mark.parametrize("M,N,K", [(3, 200, 1024), (9, 200, 1024), (9, 200, 3584), (130, 200, 1024),
                                    (9, 8192, 2048)])
 def test_gemm_partials_bit_exact(which, M, N, K):
     """M = 3 runs on the batched mat-vec, M = 9 on the 16-token MFMA tile
     (K = 3584: three splits) or, on 8192 rows, the wave-split tile (two
-    super-blocks per wave), M = 70 on the 64-token tile."""
+    super-blocks per wave), M = 130 on the 64-token tile."""
     g = wl.rng(7200)
     w = wl.q4k_isolation_weights(N, K, g, which)
     wd = dev(w)
@@ -939,7 +947,7 @@ def test_zero_activations_give_exact_zeros():
         fn(y, dev(w), dev(zq), N, K)
         got = take_f32(y, N)
         assert np.array_equal(got, np.zeros(N)), name
-    for M in (3, 16, 70):  # batched mat-vec, 16-token tile, 64-token tile
+    for M in (3, 16, 130):  # batched mat-vec, 16-token tile, 64-token tile
         x = wl.activations(M, K, g)
         x[1::2] = 0.0
         xqb = oracle.quantize_q8k(x)

@@ -70,6 +70,7 @@ def _product_shapes():
         ((33, 129), (100, 4200), (4096, 8192, 14336)),
         ((129, 320), (4000, 9000), (2048, 4096)),
         ((320, 700), (7000, 15000), (2048, 4096, 8192)),
+        ((129, 200), (100, 2000), (4096, 14336)),      # the 64-token tile on few tiles, split K
     ]
     for (m_lo, m_hi), (n_lo, n_hi), ks in regimes:
         for _ in range(3):
