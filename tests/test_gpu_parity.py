@@ -898,8 +898,8 @@ def _subnormal_scales(g, shape):
 def test_subnormal_block_scales():
     """f16 block scales that are subnormal or negative (valid f16 numbers the
     weights' scales can take) decode as the oracle's f16 decoder does, on the Q4_K
-    mat-vec, the batched mat-vec, the MFMA tile, and the IQ4_NL and Q4_0
-    mat-vecs."""
+    mat-vec, the batched mat-vec, the 16- and 64-token MFMA tiles, and the
+    IQ4_NL and Q4_0 mat-vecs."""
     g = wl.rng(7700)
     N, K = 1000, 2048
     nb = K // 256
@@ -910,7 +910,7 @@ def test_subnormal_block_scales():
     xqb = oracle.quantize_q8k(wl.activations(1, K, g))
     ref, T = oracle.gemv_q4k(w, xqb, N, K)
     assert_close(gpu_gemv_q4k(w, xqb, N, K), ref, T, "q4k subnormal")
-    for M in (3, 70):
+    for M in (3, 70, 130):
         _note("subnormal scales: Q4_K product M=%d" % M)
         xqm = oracle.quantize_q8k(wl.activations(M, K, g))
         ref, T = oracle.gemm_q4k(w, xqm, M, N, K)
