@@ -694,8 +694,9 @@ void gemm_q4k_deep_ring_kernel(float* __restrict__ y, const uint8_t* __restrict_
 // The four partial tiles are summed in LDS in the fixed order 0..3, so a
 // grid of one workgroup per 32 rows fills the device without the split-K
 // workspace and its cross-workgroup hand-off (section 25.3: fill the device;
-// the hand-off costs about 2 us at 16 x 14336 x 4096). The price is four
-// copies of the tokens' q8_K rows per workgroup, read from L2.
+// a timing probe put the hand-off at about 2 us of the 16-token tile's 13 us
+// at 16 x 14336 x 4096). The price is four copies of the tokens' q8_K rows
+// per workgroup, read from L2, and one stage in flight per wave.
 struct WsStage {
   static constexpr int kRows = 32;
   static constexpr int kActBytes = 16 * 256;              // codes, chunks XOR-swizzled
