@@ -10,13 +10,14 @@
 // applied once per block afterwards (section 25.2.1).
 //
 // Mapping (MI355X-first, not the pages' wave32 one-lane-per-block design):
-//  * One wave owns R rows. A "unit" is 8 consecutive super-blocks of one row;
-//    lane l takes block 8u + l/8 and its 16-byte nibble chunk c = l%8, which
-//    is half of nibble group g = c/2 (h = c%2). A wave's nibble load covers
-//    8 x 128 B of the 8 x 144 B span, the header load the other 8 x 16 B:
-//    every byte the wave touches is a byte it needs (section 25.2: the
-//    cache lines a wave touches are what costs, not its load count).
-//  * Each lane also loads its block's 16-byte header; the eight lanes of a
+//  * One wave owns R rows. A "unit" is 16 consecutive super-blocks of one
+//    row; lane l takes block 16u + l/4 and its whole 32-byte nibble group
+//    g = l%4 in two 16-byte loads, so a lane's header decode and float pass
+//    cover 64 weights. The two nibble loads of a wave cover 16 x 128 B of the
+//    16 x 144 B span and the header load the other 16 x 16 B: every line the
+//    wave touches is one it needs (section 25.2: the cache lines a wave
+//    touches are what costs, not its load count).
+//  * Each lane also loads its block's 16-byte header; the four lanes of a
 //    block load the same 16 bytes, which the cache serves once per line.
 //  * All of a lane's loads for a batch of PF units are issued before any is
 //    used, and the first batch before the activation's LDS stores (whose
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_kernel(float* __restrict__
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * W + wave) * R;
-  const int units = (nb + 7) >> 3;
+  const int units = (nb + kUnitBlocks - 1) / kUnitBlocks;
   const LaneGeom L = lane_geom(lane);
   const int64_t row_bytes = static_cast<int64_t>(nb) * kQ4KBytes;
   const int n16 = nb * (kQ8KBytes / 16);
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_kernel(float* __restrict__
     xq += static_cast<int64_t>(kk) * x_stride;
   }
 
-  uint4 nib[R][PF];
+  Nib nib[R][PF];
   uint4 hdr[R][PF];
   auto load_batch = [&](int u0) {
 #pragma unroll
@@ -133,14 +134,14 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_kernel(float* __restrict__
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int row = min(row0 + r, N - 1);
-        const int bb = (u0 + p) * 8 + L.bsub;
+        const int bb = (u0 + p) * kUnitBlocks + L.bsub;
         const uint8_t* wr = w + static_cast<int64_t>(row) * row_bytes;
         if (CLAMP || bb < nb) {
           const uint8_t* blk = wr + static_cast<int64_t>(min(bb, nb - 1)) * kQ4KBytes;
-          nib[r][p] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (2 * L.g + L.h));
+          nib[r][p] = load_group(blk, L);
           hdr[r][p] = *reinterpret_cast<const uint4*>(blk);
         } else {
-          nib[r][p] = make_uint4(0, 0, 0, 0);
+          nib[r][p] = zero_group();
           hdr[r][p] = make_uint4(0, 0, 0, 0);
         }
       }
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_kernel(float* __restrict__
     if (u0 > 0) load_batch(u0);
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      const int bb = (u0 + p) * 8 + L.bsub;
+      const int bb = (u0 + p) * kUnitBlocks + L.bsub;
       if (CLAMP) {
         const int b = min(bb, nb - 1);
 #pragma unroll
@@ -238,13 +239,13 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_multi_kernel(float* __rest
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * W + wave) * R;
-  const int units = (nb + 7) >> 3;
+  const int units = (nb + kUnitBlocks - 1) / kUnitBlocks;
   const LaneGeom L = lane_geom(lane);
   const int64_t row_bytes = static_cast<int64_t>(nb) * kQ4KBytes;
   const int xrow = nb * kQ8KBytes;
   const int n16 = tokens * nb * (kQ8KBytes / 16);
 
-  uint4 nib[R][PF];
+  Nib nib[R][PF];
   uint4 hdr[R][PF];
   auto load_batch = [&](int u0) {
 #pragma unroll
@@ -252,14 +253,14 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_multi_kernel(float* __rest
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int row = min(row0 + r, N - 1);
-        const int bb = (u0 + p) * 8 + L.bsub;
+        const int bb = (u0 + p) * kUnitBlocks + L.bsub;
         const uint8_t* wr = w + static_cast<int64_t>(row) * row_bytes;
         if (CLAMP || bb < nb) {
           const uint8_t* blk = wr + static_cast<int64_t>(min(bb, nb - 1)) * kQ4KBytes;
-          nib[r][p] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (2 * L.g + L.h));
+          nib[r][p] = load_group(blk, L);
           hdr[r][p] = *reinterpret_cast<const uint4*>(blk);
         } else {
-          nib[r][p] = make_uint4(0, 0, 0, 0);
+          nib[r][p] = zero_group();
           hdr[r][p] = make_uint4(0, 0, 0, 0);
         }
       }
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_multi_kernel(float* __rest
     if (u0 > 0) load_batch(u0);
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      const int bb = (u0 + p) * 8 + L.bsub;
+      const int bb = (u0 + p) * kUnitBlocks + L.bsub;
       if (CLAMP) {
         const int b = min(bb, nb - 1);
 #pragma unroll
@@ -296,10 +297,8 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_multi_kernel(float* __rest
           }
         }
       } else if (bb < nb) {
-        // Rows of eight or more units hold at most three tokens in 64 KB, so
-        // the header is decoded per token here, through the mat-vec's own
-        // unit_partial: the compiler then contracts the float pass the same
-        // way in both kernels.
+        // Long rows hold at most three tokens in 64 KB, so the header is
+        // decoded per token here, through the mat-vec's own unit_partial.
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -320,7 +319,7 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_multi_kernel(float* __rest
   }
 }
 
-// A short batch of up to four tokens on rows of at most two units, as a
+// A short batch of up to four tokens on rows of one unit, as a
 // persistent grid: each lane copies its slice of every token's q8_K row
 // (codes, sub-block sums and scale of its block in each unit) from the
 // workgroup's LDS copy into registers once, then the wave walks rows with a
@@ -356,24 +355,25 @@ __global__ __launch_bounds__(kMresThreads) void gemv_q4k_multi_res_kernel(
   TokenSlice ts[U][TM];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    bb[u] = u * 8 + L.bsub;
+    bb[u] = u * kUnitBlocks + L.bsub;
     bc[u] = min(bb[u], nb - 1);
 #pragma unroll
     for (int t = 0; t < TM; ++t)
       ts[u][t] = token_slice(act + min(t, tokens - 1) * xrow, bc[u], L);
   }
 
-  uint4 na[U], ha[U], nq[U], hq[U];
-  auto load_row = [&](uint4 (&n)[U], uint4 (&h)[U], int row) {
+  Nib na[U], nq[U];
+  uint4 ha[U], hq[U];
+  auto load_row = [&](Nib (&n)[U], uint4 (&h)[U], int row) {
     const uint8_t* wr = w + static_cast<int64_t>(row) * row_bytes;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint8_t* blk = wr + static_cast<int64_t>(bc[u]) * kQ4KBytes;
-      n[u] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (2 * L.g + L.h));
+      n[u] = load_group(blk, L);
       h[u] = *reinterpret_cast<const uint4*>(blk);
     }
   };
-  auto reduce_row = [&](const uint4 (&n)[U], const uint4 (&h)[U], int row) {
+  auto reduce_row = [&](const Nib (&n)[U], const uint4 (&h)[U], int row) {
     float acc[TM];
 #pragma unroll
     for (int t = 0; t < TM; ++t) acc[t] = 0.0f;
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(kMresThreads) void gemv_q4k_multi_res_kernel(
   }
 }
 
-// Two or three tokens on rows of seven units (K in 12544..14336), a row's
+// Two or three tokens on rows of four units (K in 12544..14336), a row's
 // units split across the waves of a workgroup: wave u takes unit u of R
 // consecutive rows. Each lane reads its slice of every token's q8_K block of
 // that unit from global memory into registers once (no LDS staging of the
@@ -424,7 +424,7 @@ __global__ __launch_bounds__(kMresThreads) void gemv_q4k_multi_res_kernel(
 // barrier each (row, token) is summed over the units in unit order from 0.0f
 // and reduced across the wave, so the sequence of float additions, and so the
 // bits, are those of the clamped mat-vec (masked blocks add 0.0f there too).
-constexpr int kSplitMaxUnits = 7;
+constexpr int kSplitMaxUnits = 4;
 
 template <int TM, int R>
 __global__ __launch_bounds__(kSplitMaxUnits * kWave) void gemv_q4k_unit_split_kernel(
@@ -433,24 +433,25 @@ __global__ __launch_bounds__(kSplitMaxUnits * kWave) void gemv_q4k_unit_split_ke
   __shared__ float part[R * TM][kSplitMaxUnits][kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int u = threadIdx.x >> 6;          // this wave's unit
-  const int units = blockDim.x >> 6;       // the row's units: (nb + 7) / 8
+  const int units = blockDim.x >> 6;       // the row's units of 16 blocks
   const int row0 = blockIdx.x * R;
   const LaneGeom L = lane_geom(lane);
   const int64_t row_bytes = static_cast<int64_t>(nb) * kQ4KBytes;
   const int64_t xrow = static_cast<int64_t>(nb) * kQ8KBytes;
-  const int bb = u * 8 + L.bsub;
+  const int bb = u * kUnitBlocks + L.bsub;
   const int bc = min(bb, nb - 1);
 
   TokenSlice ts[TM];
 #pragma unroll
   for (int t = 0; t < TM; ++t) ts[t] = token_slice(xq + min(t, tokens - 1) * xrow, bc, L);
-  uint4 nib[R], hdr[R];
+  Nib nib[R];
+  uint4 hdr[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int row = min(row0 + r, N - 1);  // rows past N reload the last (not stored)
     const uint8_t* blk =
         w + static_cast<int64_t>(row) * row_bytes + static_cast<int64_t>(bc) * kQ4KBytes;
-    nib[r] = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (2 * L.g + L.h));
+    nib[r] = load_group(blk, L);
     hdr[r] = *reinterpret_cast<const uint4*>(blk);
   }
 #pragma unroll
@@ -509,43 +510,37 @@ hipError_t launch_cfg(float* y, const uint8_t* w, const uint8_t* xq, int N, int 
 hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64_t K,
                        const IdArgs& id, hipStream_t stream) {
   const int nb = static_cast<int>(K / 256);
-  const int units = (nb + 7) / 8;
+  const int units = (nb + kUnitBlocks - 1) / kUnitBlocks;
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   const uint8_t* xb = static_cast<const uint8_t*>(xq);
   const int n = static_cast<int>(N);
   // Launch shapes chosen by measurement on MI355X (cold weights):
-  //  * rows of one or two units: every load of a row in flight at once,
-  //    two rows per wave when there are enough rows to fill the device
-  //    (14336x4096: 7.31 us against 7.63-8.90 for one row per wave or eight
-  //    and sixteen waves per workgroup);
-  //  * rows of five to seven units: the whole row in flight at once (clamped
+  //  * rows of one unit: one row per wave, four waves per workgroup, the
+  //    whole row in flight (14336x4096: 6.75-6.96 us against 7.03 with two
+  //    rows per wave and 7.40-7.77 with two waves per workgroup; 4096x4096:
+  //    3.41 us against 3.52 with eight waves per workgroup). The fused
+  //    q8_K tail keeps two rows per wave: half as many workgroups count
+  //    their arrival on each 256-row block (14336x4096 with its tail 8.87
+  //    us against 9.38 with one row per wave);
+  //  * rows of two to four units: the whole row in flight at once (clamped
   //    loads, static wait counts), eight waves per workgroup (the activation
-  //    row is staged half as often): 3-15% faster than two batches
-  //    (4096x14336: 7.83 us; four, twelve or sixteen waves 8.8-10.8);
-  //  * longer rows: batches of four units, eight waves per workgroup, loads
-  //    past the row skipped (a whole row of eight or more units in flight
-  //    is slower).
+  //    row is staged half as often) (4096x14336: 7.66-7.70 us against
+  //    8.00 in two batches and 8.6-9.9 with four, twelve or sixteen waves or
+  //    two rows per wave);
+  //  * longer rows: batches of two units, eight waves per workgroup, loads
+  //    past the row skipped.
   // Rows of the whole launch (all selected slots of a grouped launch) decide
-  // the rows per wave; a row's arithmetic is the same either way.
-  const int64_t rows_all = N * id.used;
+  // nothing here; a row's arithmetic is the same for every shape.
   if (units == 1) {
-    if (rows_all >= 8192) return launch_cfg<2, 1, 4, 2, true>(y, wb, xb, n, nb, id, stream);
+    if (id.yq) return launch_cfg<2, 1, 4, 2, true>(y, wb, xb, n, nb, id, stream);
     return launch_cfg<1, 1, 4, 2, true>(y, wb, xb, n, nb, id, stream);
   }
-  if (units == 2) {
-    if (rows_all >= 8192) return launch_cfg<2, 2, 4, 2, true>(y, wb, xb, n, nb, id, stream);
-    // 4096x4096: 3.75 us with eight waves per workgroup against 3.88 with
-    // four (the activation row staged half as often).
-    return launch_cfg<1, 2, 8, 2, true>(y, wb, xb, n, nb, id, stream);
-  }
-  if (units == 3) return launch_cfg<1, 3, 8, 2, true>(y, wb, xb, n, nb, id, stream);
+  if (units == 2) return launch_cfg<1, 2, 8, 2, true>(y, wb, xb, n, nb, id, stream);
+  if (units == 3) return launch_cfg<1, 3, 8, 3, true>(y, wb, xb, n, nb, id, stream);
   if (units == 4) return launch_cfg<1, 4, 8, 3, true>(y, wb, xb, n, nb, id, stream);
-  if (units == 5) return launch_cfg<1, 5, 8, 3, true>(y, wb, xb, n, nb, id, stream);
-  if (units == 6) return launch_cfg<1, 6, 8, 3, true>(y, wb, xb, n, nb, id, stream);
-  if (units == 7) return launch_cfg<1, 7, 8, 3, true>(y, wb, xb, n, nb, id, stream);
-  if (K <= kMaxStagedK) return launch_cfg<1, 4, 8, 3, false>(y, wb, xb, n, nb, id, stream);
+  if (K <= kMaxStagedK) return launch_cfg<1, 2, 8, 3, false>(y, wb, xb, n, nb, id, stream);
   // Rows too long to stage: the activation from global memory.
-  return launch_cfg<1, 4, 8, 3, false, true>(y, wb, xb, n, nb, id, stream);
+  return launch_cfg<1, 2, 8, 3, false, true>(y, wb, xb, n, nb, id, stream);
 }
 
 template <int TM, int R, int PF, int W, int NA, bool CLAMP>
@@ -564,30 +559,21 @@ template <int TM>
 hipError_t launch_multi_rows(float* y, const void* w, const void* xq, int64_t N, int64_t K,
                              int tokens, hipStream_t stream) {
   const int nb = static_cast<int>(K / 256);
-  const int units = (nb + 7) / 8;
+  const int units = (nb + kUnitBlocks - 1) / kUnitBlocks;
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   const uint8_t* xb = static_cast<const uint8_t*>(xq);
   const int n = static_cast<int>(N);
-  if (units == 1) {
-    if (N >= 8192) return launch_multi_cfg<TM, 2, 1, 4, 2, true>(y, wb, xb, n, nb, tokens, stream);
-    return launch_multi_cfg<TM, 1, 1, 4, 2, true>(y, wb, xb, n, nb, tokens, stream);
-  }
-  if (units == 2) {
-    if (N >= 8192) return launch_multi_cfg<TM, 2, 2, 4, 2, true>(y, wb, xb, n, nb, tokens, stream);
-    return launch_multi_cfg<TM, 1, 2, 4, 2, true>(y, wb, xb, n, nb, tokens, stream);
-  }
-  if (units == 3) return launch_multi_cfg<TM, 1, 3, 8, 2, true>(y, wb, xb, n, nb, tokens, stream);
+  if (units == 1) return launch_multi_cfg<TM, 1, 1, 4, 2, true>(y, wb, xb, n, nb, tokens, stream);
+  if (units == 2) return launch_multi_cfg<TM, 1, 2, 8, 2, true>(y, wb, xb, n, nb, tokens, stream);
+  if (units == 3) return launch_multi_cfg<TM, 1, 3, 8, 3, true>(y, wb, xb, n, nb, tokens, stream);
   if (units == 4) return launch_multi_cfg<TM, 1, 4, 8, 3, true>(y, wb, xb, n, nb, tokens, stream);
-  if (units == 5) return launch_multi_cfg<TM, 1, 5, 8, 3, true>(y, wb, xb, n, nb, tokens, stream);
-  if (units == 6) return launch_multi_cfg<TM, 1, 6, 8, 3, true>(y, wb, xb, n, nb, tokens, stream);
-  if (units == 7) return launch_multi_cfg<TM, 1, 7, 8, 3, true>(y, wb, xb, n, nb, tokens, stream);
-  return launch_multi_cfg<TM, 1, 4, 8, 3, false>(y, wb, xb, n, nb, tokens, stream);
+  return launch_multi_cfg<TM, 1, 2, 8, 3, false>(y, wb, xb, n, nb, tokens, stream);
 }
 
 template <int TM, int R>
 hipError_t launch_unit_split(float* y, const uint8_t* w, const uint8_t* xq, int N, int nb,
                              int tokens, hipStream_t stream) {
-  const int units = (nb + 7) / 8;
+  const int units = (nb + kUnitBlocks - 1) / kUnitBlocks;
   if (units < 1 || units > kSplitMaxUnits || tokens < 1 || tokens > TM)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemv_q4k_unit_split_kernel<TM, R>), dim3((N + R - 1) / R),
@@ -641,8 +627,8 @@ hipError_t launch_gemv_q4k_multi(float* y, const void* w, const void* xq, int64_
   const int nb = static_cast<int>(K / 256);
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   const uint8_t* xb = static_cast<const uint8_t*>(xq);
-  if (nb <= 16 && M <= 4) {
-    // Rows of one or two units: the persistent grid with the activation in
+  if (nb <= kUnitBlocks && M <= 4) {
+    // Rows of one unit: the persistent grid with the activation in
     // registers, one instantiation per token count (registers, and so
     // resident waves, grow with it). Measured on MI355X (cold weights),
     // against the kernel below: 14336x4096 at 2 and 3 tokens 8.7 and 10.2 us
@@ -650,24 +636,16 @@ hipError_t launch_gemv_q4k_multi(float* y, const void* w, const void* xq, int64_
     // against 4.4, 5.5, 6.1. (Four tokens on larger matrices take the MFMA
     // tile: 12.4 us there against 13.1 on this grid.)
     const int n = static_cast<int>(N);
-    if (nb <= 8) {
-      if (M <= 2) return launch_multi_res<2, 1>(y, wb, xb, n, nb, t, stream);
-      if (M == 3) return launch_multi_res<3, 1>(y, wb, xb, n, nb, t, stream);
-      return launch_multi_res<4, 1>(y, wb, xb, n, nb, t, stream);
-    }
-    if (M <= 2) return launch_multi_res<2, 2>(y, wb, xb, n, nb, t, stream);
-    if (M == 3) return launch_multi_res<3, 2>(y, wb, xb, n, nb, t, stream);
-    return launch_multi_res<4, 2>(y, wb, xb, n, nb, t, stream);
+    if (M <= 2) return launch_multi_res<2, 1>(y, wb, xb, n, nb, t, stream);
+    if (M == 3) return launch_multi_res<3, 1>(y, wb, xb, n, nb, t, stream);
+    return launch_multi_res<4, 1>(y, wb, xb, n, nb, t, stream);
   }
-  if (nb > 48 && nb <= 56 && M <= 3) {
-    // Rows of seven units: the units split across a workgroup's waves.
-    // Measured on MI355X (cold weights), 4096x14336 at 2 and 3 tokens:
-    // 10.1 and 11.8 us against 11.2 and 14.1 for the kernel below. At four
-    // and five units it measured slower (4096x8192, 6000x5120), and for one
-    // token the mat-vec stays ahead (8.9 against 8.0 us).
-    const int n = static_cast<int>(N);
-    if (M <= 2) return launch_unit_split<2, 8>(y, wb, xb, n, nb, t, stream);
-    return launch_unit_split<3, 4>(y, wb, xb, n, nb, t, stream);
+  if (nb > 48 && nb <= 56 && M == 3) {
+    // Three tokens on rows of 49 to 56 blocks (four units): the units split
+    // across a workgroup's waves, eight rows per workgroup (4096x14336: 12.3
+    // us against 12.6-15.2 with 4, 6, 12 or 16 rows and 14.1 for the kernel
+    // below). Two tokens run below (9.8-9.9 us against 10.3 split).
+    return launch_unit_split<3, 8>(y, wb, xb, static_cast<int>(N), nb, t, stream);
   }
   if (M <= 2) return launch_multi_rows<2>(y, w, xq, N, K, t, stream);
   if (M <= 4) return launch_multi_rows<4>(y, w, xq, N, K, t, stream);

@@ -133,9 +133,9 @@ def test_id_out_of_range_selection(fmt):
 ID_SHAPES = [
     # fmt, E, rows, K, ids: the other launch shapes of the dense kernels
     ("q4k", 4, 8192, 4096, [3, 1]),         # two rows per wave
-    ("q4k", 3, 300, 14336, [2, 0]),         # whole row in flight (7 units)
-    ("q4k", 3, 130, 20480, [1, 0]),         # loads past the row skipped (10 units)
-    ("q4k", 3, 257, 6144, [1, 2, 0]),       # three units
+    ("q4k", 3, 300, 14336, [2, 0]),         # whole row in flight (four units)
+    ("q4k", 3, 130, 20480, [1, 0]),         # loads past the row skipped (five units)
+    ("q4k", 3, 257, 6144, [1, 2, 0]),       # two units, the last half full
     ("iq4nl", 3, 20000, 512, [2, 0]),       # persistent grid, waves take a second row
     ("iq4nl", 3, 4096, 2048, [2, 0]),       # single-unit rows, the most a grouped staged launch takes
     ("iq4nl", 3, 4097, 2048, [0, 1]),       # one row more: the persistent grid
@@ -143,10 +143,10 @@ ID_SHAPES = [
     ("iq4nl", 2, 130, 8192, [1, 0, 1]),     # four units
     ("q4k", 3, 70, 53248, [2, 0]),          # rows past the staged limit
     ("iq4nl", 3, 70, 53248, [1, 2]),        # rows past the staged limit
-    ("q4k", 3, 1000, 4096, [2, 1]),         # two units, one row per wave (under 8192 rows in all)
-    ("q4k", 2, 200, 8192, [1, 0]),          # four units
-    ("q4k", 2, 100, 10240, [0, 1]),         # five units
-    ("q4k", 2, 100, 12288, [1, 0]),         # six units
+    ("q4k", 3, 1000, 4096, [2, 1]),         # one unit, one row per wave
+    ("q4k", 2, 200, 8192, [1, 0]),          # two units
+    ("q4k", 2, 100, 10240, [0, 1]),         # three units, the last half full
+    ("q4k", 2, 100, 12288, [1, 0]),         # three units
     ("iq4nl", 3, 3000, 4096, [2, 0]),       # persistent grid, two units
     ("iq4nl", 2, 500, 6144, [1, 0]),        # persistent grid, three units
     ("iq4nl", 2, 100, 12288, [0, 1]),       # staged kernel, six units

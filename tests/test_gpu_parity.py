@@ -212,16 +212,18 @@ Q4K_SHAPES = [
     ("n37_k768", 37, 768, 3002),
     ("n130_k2304", 130, 2304, 3003),
     ("n9000_k4352", 9000, 4352, 3004),
-    ("n8193_k2048_tworow", 8193, 2048, 3005),
-    ("n64_kmax", 64, 49152, 3006),
-    ("n300_k8192_four_units", 300, 8192, 3016),
-    ("n100_k7424_four_units_ragged", 100, 7424, 3017),  # 29 super-blocks: a last unit of five
-    ("n77_k10240_five_units", 77, 10240, 3007),
-    ("n300_k9472_five_units_ragged", 300, 9472, 3008),
-    ("n257_k12288_six_units", 257, 12288, 3009),
-    ("n33_k11264_six_units_ragged", 33, 11264, 3010),
-    ("n1000_k14080_seven_units_ragged", 1000, 14080, 3011),
-    ("n50_k16384_eight_units", 50, 16384, 3012),
+    ("n8193_k2048_ragged_rows", 8193, 2048, 3005),
+    ("n64_kmax", 64, 49152, 3006),                     # twelve units, batches of two
+    ("n300_k8192_two_units", 300, 8192, 3016),
+    ("n100_k7424_two_units_ragged", 100, 7424, 3017),  # 29 super-blocks: a last unit of 13
+    ("n77_k10240_three_units_ragged", 77, 10240, 3007),
+    ("n300_k9472_three_units_ragged", 300, 9472, 3008),
+    ("n257_k12288_three_units", 257, 12288, 3009),
+    ("n33_k11264_three_units_ragged", 33, 11264, 3010),
+    ("n1000_k14080_four_units_ragged", 1000, 14080, 3011),
+    ("n50_k16384_four_units", 50, 16384, 3012),
+    ("n90_k17408_five_units_ragged", 90, 17408, 3018),  # batches of two, loads past the row skipped
+    ("n45_k20736_six_units_ragged", 45, 20736, 3019),   # the last unit one block
     ("n64_k49408_unstaged", 64, 49408, 3013),          # one block past the staged limit
     ("n40_k53248_unstaged", 40, 53248, 3014),
     ("n3_k1048576_max", 3, 1048576, 3015),             # the largest K accepted
@@ -304,17 +306,17 @@ def test_ffn_pair_chain():
 # fused tail): y is xq_gemv_q4k's, bit for bit, and yq is what
 # xq_quantize_q8k writes for that y.
 GEMV_Q8K = [
-    ("up_14336x4096", 14336, 4096, wl.SEEDS["ffn_up"]),        # 8 rows per workgroup
-    ("down_4096x14336", 4096, 14336, wl.SEEDS["ffn_down"]),    # whole row in flight
-    ("n256_k1024", 256, 1024, 7601),                           # 4 rows per workgroup
+    ("up_14336x4096", 14336, 4096, wl.SEEDS["ffn_up"]),        # one unit, 8 rows per workgroup
+    ("down_4096x14336", 4096, 14336, wl.SEEDS["ffn_down"]),    # four units, whole row in flight
+    ("n256_k1024", 256, 1024, 7601),                           # one ragged unit
     ("n512_k20480", 512, 20480, 7602),                         # loads past the row skipped
     ("n1280_k2304", 1280, 2304, 7603),                         # ragged unit tail
-    ("n512_k7424", 512, 7424, 7605),                           # four units, the last ragged
+    ("n512_k7424", 512, 7424, 7605),                           # two units, the last ragged
     ("n512_k53248", 512, 53248, 7604),                         # activation from global memory
     ("n8192_k2048", 8192, 2048, 7606),                         # one unit, two rows per wave
-    ("n768_k6144", 768, 6144, 7607),                           # three units
-    ("n256_k10240", 256, 10240, 7608),                         # five units
-    ("n512_k12288", 512, 12288, 7609),                         # six units
+    ("n768_k6144", 768, 6144, 7607),                           # two units, the last half full
+    ("n256_k10240", 256, 10240, 7608),                         # three units
+    ("n512_k12288", 512, 12288, 7609),                         # three units
 ]
 
 
@@ -561,24 +563,24 @@ def test_gemm_whole_and_split_tiles(M, N, K, first_split_row):
 GEMM_SHORT = [
     (2, 14336, 4096, 7501),    # two rows per wave, clamped
     (3, 14336, 4096, 7502),    # the longest batch on this shape
-    (3, 4096, 14336, 7503),    # seven units, three tokens fill the LDS cap
+    (3, 4096, 14336, 7503),    # four units split across a workgroup's waves, three tokens
     (6, 4096, 4096, 7504),     # six tokens on a 2^24-weight matrix (the eight-token instance)
     (5, 300, 2304, 7505),      # ragged unit tail
-    (2, 130, 20480, 7506),     # ten units (two tokens fit): batches of four, loads past the row skipped
+    (2, 130, 20480, 7506),     # five units (two tokens fit): batches of two, loads past the row skipped
     (6, 8191, 2048, 7507),     # two rows per wave with an odd tail
     (4, 4096, 4096, 7508),     # persistent grid, activation in registers, four tokens
     (3, 3000, 1280, 7509),     # persistent grid, one ragged unit
-    (2, 20000, 3840, 7510),    # persistent grid, the second unit ragged, rows past one pass
+    (2, 20000, 3840, 7510),    # persistent grid, the unit ragged, rows past one pass
     (4, 100, 256, 7511),       # persistent grid smaller than a workgroup's waves allow
-    (2, 4096, 14336, 7512),    # seven units split across a workgroup's waves
-    (2, 1000, 7424, 7519),     # four units (the last ragged) on the LDS form
-    (4, 3000, 8192, 7541),     # four tokens, four units (a 2^25-weight matrix)
-    (6, 2000, 8192, 7542),     # six tokens fill the LDS at four units
-    (6, 2000, 6144, 7543),     # three units, the eight-token instance
-    (3, 2500, 10240, 7544),    # five units, the four-token instance
-    (2, 1500, 12288, 7545),    # six units, below the unit split's row lengths
-    (2, 1001, 12544, 7513),    # the same, the last unit one block, rows past a workgroup's eight
-    (3, 4099, 13312, 7514),    # three tokens, four rows per workgroup and a ragged row tail
+    (2, 4096, 14336, 7512),    # two tokens on four-unit rows: the LDS form
+    (2, 1000, 7424, 7519),     # two units (the last ragged) on the LDS form
+    (4, 3000, 8192, 7541),     # four tokens, two units (a 2^25-weight matrix)
+    (6, 2000, 8192, 7542),     # six tokens fill the LDS at two units
+    (6, 2000, 6144, 7543),     # two units, the last half full, the eight-token instance
+    (3, 2500, 10240, 7544),    # three units, the four-token instance
+    (2, 1500, 12288, 7545),    # three units, below the unit split's row lengths
+    (2, 1001, 12544, 7513),    # four units, the last one block, rows past a workgroup's eight
+    (3, 4099, 13312, 7514),    # three tokens split over four units, eight rows per workgroup, a ragged row tail
 ]
 
 

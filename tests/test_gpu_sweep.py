@@ -91,7 +91,7 @@ PRODUCT = _product_shapes()
 
 
 def _short_shapes():
-    # Two to four tokens on rows of one or two units (K <= 4096): the batched
+    # Two to four tokens on rows of one unit (K <= 4096): the batched
     # mat-vec on its persistent grid; every token's row must be the mat-vec's.
     g = wl.rng(8200)
     out = []
