@@ -57,10 +57,10 @@ BUILD_SCRIPT = os.path.join(ROOT, "quantized_decode_mat_amd", "build.py")
 # comes from (the summary is void once any of them changes).
 COUNTED = {
     "gemv_q4k_up_14336x4096": (
-        "void xq::(anonymous namespace)::gemv_q4k_kernel<2, 2, 4, 2, true, false, false, false>", 20,
+        "void xq::(anonymous namespace)::gemv_q4k_kernel<1, 1, 4, 2, true, false, false, false>", 20,
         33030144 + 5120 + 4 * 14336, ("gemv_q4k.hip", "q4k_row.h", "xq_device.h")),
     "gemv_q4k_down_4096x14336": (
-        "void xq::(anonymous namespace)::gemv_q4k_kernel<1, 7, 8, 3, true, false, false, false>", 20,
+        "void xq::(anonymous namespace)::gemv_q4k_kernel<1, 4, 8, 3, true, false, false, false>", 20,
         33030144 + 17920 + 4 * 4096, ("gemv_q4k.hip", "q4k_row.h", "xq_device.h")),
     "gemv_iq4nl_head_128256x4096": (
         "void xq::(anonymous namespace)::gemv_iq4nl_resident_kernel<2, false, 0>", 8,
