@@ -53,11 +53,12 @@
 // launches (the caller zeroes a workspace once, before its first use).
 //
 // Short batches (M = 1, or up to the LDS token cap while M <= 3, M = 4 on
-// matrices of at most 2^25 weights, M <= 6 on at most 2^24 or M <= 8 on at
-// most 2^23; see gemm_q4k_uses_matvec) skip the MFMA tile: they are a weight stream, and the
-// dot4 mat-vec reads the weights once for all M tokens
-// (launch_gemv_q4k_multi; each token's row is the mat-vec's bits). 4 to 16
-// tokens on tall matrices of 8 to 16 super-blocks per row use the
+// rows of at most 16 super-blocks or matrices of at most 2^25 weights, M <= 6
+// on at most 2^24 or M <= 8 on at most 2^23; see gemm_q4k_uses_matvec) skip
+// the MFMA tile: they are a weight stream, and the dot4 mat-vec reads the
+// weights once for all M tokens (launch_gemv_q4k_multi; each token's row is
+// the mat-vec's bits). 5 to 16 tokens on tall matrices of 8 to 16
+// super-blocks per row use the
 // wave-split tile (gemm_q4k_wave_split_kernel); other batches of up to 32
 // tokens (up to 128 on matrices with few weight tiles; see
 // gemm_q4k_token_tile) use the 16-token tile.
@@ -1134,8 +1135,12 @@ bool gemm_q4k_uses_matvec(int64_t M, int64_t N, int64_t K) {
   if (M > gemv_q4k_multi_max_tokens(K)) return false;
   const int64_t nk = N * K;
   if (M <= 3 || nk <= (int64_t{1} << 23)) return true;
-  if (M == 4)
-    return nk <= (int64_t{1} << 25) && !(wave_split_shape(N, K) && K / 256 >= 16);
+  // Four tokens on rows of one unit (K <= 4096) run on the batched mat-vec's
+  // persistent grid (14336x4096: 9.6 us against 11.0 on the wave-split
+  // tile; 12288x4096 8.9 against 10.7; 16384x4096 10.9 against 11.4;
+  // 8192x4096 6.8 against 7.1); five or more lose there (5, 6, 8 x
+  // 14336x4096: 17.0, 19.7, 25.7 us against 11.1, 11.4, 11.6).
+  if (M == 4) return K <= 4096 || nk <= (int64_t{1} << 25);
   return M <= 6 && nk <= (int64_t{1} << 24);
 }
 

@@ -640,7 +640,7 @@ def test_gemm_token_tile_16(M, N, K, seed):
 # Short batches on tall matrices: the wave-split tile (four waves split K,
 # their partial tiles summed in LDS; no workspace).
 GEMM_WAVE_SPLIT = [
-    (4, 14336, 4096, 7551),    # 448 workgroups, four super-blocks per wave
+    (6, 14336, 4096, 7551),    # 448 workgroups, four super-blocks per wave
     (16, 14336, 4096, 7552),   # a full token tile
     (7, 8192, 4096, 7553),     # one workgroup per CU
     (16, 8200, 2304, 7554),    # a last row tile of 8 rows; 9 super-blocks (2, 2, 2, 3 per wave)
@@ -678,14 +678,17 @@ def test_gemm_wave_split(M, N, K, seed):
 
 
 # Both sides of every dispatch boundary of the small-M product: the batched
-# mat-vec against the MFMA tiles (3|4 tokens on a large matrix, 4|5 on 2^25
-# weights, 6|7 on 2^24, 8|9 on 2^23, and 4 tokens on the wave-split tile's
-# shapes: 16 and 8 super-blocks), the wave-split tile against the 16-token
+# mat-vec against the MFMA tiles (4|5 tokens on rows of one unit, 16 and 8
+# super-blocks, where five take the wave-split tile; 3|4 on a large matrix of
+# longer rows, 4|5 on 2^25 weights, 6|7 on 2^24, 8|9 on 2^23), the wave-split tile against the 16-token
 # tile (16|17 tokens), the 16-token tile against the 64-token tile (32|33 on a
 # large matrix, 64|65 on 4096 rows of a long K, 96|97 on 2^25 weights, 128|129
 # on 2^24).
 GEMM_BOUNDARY = [
     (4, 14336, 4096, 7531),
+    (5, 14336, 4096, 7559),
+    (5, 11008, 2048, 7560),
+    (4, 4096, 14336, 7561),
     (4, 4096, 8192, 7538),
     (5, 4096, 8192, 7539),
     (6, 4096, 4096, 7540),

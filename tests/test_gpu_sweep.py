@@ -64,8 +64,8 @@ def _product_shapes():
     out = []
     # (token range, rows range, K choices): short batches, the 16-token tile,
     # the 64-token tile with split K, grids past one round of workgroups, and
-    # the wave-split tile's range (4-16 tokens, 256-512 row tiles of 32, 8-16
-    # super-blocks).
+    # the wave-split tile's range (5-16 tokens, 256-512 row tiles of 32, 8-16
+    # super-blocks; four tokens there take the batched mat-vec).
     regimes = [
         ((2, 4), (1000, 16000), (2048, 4096, 14336)),
         ((4, 33), (100, 16000), (1024, 4096, 7936)),
@@ -73,7 +73,7 @@ def _product_shapes():
         ((129, 320), (4000, 9000), (2048, 4096)),
         ((320, 700), (7000, 15000), (2048, 4096, 8192)),
         ((129, 200), (100, 2000), (4096, 14336)),      # the 64-token tile on few tiles, split K
-        ((4, 17), (8161, 16385), tuple(256 * u for u in range(8, 17))),  # the wave-split tile
+        ((5, 17), (8161, 16385), tuple(256 * u for u in range(8, 17))),  # the wave-split tile
     ]
     for (m_lo, m_hi), (n_lo, n_hi), ks in regimes:
         for _ in range(3):
