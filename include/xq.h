@@ -158,14 +158,13 @@ xq_status xq_gemv_iq4nl(float *y, const void *w, const void *xq, int64_t N, int6
  *  xq  device, in: q8_K [M][K/256], 16-byte aligned.
  *  1 <= M <= 2^30.  1 <= N <= 2^30.  K >= 256, a multiple of 256. Each of
  *  xq and w below 2 GiB (the kernel's loads use 32-bit offsets).
- * A very short batch (M = 1; M <= 3; M = 4 when N*K <= 2^25, M <= 6 when
- * N*K <= 2^24, M <= 8 when N*K <= 2^23, in each while the M q8_K rows fit
- * 64 KB) is a weight stream
+ * A very short batch (M = 1; M <= 3; M = 4 when K <= 4096 or N*K <= 2^25,
+ * M <= 6 when N*K <= 2^24, M <= 8 when N*K <= 2^23, in each while the M q8_K
+ * rows fit 64 KB) is a weight stream
  * rather than a dense contraction: it runs on the mat-vec kernels, one pass
  * over the weights for all M tokens, and row m is then bit-identical to
- * xq_gemv_q4k on token m. Larger M runs on int8 MFMA: 4 to 16 tokens on
- * matrices of 8161 to 16384 rows and 8 to 16 super-blocks per row (but 4
- * tokens of 8 to 15 super-blocks within N*K <= 2^25 stay on the mat-vec) in
+ * xq_gemv_q4k on token m. Larger M runs on int8 MFMA: 5 to 16 tokens on
+ * matrices of 8161 to 16384 rows and 8 to 16 super-blocks per row in
  * tiles of 32 rows whose four waves split K and sum their partial tiles in
  * a fixed order (no workspace); otherwise in tiles of 16 tokens up to M = 32
  * (64 when N*K <= 2^25 or N <= 4096, 96 when N*K <= 2^25, 128 when
