@@ -159,8 +159,8 @@ xq_status xq_gemv_iq4nl(float *y, const void *w, const void *xq, int64_t N, int6
  *  1 <= M <= 2^30.  1 <= N <= 2^30.  K >= 256, a multiple of 256. Each of
  *  xq and w below 2 GiB (the kernel's loads use 32-bit offsets).
  * A very short batch (M = 1; M <= 3; M = 4 when K <= 4096 or N*K <= 2^25,
- * M <= 6 when N*K <= 2^24, M <= 8 when N*K <= 2^23, in each while the M q8_K
- * rows fit 64 KB) is a weight stream
+ * M <= 6 when N*K <= 2^24, M <= 8 when N*K <= 2^23 or when K <= 4096 and
+ * N*K <= 2^24, in each while the M q8_K rows fit 64 KB) is a weight stream
  * rather than a dense contraction: it runs on the mat-vec kernels, one pass
  * over the weights for all M tokens, and row m is then bit-identical to
  * xq_gemv_q4k on token m. Larger M runs on int8 MFMA: 5 to 16 tokens on

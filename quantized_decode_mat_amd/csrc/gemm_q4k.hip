@@ -54,7 +54,8 @@
 //
 // Short batches (M = 1, or up to the LDS token cap while M <= 3, M = 4 on
 // rows of at most 16 super-blocks or matrices of at most 2^25 weights, M <= 6
-// on at most 2^24 or M <= 8 on at most 2^23; see gemm_q4k_uses_matvec) skip
+// on at most 2^24, M <= 8 on at most 2^23 or on rows of at most 16
+// super-blocks of at most 2^24 weights; see gemm_q4k_uses_matvec) skip
 // the MFMA tile: they are a weight stream, and the dot4 mat-vec reads the
 // weights once for all M tokens (launch_gemv_q4k_multi; each token's row is
 // the mat-vec's bits). 5 to 16 tokens on tall matrices of 8 to 16
@@ -1135,6 +1136,11 @@ bool gemm_q4k_uses_matvec(int64_t M, int64_t N, int64_t K) {
   if (M > gemv_q4k_multi_max_tokens(K)) return false;
   const int64_t nk = N * K;
   if (M <= 3 || nk <= (int64_t{1} << 23)) return true;
+  // Up to eight tokens on rows of one unit of at most 2^24 weights: the
+  // batched mat-vec's persistent grid (4096x4096 at 6 and 8 tokens: 6.5 and
+  // 7.4 us against 7.6 and 8.6; on 8192x4096 and 14336x4096 it loses from
+  // five tokens on: 8.9 against 7.3 us, 13.4 against 11.2).
+  if (M <= 8 && K <= 4096 && nk <= (int64_t{1} << 24)) return true;
   // Four tokens on rows of one unit (K <= 4096) run on the batched mat-vec's
   // persistent grid (14336x4096: 9.6 us against 11.0 on the wave-split
   // tile; 12288x4096 8.9 against 10.7; 16384x4096 10.9 against 11.4;

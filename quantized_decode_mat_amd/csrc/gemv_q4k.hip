@@ -597,7 +597,7 @@ hipError_t launch_multi_res(float* y, const uint8_t* w, const uint8_t* xq, int N
   int cap = resident[dev].load(std::memory_order_relaxed);
   if (cap == 0) {
     int per_cu = 0, cus = 0;
-    // The largest staging a call can ask for: four tokens of 16 blocks.
+    // The largest staging a call can ask for: TM tokens of 16 blocks.
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
         &per_cu, reinterpret_cast<const void*>(&gemv_q4k_multi_res_kernel<TM, U>), kMresThreads,
         static_cast<size_t>(TM) * 16 * kQ8KBytes);
@@ -627,18 +627,20 @@ hipError_t launch_gemv_q4k_multi(float* y, const void* w, const void* xq, int64_
   const int nb = static_cast<int>(K / 256);
   const uint8_t* wb = static_cast<const uint8_t*>(w);
   const uint8_t* xb = static_cast<const uint8_t*>(xq);
-  if (nb <= kUnitBlocks && M <= 4) {
+  if (nb <= kUnitBlocks) {
     // Rows of one unit: the persistent grid with the activation in
     // registers, one instantiation per token count (registers, and so
     // resident waves, grow with it). Measured on MI355X (cold weights),
     // against the kernel below: 14336x4096 at 2 and 3 tokens 8.7 and 10.2 us
     // against 9.9 and 12.2; 4096x4096 at 2, 3, 4 tokens 4.2, 4.6, 5.3 us
-    // against 4.4, 5.5, 6.1. (Four tokens on larger matrices take the MFMA
-    // tile: 12.4 us there against 13.1 on this grid.)
+    // against 4.4, 5.5, 6.1 (first layout); 4096x4096 at 6 tokens 6.5 us
+    // against 7.6.
     const int n = static_cast<int>(N);
     if (M <= 2) return launch_multi_res<2, 1>(y, wb, xb, n, nb, t, stream);
     if (M == 3) return launch_multi_res<3, 1>(y, wb, xb, n, nb, t, stream);
-    return launch_multi_res<4, 1>(y, wb, xb, n, nb, t, stream);
+    if (M == 4) return launch_multi_res<4, 1>(y, wb, xb, n, nb, t, stream);
+    if (M <= 6) return launch_multi_res<6, 1>(y, wb, xb, n, nb, t, stream);
+    return launch_multi_res<8, 1>(y, wb, xb, n, nb, t, stream);
   }
   if (nb > 48 && nb <= 56 && M == 3) {
     // Three tokens on rows of 49 to 56 blocks (four units): the units split

@@ -50,7 +50,8 @@ def test_workspace_sizes():
     assert ws(3, 14336, 4096) == 0                 # the batched mat-vec
     assert ws(512, 14336, 4096) == 0               # whole tiles only
     assert ws(16, 14336, 4096) == 0                # the wave-split tile (no hand-off)
-    assert ws(4, 8192, 4096) == 0 and ws(7, 4096, 4096) > 0
+    assert ws(4, 8192, 4096) == 0 and ws(7, 4096, 4096) == 0  # the batched mat-vec
+    assert ws(9, 4096, 4096) > 0 and ws(7, 2048, 8192) > 0     # split MFMA tiles
     # 4 tokens x 14336 rows x 32 blocks: 112 tiles of 16 x 128, 4 splits each
     assert ws(4, 14336, 8192) == 768 * 128 + 112 * 4 * 8192
     # 16 tokens x 4096 rows x 56 blocks: 32 tiles of 16 x 128, 8 splits each

@@ -581,6 +581,9 @@ GEMM_SHORT = [
     (2, 1500, 12288, 7545),    # three units, below the unit split's row lengths
     (2, 1001, 12544, 7513),    # four units, the last one block, rows past a workgroup's eight
     (3, 4099, 13312, 7514),    # three tokens split over four units, eight rows per workgroup, a ragged row tail
+    (8, 4096, 4096, 7562),     # eight tokens on the persistent grid
+    (7, 3000, 1280, 7563),     # seven tokens (the eight-token instance), one ragged unit
+    (5, 2048, 4096, 7565),     # five tokens (the six-token instance)
 ]
 
 
@@ -679,8 +682,9 @@ def test_gemm_wave_split(M, N, K, seed):
 
 # Both sides of every dispatch boundary of the small-M product: the batched
 # mat-vec against the MFMA tiles (4|5 tokens on rows of one unit, 16 and 8
-# super-blocks, where five take the wave-split tile; 3|4 on a large matrix of
-# longer rows, 4|5 on 2^25 weights, 6|7 on 2^24, 8|9 on 2^23), the wave-split tile against the 16-token
+# super-blocks, where five take the wave-split tile, and 8|9 on such rows of
+# 2^24 weights; 3|4 on a large matrix of longer rows, 4|5 on 2^25 weights,
+# 6|7 on 2^24, 8|9 on 2^23), the wave-split tile against the 16-token
 # tile (16|17 tokens), the 16-token tile against the 64-token tile (32|33 on a
 # large matrix, 64|65 on 4096 rows of a long K, 96|97 on 2^25 weights, 128|129
 # on 2^24).
@@ -693,6 +697,9 @@ GEMM_BOUNDARY = [
     (5, 4096, 8192, 7539),
     (6, 4096, 4096, 7540),
     (7, 4096, 4096, 7532),
+    (9, 4096, 4096, 7564),
+    (6, 2048, 8192, 7566),
+    (7, 2048, 8192, 7567),
     (4, 8192, 4096, 7546),
     (4, 11008, 2048, 7547),
     (17, 14336, 4096, 7548),
