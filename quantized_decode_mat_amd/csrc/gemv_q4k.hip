@@ -319,7 +319,7 @@ __global__ __launch_bounds__(W * kWave) void gemv_q4k_multi_kernel(float* __rest
   }
 }
 
-// A short batch of up to four tokens on rows of one unit, as a
+// A short batch of up to eight tokens on rows of one unit, as a
 // persistent grid: each lane copies its slice of every token's q8_K row
 // (codes, sub-block sums and scale of its block in each unit) from the
 // workgroup's LDS copy into registers once, then the wave walks rows with a
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(kMresThreads) void gemv_q4k_multi_res_kernel(
   }
 }
 
-// Two or three tokens on rows of four units (K in 12544..14336), a row's
+// Three tokens on rows of four units (K in 12544..14336), a row's
 // units split across the waves of a workgroup: wave u takes unit u of R
 // consecutive rows. Each lane reads its slice of every token's q8_K block of
 // that unit from global memory into registers once (no LDS staging of the
@@ -529,8 +529,8 @@ hipError_t launch_rows(float* y, const void* w, const void* xq, int64_t N, int64
   //    two rows per wave);
   //  * longer rows: batches of two units, eight waves per workgroup, loads
   //    past the row skipped.
-  // Rows of the whole launch (all selected slots of a grouped launch) decide
-  // nothing here; a row's arithmetic is the same for every shape.
+  // A grouped launch takes the dense shape for its rows; a row's arithmetic
+  // is the same for every shape.
   if (units == 1) {
     if (id.yq) return launch_cfg<2, 1, 4, 2, true>(y, wb, xb, n, nb, id, stream);
     return launch_cfg<1, 1, 4, 2, true>(y, wb, xb, n, nb, id, stream);
